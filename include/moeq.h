@@ -1,0 +1,170 @@
+/*
+ * moeq: the quantized Mixture-of-Experts expert forward at decode, for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The path (per layer, per token):
+ *   router logits over E experts -> top-K -> softmax of the K selected
+ *   -> for each selected expert and the shared expert: group-wise affine
+ *      4-bit or 2-bit dequantised mat-vec for gate and up -> SwiGLU ->
+ *      dequantised down mat-vec -> weighted combine with the shared expert
+ *      and the residual.
+ * Sources: Flash-MoE (fr.news.hada.io), sections "Architecture du modèle"
+ * (512 experts, K=4 active including one shared, hidden 4096, 60 layers),
+ * "Noyau de déquantification optimisé FMA" (weight = value*scale + bias),
+ * "Shaders de calcul Metal" (4-bit/2-bit dequant mat-vec, SwiGLU, MoE
+ * combine + residual + gate), "Deferred GPU Expert Compute" (combine, norm
+ * and residual stay on the GPU and feed the next layer); openclawradar.com/fr
+ * (top-10 routing over 512 experts; experts kept in a bounded set of
+ * resident slots and loaded on router demand).
+ *
+ * Conventions (all entry points):
+ *   - Every call returns MOEQ_OK (0) or a negative MOEQ_E_* code and then
+ *     sets a thread-local message readable with moeq_last_error().
+ *     Unsupported inputs are refused with MOEQ_E_UNSUPPORTED, never
+ *     silently ignored.
+ *   - Pointers marked "device" are HIP device pointers owned by the caller
+ *     and must stay valid until the work queued on `stream` completes.
+ *     `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *   - Calls validate their arguments on the host, enqueue kernels on
+ *     `stream` and return without synchronising; no entry point allocates
+ *     device memory except moe_pool_create (host metadata + events).
+ *   - `workspace` is caller-owned device memory of moeq_workspace_bytes()
+ *     bytes, zero-filled once after allocation; the kernels leave it ready
+ *     for the next call.  Calls sharing one workspace must not overlap.
+ *   - Results are bit-reproducible run to run: no floating-point atomics.
+ *
+ * Expert blob layout (one contiguous blob per expert, 256-byte aligned):
+ *   [gate.q | up.q | down.q | gate.sb | up.sb | down.sb]
+ *   gate.q, up.q: inter rows x hidden values; down.q: hidden rows x inter
+ *   values; each row packs 32/bits unsigned values per little-endian u32,
+ *   value j at bit bits*(j mod (32/bits)) of word j/(32/bits).
+ *   *.sb: one u32 per (row, group of 64 consecutive inputs): bf16 scale in
+ *   the low 16 bits, bf16 bias in the high 16 bits.  w = value*scale + bias.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOEQ_OK = 0,
+  MOEQ_E_INVALID = -1,        /* bad argument (null pointer, negative size, ...) */
+  MOEQ_E_UNSUPPORTED = -2,    /* valid but outside what the kernels implement */
+  MOEQ_E_HIP = -3,            /* a HIP runtime call failed */
+  MOEQ_E_POOL_EXHAUSTED = -4, /* every pool slot is pinned by the current layer */
+  MOEQ_E_DEVICE = -5          /* a kernel flagged bad data (see moe_read_device_status) */
+};
+
+enum { MOEQ_BF16 = 0, MOEQ_F32 = 1 };   /* activation dtypes */
+
+enum {
+  /* Weights = full softmax over all E logits read at the selected experts
+   * (default: softmax over the K selected logits). */
+  MOEQ_F_NO_RENORM = 1u,
+  /* The layer input is normalised as x / sqrt(mean(x^2) + 1e-6) (unit-weight
+   * RMS norm) before the router and the experts; the residual stays x. */
+  MOEQ_F_RMSNORM = 2u
+};
+
+/* Limits of the current kernels (larger values return MOEQ_E_UNSUPPORTED). */
+#define MOEQ_MAX_HIDDEN 8192
+#define MOEQ_MAX_INTER 8192
+#define MOEQ_MAX_EXPERTS 4096
+#define MOEQ_MAX_TOPK 16
+#define MOEQ_MAX_DECODE_TOKENS 64
+
+typedef struct moeq_shape {
+  int32_t hidden;     /* H, multiple of 64 */
+  int32_t inter;      /* I, multiple of 64 */
+  int32_t n_experts;  /* E routed experts per layer */
+  int32_t n_shared;   /* S always-active experts per layer, 0 or 1 */
+  int32_t bits;       /* 4 or 2 */
+  int32_t group;      /* 64 */
+} moeq_shape;
+
+/* Where the expert blobs of each layer live.  `blobs` is a device array of
+ * n_layers * (n_experts + n_shared) device pointers, row-major by layer;
+ * shared experts follow the routed ones.  Only the entries of experts that
+ * a call actually reads need to be valid. */
+typedef struct moeq_experts {
+  const void* const* blobs;
+  int32_t n_layers;
+} moeq_experts;
+
+/* Bytes of one expert blob: 3 * (H*I*bits/8 + H*I/64*4).  7,077,888 for
+ * H=4096, I=1024, 4-bit (6.75 MiB, the per-expert size given in Flash-MoE,
+ * "SSD Expert Streaming"); 3,932,160 at 2-bit.  Returns -1 for a bad shape. */
+int64_t moeq_expert_bytes(const moeq_shape* shape);
+
+/* Workspace bytes needed by the calls below for T tokens and top-k. */
+int moeq_workspace_bytes(const moeq_shape* shape, int T, int k, int64_t* bytes);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moeq_last_error(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+int moeq_abi_version(void);
+
+/* Router and top-K (Flash-MoE, "Architecture du modèle": K of 512 experts
+ * active per token; openclawradar.com/fr: top-10 routing).
+ *   x             device [T][H] in x_dtype (MOEQ_BF16 or MOEQ_F32)
+ *   w_router      device [E][H] bf16 router matrix, row-major
+ *   shared_gate   device [H] bf16 or NULL: if given, the shared expert's
+ *                 weight is sigmoid(shared_gate . xhat), else 1
+ *   flags         MOEQ_F_RMSNORM, MOEQ_F_NO_RENORM
+ *   topk_idx      device [T][k] int32 out: experts by logit descending,
+ *                 ties to the lower index
+ *   topk_w        device [T][k] f32 out: softmax weights of the selection
+ *   shared_w      device [T] f32 out (may be NULL when n_shared == 0)
+ *   logits        device [T][E] f64 out, or NULL
+ * Logits accumulate in fp64 (bf16 x bf16/fp32 products are exact there),
+ * so the selection equals an fp64 evaluation except at gaps near 1e-15.
+ * T == 0 is a no-op.  1 <= k <= min(E, 16); T <= 64. */
+int moe_router_topk(const moeq_shape* shape, const void* x, int x_dtype, uint32_t flags,
+                    const uint16_t* w_router, const uint16_t* shared_gate, int T, int k,
+                    int32_t* topk_idx, float* topk_w, float* shared_w, double* logits,
+                    void* workspace, void* stream);
+
+/* Gate and up projections of every selected expert and the shared expert
+ * (Flash-MoE, "Noyau de déquantification optimisé FMA" and "Shaders de
+ * calcul Metal": dequantised 4-bit / 2-bit mat-vec).  Each expert's rows
+ * are streamed once per call and applied to every token routed to it.
+ *   x         device [T][H] in x_dtype; with MOEQ_F_RMSNORM normalised first
+ *   topk_idx  device [T][k] int32 (ids outside [0, E) are skipped, their
+ *             outputs left unwritten, and the workspace status word is set)
+ *   gate_up   device [T][k + S][2][I] f32 out: slot s < k is the s-th
+ *             selected expert, slot k the shared expert; [.][0] = gate,
+ *             [.][1] = up
+ * Bits 2 and 4 are both handled (the name keeps the 4-bit case). */
+int moe_q4_expert_gemv(const moeq_shape* shape, const moeq_experts* experts, int layer,
+                       const void* x, int x_dtype, uint32_t flags, const int32_t* topk_idx,
+                       int T, int k, void* workspace, float* gate_up, void* stream);
+
+/* SwiGLU, down projection and combine (Flash-MoE, "Shaders de calcul
+ * Metal": SwiGLU and MoE combine + residual + gate; "Deferred GPU Expert
+ * Compute"):
+ *   out[t] = residual[t] + sum_s topk_w[t][s] * d_s + shared_w[t] * d_shared
+ *   d_s = Wd_s (silu(g_s) * u_s), summed in slot order.
+ *   gate_up   device [T][k + S][2][I] f32 (from moe_q4_expert_gemv)
+ *   shared_w  device [T] f32 or NULL (= 1)
+ *   residual  device [T][H] in res_dtype
+ *   out       device [T][H] f32 (may alias residual when res_dtype is f32) */
+int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts, int layer,
+                            const float* gate_up, const int32_t* topk_idx, const float* topk_w,
+                            const float* shared_w, const void* residual, int res_dtype,
+                            int T, int k, void* workspace, float* out, void* stream);
+
+/* Synchronise `stream` and read the workspace status word: 0 = clean,
+ * else a bitmask (1 = an expert id outside [0, E) was seen).  Clears it. */
+int moe_read_device_status(void* workspace, void* stream, int32_t* status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

@@ -1,0 +1,17 @@
+"""quantized_expert_gemv_router_amd: the quantized MoE expert forward at
+decode on AMD MI355X (gfx950).
+
+This package is a thin ctypes binding over libmoeq.so (HIP kernels + C ABI,
+declared in include/moeq.h).  The functions keep the C names and only
+marshal arguments: torch tensors provide device memory and the current HIP
+stream; every step of the path runs in the library's kernels.  If the
+library has not been built the import of the binding functions fails
+loudly; there is no CPU fallback.
+"""
+from ._binding import (  # noqa: F401
+    BF16, F32, F_NO_RENORM, F_RMSNORM,
+    MoeqError, Shape, ExpertTable, lib, library_path,
+    moeq_abi_version, moeq_expert_bytes, moeq_workspace_bytes, moeq_last_error,
+    moe_router_topk, moe_q4_expert_gemv, moe_swiglu_down_combine, moe_read_device_status,
+    new_workspace, moe_layer,
+)

@@ -1,0 +1,229 @@
+"""ctypes marshalling for libmoeq.so.  No arithmetic of the path lives here."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_PKG, "libmoeq.so")
+
+BF16, F32 = 0, 1
+F_NO_RENORM, F_RMSNORM = 1, 2
+
+OK, E_INVALID, E_UNSUPPORTED, E_HIP, E_POOL_EXHAUSTED, E_DEVICE = 0, -1, -2, -3, -4, -5
+_CODE_NAMES = {E_INVALID: "MOEQ_E_INVALID", E_UNSUPPORTED: "MOEQ_E_UNSUPPORTED", E_HIP: "MOEQ_E_HIP",
+               E_POOL_EXHAUSTED: "MOEQ_E_POOL_EXHAUSTED", E_DEVICE: "MOEQ_E_DEVICE"}
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODE_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, cfg) -> "Shape":
+        return cls(cfg.hidden, cfg.inter, cfg.n_experts, cfg.n_shared, cfg.bits, cfg.group)
+
+    @property
+    def n_slots(self) -> int:
+        return self.n_experts + self.n_shared
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("blobs", ctypes.c_void_p), ("n_layers", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_lib = None
+
+
+def library_path() -> str:
+    return _SO
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoeq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            raise ImportError(f"{_SO} is missing: build it with "
+                              "`python -m quantized_expert_gemv_router_amd.build`")
+        L = ctypes.CDLL(_SO)
+        S = ctypes.POINTER(Shape)
+        X = ctypes.POINTER(_Experts)
+        L.moeq_abi_version.restype = _I
+        L.moeq_last_error.restype = ctypes.c_char_p
+        L.moeq_expert_bytes.restype = ctypes.c_int64
+        L.moeq_expert_bytes.argtypes = [S]
+        L.moeq_workspace_bytes.argtypes = [S, _I, _I, ctypes.POINTER(ctypes.c_int64)]
+        L.moe_router_topk.argtypes = [S, _P, _I, ctypes.c_uint32, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
+        L.moe_q4_expert_gemv.argtypes = [S, X, _I, _P, _I, ctypes.c_uint32, _P, _I, _I, _P, _P, _P]
+        L.moe_swiglu_down_combine.argtypes = [S, X, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P]
+        L.moe_read_device_status.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MoeqError(rc, lib().moeq_last_error().decode())
+
+
+def moeq_abi_version() -> int:
+    return lib().moeq_abi_version()
+
+
+def moeq_last_error() -> str:
+    return lib().moeq_last_error().decode()
+
+
+def moeq_expert_bytes(shape: Shape) -> int:
+    return lib().moeq_expert_bytes(ctypes.byref(shape))
+
+
+def moeq_workspace_bytes(shape: Shape, T: int, k: int) -> int:
+    out = ctypes.c_int64()
+    _check(lib().moeq_workspace_bytes(ctypes.byref(shape), T, k, ctypes.byref(out)))
+    return out.value
+
+
+def new_workspace(shape: Shape, T: int, k: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace of moeq_workspace_bytes(shape, T, k) bytes."""
+    return torch.zeros(moeq_workspace_bytes(shape, T, k), dtype=torch.uint8, device=device)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoeq must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported activation dtype {t.dtype}")
+
+
+class ExpertTable:
+    """Device table of expert blob pointers, [n_layers][n_experts + n_shared]
+    (the `moeq_experts` view).  Built from per-layer uint8 arenas whose slot
+    e holds expert e's blob at byte offset e * stride."""
+
+    def __init__(self, shape: Shape, arenas: list, stride: int, device="cuda"):
+        ptrs = []
+        for arena in arenas:
+            base = arena.data_ptr()
+            ptrs.extend(base + e * stride for e in range(shape.n_slots))
+        self.table = torch.tensor(ptrs, dtype=torch.int64, device=device)
+        self.arenas = arenas
+        self.n_layers = len(arenas)
+        self._view = _Experts(self.table.data_ptr(), self.n_layers)
+
+    @classmethod
+    def from_pointers(cls, ptr_table: torch.Tensor, n_layers: int):
+        self = cls.__new__(cls)
+        self.table = ptr_table
+        self.arenas = []
+        self.n_layers = n_layers
+        self._view = _Experts(ptr_table.data_ptr(), n_layers)
+        return self
+
+    def view(self):
+        return ctypes.byref(self._view)
+
+
+def moe_router_topk(shape: Shape, x: torch.Tensor, w_router: torch.Tensor, k: int, flags: int = 0,
+                    shared_gate: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    want_logits: bool = False, out=None, stream=None):
+    """Returns (topk_idx int32 [T,k], topk_w f32 [T,k], shared_w f32 [T], logits f64 [T,E] | None)."""
+    T = x.shape[0]
+    dev = x.device
+    if workspace is None:
+        workspace = new_workspace(shape, T, k, dev)
+    if out is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        sw = torch.empty((T,), dtype=torch.float32, device=dev)
+    else:
+        idx, w, sw = out
+    logits = torch.empty((T, shape.n_experts), dtype=torch.float64, device=dev) if want_logits else None
+    _check(lib().moe_router_topk(ctypes.byref(shape), _ptr(x), _dtype_code(x), flags, _ptr(w_router),
+                                 _ptr(shared_gate), T, k, _ptr(idx), _ptr(w),
+                                 _ptr(sw) if shape.n_shared else None, _ptr(logits),
+                                 _ptr(workspace), _stream(stream)))
+    return idx, w, sw, logits
+
+
+def moe_q4_expert_gemv(shape: Shape, experts: ExpertTable, layer: int, x: torch.Tensor,
+                       topk_idx: torch.Tensor, k: int, flags: int = 0,
+                       workspace: torch.Tensor | None = None, gate_up: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """gate_up f32 [T, k + S, 2, I] (slot k = shared expert)."""
+    T = x.shape[0]
+    if workspace is None:
+        workspace = new_workspace(shape, T, k, x.device)
+    if gate_up is None:
+        gate_up = torch.empty((T, k + shape.n_shared, 2, shape.inter), dtype=torch.float32,
+                              device=x.device)
+    _check(lib().moe_q4_expert_gemv(ctypes.byref(shape), experts.view(), layer, _ptr(x),
+                                    _dtype_code(x), flags, _ptr(topk_idx), T, k, _ptr(workspace),
+                                    _ptr(gate_up), _stream(stream)))
+    return gate_up
+
+
+def moe_swiglu_down_combine(shape: Shape, experts: ExpertTable, layer: int, gate_up: torch.Tensor,
+                            topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                            shared_w: torch.Tensor | None, residual: torch.Tensor, k: int,
+                            workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """out f32 [T, H] = residual + sum_k w_k d_k + shared_w * d_shared."""
+    T = residual.shape[0]
+    if workspace is None:
+        workspace = new_workspace(shape, T, k, residual.device)
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.float32, device=residual.device)
+    _check(lib().moe_swiglu_down_combine(ctypes.byref(shape), experts.view(), layer, _ptr(gate_up),
+                                         _ptr(topk_idx), _ptr(topk_w), _ptr(shared_w),
+                                         _ptr(residual), _dtype_code(residual), T, k,
+                                         _ptr(workspace), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_read_device_status(workspace: torch.Tensor, stream=None) -> int:
+    st = ctypes.c_int32()
+    _check(lib().moe_read_device_status(_ptr(workspace), _stream(stream), ctypes.byref(st)))
+    return st.value
+
+
+def moe_layer(shape: Shape, experts: ExpertTable, layer: int, x: torch.Tensor,
+              w_router: torch.Tensor, k: int, flags: int = 0, shared_gate=None, workspace=None,
+              stream=None) -> dict:
+    """The three calls of one decode layer, in order, on one stream."""
+    T = x.shape[0]
+    if workspace is None:
+        workspace = new_workspace(shape, T, k, x.device)
+    idx, w, sw, logits = moe_router_topk(shape, x, w_router, k, flags, shared_gate, workspace,
+                                         want_logits=True, stream=stream)
+    gu = moe_q4_expert_gemv(shape, experts, layer, x, idx, k, flags, workspace, stream=stream)
+    out = moe_swiglu_down_combine(shape, experts, layer, gu, idx, w,
+                                  sw if shape.n_shared else None, x, k, workspace, stream=stream)
+    return dict(idx=idx, w=w, shared_w=sw, logits=logits, gate_up=gu, y=out)

@@ -1,0 +1,234 @@
+// C-ABI entry points of libmoeq: argument validation, workspace layout and
+// kernel dispatch.  The arithmetic lives in the .hip kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "moeq.h"
+#include "moeq_internal.hpp"
+
+namespace moeq {
+int down_row_blocks(int H);
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOEQ_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOEQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_shape(const moeq_shape* s) {
+  if (!s) return fail(MOEQ_E_INVALID, "shape is NULL");
+  if (s->hidden <= 0 || s->inter <= 0 || s->n_experts <= 0 || s->n_shared < 0)
+    return fail(MOEQ_E_INVALID, "shape sizes must be positive (hidden=%d inter=%d n_experts=%d n_shared=%d)",
+                s->hidden, s->inter, s->n_experts, s->n_shared);
+  if (s->bits != 4 && s->bits != 2)
+    return fail(MOEQ_E_UNSUPPORTED, "bits=%d: only 4-bit and 2-bit experts are implemented", s->bits);
+  if (s->group != 64)
+    return fail(MOEQ_E_UNSUPPORTED, "group=%d: only groups of 64 are implemented", s->group);
+  if (s->hidden % 64 || s->inter % 64)
+    return fail(MOEQ_E_UNSUPPORTED, "hidden=%d inter=%d must be multiples of 64", s->hidden, s->inter);
+  if (s->hidden > MOEQ_MAX_HIDDEN || s->inter > MOEQ_MAX_INTER)
+    return fail(MOEQ_E_UNSUPPORTED, "hidden=%d inter=%d exceed %d/%d", s->hidden, s->inter,
+                MOEQ_MAX_HIDDEN, MOEQ_MAX_INTER);
+  if (s->n_experts > MOEQ_MAX_EXPERTS)
+    return fail(MOEQ_E_UNSUPPORTED, "n_experts=%d exceeds %d", s->n_experts, MOEQ_MAX_EXPERTS);
+  if (s->n_shared > 1)
+    return fail(MOEQ_E_UNSUPPORTED, "n_shared=%d: at most one shared expert", s->n_shared);
+  return MOEQ_OK;
+}
+
+int check_tk(const moeq_shape* s, int T, int k) {
+  if (T < 0) return fail(MOEQ_E_INVALID, "T=%d is negative", T);
+  if (k < 0) return fail(MOEQ_E_INVALID, "k=%d is negative", k);
+  if (k > s->n_experts) return fail(MOEQ_E_INVALID, "k=%d exceeds n_experts=%d", k, s->n_experts);
+  if (k > MOEQ_MAX_TOPK) return fail(MOEQ_E_UNSUPPORTED, "k=%d exceeds %d", k, MOEQ_MAX_TOPK);
+  if (T > MOEQ_MAX_DECODE_TOKENS)
+    return fail(MOEQ_E_UNSUPPORTED, "T=%d exceeds the decode batch limit %d", T, MOEQ_MAX_DECODE_TOKENS);
+  return MOEQ_OK;
+}
+
+int check_dtype(int d, const char* what) {
+  if (d != MOEQ_BF16 && d != MOEQ_F32)
+    return fail(MOEQ_E_UNSUPPORTED, "%s dtype %d: expected MOEQ_BF16 or MOEQ_F32", what, d);
+  return MOEQ_OK;
+}
+
+int check_experts(const moeq_shape* s, const moeq_experts* ex, int layer) {
+  if (!ex || !ex->blobs) return fail(MOEQ_E_INVALID, "experts view or its blob table is NULL");
+  if (layer < 0 || layer >= ex->n_layers)
+    return fail(MOEQ_E_INVALID, "layer=%d outside [0, %d)", layer, ex->n_layers);
+  (void)s;
+  return MOEQ_OK;
+}
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(const moeq_shape& s, int T, int k) {
+  WorkspaceLayout w;
+  const int64_t KS = (int64_t)k + s.n_shared;
+  w.counters = 0;
+  w.logits = 4096;
+  w.dbuf = w.logits + align_up((int64_t)T * (s.n_experts + 1) * 8);
+  w.total = w.dbuf + align_up((int64_t)T * KS * s.hidden * 4);
+  return w;
+}
+
+}  // namespace moeq
+
+using namespace moeq;
+
+extern "C" {
+
+int moeq_abi_version(void) { return 1; }
+
+const char* moeq_last_error(void) { return g_last_error.c_str(); }
+
+int64_t moeq_expert_bytes(const moeq_shape* s) {
+  if (check_shape(s) != MOEQ_OK) return -1;
+  const int64_t q = (int64_t)s->hidden * s->inter * s->bits / 8;
+  const int64_t sb = (int64_t)s->hidden * s->inter / s->group * 4;
+  return 3 * (q + sb);
+}
+
+int moeq_workspace_bytes(const moeq_shape* s, int T, int k, int64_t* bytes) {
+  if (int rc = check_shape(s)) return rc;
+  if (int rc = check_tk(s, T, k)) return rc;
+  if (!bytes) return fail(MOEQ_E_INVALID, "bytes is NULL");
+  *bytes = workspace_layout(*s, T, k).total;
+  return ok();
+}
+
+int moe_router_topk(const moeq_shape* s, const void* x, int x_dtype, uint32_t flags,
+                    const uint16_t* w_router, const uint16_t* shared_gate, int T, int k,
+                    int32_t* topk_idx, float* topk_w, float* shared_w, double* logits,
+                    void* workspace, void* stream) {
+  if (int rc = check_shape(s)) return rc;
+  if (int rc = check_tk(s, T, k)) return rc;
+  if (int rc = check_dtype(x_dtype, "x")) return rc;
+  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_RMSNORM))
+    return fail(MOEQ_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (k < 1) return fail(MOEQ_E_INVALID, "router needs k >= 1 (got %d)", k);
+  if (T == 0) return ok();
+  if (!x || !w_router || !topk_idx || !topk_w || !workspace)
+    return fail(MOEQ_E_INVALID, "x, w_router, topk_idx, topk_w and workspace must be non-NULL");
+  if (shared_gate && s->n_shared == 0)
+    return fail(MOEQ_E_INVALID, "shared_gate given but n_shared == 0");
+  const WorkspaceLayout L = workspace_layout(*s, T, k);
+  char* ws = static_cast<char*>(workspace);
+  RouterArgs a{};
+  a.x = x;
+  a.x_f32 = x_dtype == MOEQ_F32;
+  a.rmsnorm = (flags & MOEQ_F_RMSNORM) != 0;
+  a.no_renorm = (flags & MOEQ_F_NO_RENORM) != 0;
+  a.w_router = w_router;
+  a.shared_gate = shared_gate;
+  a.H = s->hidden; a.E = s->n_experts; a.T = T; a.k = k;
+  a.topk_idx = topk_idx; a.topk_w = topk_w; a.shared_w = shared_w;
+  a.logits = reinterpret_cast<double*>(ws + L.logits);
+  a.logits_out = logits;
+  a.counter = reinterpret_cast<uint32_t*>(ws + L.counters) + kCounterRouter;
+  hipError_t e = launch_router_topk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+  return ok();
+}
+
+int moe_q4_expert_gemv(const moeq_shape* s, const moeq_experts* ex, int layer, const void* x,
+                       int x_dtype, uint32_t flags, const int32_t* topk_idx, int T, int k,
+                       void* workspace, float* gate_up, void* stream) {
+  if (int rc = check_shape(s)) return rc;
+  if (int rc = check_tk(s, T, k)) return rc;
+  if (int rc = check_dtype(x_dtype, "x")) return rc;
+  if (int rc = check_experts(s, ex, layer)) return rc;
+  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_RMSNORM))
+    return fail(MOEQ_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (T == 0 || k + s->n_shared == 0) return ok();
+  if (!x || !gate_up || !workspace || (k > 0 && !topk_idx))
+    return fail(MOEQ_E_INVALID, "x, topk_idx, gate_up and workspace must be non-NULL");
+  const WorkspaceLayout L = workspace_layout(*s, T, k);
+  char* ws = static_cast<char*>(workspace);
+  GemvArgs a{};
+  a.x = x;
+  a.x_f32 = x_dtype == MOEQ_F32;
+  a.rmsnorm = (flags & MOEQ_F_RMSNORM) != 0;
+  a.blobs = ex->blobs + (int64_t)layer * (s->n_experts + s->n_shared);
+  a.topk_idx = topk_idx;
+  a.H = s->hidden; a.I = s->inter; a.E = s->n_experts; a.S = s->n_shared;
+  a.T = T; a.k = k; a.bits = s->bits;
+  a.gate_up = gate_up;
+  a.status = reinterpret_cast<int32_t*>(ws + L.counters) + kCounterStatus;
+  hipError_t e = launch_expert_gemv(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gate/up kernel launch");
+  return ok();
+}
+
+int moe_swiglu_down_combine(const moeq_shape* s, const moeq_experts* ex, int layer,
+                            const float* gate_up, const int32_t* topk_idx, const float* topk_w,
+                            const float* shared_w, const void* residual, int res_dtype, int T,
+                            int k, void* workspace, float* out, void* stream) {
+  if (int rc = check_shape(s)) return rc;
+  if (int rc = check_tk(s, T, k)) return rc;
+  if (int rc = check_dtype(res_dtype, "residual")) return rc;
+  if (int rc = check_experts(s, ex, layer)) return rc;
+  if (T == 0) return ok();
+  if (!gate_up || !residual || !out || !workspace || (k > 0 && (!topk_idx || !topk_w)))
+    return fail(MOEQ_E_INVALID, "gate_up, topk_idx, topk_w, residual, out and workspace must be non-NULL");
+  if (moeq::down_row_blocks(s->hidden) > kMaxRowBlockCounters)
+    return fail(MOEQ_E_UNSUPPORTED, "hidden=%d needs too many row blocks", s->hidden);
+  if (k + s->n_shared == 0) {
+    return fail(MOEQ_E_UNSUPPORTED, "k == 0 without a shared expert: the layer is the identity");
+  }
+  const WorkspaceLayout L = workspace_layout(*s, T, k);
+  char* ws = static_cast<char*>(workspace);
+  DownArgs a{};
+  a.gate_up = gate_up;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.shared_w = shared_w;
+  a.residual = residual;
+  a.res_f32 = res_dtype == MOEQ_F32;
+  a.blobs = ex->blobs + (int64_t)layer * (s->n_experts + s->n_shared);
+  a.H = s->hidden; a.I = s->inter; a.E = s->n_experts; a.S = s->n_shared;
+  a.T = T; a.k = k; a.bits = s->bits;
+  a.out = out;
+  a.dbuf = reinterpret_cast<float*>(ws + L.dbuf);
+  a.rb_counters = reinterpret_cast<uint32_t*>(ws + L.counters) + kCounterRowBlocks;
+  a.status = reinterpret_cast<int32_t*>(ws + L.counters) + kCounterStatus;
+  hipError_t e = launch_down_combine(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "down/combine kernel launch");
+  return ok();
+}
+
+int moe_read_device_status(void* workspace, void* stream, int32_t* status) {
+  if (!workspace || !status) return fail(MOEQ_E_INVALID, "workspace and status must be non-NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* word = reinterpret_cast<int32_t*>(workspace) + kCounterStatus;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  e = hipMemcpy(status, word, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy status");
+  const int32_t zero = 0;
+  e = hipMemcpy(word, &zero, sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy clear status");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// Device building blocks shared by the moeq kernels (gfx950, wave64).
+//
+// Dequantised dot products use the fp16 "magic exponent" form: a packed
+// unsigned value q (< 1024) OR-ed into the mantissa of fp16 1024.0 is the
+// fp16 number 1024 + q exactly, so one v_and_or per pair of values and one
+// v_dot2_f32_f16 per pair give sum_j (1024 + q_j) x_j in fp32.  Per chunk
+// of consecutive inputs sharing a scale s and bias b (Flash-MoE,
+// "Noyau de déquantification optimisé FMA": w = q*s + b):
+//     sum_j (q_j s + b) x_j = s * dot + (b - 1024 s) * X,   X = sum_j x_j
+// with dot the magic-exponent sum and X precomputed once per input vector
+// in LDS.  Activations are staged in LDS as fp16 pairs laid out to match
+// the pair order the masks produce, after a power-of-two rescale per
+// vector (exact) that puts max|x| in [2^14, 2^15) so no input overflows or
+// loses precision to fp16 subnormals.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moeq.h"
+
+namespace moeq {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagicPair = 0x64006400u;   // two fp16 1024.0
+constexpr float kMagic = 1024.0f;
+
+// status bits written to the workspace status word
+constexpr int32_t kStatusBadExpert = 1;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
+                                false);
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+  half2v h;
+  h.x = (_Float16)a;
+  h.y = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float half_lo(uint32_t p) {
+  return (float)__builtin_bit_cast(half2v, p).x;
+}
+__device__ __forceinline__ float half_hi(uint32_t p) {
+  return (float)__builtin_bit_cast(half2v, p).y;
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int o) {
+  int2 p = __builtin_bit_cast(int2, v);
+  p.x = __shfl_xor(p.x, o, 64);
+  p.y = __shfl_xor(p.y, o, 64);
+  return __builtin_bit_cast(double, p);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += shfl_xor_f64(v, o);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64);
+// every lane of a group receives its group's sum.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ----------------------------------------------------------- packed layout
+
+// Values per u32 word, fp16 pairs per word, u32x4 chunks per row.
+template <int BITS> struct Pack {
+  static constexpr int kPerWord = 32 / BITS;          // 8 or 16
+  static constexpr int kPairsPerWord = kPerWord / 2;  // 4 or 8
+  static constexpr int kPerChunk = 4 * kPerWord;      // values per 16-byte chunk: 32 or 64
+  static constexpr uint32_t kPairMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+};
+
+// Magic-exponent dot of one 16-byte chunk of packed values against the
+// staged fp16 pairs of the same chunk (xp points at the chunk's first pair).
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* __restrict__ xp) {
+  float acc = 0.0f;
+  const uint4* xv = reinterpret_cast<const uint4*>(xp);
+  constexpr uint32_t M = Pack<BITS>::kPairMask;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 x = xv[i];
+      uint32_t w = q[i];
+      acc = dot2(kMagicPair | (w & M), x.x, acc);
+      acc = dot2(kMagicPair | ((w >> 4) & M), x.y, acc);
+      acc = dot2(kMagicPair | ((w >> 8) & M), x.z, acc);
+      acc = dot2(kMagicPair | ((w >> 12) & M), x.w, acc);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 xa = xv[2 * i];
+      uint4 xb = xv[2 * i + 1];
+      uint32_t w = q[i];
+      acc = dot2(kMagicPair | (w & M), xa.x, acc);
+      acc = dot2(kMagicPair | ((w >> 2) & M), xa.y, acc);
+      acc = dot2(kMagicPair | ((w >> 4) & M), xa.z, acc);
+      acc = dot2(kMagicPair | ((w >> 6) & M), xa.w, acc);
+      acc = dot2(kMagicPair | ((w >> 8) & M), xb.x, acc);
+      acc = dot2(kMagicPair | ((w >> 10) & M), xb.y, acc);
+      acc = dot2(kMagicPair | ((w >> 12) & M), xb.z, acc);
+      acc = dot2(kMagicPair | ((w >> 14) & M), xb.w, acc);
+    }
+  }
+  return acc;
+}
+
+// One chunk's contribution: s * dot + (b - 1024 s) * X_chunk.
+__device__ __forceinline__ float chunk_affine(float dot, uint32_t sb, float xsum) {
+  float s = bf16_lo(sb);
+  float b = bf16_hi(sb);
+  return fmaf(s, dot, fmaf(-kMagic, s, b) * xsum);
+}
+
+// ------------------------------------------------------------- LDS staging
+//
+// A staged vector of n values (n a multiple of 64) occupies
+//   pairs : n/2 u32   (pair m of word w = (v[w*PW + m], v[w*PW + m + PW/2]))
+//   xsum  : n/kPerChunk floats (sum of the fp16-rounded values per chunk)
+// plus one float per vector: the power of two that undoes the rescale.
+
+// Power-of-two factor p with max_abs * p in [2^14, 2^15) (1 if max_abs == 0
+// or not finite).
+__device__ __forceinline__ float pow2_stage_factor(float max_abs) {
+  if (!(max_abs > 0.0f) || !isfinite(max_abs)) return 1.0f;
+  int e = ilogbf(max_abs);          // max_abs in [2^e, 2^(e+1))
+  return ldexpf(1.0f, min(14 - e, 126));   // 2^126 keeps 1/p a normal float
+}
+
+// ----------------------------------------------------------- memory access
+
+template <class T>
+__device__ __forceinline__ T load_stream(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// Agent-scope release/acquire helpers for last-arriver patterns.
+__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_store_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void set_status(int32_t* status, int32_t bits) {
+  if (status) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace moeq

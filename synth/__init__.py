@@ -194,3 +194,48 @@ def bf16_to_f64(a: np.ndarray) -> np.ndarray:
 
 def with_changes(cfg: MoEConfig, **kw) -> MoEConfig:
     return replace(cfg, **kw)
+
+
+# ---------------------------------------------------------------- device twin
+
+_DEV_SO = os.path.join(_HERE, "libsynth_device.so")
+_dev_lib = None
+
+
+def build_device(force: bool = True) -> str:
+    """Compile the HIP twin of the generator (gfx950)."""
+    src = os.path.join(_HERE, "synth_device.hip")
+    if force or not os.path.exists(_DEV_SO) or os.path.getmtime(_DEV_SO) < os.path.getmtime(src):
+        tmp = _DEV_SO + ".tmp%d" % os.getpid()
+        hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+        subprocess.check_call([hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+                               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                               "-o", tmp, src], stderr=subprocess.DEVNULL)
+        os.replace(tmp, _DEV_SO)
+    return _DEV_SO
+
+
+def dev_lib() -> ctypes.CDLL:
+    global _dev_lib
+    if _dev_lib is None:
+        if not os.path.exists(_DEV_SO):
+            raise ImportError(f"{_DEV_SO} is missing: call synth.build_device()")
+        L = ctypes.CDLL(_DEV_SO)
+        L.synth_device_fill_experts.restype = ctypes.c_int
+        L.synth_device_fill_experts.argtypes = [ctypes.POINTER(_Spec), ctypes.c_uint32,
+                                                ctypes.c_uint32, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+        _dev_lib = L
+    return _dev_lib
+
+
+def device_fill_experts(cfg: MoEConfig, layer: int, out_ptr: int, stride: int,
+                        first_expert: int = 0, count: int | None = None, stream: int = 0):
+    """Fill blobs [first, first+count) of a layer into device memory at
+    out_ptr + i*stride, asynchronously on `stream` (a hipStream_t value)."""
+    count = cfg.n_slots - first_expert if count is None else count
+    s = spec(cfg)
+    rc = dev_lib().synth_device_fill_experts(ctypes.byref(s), layer, first_expert, count, stride,
+                                             out_ptr, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_device_fill_experts failed with hipError {rc}")

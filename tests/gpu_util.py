@@ -1,0 +1,51 @@
+"""Helpers for the GPU tests: seeded inputs moved to device memory, and the
+parity bar (exact top-K; max |gpu - oracle| <= 2e-3 * max |oracle|)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import quantized_expert_gemv_router_amd as q
+import synth
+
+TOL = 2e-3
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def slot_stride(cfg) -> int:
+    return (cfg.expert_bytes + 255) // 256 * 256
+
+
+def bf16_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def layer_arena(cfg, layer: int) -> torch.Tensor:
+    host = synth.layer_blobs(cfg, layer, slot_stride(cfg))
+    return torch.from_numpy(host.reshape(-1)).cuda()
+
+
+def experts_for(cfg, layers=(0,)):
+    shape = q.Shape.of(cfg)
+    arenas = [layer_arena(cfg, l) for l in layers]
+    return shape, q.ExpertTable(shape, arenas, slot_stride(cfg))
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = np.abs(ref).max()
+    return float(np.abs(gpu - ref).max() / denom) if denom > 0 else float(np.abs(gpu).max())
+
+
+def assert_close(gpu, ref, what: str, tol: float = TOL):
+    e = rel_err(gpu, ref)
+    assert np.all(np.isfinite(np.asarray(gpu))), f"{what}: non-finite values"
+    assert e <= tol, f"{what}: max|gpu-oracle|/max|oracle| = {e:.3e} > {tol:g}"
+    return e

@@ -1,0 +1,160 @@
+"""GPU parity of one decode layer (router -> gate/up -> SwiGLU/down/combine)
+against the fp64 oracle on the same seeded inputs.
+
+Bar: top-K indices and order bit-exact; router logits to fp64 rounding;
+softmax weights to 1e-6 relative; gate/up and the layer output within
+max |gpu - oracle| <= 2e-3 * max |oracle|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_expert_gemv_router_amd as q
+import synth
+from tests.gpu_util import assert_close, bf16_dev, experts_for, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(cfg, flags=0, shared_gate=None, x_np=None, x_dev=None, check_gate_up=True):
+    say(f"[parity] {cfg.name} H={cfg.hidden} I={cfg.inter} E={cfg.n_experts} S={cfg.n_shared} "
+        f"k={cfg.top_k} T={cfg.tokens} bits={cfg.bits} flags={flags}")
+    shape, ex = experts_for(cfg)
+    if x_dev is None:
+        x_np = synth.tokens(cfg, 0) if x_np is None else x_np
+        x_dev = bf16_dev(x_np)
+        x64 = synth.bf16_to_f64(x_np)
+    else:
+        x64 = x_dev.double().cpu().numpy()
+    wr_np = synth.router(cfg, 0)
+    sg_dev = None if shared_gate is None else bf16_dev(shared_gate)
+    out = q.moe_layer(shape, ex, 0, x_dev, bf16_dev(wr_np), cfg.top_k, flags, sg_dev)
+    torch.cuda.synchronize()
+    shape_o = oracle.shape_of(cfg)
+    blobs = {}
+    _, idx_o, _, _ = oracle.route(shape_o, wr_np, x64, cfg.top_k, flags, shared_gate)
+    for e in set(np.unique(idx_o).tolist()) | set(range(cfg.n_experts, cfg.n_slots)):
+        blobs[e] = synth.expert_blob(cfg, 0, e)
+    ref = oracle.moe_layer(shape_o, blobs, wr_np, x64, cfg.top_k, flags, shared_gate)
+    idx = out["idx"].cpu().numpy()
+    assert np.array_equal(idx, ref["idx"]), (idx, ref["idx"])
+    lg = out["logits"].cpu().numpy()
+    np.testing.assert_allclose(lg, ref["logits"], rtol=0, atol=1e-12 * np.abs(ref["logits"]).max())
+    np.testing.assert_allclose(out["w"].cpu().numpy(), ref["w"], rtol=1e-6, atol=1e-7)
+    if cfg.n_shared:
+        np.testing.assert_allclose(out["shared_w"].cpu().numpy(), ref["gamma"], rtol=1e-6)
+    e_gu = assert_close(out["gate_up"].cpu().numpy(), ref["gu"], "gate_up") if check_gate_up else 0
+    e_y = assert_close(out["y"].cpu().numpy(), ref["y"], "output")
+    say(f"  ok: gate_up rel {e_gu:.2e}, output rel {e_y:.2e}")
+    return out, ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit", "batch16_top10"])
+def test_config_parity(name):
+    run_and_check(synth.CONFIGS[name])
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_ragged_shapes(bits):
+    """Sizes that are not multiples of the kernels' tiles: 320 = 5*64 hidden,
+    192 = 3*64 intermediate, 37 experts, 3 tokens."""
+    base = synth.CONFIGS["decode_4bit" if bits == 4 else "decode_2bit"]
+    cfg = synth.with_changes(base, name=f"ragged{bits}", hidden=320, inter=192, n_experts=37,
+                             top_k=5, tokens=3)
+    run_and_check(cfg)
+
+
+@pytest.mark.parametrize("bits,H,I", [(4, 8192, 4096), (2, 8192, 8192)])
+def test_largest_supported_rows(bits, H, I):
+    base = synth.CONFIGS["decode_4bit" if bits == 4 else "decode_2bit"]
+    cfg = synth.with_changes(base, name=f"max{bits}", hidden=H, inter=I, n_experts=6, top_k=2,
+                             tokens=2)
+    run_and_check(cfg)
+
+
+@pytest.mark.parametrize("k,E", [(1, 8), (8, 8), (16, 64)])
+def test_topk_edges(k, E):
+    cfg = synth.with_changes(synth.CONFIGS["tiny"], name=f"k{k}E{E}", n_experts=E, top_k=k, tokens=2)
+    run_and_check(cfg)
+
+
+def test_without_shared_expert():
+    cfg = synth.with_changes(synth.CONFIGS["tiny"], name="noshared", n_shared=0, tokens=3)
+    run_and_check(cfg)
+
+
+def test_shared_gate_and_full_softmax():
+    cfg = synth.with_changes(synth.CONFIGS["decode_4bit"], name="gated", tokens=2)
+    run_and_check(cfg, flags=q.F_NO_RENORM, shared_gate=synth.shared_gate_vector(cfg, 0))
+
+
+def test_rmsnorm_fp32_input():
+    """fp32 input with a large scale and the RMS-norm flag (the stacked-layer form)."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_4bit"], name="rms", tokens=4)
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(4, cfg.hidden, generator=g, dtype=torch.float32) * 37.0).cuda()
+    run_and_check(cfg, flags=q.F_RMSNORM, x_dev=x)
+
+
+def test_empty_batch_is_noop():
+    cfg = synth.CONFIGS["tiny"]
+    shape, ex = experts_for(cfg)
+    x = torch.zeros((0, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    wr = bf16_dev(synth.router(cfg, 0))
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    idx, w, sw, _ = q.moe_router_topk(shape, x, wr, cfg.top_k, workspace=ws)
+    gu = q.moe_q4_expert_gemv(shape, ex, 0, x, idx, cfg.top_k, workspace=ws)
+    y = q.moe_swiglu_down_combine(shape, ex, 0, gu, idx, w, sw, x, cfg.top_k, workspace=ws)
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.hidden)
+
+
+def test_run_to_run_bit_identical():
+    cfg = synth.CONFIGS["batch16_top10"]
+    shape, ex = experts_for(cfg)
+    x = bf16_dev(synth.tokens(cfg, 0))
+    wr = bf16_dev(synth.router(cfg, 0))
+    a = q.moe_layer(shape, ex, 0, x, wr, cfg.top_k)
+    b = q.moe_layer(shape, ex, 0, x, wr, cfg.top_k)
+    torch.cuda.synchronize()
+    for key in ("idx", "w", "gate_up", "y"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_batch_invariance():
+    """Token t's output in the 16-token batch equals its output alone, bit for bit."""
+    cfg = synth.CONFIGS["batch16_top10"]
+    shape, ex = experts_for(cfg)
+    x = bf16_dev(synth.tokens(cfg, 0))
+    wr = bf16_dev(synth.router(cfg, 0))
+    full = q.moe_layer(shape, ex, 0, x, wr, cfg.top_k)
+    for t in (0, 7, 15):
+        one = q.moe_layer(shape, ex, 0, x[t:t + 1].contiguous(), wr, cfg.top_k)
+        torch.cuda.synchronize()
+        assert torch.equal(one["idx"][0], full["idx"][t])
+        assert torch.equal(one["y"][0], full["y"][t]), t
+
+
+def test_given_ids_with_duplicates_and_bad_id():
+    """Caller-supplied routing: a repeated expert is computed per slot; an id
+    outside [0, E) sets the status word and leaves the other slots intact."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_4bit"], name="given", tokens=2)
+    shape, ex = experts_for(cfg)
+    x_np = synth.tokens(cfg, 0, 2)
+    x = bf16_dev(x_np)
+    idx = torch.tensor([[5, 5, 100], [7, 600, 5]], dtype=torch.int32, device="cuda")
+    ws = q.new_workspace(shape, 2, 3)
+    gu = torch.zeros((2, 4, 2, cfg.inter), dtype=torch.float32, device="cuda")
+    q.moe_q4_expert_gemv(shape, ex, 0, x, idx, 3, workspace=ws, gate_up=gu)
+    status = q.moe_read_device_status(ws)
+    assert status == 1
+    gu = gu.cpu().numpy()
+    x64 = synth.bf16_to_f64(x_np)
+    sh = oracle.shape_of(cfg)
+    for t, slot, e in [(0, 0, 5), (0, 1, 5), (0, 2, 100), (1, 0, 7), (1, 2, 5), (0, 3, 512), (1, 3, 512)]:
+        g, u, _, _ = oracle.expert_ffn(sh, synth.expert_blob(cfg, 0, e), x64[t])
+        assert_close(gu[t, slot, 0], g, f"gate t{t} s{slot}")
+        assert_close(gu[t, slot, 1], u, f"up t{t} s{slot}")
+    assert np.all(gu[1, 1] == 0)
+    assert q.moe_read_device_status(ws) == 0
