@@ -4,13 +4,16 @@
 // calcul Metal").  For row r of [gate; up] and token t:
 //   y[r] = sum_g ( s[r,g] * sum_{j in g} q[r,j] x[t,j] + b[r,g] * sum_{j in g} x[t,j] )
 //
-// Grid: one workgroup per (expert item, block of 16 rows of [gate; up]),
+// Grid: one workgroup per (expert item, block of 4*RPW rows of [gate; up]),
 // every selected expert of the batch and the shared expert in one launch.
-// Each wave streams its 4 rows once with 16-byte non-temporal loads kept in
-// registers, then applies them to every token routed to the expert (tokens
-// staged 4 at a time in LDS as fp16 pairs); one wave-wide sum per (row,
-// token).  Gate rows and up rows are contiguous in the blob, so the
+// Each wave requests its RPW rows with 16-byte non-temporal loads into
+// registers as soon as its expert is known, stages the tokens routed to the
+// expert (up to 4 at a time) into LDS as fp16 pairs while those loads are
+// in flight, then applies the rows to every token: one wave-wide sum per
+// (row, token).  Gate rows and up rows are contiguous in the blob, so the
 // [gate; up] block is addressed as 2I rows of one matrix.
+#include <cstdlib>
+
 #include "grouping.hpp"
 #include "moeq_internal.hpp"
 #include "staging.hpp"
@@ -19,46 +22,44 @@ namespace moeq {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 4;
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTokensPerStage = 4;
 
-__device__ __forceinline__ float x_value(const void* x, int x_f32, int64_t i) {
-  return x_f32 ? static_cast<const float*>(x)[i]
-               : __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[i] << 16);
-}
-
-template <int BITS, int CPL>
-__global__ __launch_bounds__(64 * kWaves) void gemv_kernel(GemvArgs a, int n_rb, int list_words,
-                                                           int mc) {
+template <int BITS, int CPL, int RPW, int WMAX, int MMAX>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, int list_words) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ GroupLds g;
-  __shared__ float red[2 * kMaxStage * kWaves];
-  __shared__ float undo[kMaxStage];
+  __shared__ float red[2 * kTokensPerStage * kWaves];
+  __shared__ float undo[kTokensPerStage];
   constexpr int PC = Pack<BITS>::kPerChunk;
   constexpr int PPC = PC / 2;
+  constexpr int RPB = kWaves * RPW;
   const int item = blockIdx.x / n_rb, rb = blockIdx.x - item * n_rb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I, KS = a.k + a.S;
   const int nch = H / PC;
-  uint32_t* list = smem;
-  uint32_t* pairs = smem + list_words;
-  float* xsum = reinterpret_cast<float*>(pairs + (int64_t)mc * (H / 2));
+  const int P = a.T * a.k;
+  // dynamic LDS: pairs [4][H/2] | xsum [4][nch] | list | ids | ptrs
+  uint32_t* pairs = smem;
+  float* xsum = reinterpret_cast<float*>(pairs + kTokensPerStage * (H / 2));
+  uint32_t* list = reinterpret_cast<uint32_t*>(xsum + kTokensPerStage * nch);
+  int* ids = reinterpret_cast<int*>(list + list_words);
+  const uint8_t** ptrs = reinterpret_cast<const uint8_t**>(ids + list_words);
 
-  group_item(item, a.topk_idx, a.T, a.k, a.E, a.S, g, list, a.status);
-  if (g.expert < 0 || g.count == 0) return;
-  const uint8_t* blob = static_cast<const uint8_t*>(a.blobs[g.expert]);
-  if (blob == nullptr) return;
+  group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
+  if (g.expert < 0) return;
+  const uint8_t* blob = g.blob;
+  (void)P;
 
   const int64_t row_bytes = (int64_t)H * BITS / 8;
   const int gpr = H / 64;   // scale/bias groups per row
   const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8);
-  const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave;
+  const int row0 = rb * RPB + wave * RPW;
 
-  u32x4 q[kRowsPerWave][CPL];
-  uint32_t sbw[kRowsPerWave][CPL];
+  u32x4 q[RPW][CPL];
+  uint32_t sbw[RPW][CPL];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
+  for (int i = 0; i < RPW; ++i) {
     const int r = row0 + i;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -73,15 +74,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(GemvArgs a, int n_rb,
     }
   }
 
-  for (int m0 = 0; m0 < g.count; m0 += mc) {
-    const int nv = min(mc, g.count - m0);
-    auto src = [&](int m, int j) -> float {
+  for (int m0 = 0; m0 < g.count; m0 += MMAX) {
+    const int nv = min(MMAX, g.count - m0);
+    auto loader = [&](int m, int64_t o, float* v) {
       const int t = (int)(list[m0 + m] >> 8);
-      return x_value(a.x, a.x_f32, (int64_t)t * H + j);
+      load_act<Pack<BITS>::kPerWord>(a.x, a.x_f32, (int64_t)t * H + o, v);
     };
-    stage_many<BITS>(nv, H, src, a.rmsnorm != 0, pairs, xsum, undo, red);
+    stage_batch<BITS, WMAX, MMAX>(nv, H, loader, a.rmsnorm != 0, pairs, xsum, undo, red);
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
+    for (int i = 0; i < RPW; ++i) {
       const int r = row0 + i;
       if (r >= 2 * I) break;
       for (int m = 0; m < nv; ++m) {
@@ -106,31 +107,61 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(GemvArgs a, int n_rb,
   }
 }
 
-template <int BITS, int CPL>
+int rows_per_wave_setting() {
+  static int v = [] {
+    const char* s = std::getenv("MOEQ_GEMV_ROWS_PER_WAVE");
+    int r = s ? std::atoi(s) : 0;
+    return (r == 2 || r == 4 || r == 8) ? r : 0;
+  }();
+  return v;
+}
+
+template <int BITS, int CPL, int RPW, int WMAX>
 hipError_t launch_t(const GemvArgs& a, hipStream_t stream) {
-  const int n_rb = (2 * a.I + kRowsPerBlock - 1) / kRowsPerBlock;
+  constexpr int RPB = kWaves * RPW;
+  const int n_rb = (2 * a.I + RPB - 1) / RPB;
   const int items = min(a.E, a.T * a.k) + a.S;
-  const int list_words = ((a.T * (a.k > 0 ? a.k : 1)) + 3) & ~3;
-  const int mc = min(kTokensPerStage, a.T);
+  const int list_words = (max(a.T * a.k, a.T) + 3) & ~3;
   const int nch = a.H / Pack<BITS>::kPerChunk;
-  const size_t lds = sizeof(uint32_t) * ((size_t)list_words + (size_t)mc * (a.H / 2) + (size_t)mc * nch);
-  hipLaunchKernelGGL((gemv_kernel<BITS, CPL>), dim3(items * n_rb), dim3(64 * kWaves), lds, stream,
-                     a, n_rb, list_words, mc);
+  const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.H / 2) + (size_t)kTokensPerStage * nch +
+                                         2 * (size_t)list_words) +
+                     sizeof(void*) * (size_t)list_words;
+  if (a.T == 1)
+    hipLaunchKernelGGL((gemv_kernel<BITS, CPL, RPW, WMAX, 1>), dim3(items * n_rb), dim3(kThreads), lds,
+                       stream, a, n_rb, list_words);
+  else
+    hipLaunchKernelGGL((gemv_kernel<BITS, CPL, RPW, WMAX, kTokensPerStage>), dim3(items * n_rb),
+                       dim3(kThreads), lds, stream, a, n_rb, list_words);
   return hipGetLastError();
+}
+
+template <int BITS, int CPL, int WMAX>
+hipError_t launch_rpw(const GemvArgs& a, hipStream_t stream) {
+  int rpw = rows_per_wave_setting();
+  if (rpw == 0) {
+    // enough workgroups to cover every CU twice with 8-row waves, else 4
+    const int items = min(a.E, a.T * a.k) + a.S;
+    rpw = (items * ((2 * a.I + 31) / 32) >= 512) ? 8 : 4;
+  }
+  if (rpw == 8) return launch_t<BITS, CPL, 8, WMAX>(a, stream);
+  if (rpw == 2) return launch_t<BITS, CPL, 2, WMAX>(a, stream);
+  return launch_t<BITS, CPL, 4, WMAX>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_expert_gemv(const GemvArgs& a, hipStream_t stream) {
-  const int nch = a.H * a.bits / 128;   // 16-byte chunks per row
+  const int nch = a.H * a.bits / 128;                 // 16-byte chunks per row
   const int cpl = (nch + 63) / 64;
+  const int nwords = a.H * a.bits / 32;               // packed words per input vector
+  const int wmax = (nwords + kThreads - 1) / kThreads;
   if (a.bits == 4) {
-    if (cpl <= 1) return launch_t<4, 1>(a, stream);
-    if (cpl <= 2) return launch_t<4, 2>(a, stream);
-    return launch_t<4, 4>(a, stream);
+    if (cpl <= 1) return wmax <= 1 ? launch_rpw<4, 1, 1>(a, stream) : launch_rpw<4, 1, 2>(a, stream);
+    if (cpl <= 2) return wmax <= 2 ? launch_rpw<4, 2, 2>(a, stream) : launch_rpw<4, 2, 4>(a, stream);
+    return launch_rpw<4, 4, 4>(a, stream);
   }
-  if (cpl <= 1) return launch_t<2, 1>(a, stream);
-  return launch_t<2, 2>(a, stream);
+  if (cpl <= 1) return launch_rpw<2, 1, 1>(a, stream);
+  return launch_rpw<2, 2, 2>(a, stream);
 }
 
 }  // namespace moeq

@@ -1,12 +1,14 @@
 // Per-workgroup expert grouping for decode batches.
 //
-// Each workgroup of the expert kernels owns one (expert, row block) work
-// item.  Items are numbered by the distinct routed experts of the batch in
-// ascending id order, then the shared experts.  Every workgroup rebuilds
-// the grouping from topk_idx in LDS (a bitmap of selected experts, a
-// popcount scan to find its own expert, and a ballot compaction of the
+// Each workgroup of the expert kernels owns one (expert item, row block)
+// work item.  Items are numbered by the distinct routed experts of the
+// batch in ascending id order, then the shared experts.  Every workgroup
+// rebuilds the grouping from topk_idx in LDS (a bitmap of selected experts,
+// a popcount scan to find its own expert, and a ballot compaction of the
 // (token, slot) pairs routed to it, in pair order), so no separate sort
-// launch is needed and the result is the same in every workgroup.
+// launch is needed and the result is the same in every workgroup.  The
+// blob pointer of every selected expert is fetched in the same pass as the
+// ids, so the expert's weights can be requested as soon as it is known.
 #pragma once
 
 #include "moeq.h"
@@ -18,75 +20,94 @@ constexpr int kBitmapWords = MOEQ_MAX_EXPERTS / 32;   // 128
 
 struct GroupLds {
   uint32_t bitmap[kBitmapWords];
-  int expert;       // routed id, or E + s for shared expert s, or -1 (no work)
-  int count;        // (token, slot) pairs in `list`
+  const uint8_t* blob;   // weights of this item's expert (null: no work)
+  const uint8_t* shared_blob;
+  int expert;            // routed id, or E + s for shared expert s, or -1 (no work)
+  int count;             // (token, slot) pairs in `list`
   int n_distinct;
+  int in_range;          // item < n_distinct + S (the item exists in this batch)
 };
 
-// list entries: token << 8 | slot.  `list` must hold T*k (routed) or T
-// (shared) entries.  Returns nothing; results in g / list.  Whole block.
+// LDS scratch the caller provides: list [max(T*k, T)] u32, ids [T*k] int,
+// ptrs [T*k] pointers.  list entries: token << 8 | slot.  Whole block.
 __device__ __forceinline__ void group_item(int item, const int32_t* __restrict__ topk_idx,
-                                           int T, int k, int E, int S, GroupLds& g,
-                                           uint32_t* __restrict__ list,
+                                           const void* const* __restrict__ blobs, int T, int k,
+                                           int E, int S, GroupLds& g, uint32_t* __restrict__ list,
+                                           int* __restrict__ ids, const uint8_t** __restrict__ ptrs,
                                            int32_t* status) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int P = T * k;
   for (int i = tid; i < kBitmapWords; i += blockDim.x) g.bitmap[i] = 0u;
+  if (tid == 0) g.shared_blob = S > 0 ? static_cast<const uint8_t*>(blobs[E]) : nullptr;
   __syncthreads();
   for (int p = tid; p < P; p += blockDim.x) {
-    int e = topk_idx[p];
-    if (e >= 0 && e < E) atomicOr(&g.bitmap[e >> 5], 1u << (e & 31));
+    const int e = topk_idx[p];
+    const bool ok = e >= 0 && e < E;
+    ids[p] = ok ? e : -1;
+    ptrs[p] = ok ? static_cast<const uint8_t*>(blobs[e]) : nullptr;
+    if (ok) atomicOr(&g.bitmap[e >> 5], 1u << (e & 31));
     else set_status(status, kStatusBadExpert);
   }
   __syncthreads();
   if (tid < 64) {
     // lane l owns bitmap words 2l and 2l+1
-    uint32_t w0 = g.bitmap[2 * lane], w1 = g.bitmap[2 * lane + 1];
-    int c = __popc(w0) + __popc(w1);
+    const uint32_t w0 = g.bitmap[2 * lane], w1 = g.bitmap[2 * lane + 1];
+    const int c = __popc(w0) + __popc(w1);
     int incl = c;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      int v = __shfl_up(incl, o, 64);
+      const int v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    int excl = incl - c;
-    int total = __shfl(incl, 63, 64);
-    if (lane == 0) { g.n_distinct = total; g.expert = -1; g.count = 0; }
-    __builtin_amdgcn_wave_barrier();
+    const int excl = incl - c;
+    const int total = __shfl(incl, 63, 64);
+    int e = -1;
     if (item < total) {
+      // the owner lane finds the item-th set bit; broadcast it
+      int mine = -1;
       if (item >= excl && item < incl) {
         int r = item - excl;
         uint32_t w = w0;
         int base = 64 * lane;
         if (r >= __popc(w0)) { r -= __popc(w0); w = w1; base += 32; }
         for (int i = 0; i < r; ++i) w &= w - 1;   // drop the r lowest set bits
-        g.expert = base + __builtin_ctz(w);
+        mine = base + __builtin_ctz(w);
       }
+      const uint64_t owner = __ballot(mine >= 0);
+      e = __shfl(mine, (int)__builtin_ctzll(owner), 64);
     } else if (item < total + S) {
-      if (lane == 0) g.expert = E + (item - total);
+      e = E + (item - total);
     }
-  }
-  __syncthreads();
-  const int e = g.expert;
-  if (tid < 64 && e >= 0) {
-    if (e < E) {
-      int cnt = 0;
+    int cnt = 0;
+    const uint8_t* blob = nullptr;
+    if (e >= 0 && e < E) {
       for (int base = 0; base < P; base += 64) {
-        int p = base + lane;
-        bool hit = p < P && topk_idx[p] == e;
-        uint64_t m = __ballot(hit);
+        const int p = base + lane;
+        const bool hit = p < P && ids[p] == e;
+        const uint64_t m = __ballot(hit);
         if (hit) {
-          int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
-          int t = p / k;
+          const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+          const int t = p / k;
           list[pos] = ((uint32_t)t << 8) | (uint32_t)(p - t * k);
+          if (pos == 0) blob = ptrs[p];
         }
         cnt += __popcll(m);
       }
-      if (lane == 0) g.count = cnt;
-    } else {
+      const uint64_t hb = __ballot(blob != nullptr);
+      if (hb) blob = reinterpret_cast<const uint8_t*>(
+                  __shfl((long long)(uintptr_t)blob, (int)__builtin_ctzll(hb), 64));
+    } else if (e >= E) {
       const int slot = k + (e - E);
       for (int t = lane; t < T; t += 64) list[t] = ((uint32_t)t << 8) | (uint32_t)slot;
-      if (lane == 0) g.count = T;
+      cnt = T;
+      blob = (e == E) ? g.shared_blob : static_cast<const uint8_t*>(blobs[e]);
+    }
+    if (lane == 0) {
+      g.n_distinct = total;
+      g.in_range = item < total + S;
+      g.expert = (blob != nullptr && cnt > 0) ? e : -1;
+      g.blob = blob;
+      g.count = cnt;
     }
   }
   __syncthreads();

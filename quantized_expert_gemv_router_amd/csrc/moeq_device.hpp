@@ -161,13 +161,31 @@ __device__ __forceinline__ T load_stream(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
-// Agent-scope release/acquire helpers for last-arriver patterns.
-__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-workgroup hand-off without cache-wide flushes.  Data that another
+// workgroup (possibly on another XCD, with its own L2) will read is written
+// with agent-scope atomic stores (write-through) and read with agent-scope
+// atomic loads; the producer then waits for its stores to complete before
+// bumping an arrival counter.  Because every shared access is itself an
+// agent-scope atomic, no L2 write-back or invalidate (which an agent-scope
+// fence would issue per wave) is needed.
+template <class T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void atomic_store_relaxed(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <class T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's outstanding memory operations have completed.
+__device__ __forceinline__ void drain_memory() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void set_status(int32_t* status, int32_t bits) {

@@ -11,30 +11,23 @@
 // once and dotted with every token in fp64 (bf16 x bf16 and bf16 x fp32
 // products are exact in fp64).  With RMS norm the same pass accumulates
 // sum(x^2) (the lanes of a wave cover every column exactly once), and the
-// logit is inv_rms * sum(W x).  The last workgroup to finish (arrival
-// counter, agent-scope acquire/release) selects top-K for every token from
-// the fp64 logits staged in LDS and writes indices, weights and the shared
-// expert's weight.
+// logit is inv_rms * sum(W x).  Logits are written with agent-scope
+// write-through stores; the last workgroup to bump the arrival counter
+// selects top-K for every token from the fp64 logits staged in LDS and
+// writes indices, weights and the shared expert's weight.
 #include "moeq_device.hpp"
 #include "moeq_internal.hpp"
 
 namespace moeq {
 namespace {
 
-constexpr int kWaves = 2;            // router rows per workgroup
-constexpr int kTokGroup = 8;         // tokens dotted per pass over a row
+constexpr int kWaves = 2;            // router rows per workgroup (one per wave)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStageVec = 16;        // 16-byte loads in flight per thread while staging x
 
-__device__ __forceinline__ void load_x8(const void* x, int x_f32, int64_t off, double v[8]) {
-  if (x_f32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
-    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
-  }
+__host__ __device__ inline int token_group(int H) {
+  const int tg = 16384 / H;
+  return tg < 1 ? 1 : (tg > 4 ? 4 : tg);
 }
 
 // (value desc, index asc) total order: does (va, ia) rank before (vb, ib)?
@@ -46,9 +39,21 @@ __device__ void select_token(const RouterArgs& a, int t, double* lg, int* sel, d
   const int lane = threadIdx.x & 63;
   const int E = a.E;
   const double* src = a.logits + (int64_t)t * (E + 1);
-  for (int e = lane; e < E; e += 64) lg[e] = src[e];
+  for (int base = 0; base < E; base += 64 * 8) {
+    double b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = base + 64 * i + lane;
+      b[i] = e < E ? ld_agent(src + e) : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = base + 64 * i + lane;
+      if (e < E) lg[e] = b[i];
+    }
+  }
   if (a.logits_out)
-    for (int e = lane; e < E; e += 64) a.logits_out[(int64_t)t * E + e] = src[e];
+    for (int e = lane; e < E; e += 64) a.logits_out[(int64_t)t * E + e] = lg[e];
   __builtin_amdgcn_wave_barrier();
   uint64_t taken = 0;
   for (int r = 0; r < a.k; ++r) {
@@ -82,72 +87,112 @@ __device__ void select_token(const RouterArgs& a, int t, double* lg, int* sel, d
     a.topk_w[(int64_t)t * a.k + lane] = (float)(exp(selv[lane] - m) / z);
   }
   if (lane == 0 && a.shared_w) {
-    a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-src[E]))) : 1.0f;
+    a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-ld_agent(src + E)))) : 1.0f;
   }
   __builtin_amdgcn_wave_barrier();
 }
 
-__global__ __launch_bounds__(64 * kWaves) void router_kernel(RouterArgs a) {
-  extern __shared__ double lds_lg[];   // [kWaves][E]
+// One wave per router row (rows E.. hold the optional shared-gate vector).
+// The row's bf16 chunks (CPL per lane) are loaded once into registers; the
+// tokens are staged TG at a time into LDS as fp32 with all loads of a group
+// in flight together.
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int sel[kWaves][MOEQ_MAX_TOPK];
   __shared__ double selv[kWaves][MOEQ_MAX_TOPK];
   __shared__ int is_last;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rows = a.E + (a.shared_gate ? 1 : 0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, E = a.E;
+  const int TG = token_group(H);
+  float* xs = reinterpret_cast<float*>(smem_raw);                          // [TG][H]
+  double* lds_lg = reinterpret_cast<double*>(smem_raw + sizeof(float) * (size_t)TG * H);  // [kWaves][E]
+  const int rows = E + (a.shared_gate ? 1 : 0);
   const int row = blockIdx.x * kWaves + wave;
-  const int nch = a.H / 8;
+  const bool has_row = row < rows;
+  const int nch = H / 8;
 
-  if (row < rows) {
-    const uint16_t* wrow = row < a.E ? a.w_router + (int64_t)row * a.H : a.shared_gate;
-    for (int t0 = 0; t0 < a.T; t0 += kTokGroup) {
-      const int nt = min(kTokGroup, a.T - t0);
-      double acc[kTokGroup], ss[kTokGroup];
+  u32x4 wv[CPL];
+  {
+    const uint16_t* wrow = row < E ? a.w_router + (int64_t)row * H : a.shared_gate;
 #pragma unroll
-      for (int i = 0; i < kTokGroup; ++i) { acc[i] = 0.0; ss[i] = 0.0; }
-      for (int c = lane; c < nch; c += 64) {
-        u32x4 u = load_stream(reinterpret_cast<const u32x4*>(wrow) + c);
-        double w[8] = {bf16_lo(u[0]), bf16_hi(u[0]), bf16_lo(u[1]), bf16_hi(u[1]),
-                       bf16_lo(u[2]), bf16_hi(u[2]), bf16_lo(u[3]), bf16_hi(u[3])};
+    for (int c = 0; c < CPL; ++c) {
+      const int cc = lane + 64 * c;
+      wv[c] = (has_row && cc < nch) ? load_stream(reinterpret_cast<const u32x4*>(wrow) + cc)
+                                    : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  for (int t0 = 0; t0 < a.T; t0 += TG) {
+    const int nt = min(TG, a.T - t0);
+    // stage nt tokens (contiguous rows of x) into xs as fp32
+    const int esz = a.x_f32 ? 4 : 2;
+    const int n16 = nt * H * esz / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + (int64_t)t0 * H * esz);
+    __syncthreads();
+    for (int base = 0; base < n16; base += kThreads * kStageVec) {
+      uint4 buf[kStageVec];
 #pragma unroll
-        for (int i = 0; i < kTokGroup; ++i) {
-          if (i < nt) {
-            double xv[8];
-            load_x8(a.x, a.x_f32, (int64_t)(t0 + i) * a.H + 8 * c, xv);
+      for (int i = 0; i < kStageVec; ++i) {
+        const int v = base + i * kThreads + tid;
+        if (v < n16) buf[i] = src[v];
+      }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              acc[i] = fma(w[j], xv[j], acc[i]);
-              ss[i] = fma(xv[j], xv[j], ss[i]);
-            }
+      for (int i = 0; i < kStageVec; ++i) {
+        const int v = base + i * kThreads + tid;
+        if (v < n16) {
+          float4* d = reinterpret_cast<float4*>(xs);
+          const uint4 u = buf[i];
+          if (a.x_f32) {
+            d[v] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                               __uint_as_float(u.w));
+          } else {
+            d[2 * v] = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+            d[2 * v + 1] = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
           }
         }
       }
+    }
+    __syncthreads();
+    if (has_row) {
+      for (int i = 0; i < nt; ++i) {
+        const float4* xt = reinterpret_cast<const float4*>(xs + (int64_t)i * H);
+        double acc = 0.0, ss = 0.0;
 #pragma unroll
-      for (int i = 0; i < kTokGroup; ++i) {
-        if (i < nt) {
-          double d = wave_sum_f64(acc[i]);
-          if (a.rmsnorm) {
-            double s2 = wave_sum_f64(ss[i]);
-            d = d * (1.0 / sqrt(s2 / (double)a.H + 1e-6));
+        for (int c = 0; c < CPL; ++c) {
+          const int cc = lane + 64 * c;
+          if (cc < nch) {
+            const float4 xa = xt[2 * cc], xb = xt[2 * cc + 1];
+            const double xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            const double w[8] = {bf16_lo(wv[c][0]), bf16_hi(wv[c][0]), bf16_lo(wv[c][1]),
+                                 bf16_hi(wv[c][1]), bf16_lo(wv[c][2]), bf16_hi(wv[c][2]),
+                                 bf16_lo(wv[c][3]), bf16_hi(wv[c][3])};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              acc = fma(w[j], xv[j], acc);
+              ss = fma(xv[j], xv[j], ss);
+            }
           }
-          if (lane == 0) a.logits[(int64_t)(t0 + i) * (a.E + 1) + row] = d;
         }
+        double d = wave_sum_f64(acc);
+        if (a.rmsnorm) {
+          const double s2 = wave_sum_f64(ss);
+          d = d * (1.0 / sqrt(s2 / (double)H + 1e-6));
+        }
+        if (lane == 0) st_agent(a.logits + (int64_t)(t0 + i) * (E + 1) + row, d);
       }
     }
   }
 
-  // last workgroup to arrive selects top-K for every token
-  __threadfence();
+  // the last workgroup to arrive selects top-K for every token
+  drain_memory();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t old = atomic_add_acq_rel(a.counter, 1u);
-    is_last = (old == gridDim.x - 1);
-  }
+  if (tid == 0) is_last = atomic_add_agent(a.counter, 1u) == gridDim.x - 1;
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) atomic_store_relaxed(a.counter, 0u);
+  if (tid == 0) st_agent(a.counter, 0u);
   for (int t = wave; t < a.T; t += kWaves)
-    select_token(a, t, lds_lg + (int64_t)wave * a.E, sel[wave], selv[wave]);
+    select_token(a, t, lds_lg + (int64_t)wave * E, sel[wave], selv[wave]);
 }
 
 }  // namespace
@@ -155,8 +200,19 @@ __global__ __launch_bounds__(64 * kWaves) void router_kernel(RouterArgs a) {
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t stream) {
   const int rows = a.E + (a.shared_gate ? 1 : 0);
   const int grid = (rows + kWaves - 1) / kWaves;
-  const size_t lds = sizeof(double) * (size_t)kWaves * (size_t)a.E;
-  hipLaunchKernelGGL(router_kernel, dim3(grid), dim3(64 * kWaves), lds, stream, a);
+  const size_t lds = sizeof(float) * (size_t)token_group(a.H) * a.H +
+                     sizeof(double) * (size_t)kWaves * (size_t)a.E;
+  const int cpl = (a.H / 8 + 63) / 64;
+  if (cpl <= 1)
+    hipLaunchKernelGGL(router_kernel<1>, dim3(grid), dim3(kThreads), lds, stream, a);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL(router_kernel<2>, dim3(grid), dim3(kThreads), lds, stream, a);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(router_kernel<4>, dim3(grid), dim3(kThreads), lds, stream, a);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(router_kernel<8>, dim3(grid), dim3(kThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(router_kernel<16>, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

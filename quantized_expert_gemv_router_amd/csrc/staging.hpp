@@ -1,64 +1,151 @@
-// Block-cooperative staging of several activation vectors into LDS in the
-// fp16 pair layout the dequantised dot products read (see moeq_device.hpp).
+// Block-cooperative staging of activation vectors into LDS in the fp16 pair
+// layout the dequantised dot products read (see moeq_device.hpp).
+//
+// Work unit: one packed word's worth of inputs (8 values at 4-bit, 16 at
+// 2-bit).  Thread i owns words i, i + blockDim, ... of every vector; all
+// its global loads are issued before any use, so a staging pass costs one
+// memory latency.  Each thread then writes its words' fp16 pairs and sums
+// them; the four words of a 16-byte chunk belong to four consecutive
+// threads, whose sums are combined with two lane shuffles.
 #pragma once
 
 #include "moeq_device.hpp"
 
 namespace moeq {
 
-constexpr int kMaxStage = 8;   // vectors staged at once
+// Loads PW consecutive activation values starting at element o of x
+// (bf16 or fp32, 16-byte aligned runs).
+template <int PW>
+__device__ __forceinline__ void load_act(const void* x, int x_f32, int64_t o, float* v) {
+  if (x_f32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + o);
+#pragma unroll
+    for (int i = 0; i < PW / 4; ++i) {
+      float4 f = p[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + o);
+#pragma unroll
+    for (int i = 0; i < PW / 8; ++i) {
+      uint4 u = p[i];
+      v[8 * i + 0] = bf16_lo(u.x); v[8 * i + 1] = bf16_hi(u.x);
+      v[8 * i + 2] = bf16_lo(u.y); v[8 * i + 3] = bf16_hi(u.y);
+      v[8 * i + 4] = bf16_lo(u.z); v[8 * i + 5] = bf16_hi(u.z);
+      v[8 * i + 6] = bf16_lo(u.w); v[8 * i + 7] = bf16_hi(u.w);
+    }
+  }
+}
 
-// Stage nvec vectors of n values.  src(m, j) gives the raw value j of vector
-// m; with `rmsnorm` each vector is first scaled by 1/sqrt(mean(v^2) + 1e-6).
-// pairs: [nvec][n/2] u32, xsum: [nvec][n / chunk] f32, undo: [nvec] f32,
-// red: 2 * kMaxStage * nwaves floats of scratch.  Whole block; ends synced.
-template <int BITS, class Src>
-__device__ __forceinline__ void stage_many(int nvec, int n, Src src, bool rmsnorm,
-                                           uint32_t* __restrict__ pairs,
-                                           float* __restrict__ xsum, float* __restrict__ undo,
-                                           float* __restrict__ red) {
+// SwiGLU of PW consecutive intermediate values: silu(g) * u, reading
+// g at gu[o..] and u at gu[I + o..] (fp32).
+template <int PW>
+__device__ __forceinline__ void load_swiglu(const float* gu, int I, int64_t o, float* v) {
+  const float4* pg = reinterpret_cast<const float4*>(gu + o);
+  const float4* pu = reinterpret_cast<const float4*>(gu + I + o);
+#pragma unroll
+  for (int i = 0; i < PW / 4; ++i) {
+    float4 g = pg[i], u = pu[i];
+    v[4 * i + 0] = g.x / (1.0f + __expf(-g.x)) * u.x;
+    v[4 * i + 1] = g.y / (1.0f + __expf(-g.y)) * u.y;
+    v[4 * i + 2] = g.z / (1.0f + __expf(-g.z)) * u.z;
+    v[4 * i + 3] = g.w / (1.0f + __expf(-g.w)) * u.w;
+  }
+}
+
+// Stage nvec (<= MMAX) vectors of n values (n a multiple of 64, n / PW <=
+// WMAX * blockDim).  load(m, o, v) fills v[0..PW) with values o..o+PW of
+// vector m.  With `rmsnorm` each vector is scaled by 1/sqrt(mean(v^2)+1e-6)
+// first.  Then each vector is rescaled by a power of two p (max|v| * p in
+// [2^14, 2^15)), rounded to fp16 pairs and summed per 16-byte chunk.
+// pairs: [nvec][n/2] u32 (16-byte aligned), xsum: [nvec][n / chunk] f32,
+// undo: [nvec] f32 (= 1/p), red: 2 * MMAX * nwaves floats.
+// Whole block; returns after a barrier.
+template <int BITS, int WMAX, int MMAX, class Loader>
+__device__ __forceinline__ void stage_batch(int nvec, int n, Loader load, bool rmsnorm,
+                                            uint32_t* __restrict__ pairs,
+                                            float* __restrict__ xsum, float* __restrict__ undo,
+                                            float* __restrict__ red) {
   constexpr int PW = Pack<BITS>::kPerWord;
   constexpr int HP = PW / 2;
-  constexpr int PPC = 4 * HP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  // pass 1: sum of squares and max |v| per vector
-  for (int m = 0; m < nvec; ++m) {
-    float ss = 0.0f, mx = 0.0f;
-    for (int j = tid; j < n; j += blockDim.x) {
-      float v = src(m, j);
-      ss = fmaf(v, v, ss);
-      mx = fmaxf(mx, fabsf(v));
-    }
-    ss = wave_sum(ss);
-    mx = wave_max(mx);
-    if (lane == 0) { red[(2 * m) * nw + wave] = ss; red[(2 * m + 1) * nw + wave] = mx; }
-  }
-  __syncthreads();
-  // pass 2: fp16 pairs, after the per-vector norm and power-of-two rescale
+  const int nwords = n / PW;
   const int np = n / 2;
-  for (int m = 0; m < nvec; ++m) {
-    float ss = 0.0f, mx = 0.0f;
-    for (int i = 0; i < nw; ++i) { ss += red[(2 * m) * nw + i]; mx = fmaxf(mx, red[(2 * m + 1) * nw + i]); }
-    const float mul = rmsnorm ? 1.0f / sqrtf(ss / (float)n + 1e-6f) : 1.0f;
-    const float p = pow2_stage_factor(mx * mul);
-    const float f = mul * p;
-    if (tid == 0) undo[m] = 1.0f / p;
-    uint32_t* dst = pairs + (int64_t)m * np;
-    for (int i = tid; i < np; i += blockDim.x) {
-      int w = i / HP, mm = i - w * HP;
-      int j = w * PW + mm;
-      dst[i] = pack_half2(src(m, j) * f, src(m, j + HP) * f);
+  const int nch = n / Pack<BITS>::kPerChunk;
+  float v[MMAX][WMAX][PW];
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      const int w = tid + i * blockDim.x;
+      if (m < nvec && w < nwords) {
+        load(m, (int64_t)w * PW, v[m][i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < PW; ++j) v[m][i][j] = 0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    if (m < nvec) {
+      float ss = 0.0f, mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < WMAX; ++i)
+#pragma unroll
+        for (int j = 0; j < PW; ++j) {
+          ss = fmaf(v[m][i][j], v[m][i][j], ss);
+          mx = fmaxf(mx, fabsf(v[m][i][j]));
+        }
+      ss = wave_sum(ss);
+      mx = wave_max(mx);
+      if (lane == 0) { red[(2 * m) * nw + wave] = ss; red[(2 * m + 1) * nw + wave] = mx; }
     }
   }
   __syncthreads();
-  // pass 3: per-chunk sums of the rounded values
-  const int nch = n / Pack<BITS>::kPerChunk;
-  for (int idx = tid; idx < nvec * nch; idx += blockDim.x) {
-    int m = idx / nch, c = idx - m * nch;
-    const uint32_t* p = pairs + (int64_t)m * np + c * PPC;
-    float s = 0.0f;
-    for (int i = 0; i < PPC; ++i) s += half_lo(p[i]) + half_hi(p[i]);
-    xsum[idx] = s;
+#pragma unroll
+  for (int m = 0; m < MMAX; ++m) {
+    if (m < nvec) {
+      float ss = 0.0f, mx = 0.0f;
+      for (int i = 0; i < nw; ++i) {
+        ss += red[(2 * m) * nw + i];
+        mx = fmaxf(mx, red[(2 * m + 1) * nw + i]);
+      }
+      const float mul = rmsnorm ? 1.0f / sqrtf(ss / (float)n + 1e-6f) : 1.0f;
+      const float p = pow2_stage_factor(mx * mul);
+      const float f = mul * p;
+      if (tid == 0) undo[m] = 1.0f / p;
+#pragma unroll
+      for (int i = 0; i < WMAX; ++i) {
+        const int w = tid + i * blockDim.x;
+        float s = 0.0f;
+        if (w < nwords) {
+          uint32_t pr[HP];
+#pragma unroll
+          for (int j = 0; j < HP; ++j) {
+            // The chunk sum must add exactly the fp16 values stored: the
+            // bias term b*X cancels 1024*X inside the magic-exponent dot.
+            // Pin the fp32 product and the packed pair so the compiler
+            // cannot re-derive the fp16 values with a differently rounded
+            // fused multiply-convert (which it does when f is not a power
+            // of two).
+            float lo = v[m][i][j] * f, hi = v[m][i][j + HP] * f;
+            asm volatile("" : "+v"(lo), "+v"(hi));
+            pr[j] = pack_half2(lo, hi);
+            asm volatile("" : "+v"(pr[j]));
+            s += half_lo(pr[j]) + half_hi(pr[j]);
+          }
+          uint4* dst = reinterpret_cast<uint4*>(pairs + (int64_t)m * np + (int64_t)w * HP);
+#pragma unroll
+          for (int j = 0; j < HP / 4; ++j)
+            dst[j] = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
+        }
+        // words 4c..4c+3 of chunk c sit in four consecutive lanes
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if ((tid & 3) == 0 && w < nwords) xsum[(int64_t)m * nch + (w >> 2)] = s;
+      }
+    }
   }
   __syncthreads();
 }
