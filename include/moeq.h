@@ -68,7 +68,10 @@ enum {
   MOEQ_F_NO_RENORM = 1u,
   /* The layer input is normalised as x / sqrt(mean(x^2) + 1e-6) (unit-weight
    * RMS norm) before the router and the experts; the residual stays x. */
-  MOEQ_F_RMSNORM = 2u
+  MOEQ_F_RMSNORM = 2u,
+  /* moe_expert_stack_decode only: run the layers one launch sequence at a
+   * time (router, gate/up, down per layer) instead of the persistent kernel. */
+  MOEQ_F_STACK_LAYERWISE = 4u
 };
 
 /* Limits of the current kernels (larger values return MOEQ_E_UNSUPPORTED). */
@@ -159,8 +162,32 @@ int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts
                             const float* shared_w, const void* residual, int res_dtype,
                             int T, int k, void* workspace, float* out, void* stream);
 
+/* L stacked decode layers [layer0, layer0 + L) on a resident fp32 residual
+ * stream h, in place (Flash-MoE, fr.news.hada.io, "Architecture du
+ * modèle": 60 layers, each with 512 experts, K active including one shared;
+ * "Deferred GPU Expert Compute": combine + norm + residual stay on the GPU
+ * and feed the next layer).  Per layer: xhat = h / sqrt(mean(h^2) + 1e-6)
+ * (unit-weight RMS norm), router + top-k + softmax on xhat, experts on xhat,
+ * h <- h + sum_s w_s d_s + d_shared.
+ *   w_router    device array [n_layers] of device pointers to [E][H] bf16
+ *   h           device [T][H] f32, in/out
+ *   topk_trace  device [L][T][k] int32 out, or NULL
+ *   h_trace     device [L][T][H] f32 out (the input of each layer), or NULL
+ *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE
+ * T == 1 runs one persistent cooperative launch for all L layers (grid
+ * barriers between the dependent steps, no host involvement) when the
+ * shape has a persistent instantiation; otherwise, or with
+ * MOEQ_F_STACK_LAYERWISE or T > 1, it enqueues the three per-layer calls
+ * for each layer.  A grid barrier that waits too long sets status bit 2
+ * (see moe_read_device_status) and the launch ends early. */
+int moe_expert_stack_decode(const moeq_shape* shape, const moeq_experts* experts,
+                            const uint16_t* const* w_router, int layer0, int L, int T, int k,
+                            uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
+                            void* workspace, void* stream);
+
 /* Synchronise `stream` and read the workspace status word: 0 = clean,
- * else a bitmask (1 = an expert id outside [0, E) was seen).  Clears it. */
+ * else a bitmask (1 = an expert id outside [0, E) was seen, 2 = a grid
+ * barrier of the persistent stack kernel timed out).  Clears it. */
 int moe_read_device_status(void* workspace, void* stream, int32_t* status);
 
 #ifdef __cplusplus

@@ -9,9 +9,10 @@ library has not been built the import of the binding functions fails
 loudly; there is no CPU fallback.
 """
 from ._binding import (  # noqa: F401
-    BF16, F32, F_NO_RENORM, F_RMSNORM,
-    MoeqError, Shape, ExpertTable, lib, library_path,
+    BF16, F32, F_NO_RENORM, F_RMSNORM, F_STACK_LAYERWISE,
+    MoeqError, Shape, ExpertTable, RouterTable, lib, library_path,
     moeq_abi_version, moeq_expert_bytes, moeq_workspace_bytes, moeq_last_error,
     moe_router_topk, moe_q4_expert_gemv, moe_swiglu_down_combine, moe_read_device_status,
+    moe_expert_stack_decode,
     new_workspace, moe_layer,
 )

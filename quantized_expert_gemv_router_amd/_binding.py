@@ -10,7 +10,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_PKG, "libmoeq.so")
 
 BF16, F32 = 0, 1
-F_NO_RENORM, F_RMSNORM = 1, 2
+F_NO_RENORM, F_RMSNORM, F_STACK_LAYERWISE = 1, 2, 4
 
 OK, E_INVALID, E_UNSUPPORTED, E_HIP, E_POOL_EXHAUSTED, E_DEVICE = 0, -1, -2, -3, -4, -5
 _CODE_NAMES = {E_INVALID: "MOEQ_E_INVALID", E_UNSUPPORTED: "MOEQ_E_UNSUPPORTED", E_HIP: "MOEQ_E_HIP",
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_expert_gemv.argtypes = [S, X, _I, _P, _I, ctypes.c_uint32, _P, _I, _I, _P, _P, _P]
         L.moe_swiglu_down_combine.argtypes = [S, X, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P]
         L.moe_read_device_status.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
+                                              _P, _P]
         _lib = L
     return _lib
 
@@ -206,6 +208,38 @@ def moe_swiglu_down_combine(shape: Shape, experts: ExpertTable, layer: int, gate
                                          _ptr(residual), _dtype_code(residual), T, k,
                                          _ptr(workspace), _ptr(out), _stream(stream)))
     return out
+
+
+class RouterTable:
+    """Device array of per-layer router matrix pointers ([E][H] bf16 each)."""
+
+    def __init__(self, routers: list, device="cuda"):
+        self.routers = routers
+        self.table = torch.tensor([r.data_ptr() for r in routers], dtype=torch.int64, device=device)
+
+    def ptr(self):
+        return self.table.data_ptr()
+
+
+def moe_expert_stack_decode(shape: Shape, experts: ExpertTable, routers: RouterTable, h: torch.Tensor,
+                            k: int, layer0: int = 0, L: int | None = None, flags: int = 0,
+                            workspace: torch.Tensor | None = None, trace: bool = False, stream=None):
+    """Run layers [layer0, layer0 + L) in place on h (f32 [T, H]).  Returns
+    (topk_trace int32 [L, T, k], h_trace f32 [L, T, H]) when trace, else None."""
+    T = h.shape[0]
+    L = experts.n_layers - layer0 if L is None else L
+    if h.dtype != torch.float32:
+        raise ValueError("the stack runs on an fp32 residual stream")
+    if workspace is None:
+        workspace = new_workspace(shape, T, k, h.device)
+    tk = hk = None
+    if trace:
+        tk = torch.empty((L, T, k), dtype=torch.int32, device=h.device)
+        hk = torch.empty((L, T, shape.hidden), dtype=torch.float32, device=h.device)
+    _check(lib().moe_expert_stack_decode(ctypes.byref(shape), experts.view(), routers.ptr(), layer0, L, T,
+                                         k, flags, _ptr(h), _ptr(tk), _ptr(hk), _ptr(workspace),
+                                         _stream(stream)))
+    return (tk, hk) if trace else None
 
 
 def moe_read_device_status(workspace: torch.Tensor, stream=None) -> int:

@@ -88,7 +88,14 @@ WorkspaceLayout workspace_layout(const moeq_shape& s, int T, int k) {
   w.counters = 0;
   w.logits = 4096;
   w.dbuf = w.logits + align_up((int64_t)T * (s.n_experts + 1) * 8);
-  w.total = w.dbuf + align_up((int64_t)T * KS * s.hidden * 4);
+  w.st_bar = w.dbuf + align_up((int64_t)T * KS * s.hidden * 4);
+  w.st_logits = w.st_bar + align_up((int64_t)stack_barrier_words() * 4);
+  w.st_abuf = w.st_logits + align_up((int64_t)s.n_experts * 8);
+  w.st_idx = w.st_abuf + align_up(KS * s.inter * 4);
+  w.st_w = w.st_idx + align_up((int64_t)T * k * 4);
+  w.st_sw = w.st_w + align_up((int64_t)T * k * 4);
+  w.st_gu = w.st_sw + align_up((int64_t)T * 4);
+  w.total = w.st_gu + align_up((int64_t)T * KS * 2 * s.inter * 4);
   return w;
 }
 
@@ -214,6 +221,91 @@ int moe_swiglu_down_combine(const moeq_shape* s, const moeq_experts* ex, int lay
   a.status = reinterpret_cast<int32_t*>(ws + L.counters) + kCounterStatus;
   hipError_t e = launch_down_combine(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "down/combine kernel launch");
+  return ok();
+}
+
+int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
+                            const uint16_t* const* w_router, int layer0, int L, int T, int k,
+                            uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
+                            void* workspace, void* stream) {
+  if (int rc = check_shape(s)) return rc;
+  if (int rc = check_tk(s, T, k)) return rc;
+  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_STACK_LAYERWISE))
+    return fail(MOEQ_E_UNSUPPORTED, "unknown or inapplicable flag bits 0x%x", flags);
+  if (!ex || !ex->blobs) return fail(MOEQ_E_INVALID, "experts view or its blob table is NULL");
+  if (L < 0 || layer0 < 0 || layer0 + L > ex->n_layers)
+    return fail(MOEQ_E_INVALID, "layers [%d, %d) outside [0, %d)", layer0, layer0 + L, ex->n_layers);
+  if (k < 1) return fail(MOEQ_E_INVALID, "k=%d: the stack needs k >= 1", k);
+  if (T == 0 || L == 0) return ok();
+  if (!w_router || !h || !workspace)
+    return fail(MOEQ_E_INVALID, "w_router, h and workspace must be non-NULL");
+  const WorkspaceLayout W = workspace_layout(*s, T, k);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + W.counters) + kCounterStatus;
+
+  if (T == 1 && !(flags & MOEQ_F_STACK_LAYERWISE)) {
+    StackArgs a{};
+    a.blobs = ex->blobs;
+    a.routers = w_router;
+    a.layer0 = layer0; a.L = L;
+    a.H = s->hidden; a.I = s->inter; a.E = s->n_experts; a.S = s->n_shared; a.K = k;
+    a.bits = s->bits;
+    a.no_renorm = (flags & MOEQ_F_NO_RENORM) != 0;
+    a.h = h;
+    a.topk_trace = topk_trace;
+    a.h_trace = h_trace;
+    a.logits = reinterpret_cast<double*>(ws + W.st_logits);
+    a.abuf = reinterpret_cast<float*>(ws + W.st_abuf);
+    a.bar = reinterpret_cast<uint32_t*>(ws + W.st_bar);
+    a.status = status;
+    hipError_t e = launch_stack_decode(a, st);
+    if (e == hipSuccess) return ok();
+    // no persistent instantiation for this shape, or the device cannot hold
+    // the whole grid at once: run the layers one launch sequence at a time
+    if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
+      return hip_fail(e, "persistent stack kernel launch");
+    (void)hipGetLastError();
+  }
+
+  // per-layer path: router -> gate/up -> down/combine per layer, in place on h
+  const int KS = k + s->n_shared;
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + W.st_idx);
+  float* w = reinterpret_cast<float*>(ws + W.st_w);
+  float* sw = reinterpret_cast<float*>(ws + W.st_sw);
+  float* gu = reinterpret_cast<float*>(ws + W.st_gu);
+  const uint32_t lf = MOEQ_F_RMSNORM | (flags & MOEQ_F_NO_RENORM);
+  for (int l = 0; l < L; ++l) {
+    const int layer = layer0 + l;
+    if (h_trace) {
+      hipError_t e = hipMemcpyAsync(h_trace + (int64_t)l * T * s->hidden, h,
+                                    sizeof(float) * (size_t)T * s->hidden, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync h_trace");
+    }
+    int32_t* idx_l = topk_trace ? topk_trace + (int64_t)l * T * k : idx;
+    {
+      // the router kernel reads this layer's matrix pointer from the device table
+      RouterArgs a{};
+      a.x = h;
+      a.x_f32 = 1;
+      a.rmsnorm = 1;
+      a.no_renorm = (lf & MOEQ_F_NO_RENORM) != 0;
+      a.w_table = w_router;
+      a.w_layer = layer;
+      a.H = s->hidden; a.E = s->n_experts; a.T = T; a.k = k;
+      a.topk_idx = idx_l; a.topk_w = w; a.shared_w = s->n_shared ? sw : nullptr;
+      a.logits = reinterpret_cast<double*>(ws + W.logits);
+      a.counter = reinterpret_cast<uint32_t*>(ws + W.counters) + kCounterRouter;
+      hipError_t e = launch_router_topk(a, st);
+      if (e != hipSuccess) return hip_fail(e, "router kernel launch");
+    }
+    int rc = moe_q4_expert_gemv(s, ex, layer, h, MOEQ_F32, MOEQ_F_RMSNORM, idx_l, T, k, workspace, gu, stream);
+    if (rc) return rc;
+    rc = moe_swiglu_down_combine(s, ex, layer, gu, idx_l, w, s->n_shared ? sw : nullptr, h, MOEQ_F32, T,
+                                 k, workspace, h, stream);
+    if (rc) return rc;
+  }
+  (void)KS;
   return ok();
 }
 

@@ -17,15 +17,27 @@ inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; 
 //                    [64 .. 64 + n_rowblocks) down-combine row-block counters
 //   logits           f64 [T][E + 1]   (last column: shared-gate logit)
 //   dbuf             f32 [T][k + S][H] per-slot down outputs (multi-token)
+//   stack area       barrier words, fp64 logits [E], activations
+//                    [k + S][I], and the per-layer path's routing
+//                    (idx [T][k], w [T][k], shared w [T]) and gate_up
+//                    [T][k + S][2][I]
 struct WorkspaceLayout {
   int64_t counters = 0;
   int64_t logits = 0;
   int64_t dbuf = 0;
+  int64_t st_bar = 0;
+  int64_t st_logits = 0;
+  int64_t st_abuf = 0;
+  int64_t st_idx = 0;
+  int64_t st_w = 0;
+  int64_t st_sw = 0;
+  int64_t st_gu = 0;
   int64_t total = 0;
 };
 
 constexpr int kCounterRouter = 0;
 constexpr int kCounterStatus = 1;
+constexpr int32_t kStatusTimeout = 2;   // a grid barrier gave up waiting
 constexpr int kCounterRowBlocks = 64;
 constexpr int kMaxRowBlockCounters = 1024 - kCounterRowBlocks;
 
@@ -38,6 +50,8 @@ struct RouterArgs {
   int rmsnorm;
   int no_renorm;
   const uint16_t* w_router;
+  const uint16_t* const* w_table;  // if set, the router matrix is w_table[w_layer] (device)
+  int w_layer;
   const uint16_t* shared_gate;
   int H, E, T, k;
   int32_t* topk_idx;
@@ -78,5 +92,25 @@ struct DownArgs {
   int32_t* status;
 };
 hipError_t launch_down_combine(const DownArgs& a, hipStream_t stream);
+
+// ----------------------------------------------- persistent stack decode
+struct StackArgs {
+  const void* const* blobs;        // pointer table base, [n_layers][E + S]
+  const uint16_t* const* routers;  // device array [n_layers] of [E][H] bf16
+  int layer0, L;
+  int H, I, E, S, K, bits;
+  int no_renorm;
+  int router_rows;                 // set by the launcher
+  float* h;                        // [H] in/out
+  int32_t* topk_trace;             // [L][K] or null
+  float* h_trace;                  // [L][H] or null
+  double* logits;                  // [E] scratch
+  float* abuf;                     // [K + S][I] scratch
+  uint32_t* bar;                   // barrier counters (stack_barrier_words())
+  int32_t* status;
+};
+int stack_barrier_words();
+// hipErrorNotSupported: no persistent instantiation for this shape.
+hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream);
 
 }  // namespace moeq

@@ -17,6 +17,7 @@
 // writes indices, weights and the shared expert's weight.
 #include "moeq_device.hpp"
 #include "moeq_internal.hpp"
+#include "topk.hpp"
 
 namespace moeq {
 namespace {
@@ -30,11 +31,8 @@ __host__ __device__ inline int token_group(int H) {
   return tg < 1 ? 1 : (tg > 4 ? 4 : tg);
 }
 
-// (value desc, index asc) total order: does (va, ia) rank before (vb, ib)?
-__device__ __forceinline__ bool ranks_before(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
+// Last-workgroup selection for token t by one wave: stage its fp64 logits
+// in LDS (all loads in flight together), pick top-K, write the outputs.
 __device__ void select_token(const RouterArgs& a, int t, double* lg, int* sel, double* selv) {
   const int lane = threadIdx.x & 63;
   const int E = a.E;
@@ -55,36 +53,11 @@ __device__ void select_token(const RouterArgs& a, int t, double* lg, int* sel, d
   if (a.logits_out)
     for (int e = lane; e < E; e += 64) a.logits_out[(int64_t)t * E + e] = lg[e];
   __builtin_amdgcn_wave_barrier();
-  uint64_t taken = 0;
-  for (int r = 0; r < a.k; ++r) {
-    double bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int m = 0, e = lane; e < E; ++m, e += 64) {
-      double v = lg[e];
-      if (!((taken >> m) & 1) && ranks_before(v, e, bv, bi)) { bv = v; bi = e; }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      double ov = shfl_xor_f64(bv, o);
-      int oi = __shfl_xor(bi, o, 64);
-      if (ranks_before(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
-    if (lane == 0) { sel[r] = bi; selv[r] = bv; }
-  }
-  __builtin_amdgcn_wave_barrier();
-  const double m = selv[0];   // the top-ranked logit is the maximum
-  double z = 0.0;
-  if (a.no_renorm) {
-    double part = 0.0;
-    for (int e = lane; e < E; e += 64) part += exp(lg[e] - m);
-    z = wave_sum_f64(part);
-  } else {
-    for (int r = 0; r < a.k; ++r) z += exp(selv[r] - m);
-  }
+  wave_topk(lg, E, a.k, sel, selv);
+  const float w = wave_softmax_weight(lg, E, a.k, selv, a.no_renorm != 0);
   if (lane < a.k) {
     a.topk_idx[(int64_t)t * a.k + lane] = sel[lane];
-    a.topk_w[(int64_t)t * a.k + lane] = (float)(exp(selv[lane] - m) / z);
+    a.topk_w[(int64_t)t * a.k + lane] = w;
   }
   if (lane == 0 && a.shared_w) {
     a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-ld_agent(src + E)))) : 1.0f;
@@ -114,7 +87,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 
   u32x4 wv[CPL];
   {
-    const uint16_t* wrow = row < E ? a.w_router + (int64_t)row * H : a.shared_gate;
+    const uint16_t* wmat = a.w_table ? a.w_table[a.w_layer] : a.w_router;
+    const uint16_t* wrow = row < E ? wmat + (int64_t)row * H : a.shared_gate;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int cc = lane + 64 * c;

@@ -1,0 +1,128 @@
+"""GPU parity of the stacked decode path (persistent launch and per-layer
+launches) against the fp64 oracle.
+
+Free-running: the oracle and the GPU each run all layers from the same
+token; top-K must be bit-exact at every layer and the final residual stream
+within max|gpu - oracle| <= 2e-3 * max|oracle|.  Exactness is asserted only
+where the oracle's own gap between the K-th and (K+1)-th logit exceeds what
+the GPU's fp32 residual stream can move a logit (MARGIN); past a layer with
+a smaller gap both selections are valid and later layers are not compared.
+Oracle-fed: the oracle's h_l is given to the GPU for one layer, and top-K
+and h_{l+1} are compared with the oracle's layer on the same input.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_expert_gemv_router_amd as q
+import synth
+from tests.gpu_util import TOL, assert_close, bf16_dev, say, slot_stride
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-3   # absolute logit gap below which two selections are both valid
+
+
+def build_stack(cfg, L):
+    shape = q.Shape.of(cfg)
+    stride = slot_stride(cfg)
+    arenas = []
+    for l in range(L):
+        a = torch.empty(cfg.n_slots * stride, dtype=torch.uint8, device="cuda")
+        synth.device_fill_experts(cfg, l, a.data_ptr(), stride)
+        arenas.append(a)
+    routers = q.RouterTable([bf16_dev(synth.router(cfg, l)) for l in range(L)])
+    torch.cuda.synchronize()
+    return shape, q.ExpertTable(shape, arenas, stride), routers
+
+
+def compare_free_running(cfg, L, token_set, traces, gpu_h):
+    tk, hk = traces
+    x64 = synth.bf16_to_f64(synth.tokens(cfg, token_set, 1))
+    ref = oracle.run_stack(cfg, x64, layers=L)
+    idx = tk.cpu().numpy()[:, 0, :]
+    hs = hk.cpu().numpy()[:, 0, :]
+    first_amb = L
+    for l in range(L):
+        if ref["margin"][l, 0] < MARGIN:
+            first_amb = l
+            break
+    for l in range(first_amb + 1 if first_amb < L else L):
+        if l < first_amb:
+            assert np.array_equal(idx[l], ref["idx"][l, 0]), (l, idx[l], ref["idx"][l, 0])
+        assert_close(hs[l], ref["h"][l, 0], f"h input of layer {l}")
+    if first_amb == L:
+        e = assert_close(gpu_h, ref["h"][L, 0], "final h")
+        say(f"  token set {token_set}: {L} layers exact top-K, final h rel err {e:.2e}, "
+            f"min margin {ref['margin'].min():.3e}")
+    else:
+        say(f"  token set {token_set}: near-tie at layer {first_amb} "
+            f"(margin {ref['margin'][first_amb, 0]:.2e}); compared layers < {first_amb}")
+
+
+@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
+def test_stack_small_shape(flags):
+    cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_tiny", hidden=256, inter=128,
+                             n_experts=8, top_k=2, layers=6)
+    say(f"[stack] tiny 6 layers flags={flags}")
+    shape, ex, rt = build_stack(cfg, cfg.layers)
+    for ts in (0, 1, 2):
+        h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+        ws = q.new_workspace(shape, 1, cfg.top_k)
+        traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws,
+                                           trace=True)
+        assert q.moe_read_device_status(ws) == 0
+        compare_free_running(cfg, cfg.layers, ts, traces, h.cpu().numpy()[0])
+
+
+@pytest.fixture(scope="module")
+def stack60():
+    cfg = synth.CONFIGS["stack60_decode"]
+    say(f"[stack60] filling {cfg.layers} layers x {cfg.n_slots} experts on device")
+    built = build_stack(cfg, cfg.layers)
+    yield cfg, built
+    del built
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("token_set", [0, 1])
+def test_stack60_free_running(stack60, token_set):
+    cfg, (shape, ex, rt) = stack60
+    say(f"[stack60] persistent, token set {token_set}")
+    h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, token_set, 1)).astype(np.float32)).cuda()
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, workspace=ws, trace=True)
+    assert q.moe_read_device_status(ws) == 0
+    compare_free_running(cfg, cfg.layers, token_set, traces, h.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
+def test_stack60_oracle_fed_layers(stack60, flags):
+    """Layers 0, 17, 42 and 59 each run once on the oracle's own input."""
+    cfg, (shape, ex, rt) = stack60
+    x64 = synth.bf16_to_f64(synth.tokens(cfg, 7, 1))
+    ref = oracle.run_stack(cfg, x64, layers=cfg.layers)
+    for l in (0, 17, 42, 59):
+        h_in = ref["h"][l].astype(np.float32)           # what the GPU is given
+        exp = oracle.run_layer(cfg, l, h_in.astype(np.float64), want_intermediates=False)
+        h = torch.from_numpy(h_in).cuda()
+        ws = q.new_workspace(shape, 1, cfg.top_k)
+        tk, _ = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, layer0=l, L=1, flags=flags,
+                                          workspace=ws, trace=True)
+        assert q.moe_read_device_status(ws) == 0
+        assert np.array_equal(tk.cpu().numpy()[0], exp["idx"]), l
+        e = assert_close(h.cpu().numpy(), exp["y"], f"layer {l} output")
+        say(f"  layer {l} flags={flags}: exact top-K, output rel err {e:.2e}")
+
+
+def test_stack60_persistent_is_reproducible(stack60):
+    cfg, (shape, ex, rt) = stack60
+    x = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, 3, 1)).astype(np.float32)).cuda()
+    outs = []
+    for _ in range(2):
+        h = x.clone()
+        q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k)
+        outs.append(h)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
