@@ -185,6 +185,16 @@ int moe_expert_stack_decode(const moeq_shape* shape, const moeq_experts* experts
                             uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
                             void* workspace, void* stream);
 
+/* Which path the last successful moe_expert_stack_decode on this thread
+ * took: 1 = persistent launch, 2 = per-layer launches, 0 = none yet. */
+int moeq_last_stack_path(void);
+
+/* Diagnostic: the next persistent moe_expert_stack_decode launch writes
+ * wall-clock stamps (100 MHz device counter) of its phase boundaries, as
+ * seen by workgroup 0, to the device array `clocks` [L][n] where n is the
+ * return value (12).  The pointer is consumed by that launch. */
+int moeq_stack_clock_trace(int64_t* clocks);
+
 /* Synchronise `stream` and read the workspace status word: 0 = clean,
  * else a bitmask (1 = an expert id outside [0, E) was seen, 2 = a grid
  * barrier of the persistent stack kernel timed out).  Clears it. */

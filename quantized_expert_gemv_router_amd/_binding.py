@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.moe_q4_expert_gemv.argtypes = [S, X, _I, _P, _I, ctypes.c_uint32, _P, _I, _I, _P, _P, _P]
         L.moe_swiglu_down_combine.argtypes = [S, X, _I, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P]
         L.moe_read_device_status.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)]
+        L.moeq_last_stack_path.restype = _I
+        L.moeq_stack_clock_trace.argtypes = [_P]
         L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                               _P, _P]
         _lib = L
@@ -240,6 +242,16 @@ def moe_expert_stack_decode(shape: Shape, experts: ExpertTable, routers: RouterT
                                          k, flags, _ptr(h), _ptr(tk), _ptr(hk), _ptr(workspace),
                                          _stream(stream)))
     return (tk, hk) if trace else None
+
+
+def moeq_last_stack_path() -> int:
+    """1 = the last stack call ran the persistent launch, 2 = per-layer launches."""
+    return lib().moeq_last_stack_path()
+
+
+def moeq_stack_clock_trace(clocks: torch.Tensor) -> int:
+    """Arm the diagnostic phase clock trace (int64 device tensor [L, 12])."""
+    return lib().moeq_stack_clock_trace(_ptr(clocks))
 
 
 def moe_read_device_status(workspace: torch.Tensor, stream=None) -> int:

@@ -15,6 +15,8 @@ int down_row_blocks(int H);
 namespace {
 
 thread_local std::string g_last_error;
+thread_local int g_last_stack_path = 0;
+int64_t* g_stack_clocks = nullptr;   // diagnostic phase stamps for the next persistent launch
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -259,8 +261,13 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     a.abuf = reinterpret_cast<float*>(ws + W.st_abuf);
     a.bar = reinterpret_cast<uint32_t*>(ws + W.st_bar);
     a.status = status;
+    a.clocks = g_stack_clocks;
+    g_stack_clocks = nullptr;
     hipError_t e = launch_stack_decode(a, st);
-    if (e == hipSuccess) return ok();
+    if (e == hipSuccess) {
+      g_last_stack_path = 1;
+      return ok();
+    }
     // no persistent instantiation for this shape, or the device cannot hold
     // the whole grid at once: run the layers one launch sequence at a time
     if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
@@ -306,7 +313,15 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     if (rc) return rc;
   }
   (void)KS;
+  g_last_stack_path = 2;
   return ok();
+}
+
+int moeq_last_stack_path(void) { return g_last_stack_path; }
+
+int moeq_stack_clock_trace(int64_t* clocks) {
+  g_stack_clocks = clocks;
+  return kStackClockEvents;
 }
 
 int moe_read_device_status(void* workspace, void* stream, int32_t* status) {

@@ -108,7 +108,9 @@ struct StackArgs {
   float* abuf;                     // [K + S][I] scratch
   uint32_t* bar;                   // barrier counters (stack_barrier_words())
   int32_t* status;
+  int64_t* clocks;                 // diagnostic: [L][kStackClockEvents] wall-clock stamps of block 0, or null
 };
+constexpr int kStackClockEvents = 12;
 int stack_barrier_words();
 // hipErrorNotSupported: no persistent instantiation for this shape.
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream);

@@ -244,6 +244,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     }
   };
 
+  // diagnostic phase stamps (block 0, after a block-wide barrier)
+  auto stamp = [&](int li, int ev) {
+    if (a.clocks && b == 0) {
+      __syncthreads();
+      if (tid == 0) a.clocks[(int64_t)li * kStackClockEvents + ev] = (int64_t)wall_clock64();
+    }
+  };
+
   // prologue: first layer's router rows and shared-expert gate/up rows
   const int l0 = a.layer0;
   if (tid < S) eblob[K + tid] = blob_of(a, l0, E + tid);
@@ -253,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 
   for (int li = 0; li < a.L; ++li) {
     const int layer = l0 + li;
+    stamp(li, 0);
     // ---------------------------------------------------------- phase R
     // h -> LDS (agent-scope loads: h was written by every block)
     {
@@ -280,6 +289,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (lane == 0) ssum[wave] = ss;
     }
     __syncthreads();
+    stamp(li, 1);
     double ss = 0.0;
     for (int i = 0; i < kWaves; ++i) ss += ssum[i];
     const double inv = 1.0 / sqrt(ss / (double)H + 1e-6);
@@ -315,6 +325,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       for (int sgi = 0; sgi < NSEG; ++sgi) d += rpart[wave + sgi];
       st_agent(a.logits + r_row, d * inv);
     }
+    stamp(li, 2);
     // stage xhat (fp16 pairs) from the LDS copy of h while others finish
     {
       auto loader = [&](int, int64_t o, float* v) {
@@ -323,7 +334,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       };
       stage_batch<BITS, 1, 1>(1, H, loader, true, xp, xs, undo_x, red);
     }
+    stamp(li, 3);
     if (!bar.sync(a.status, &bar_flag)) return;
+    stamp(li, 4);
 
     // ---------------------------------------------------------- phase G
     if (wave == 0) {
@@ -351,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
     }
     __syncthreads();
+    stamp(li, 5);
     load_gu(layer, 0, K, eblob);     // routed gate/up rows
     load_down(eblob);                // down rows of every slot
     {
@@ -371,6 +385,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
     }
     __syncthreads();
+    stamp(li, 6);
     for (int t = tid; t < KS * RG; t += kThreads) {
       const int j = t / RG, i = t - j * RG, row = b + NB * i;
       if (row < I) {
@@ -378,7 +393,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         st_agent(a.abuf + (int64_t)j * I + row, g / (1.0f + __expf(-g)) * u);
       }
     }
+    stamp(li, 7);
     if (!bar.sync(a.status, &bar_flag)) return;
+    stamp(li, 8);
 
     // ---------------------------------------------------------- phase D
     {
@@ -393,6 +410,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       };
       stage_batch<BITS, 1, KSMAX>(KS, I, loader, false, ap, as, undo_a, red);
     }
+    stamp(li, 9);
     {
       const int sub = lane % LPRD;
 #pragma unroll
@@ -425,6 +443,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         st_agent(a.h + row, acc);
       }
     }
+    stamp(li, 10);
     if (last) break;   // h of the last layer is complete when the launch ends
     {
       const int next = layer + 1;
@@ -433,6 +452,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       load_router(next);
       load_gu(next, K, KS, eblob);
     }
+    stamp(li, 11);
     if (!bar.sync(a.status, &bar_flag)) return;
   }
 }

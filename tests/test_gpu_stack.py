@@ -3,10 +3,14 @@ launches) against the fp64 oracle.
 
 Free-running: the oracle and the GPU each run all layers from the same
 token; top-K must be bit-exact at every layer and the final residual stream
-within max|gpu - oracle| <= 2e-3 * max|oracle|.  Exactness is asserted only
-where the oracle's own gap between the K-th and (K+1)-th logit exceeds what
-the GPU's fp32 residual stream can move a logit (MARGIN); past a layer with
-a smaller gap both selections are valid and later layers are not compared.
+within max|gpu - oracle| <= 2e-3 * max|oracle|.  The GPU carries the
+residual stream in fp32, so its normalised input at layer l differs from the
+oracle's by some dx; a logit can then move by at most
+delta_l = max_e |Wr_e|_2 * |dx|_2 (Cauchy-Schwarz).  Where the oracle's gap
+between its K-th and (K+1)-th logits exceeds 2*delta_l the selection is
+unique and must match exactly; where it does not, any selection whose
+oracle logits are within 2*delta_l of the oracle's K-th is valid, the
+trajectories may then part, and later layers are not compared.
 Oracle-fed: the oracle's h_l is given to the GPU for one layer, and top-K
 and h_{l+1} are compared with the oracle's layer on the same input.
 """
@@ -17,11 +21,10 @@ import torch
 import oracle
 import quantized_expert_gemv_router_amd as q
 import synth
-from tests.gpu_util import TOL, assert_close, bf16_dev, say, slot_stride
+from tests.gpu_util import assert_close, bf16_dev, say, slot_stride
 
 pytestmark = pytest.mark.gpu
 
-MARGIN = 1e-3   # absolute logit gap below which two selections are both valid
 
 
 def build_stack(cfg, L):
@@ -42,23 +45,28 @@ def compare_free_running(cfg, L, token_set, traces, gpu_h):
     x64 = synth.bf16_to_f64(synth.tokens(cfg, token_set, 1))
     ref = oracle.run_stack(cfg, x64, layers=L)
     idx = tk.cpu().numpy()[:, 0, :]
-    hs = hk.cpu().numpy()[:, 0, :]
-    first_amb = L
+    hs = hk.cpu().numpy()[:, 0, :].astype(np.float64)
+    K = cfg.top_k
     for l in range(L):
-        if ref["margin"][l, 0] < MARGIN:
-            first_amb = l
-            break
-    for l in range(first_amb + 1 if first_amb < L else L):
-        if l < first_amb:
-            assert np.array_equal(idx[l], ref["idx"][l, 0]), (l, idx[l], ref["idx"][l, 0])
         assert_close(hs[l], ref["h"][l, 0], f"h input of layer {l}")
-    if first_amb == L:
-        e = assert_close(gpu_h, ref["h"][L, 0], "final h")
-        say(f"  token set {token_set}: {L} layers exact top-K, final h rel err {e:.2e}, "
-            f"min margin {ref['margin'].min():.3e}")
-    else:
-        say(f"  token set {token_set}: near-tie at layer {first_amb} "
-            f"(margin {ref['margin'][first_amb, 0]:.2e}); compared layers < {first_amb}")
+        wr = synth.bf16_to_f64(synth.router(cfg, l))
+        dx = oracle.rmsnorm(hs[l]) - oracle.rmsnorm(ref["h"][l, 0])
+        delta = np.sqrt((wr * wr).sum(axis=1)).max() * np.sqrt((dx * dx).sum())
+        logits = oracle.router_logits(oracle.shape_of(cfg), synth.router(cfg, l), oracle.rmsnorm(ref["h"][l, 0]))
+        kth = np.sort(logits)[::-1][K - 1]
+        if ref["margin"][l, 0] > 2 * delta:
+            assert np.array_equal(idx[l], ref["idx"][l, 0]), (l, idx[l], ref["idx"][l, 0], delta)
+            continue
+        # several selections are valid: each chosen expert must be within 2*delta of the K-th
+        assert np.all(logits[idx[l]] >= kth - 2 * delta), (l, idx[l], logits[idx[l]], kth, delta)
+        if not np.array_equal(idx[l], ref["idx"][l, 0]):
+            say(f"  token set {token_set}: layer {l} gap {ref['margin'][l, 0]:.2e} <= 2*delta "
+                f"{2 * delta:.2e}; valid different selection {idx[l]} vs {ref['idx'][l, 0]}; "
+                f"compared layers <= {l}")
+            return
+    e = assert_close(gpu_h, ref["h"][L, 0], "final h")
+    say(f"  token set {token_set}: {L} layers exact top-K, final h rel err {e:.2e}, "
+        f"min gap {ref['margin'].min():.3e}")
 
 
 @pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
@@ -72,6 +80,7 @@ def test_stack_small_shape(flags):
         ws = q.new_workspace(shape, 1, cfg.top_k)
         traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws,
                                            trace=True)
+        assert q.moeq_last_stack_path() == (2 if flags else 1)
         assert q.moe_read_device_status(ws) == 0
         compare_free_running(cfg, cfg.layers, ts, traces, h.cpu().numpy()[0])
 
@@ -93,27 +102,31 @@ def test_stack60_free_running(stack60, token_set):
     h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, token_set, 1)).astype(np.float32)).cuda()
     ws = q.new_workspace(shape, 1, cfg.top_k)
     traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, workspace=ws, trace=True)
+    assert q.moeq_last_stack_path() == 1
     assert q.moe_read_device_status(ws) == 0
     compare_free_running(cfg, cfg.layers, token_set, traces, h.cpu().numpy()[0])
 
 
-@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
-def test_stack60_oracle_fed_layers(stack60, flags):
-    """Layers 0, 17, 42 and 59 each run once on the oracle's own input."""
+@pytest.mark.parametrize("flags,layers", [(0, tuple(range(60))), (q.F_STACK_LAYERWISE, (0, 17, 42, 59))])
+def test_stack60_oracle_fed_layers(stack60, flags, layers):
+    """Each listed layer runs once on the oracle's own input h_l (rounded to
+    the GPU's fp32): top-K must be bit-exact and h_{l+1} within tolerance."""
     cfg, (shape, ex, rt) = stack60
     x64 = synth.bf16_to_f64(synth.tokens(cfg, 7, 1))
     ref = oracle.run_stack(cfg, x64, layers=cfg.layers)
-    for l in (0, 17, 42, 59):
+    worst = 0.0
+    for l in layers:
         h_in = ref["h"][l].astype(np.float32)           # what the GPU is given
         exp = oracle.run_layer(cfg, l, h_in.astype(np.float64), want_intermediates=False)
         h = torch.from_numpy(h_in).cuda()
         ws = q.new_workspace(shape, 1, cfg.top_k)
         tk, _ = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, layer0=l, L=1, flags=flags,
                                           workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == (2 if flags else 1)
         assert q.moe_read_device_status(ws) == 0
         assert np.array_equal(tk.cpu().numpy()[0], exp["idx"]), l
-        e = assert_close(h.cpu().numpy(), exp["y"], f"layer {l} output")
-        say(f"  layer {l} flags={flags}: exact top-K, output rel err {e:.2e}")
+        worst = max(worst, assert_close(h.cpu().numpy(), exp["y"], f"layer {l} output"))
+    say(f"  {len(layers)} layers flags={flags}: exact top-K on each, worst output rel err {worst:.2e}")
 
 
 def test_stack60_persistent_is_reproducible(stack60):
