@@ -193,3 +193,72 @@ __device__ __forceinline__ void set_status(int32_t* status, int32_t bits) {
 }
 
 }  // namespace moeq
+
+namespace moeq {
+
+// ------------------------------------------------- DPP wave reductions
+// Full-wave reductions with DPP lane moves (no LDS crossbar round trip):
+// xor-1 and xor-2 within quads, half-row and row mirrors, then row
+// broadcasts 15 and 31 fold the four rows; lane 63 ends with the result,
+// which v_readlane makes uniform.  Fixed combination order, so a sum is
+// bit-identical run to run.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_move_f64(double old, double v) {
+  const int2 o = __builtin_bit_cast(int2, old), x = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = dpp_move<CTRL, ROW_MASK>(o.x, x.x);
+  r.y = dpp_move<CTRL, ROW_MASK>(o.y, x.y);
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const int2 x = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_readlane(x.x, lane);
+  r.y = __builtin_amdgcn_readlane(x.y, lane);
+  return __builtin_bit_cast(double, r);
+}
+
+// Sum over the wave, returned in every lane (uniform).
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_move_f64<kDppQuadXor1>(0.0, v);
+  v += dpp_move_f64<kDppQuadXor2>(0.0, v);
+  v += dpp_move_f64<kDppHalfMirror>(0.0, v);
+  v += dpp_move_f64<kDppMirror>(0.0, v);
+  v += dpp_move_f64<kDppBcast15, 0xA>(0.0, v);
+  v += dpp_move_f64<kDppBcast31, 0xC>(0.0, v);
+  return readlane_f64(v, 63);
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(dpp_move<kDppQuadXor1>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppQuadXor2>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppHalfMirror>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppMirror>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppBcast15, 0xA>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppBcast31, 0xC>(0, __float_as_int(v)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, __int_as_float(dpp_move<kDppQuadXor1>(__float_as_int(v), __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppQuadXor2>(__float_as_int(v), __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppHalfMirror>(__float_as_int(v), __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppMirror>(__float_as_int(v), __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppBcast15, 0xA>(__float_as_int(v), __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppBcast31, 0xC>(__float_as_int(v), __float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+}  // namespace moeq

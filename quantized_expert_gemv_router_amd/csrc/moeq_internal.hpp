@@ -110,7 +110,7 @@ struct StackArgs {
   int32_t* status;
   int64_t* clocks;                 // diagnostic: [L][kStackClockEvents] wall-clock stamps of block 0, or null
 };
-constexpr int kStackClockEvents = 12;
+constexpr int kStackClockEvents = 16;
 int stack_barrier_words();
 // hipErrorNotSupported: no persistent instantiation for this shape.
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream);

@@ -1,9 +1,9 @@
 // One decode token through L stacked MoE layers in a single persistent
 // launch (Flash-MoE, fr.news.hada.io, "Deferred GPU Expert Compute": the
 // combined output, norm and residual stay on the GPU and feed the next
-// layer; the measured ~30 us per-layer submission cost that pre-encoding
-// removed on the openclawradar.com/ru page, "CMD2", is what a single
-// launch avoids here).
+// layer; removing per-layer submission cost, ~30 us per layer on the Metal
+// engine of the openclawradar.com/ru page ("CMD2"), is what a single
+// launch does here).
 //
 // Per layer l, with h the residual stream (fp32, resident):
 //   xhat = h / sqrt(mean(h^2) + 1e-6)           unit-weight RMS norm
@@ -13,27 +13,28 @@
 //
 // Grid: one workgroup of 8 waves per CU, all co-resident (cooperative
 // launch).  Three grid barriers per layer separate the all-to-all steps:
-// h complete -> router rows; logits complete -> top-K and gate/up;
-// activations complete -> down and combine.  Everything whose address is
-// known early is requested before the barrier that precedes its use: the
-// next layer's router rows and shared-expert gate/up rows during the
-// previous layer's last barrier, and the down rows of every selected expert
-// right after top-K.  Each workgroup keeps its own copy of h in LDS for
-// the norm, the router dots and the gate/up staging, and owns a fixed set
-// of rows in every matrix:
+//   A: h complete      -> each block reads h, router rows, xhat staging
+//   B: logits complete -> top-K (every block, redundantly), gate/up
+//   C: activations a   -> down rows and the combine
+// Loads are issued as early as their addresses are known: the router and
+// shared-expert pointers of every layer are cached in LDS at start, the next
+// layer's router rows, shared-expert gate/up rows and pointer-table row are
+// requested before barrier A, and the shared expert's gate/up is computed
+// before barrier B, so after top-K only the routed experts' rows remain on
+// the critical path (their down rows are requested right after their
+// gate/up rows).  Each block owns fixed rows of every matrix:
 //   router rows  e = b + NB*i, split into 8/RW segments across waves;
-//   gate/up rows r = b + NB*i of every selected expert (so a = silu(g)*u
-//   is formed locally);
-//   down rows    r = b + NB*i of every selected expert (so the combine is
-//   a per-row sum in registers, in slot order, no atomics).
-// Cross-workgroup data (logits, activations, h) moves with agent-scope
+//   gate/up rows r = b + NB*i of every selected expert (a = silu(g)*u is
+//   formed locally);
+//   down rows    r = b + NB*i of every selected expert (the combine is a
+//   per-row sum in slot order, no atomics).
+// Cross-block data (logits, activations, h) moves with agent-scope
 // write-through stores and loads; each barrier waits for the caller's
-// stores to complete before arriving.  Barriers are two-level counter trees
-// with a bounded spin: on time-out a workgroup sets the status word and an
-// abort flag and every workgroup leaves the kernel.
+// stores to complete before arriving.  Barriers are two-level counter
+// trees with bounded spins: on time-out a block sets the status word and
+// an abort flag, and every block leaves the kernel.
 #include "moeq_device.hpp"
 #include "moeq_internal.hpp"
-#include "staging.hpp"
 #include "topk.hpp"
 
 namespace moeq {
@@ -41,10 +42,12 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGroups = 8;                 // barrier tree: groups of workgroups
+constexpr int kGroups = 8;                 // barrier tree: groups of blocks
 constexpr int kBarWords = 32 * (kGroups + 2);
 constexpr int kSpinLimit = 1 << 18;        // polls before a barrier gives up
 constexpr int kMaxKS = 8;                  // selected + shared experts per layer
+constexpr int kMaxLayers = 128;            // per persistent launch
+constexpr int kTblPer = 8;                 // pointer-table entries per thread (E + S <= 4096)
 
 // ------------------------------------------------------------------ barrier
 struct GridBarrier {
@@ -82,21 +85,15 @@ struct GridBarrier {
   }
 };
 
-// --------------------------------------------------------------- geometry
-template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD>
-struct StackCfg {
-  static constexpr int PC = Pack<BITS>::kPerChunk;
-  static constexpr int PPC = PC / 2;
-  static constexpr int RPSD = 64 / LPRD;   // down rows per wave step
-};
-
+// ------------------------------------------------------------------ layout
 struct StackLds {
-  int hs, xp, xs, ap, as, gres, dres, lg, total;
+  int hs, xp, xs, ap, as, gres, dres, lg, tbl, total;
 };
 
 __host__ __device__ inline int al16(int v) { return (v + 15) & ~15; }
 
-__host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int KS, int PC, int RG, int RD) {
+__host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S, int KS, int PC,
+                                                     int RG, int RD) {
   StackLds L;
   L.hs = 0;
   L.xp = al16(L.hs + 4 * H);
@@ -106,45 +103,69 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int KS
   L.gres = al16(L.as + 4 * KS * (I / PC));
   L.dres = al16(L.gres + 4 * KS * 2 * RG);
   L.lg = al16(L.dres + 4 * KS * RD);
-  L.total = al16(L.lg + 8 * E);
+  L.tbl = al16(L.lg + 8 * E);
+  L.total = al16(L.tbl + 8 * (E + S));
   return L;
 }
 
-__device__ __forceinline__ const uint8_t* blob_of(const StackArgs& a, int layer, int e) {
-  return static_cast<const uint8_t*>(a.blobs[(int64_t)layer * (a.E + a.S) + e]);
+// Stage one word (PW values) into fp16 pairs at pairs + w*PW/2 and return
+// the sum of the rounded values (the caller folds the four words of a
+// chunk with lane shuffles).  The fp32 products and the packed pairs are
+// pinned so the sum adds exactly the stored fp16 values (the bias term
+// b*X of the magic-exponent dot cancels 1024*X).
+template <int BITS>
+__device__ __forceinline__ float stage_word(const float* v, float f, uint32_t* pairs, int w) {
+  constexpr int PW = Pack<BITS>::kPerWord, HP = PW / 2;
+  uint32_t pr[HP];
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < HP; ++j) {
+    float lo = v[j] * f, hi = v[j + HP] * f;
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    pr[j] = pack_half2(lo, hi);
+    asm volatile("" : "+v"(pr[j]));
+    s += half_lo(pr[j]) + half_hi(pr[j]);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(pairs + (int64_t)w * HP);
+#pragma unroll
+  for (int j = 0; j < HP / 4; ++j) dst[j] = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
+  return s;
 }
 
-template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int KSMAX>
+template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW>
 __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
-  using C = StackCfg<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD>;
-  constexpr int PC = C::PC, PPC = C::PPC, RPSD = C::RPSD;
+  constexpr int PC = Pack<BITS>::kPerChunk, PPC = PC / 2, PW = Pack<BITS>::kPerWord;
+  constexpr int RPSD = 64 / LPRD;          // down rows per wave step
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ double rpart[kWaves];
-  __shared__ float red[2 * kMaxKS * kWaves];
-  __shared__ float undo_x[1], undo_a[kMaxKS];
+  __shared__ double ssum[kWaves];
+  __shared__ float hmax[kWaves];
+  __shared__ uint32_t amax[kMaxKS];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
   __shared__ float selw[MOEQ_MAX_TOPK];
   __shared__ const uint8_t* eblob[kMaxKS];
-  __shared__ double ssum[kWaves];
+  __shared__ const uint16_t* rtr[kMaxLayers];
+  __shared__ const uint8_t* shp[kMaxLayers];
+  __shared__ float undo_x;
   __shared__ int bar_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NB = gridDim.x, b = blockIdx.x;
-  const int H = a.H, I = a.I, E = a.E, K = a.K, S = a.S, KS = K + S;
+  const int H = a.H, I = a.I, E = a.E, K = a.K, S = a.S, KS = K + S, L = a.L;
   const int nchG = H / PC, nchD = I / PC;
-
-  // LDS carve-up (byte offsets, 16-byte aligned; see stack_lds_layout)
   const int RG = (I + NB - 1) / NB, RD = (H + NB - 1) / NB;
-  const StackLds L_ = stack_lds_layout(H, I, E, KS, PC, RG, RD);
-  float* hs = reinterpret_cast<float*>(smem + L_.hs);          // [H]
-  uint32_t* xp = reinterpret_cast<uint32_t*>(smem + L_.xp);    // [H/2]
-  float* xs = reinterpret_cast<float*>(smem + L_.xs);          // [H/PC]
-  uint32_t* ap = reinterpret_cast<uint32_t*>(smem + L_.ap);    // [KS][I/2]
-  float* as = reinterpret_cast<float*>(smem + L_.as);          // [KS][I/PC]
-  float* gres = reinterpret_cast<float*>(smem + L_.gres);      // [KS][2][RG]
-  float* dres = reinterpret_cast<float*>(smem + L_.dres);      // [KS][RD]
-  double* lg = reinterpret_cast<double*>(smem + L_.lg);        // [E]
+
+  const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD);
+  float* hs = reinterpret_cast<float*>(smem + LL.hs);               // [H]
+  uint32_t* xp = reinterpret_cast<uint32_t*>(smem + LL.xp);         // [H/2]
+  float* xs = reinterpret_cast<float*>(smem + LL.xs);               // [H/PC]
+  uint32_t* ap = reinterpret_cast<uint32_t*>(smem + LL.ap);         // [KS][I/2]
+  float* as = reinterpret_cast<float*>(smem + LL.as);               // [KS][I/PC]
+  float* gres = reinterpret_cast<float*>(smem + LL.gres);           // [KS][2][RG]
+  float* dres = reinterpret_cast<float*>(smem + LL.dres);           // [KS][RD]
+  double* lg = reinterpret_cast<double*>(smem + LL.lg);             // [E]
+  const uint8_t** tbl = reinterpret_cast<const uint8_t**>(smem + LL.tbl);  // [E + S], this layer
 
   GridBarrier bar;
   bar.base = a.bar;
@@ -154,20 +175,20 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   bar.epoch = 0;
 
   // router geometry: RW rows per block, 8/RW segments per row
-  const int RW = a.router_rows;                 // power of two <= 8
+  const int RW = a.router_rows;
   const int NSEG = kWaves / RW;
   const int r_row = b + NB * (wave / NSEG);
   const int r_seg = wave % NSEG;
-  const int seg_len = H / NSEG;                 // bf16 elements per segment
-  const int seg_ch = seg_len / 8;               // 16-byte chunks per segment
+  const int seg_len = H / NSEG;
+  const int seg_ch = seg_len / 8;
+  const int tbl_n = E + S;
 
-  // gate/up tasks of this wave: t = wave*RPWG + m -> (slot j, section, row i)
-  // down tasks: u = (wave*STEPSD + s)*RPSD + lane/LPRD -> (slot j, row i)
   u32x4 wr[CPLR];
   u32x4 qg[RPWG][CPLG];
   uint32_t sg[RPWG][CPLG];
   u32x4 qd[STEPSD][CPLD];
   uint32_t sd[STEPSD][CPLD];
+  const uint8_t* tnext[kTblPer];   // next layer's pointer-table row, in flight
 
   auto gu_task = [&](int m, int& j, int& sec, int& row) -> bool {
     const int t = wave * RPWG + m;
@@ -176,9 +197,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     row = b + NB * (t % RG);
     return j < KS && row < I;
   };
-  auto load_router = [&](int layer) {
+  auto load_router = [&](int li) {
     const bool ok = r_row < E;
-    const uint16_t* w = ok ? a.routers[layer] + (int64_t)r_row * H + (int64_t)r_seg * seg_len : nullptr;
+    const uint16_t* w = ok ? rtr[li] + (int64_t)r_row * H + (int64_t)r_seg * seg_len : nullptr;
 #pragma unroll
     for (int c = 0; c < CPLR; ++c) {
       const int cc = lane + 64 * c;
@@ -186,8 +207,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
                                   : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // gate/up rows of slots in [jlo, jhi) (the shared slots are known early)
-  auto load_gu = [&](int layer, int jlo, int jhi, const uint8_t* const* blobs_by_slot) {
+  // gate/up rows of the tasks whose slot is in [jlo, jhi)
+  auto load_gu = [&](int jlo, int jhi) {
     const int64_t row_bytes = (int64_t)H * BITS / 8;
     const int gpr = H / 64;
 #pragma unroll
@@ -195,18 +216,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       int j, sec, row;
       const bool ok = gu_task(m, j, sec, row);
       if (!(ok && j >= jlo && j < jhi)) continue;
-      const uint8_t* blob = blobs_by_slot[j];
-      if (blob == nullptr) {   // missing table entry: contribute nothing
-#pragma unroll
-        for (int c = 0; c < CPLG; ++c) { qg[m][c] = u32x4{0u, 0u, 0u, 0u}; sg[m][c] = 0u; }
-        continue;
-      }
-      const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8);
+      const uint8_t* blob = eblob[j];
       const int r = sec * I + row;   // row of [gate; up]
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
         const int cc = lane + 64 * c;
-        if (cc < nchG) {
+        if (blob != nullptr && cc < nchG) {
+          const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8);
           qg[m][c] = load_stream(reinterpret_cast<const u32x4*>(blob + r * row_bytes) + cc);
           sg[m][c] = load_stream(sb + (int64_t)r * gpr + (cc * PC) / 64);
         } else {
@@ -215,9 +231,25 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         }
       }
     }
-    (void)layer;
   };
-  auto load_down = [&](const uint8_t* const* blobs_by_slot) {
+  auto gu_dots = [&](int jlo, int jhi) {
+    const float ux = undo_x;
+#pragma unroll
+    for (int m = 0; m < RPWG; ++m) {
+      int j, sec, row;
+      const bool ok = gu_task(m, j, sec, row);
+      if (!(ok && j >= jlo && j < jhi)) continue;
+      float part = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPLG; ++c) {
+        const int cc = lane + 64 * c;
+        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
+      }
+      const float v = wave_sum_dpp(part) * ux;
+      if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
+    }
+  };
+  auto load_down = [&]() {
     const int64_t row_bytes = (int64_t)I * BITS / 8;
     const int gpr = I / 64;
     const int sub = lane % LPRD;
@@ -225,12 +257,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int s = 0; s < STEPSD; ++s) {
       const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
       const int j = u / RD, row = b + NB * (u % RD);
-      const bool ok = j < KS && row < H && blobs_by_slot[j < KS ? j : 0] != nullptr;
+      const uint8_t* blob = j < KS ? eblob[j] : nullptr;
+      const bool ok = j < KS && row < H && blob != nullptr;
 #pragma unroll
       for (int c = 0; c < CPLD; ++c) {
         const int cc = sub + LPRD * c;
         if (ok && cc < nchD) {
-          const uint8_t* blob = blobs_by_slot[j];
           const int64_t qoff = 2 * (int64_t)H * I * BITS / 8;
           const uint32_t* sb = reinterpret_cast<const uint32_t*>(
               blob + 3 * (int64_t)H * I * BITS / 8 + 2 * (int64_t)H * I / 64 * 4);
@@ -243,7 +275,21 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
     }
   };
-
+  auto load_tbl_row = [&](int layer) {   // into registers; stored to LDS after the next barrier
+    const void* const* row = a.blobs + (int64_t)layer * tbl_n;
+#pragma unroll
+    for (int i = 0; i < kTblPer; ++i) {
+      const int e = tid + i * kThreads;
+      tnext[i] = e < tbl_n ? static_cast<const uint8_t*>(row[e]) : nullptr;
+    }
+  };
+  auto store_tbl_row = [&]() {
+#pragma unroll
+    for (int i = 0; i < kTblPer; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < tbl_n) tbl[e] = tnext[i];
+    }
+  };
   // diagnostic phase stamps (block 0, after a block-wide barrier)
   auto stamp = [&](int li, int ev) {
     if (a.clocks && b == 0) {
@@ -251,47 +297,59 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (tid == 0) a.clocks[(int64_t)li * kStackClockEvents + ev] = (int64_t)wall_clock64();
     }
   };
+  // diagnostic stamps from wave 0 alone (no block barrier)
+  auto stamp0 = [&](int li, int ev) {
+    if (a.clocks && b == 0 && tid == 0) a.clocks[(int64_t)li * kStackClockEvents + ev] = (int64_t)wall_clock64();
+  };
 
-  // prologue: first layer's router rows and shared-expert gate/up rows
-  const int l0 = a.layer0;
-  if (tid < S) eblob[K + tid] = blob_of(a, l0, E + tid);
+  // prologue: router and shared-expert pointers of every layer, first rows
+  for (int li = tid; li < L; li += kThreads) {
+    rtr[li] = a.routers[a.layer0 + li];
+    shp[li] = S > 0 ? static_cast<const uint8_t*>(a.blobs[(int64_t)(a.layer0 + li) * tbl_n + E]) : nullptr;
+  }
+  load_tbl_row(a.layer0);
   __syncthreads();
-  load_router(l0);
-  load_gu(l0, K, KS, eblob);
+  if (tid < S) eblob[K + tid] = shp[0];
+  __syncthreads();
+  load_router(0);
+  load_gu(K, KS);
 
-  for (int li = 0; li < a.L; ++li) {
-    const int layer = l0 + li;
+  for (int li = 0; li < L; ++li) {
     stamp(li, 0);
-    // ---------------------------------------------------------- phase R
-    // h -> LDS (agent-scope loads: h was written by every block)
+    // ------------------------------------------------------------ phase R
+    // h -> LDS with sum of squares (fp64) and max |h|
     {
-      constexpr int kMaxPer = MOEQ_MAX_HIDDEN / 2 / kThreads;   // u64 per thread
-      uint64_t hv[kMaxPer];
+      uint64_t hv[HW];
       const uint64_t* src = reinterpret_cast<const uint64_t*>(a.h);
 #pragma unroll
-      for (int i = 0; i < kMaxPer; ++i) {
+      for (int i = 0; i < HW; ++i) {
         const int p = tid + i * kThreads;
         hv[i] = (2 * p < H) ? ld_agent(src + p) : 0ull;
       }
+      store_tbl_row();
       double ss = 0.0;
+      float mx = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kMaxPer; ++i) {
+      for (int i = 0; i < HW; ++i) {
         const int p = tid + i * kThreads;
         if (2 * p < H) {
           const float lo = __uint_as_float((uint32_t)hv[i]), hi = __uint_as_float((uint32_t)(hv[i] >> 32));
-          hs[2 * p] = lo;
-          hs[2 * p + 1] = hi;
+          *reinterpret_cast<float2*>(hs + 2 * p) = make_float2(lo, hi);
           ss = fma((double)lo, (double)lo, ss);
           ss = fma((double)hi, (double)hi, ss);
+          mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
         }
       }
-      ss = wave_sum_f64(ss);
-      if (lane == 0) ssum[wave] = ss;
+      ss = wave_sum_f64_dpp(ss);
+      mx = wave_max_dpp(mx);
+      if (lane == 0) { ssum[wave] = ss; hmax[wave] = mx; }
     }
     __syncthreads();
     stamp(li, 1);
     double ss = 0.0;
-    for (int i = 0; i < kWaves; ++i) ss += ssum[i];
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) { ss += ssum[i]; mx = fmaxf(mx, hmax[i]); }
     const double inv = 1.0 / sqrt(ss / (double)H + 1e-6);
 
     // router: fp64 partial dot of this wave's segment
@@ -316,8 +374,30 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           }
         }
       }
-      acc = wave_sum_f64(acc);
+      acc = wave_sum_f64_dpp(acc);
       if (lane == 0) rpart[wave] = acc;
+    }
+    // xhat -> fp16 pairs, one packed word per thread; the norm and the
+    // rescale come from the h pass above, so no further reductions
+    {
+      const float mul = (float)inv;
+      const float p = pow2_stage_factor(mx * mul);
+      const float f = mul * p;
+      if (tid == 0) undo_x = 1.0f / p;
+      const int nw = H / PW;
+      for (int w0 = 0; w0 < nw; w0 += kThreads) {
+        const int w = w0 + tid;
+        float s = 0.0f;
+        if (w < nw) {
+          float v[PW];
+#pragma unroll
+          for (int j = 0; j < PW; ++j) v[j] = hs[w * PW + j];
+          s = stage_word<BITS>(v, f, xp, w);
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if ((tid & 3) == 0 && w < nw) xs[w >> 2] = s;
+      }
     }
     __syncthreads();
     if (lane == 0 && r_seg == 0 && r_row < E) {
@@ -326,19 +406,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       st_agent(a.logits + r_row, d * inv);
     }
     stamp(li, 2);
-    // stage xhat (fp16 pairs) from the LDS copy of h while others finish
-    {
-      auto loader = [&](int, int64_t o, float* v) {
-#pragma unroll
-        for (int j = 0; j < Pack<BITS>::kPerWord; ++j) v[j] = hs[o + j];
-      };
-      stage_batch<BITS, 1, 1>(1, H, loader, true, xp, xs, undo_x, red);
-    }
+    gu_dots(K, KS);                 // the shared expert's rows are already here
     stamp(li, 3);
     if (!bar.sync(a.status, &bar_flag)) return;
     stamp(li, 4);
 
-    // ---------------------------------------------------------- phase G
+    // ------------------------------------------------------------ phase G
     if (wave == 0) {
       for (int base = 0; base < E; base += 64 * 8) {
         double v[8];
@@ -354,36 +427,25 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         }
       }
       __builtin_amdgcn_wave_barrier();
-      wave_topk(lg, E, K, sel, selv);
+      stamp0(li, 12);
+      wave_topk_dpp(lg, E, K, sel, selv);
+      stamp0(li, 13);
       const float w = wave_softmax_weight(lg, E, K, selv, a.no_renorm != 0);
+      stamp0(li, 14);
       if (lane < K) {
         selw[lane] = w;
-        eblob[lane] = blob_of(a, layer, sel[lane]);
-        if (eblob[lane] == nullptr) set_status(a.status, kStatusBadExpert);
+        const uint8_t* bp = tbl[sel[lane]];
+        eblob[lane] = bp;
+        if (bp == nullptr) set_status(a.status, kStatusBadExpert);
         if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = sel[lane];
       }
     }
+    if (tid < KS) amax[tid] = 0u;
     __syncthreads();
     stamp(li, 5);
-    load_gu(layer, 0, K, eblob);     // routed gate/up rows
-    load_down(eblob);                // down rows of every slot
-    {
-      const float ux = undo_x[0];
-#pragma unroll
-      for (int m = 0; m < RPWG; ++m) {
-        int j, sec, row;
-        const bool ok = gu_task(m, j, sec, row);
-        if (!ok) continue;
-        float part = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CPLG; ++c) {
-          const int cc = lane + 64 * c;
-          if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
-        }
-        const float v = wave_sum(part) * ux;
-        if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
-      }
-    }
+    load_gu(0, K);                   // routed gate/up rows
+    gu_dots(0, K);
+    load_down();                     // down rows of every slot, used after barrier C
     __syncthreads();
     stamp(li, 6);
     for (int t = tid; t < KS * RG; t += kThreads) {
@@ -397,19 +459,42 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     if (!bar.sync(a.status, &bar_flag)) return;
     stamp(li, 8);
 
-    // ---------------------------------------------------------- phase D
+    // ------------------------------------------------------------ phase D
+    // activations: one packed word of one slot per thread
     {
-      auto loader = [&](int m, int64_t o, float* v) {
-        const float* src = a.abuf + (int64_t)m * I + o;
+      const int nwa = I / PW;
+      const int total = KS * nwa;
+      for (int t0 = 0; t0 < total; t0 += kThreads) {
+        const int t = t0 + tid;
+        const bool ok = t < total;
+        const int m = ok ? t / nwa : 0, w = ok ? t - m * nwa : 0;
+        float v[PW];
+        if (ok) {
+          const uint64_t* src = reinterpret_cast<const uint64_t*>(a.abuf + (int64_t)m * I + (int64_t)w * PW);
+          uint64_t raw[PW / 2];
 #pragma unroll
-        for (int j = 0; j < Pack<BITS>::kPerWord; j += 2) {
-          const uint64_t p = ld_agent(reinterpret_cast<const uint64_t*>(src + j));
-          v[j] = __uint_as_float((uint32_t)p);
-          v[j + 1] = __uint_as_float((uint32_t)(p >> 32));
+          for (int j = 0; j < PW / 2; ++j) raw[j] = ld_agent(src + j);
+          float lm = 0.0f;
+#pragma unroll
+          for (int j = 0; j < PW / 2; ++j) {
+            v[2 * j] = __uint_as_float((uint32_t)raw[j]);
+            v[2 * j + 1] = __uint_as_float((uint32_t)(raw[j] >> 32));
+            lm = fmaxf(lm, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+          }
+          atomicMax(&amax[m], __float_as_uint(lm));   // non-negative floats order as integers
         }
-      };
-      stage_batch<BITS, 1, KSMAX>(KS, I, loader, false, ap, as, undo_a, red);
+        __syncthreads();
+        float s = 0.0f;
+        if (ok) {
+          const float p = pow2_stage_factor(__uint_as_float(amax[m]));
+          s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w);
+        }
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        if (ok && (tid & 3) == 0) as[m * nchD + (w >> 2)] = s;
+      }
     }
+    __syncthreads();
     stamp(li, 9);
     {
       const int sub = lane % LPRD;
@@ -427,12 +512,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
             part += chunk_affine(chunk_dot<BITS>(qd[s][c], ap + (int64_t)jj * (I / 2) + cc * PPC), sd[s][c],
                                  as[jj * nchD + cc]);
         }
-        const float d = group_sum(part, LPRD) * undo_a[jj];
+        const float undo = 1.0f / pow2_stage_factor(__uint_as_float(amax[jj]));
+        const float d = group_sum(part, LPRD) * undo;
         if (ok && sub == 0) dres[j * RD + i] = d;
       }
     }
     __syncthreads();
-    const bool last = li + 1 == a.L;
     for (int i = tid; i < RD; i += kThreads) {
       const int row = b + NB * i;
       if (row < H) {
@@ -444,14 +529,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
     }
     stamp(li, 10);
-    if (last) break;   // h of the last layer is complete when the launch ends
-    {
-      const int next = layer + 1;
-      if (tid < S) eblob[K + tid] = blob_of(a, next, E + tid);
-      __syncthreads();
-      load_router(next);
-      load_gu(next, K, KS, eblob);
-    }
+    if (li + 1 == L) break;   // the last layer's h is complete when the launch ends
+    // next layer: router rows, shared-expert gate/up rows, pointer-table row
+    if (tid < S) eblob[K + tid] = shp[li + 1];
+    __syncthreads();
+    load_router(li + 1);
+    load_gu(K, KS);
+    load_tbl_row(a.layer0 + li + 1);
     stamp(li, 11);
     if (!bar.sync(a.status, &bar_flag)) return;
   }
@@ -461,13 +545,13 @@ __global__ void reset_barrier_kernel(uint32_t* bar) {
   for (int i = threadIdx.x; i < kBarWords; i += blockDim.x) bar[i] = 0u;
 }
 
-template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int KSMAX>
+template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW>
 hipError_t launch_t(const StackArgs& a, int nb, size_t lds, hipStream_t stream) {
   hipLaunchKernelGGL(reset_barrier_kernel, dim3(1), dim3(256), 0, stream, a.bar);
   StackArgs args = a;
   void* params[] = {&args};
   return hipLaunchCooperativeKernel(
-      reinterpret_cast<const void*>(&stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, KSMAX>),
+      reinterpret_cast<const void*>(&stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW>),
       dim3(nb), dim3(kThreads), params, (unsigned int)lds, stream);
 }
 
@@ -481,22 +565,24 @@ int device_cus() {
   return n;
 }
 
-// Does instantiation <BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, KSMAX>
-// cover this shape on nb blocks?
+// Does instantiation <BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW> cover
+// this shape on nb blocks?
 struct Geometry {
-  int nb, rw, H, I, E, KS, bits;
-  bool fits(int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int KSMAX) const {
-    if (bits != BITS || KS > KSMAX) return false;
+  int nb, rw, H, I, E, S, KS, bits;
+  bool fits(int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW) const {
+    if (bits != BITS) return false;
     const int PC = 128 / BITS;
-    const int seg_ch = H / (kWaves / rw) / 8;
-    if (seg_ch > 64 * CPLR || (H / (kWaves / rw)) % 8) return false;
+    const int seg = H / (kWaves / rw);
+    if (seg % 8 || seg / 8 > 64 * CPLR) return false;
     if (H / PC > 64 * CPLG) return false;
     const int RG = (I + nb - 1) / nb, RD = (H + nb - 1) / nb;
     if (KS * 2 * RG > kWaves * RPWG) return false;
     const int nchd = I / PC;
     if (nchd > LPRD * CPLD) return false;
+    if (KS * (I * BITS / 32) > kThreads) return false;   // one activation word per thread
     if (KS * RD > kWaves * STEPSD * (64 / LPRD)) return false;
-    if (H * BITS / 32 > kThreads || I * BITS / 32 > kThreads) return false;   // one staged word per thread
+    if (H > 2 * kThreads * HW) return false;
+    if (E + S > kTblPer * kThreads) return false;
     return true;
   }
 };
@@ -507,12 +593,12 @@ int stack_barrier_words() { return kBarWords; }
 
 // Geometry check and dispatch.  Returns hipErrorNotSupported (without
 // launching) when no persistent instantiation covers the shape; the caller
-// then runs the layers one launch at a time.
+// then runs the layers one launch sequence at a time.
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   const int nb = device_cus();
   if (nb < 1) return hipErrorNoDevice;
   const int KS = a.K + a.S;
-  if (a.K < 1 || KS > kMaxKS) return hipErrorNotSupported;
+  if (a.K < 1 || KS > kMaxKS || a.L > kMaxLayers) return hipErrorNotSupported;
   const int rw_need = (a.E + nb - 1) / nb;
   int rw = 1;
   while (rw < rw_need) rw <<= 1;
@@ -520,14 +606,14 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   a.router_rows = rw;
   const int PC = 128 / a.bits;
   const int RG = (a.I + nb - 1) / nb, RD = (a.H + nb - 1) / nb;
-  const size_t lds = (size_t)stack_lds_layout(a.H, a.I, a.E, KS, PC, RG, RD).total;
+  const size_t lds = (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD).total;
   if (lds > 96 * 1024) return hipErrorNotSupported;
-  const Geometry g{nb, rw, a.H, a.I, a.E, KS, a.bits};
-  // hidden 4096, intermediate 1024, 512 experts on 256 CUs, 4-bit K+S <= 4
-  // or 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
+  const Geometry g{nb, rw, a.H, a.I, a.E, a.S, KS, a.bits};
+  // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,
+  // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
   if (g.fits(4, 2, 2, 4, 32, 1, 4, 4)) return launch_t<4, 2, 2, 4, 32, 1, 4, 4>(a, nb, lds, stream);
-  if (g.fits(2, 2, 1, 5, 16, 1, 3, 5)) return launch_t<2, 2, 1, 5, 16, 1, 3, 5>(a, nb, lds, stream);
-  if (g.fits(4, 1, 1, 1, 4, 1, 1, 4)) return launch_t<4, 1, 1, 1, 4, 1, 1, 4>(a, nb, lds, stream);
+  if (g.fits(2, 2, 1, 5, 16, 1, 3, 4)) return launch_t<2, 2, 1, 5, 16, 1, 3, 4>(a, nb, lds, stream);
+  if (g.fits(4, 1, 1, 1, 4, 1, 1, 1)) return launch_t<4, 1, 1, 1, 4, 1, 1, 1>(a, nb, lds, stream);
   return hipErrorNotSupported;
 }
 

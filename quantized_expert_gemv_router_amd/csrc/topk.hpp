@@ -37,6 +37,40 @@ __device__ __forceinline__ void wave_topk(const double* lg, int E, int K, int* s
   __builtin_amdgcn_wave_barrier();
 }
 
+// One wave, DPP lane moves: same selection as wave_topk.  Each lane holds
+// its best untaken logit; six DPP steps fold the (value, index) pairs so
+// lane 63 holds the winner, which readlane makes uniform.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void argmax_step(double& v, int& i) {
+  const double ov = dpp_move_f64<CTRL, ROW_MASK>(v, v);
+  const int oi = dpp_move<CTRL, ROW_MASK>(i, i);
+  if (ranks_before(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+__device__ __forceinline__ void wave_topk_dpp(const double* lg, int E, int K, int* sel, double* selv) {
+  const int lane = threadIdx.x & 63;
+  uint64_t taken = 0;
+  for (int r = 0; r < K; ++r) {
+    double bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int m = 0, e = lane; e < E; ++m, e += 64) {
+      const double v = lg[e];
+      if (!((taken >> m) & 1) && ranks_before(v, e, bv, bi)) { bv = v; bi = e; }
+    }
+    argmax_step<kDppQuadXor1>(bv, bi);
+    argmax_step<kDppQuadXor2>(bv, bi);
+    argmax_step<kDppHalfMirror>(bv, bi);
+    argmax_step<kDppMirror>(bv, bi);
+    argmax_step<kDppBcast15, 0xA>(bv, bi);
+    argmax_step<kDppBcast31, 0xC>(bv, bi);
+    bi = __builtin_amdgcn_readlane(bi, 63);
+    bv = readlane_f64(bv, 63);
+    if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
+    if (lane == 0) { sel[r] = bi; selv[r] = bv; }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // One wave: softmax weights of the selection (fp64, rounded to fp32):
 // over the K selected logits, or (no_renorm) the full softmax over all E
 // logits read at the selected experts.  Returns the weight of lane's slot.
