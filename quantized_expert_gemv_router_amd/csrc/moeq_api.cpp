@@ -92,8 +92,9 @@ WorkspaceLayout workspace_layout(const moeq_shape& s, int T, int k) {
   w.dbuf = w.logits + align_up((int64_t)T * (s.n_experts + 1) * 8);
   w.st_bar = w.dbuf + align_up((int64_t)T * KS * s.hidden * 4);
   w.st_logits = w.st_bar + align_up((int64_t)stack_barrier_words() * 4);
-  w.st_abuf = w.st_logits + align_up((int64_t)s.n_experts * 8);
-  w.st_idx = w.st_abuf + align_up(KS * s.inter * 4);
+  w.st_abuf = w.st_logits + align_up((int64_t)s.n_experts * 16);
+  w.st_h = w.st_abuf + align_up(KS * s.inter * 8);
+  w.st_idx = w.st_h + align_up((int64_t)s.hidden * 8);
   w.st_w = w.st_idx + align_up((int64_t)T * k * 4);
   w.st_sw = w.st_w + align_up((int64_t)T * k * 4);
   w.st_gu = w.st_sw + align_up((int64_t)T * 4);
@@ -257,8 +258,9 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     a.h = h;
     a.topk_trace = topk_trace;
     a.h_trace = h_trace;
-    a.logits = reinterpret_cast<double*>(ws + W.st_logits);
-    a.abuf = reinterpret_cast<float*>(ws + W.st_abuf);
+    a.lwords = reinterpret_cast<uint64_t*>(ws + W.st_logits);
+    a.awords = reinterpret_cast<uint64_t*>(ws + W.st_abuf);
+    a.hwords = reinterpret_cast<uint64_t*>(ws + W.st_h);
     a.bar = reinterpret_cast<uint32_t*>(ws + W.st_bar);
     a.status = status;
     a.clocks = g_stack_clocks;

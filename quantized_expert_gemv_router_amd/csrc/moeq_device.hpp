@@ -158,7 +158,10 @@ __device__ __forceinline__ float pow2_stage_factor(float max_abs) {
 
 template <class T>
 __device__ __forceinline__ T load_stream(const T* p) {
-  return __builtin_nontemporal_load(p);
+  // A global (not flat) load: flat loads also count against the LDS
+  // counter, so every later wait on LDS traffic would wait for them too.
+  using GlobalT = __attribute__((address_space(1))) const T;
+  return __builtin_nontemporal_load((GlobalT*)p);
 }
 
 // Cross-workgroup hand-off without cache-wide flushes.  Data that another
@@ -182,6 +185,25 @@ __device__ __forceinline__ T ld_agent(const T* p) {
 __device__ __forceinline__ void drain_memory() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
+}
+
+// A pointer that is the same in every lane, made scalar so that loads from
+// it take a scalar base address.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Block barrier that orders LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads in flight.  (__syncthreads carries a
+// release fence that also waits for every outstanding vector memory
+// operation whenever a global store may be pending.)  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {

@@ -28,6 +28,7 @@ struct WorkspaceLayout {
   int64_t st_bar = 0;
   int64_t st_logits = 0;
   int64_t st_abuf = 0;
+  int64_t st_h = 0;
   int64_t st_idx = 0;
   int64_t st_w = 0;
   int64_t st_sw = 0;
@@ -104,13 +105,14 @@ struct StackArgs {
   float* h;                        // [H] in/out
   int32_t* topk_trace;             // [L][K] or null
   float* h_trace;                  // [L][H] or null
-  double* logits;                  // [E] scratch
-  float* abuf;                     // [K + S][I] scratch
+  uint64_t* lwords;                // [E][2] tagged halves of the fp64 logits
+  uint64_t* awords;                // [K + S][I] tagged activations
+  uint64_t* hwords;                // [H] tagged hidden state between layers
   uint32_t* bar;                   // barrier counters (stack_barrier_words())
   int32_t* status;
   int64_t* clocks;                 // diagnostic: [L][kStackClockEvents] wall-clock stamps of block 0, or null
 };
-constexpr int kStackClockEvents = 16;
+constexpr int kStackClockEvents = 24;
 int stack_barrier_words();
 // hipErrorNotSupported: no persistent instantiation for this shape.
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream);

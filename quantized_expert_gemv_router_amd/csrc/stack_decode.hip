@@ -48,6 +48,7 @@ constexpr int kSpinLimit = 1 << 18;        // polls before a barrier gives up
 constexpr int kMaxKS = 8;                  // selected + shared experts per layer
 constexpr int kMaxLayers = 128;            // per persistent launch
 constexpr int kTblPer = 8;                 // pointer-table entries per thread (E + S <= 4096)
+static_assert(kWaves * MOEQ_MAX_TOPK <= 64 * 2, "top-K merge holds two candidates per lane");
 
 // ------------------------------------------------------------------ barrier
 struct GridBarrier {
@@ -55,17 +56,24 @@ struct GridBarrier {
   int group, gsize, ngroups;
   uint32_t epoch;
 
-  // Whole block.  Returns false if the grid is aborting.
-  __device__ __forceinline__ bool sync(int32_t* status, int* flag) {
-    drain_memory();
-    __syncthreads();
+  // Thread 0 arrives for the whole block.  The caller has drained the
+  // block's global stores and passed a block barrier after that.
+  __device__ __forceinline__ void arrive() {
     if (threadIdx.x == 0) {
       ++epoch;
       uint32_t* gc = base + 32 * (1 + group);
-      uint32_t* top = base;
-      uint32_t* abort = base + 32 * (1 + kGroups);
       const uint32_t old = atomic_add_agent(gc, 1u);
-      if (old == epoch * (uint32_t)gsize - 1u) atomic_add_agent(top, 1u);
+      if (old == epoch * (uint32_t)gsize - 1u) atomic_add_agent(base, 1u);
+    }
+  }
+
+  // Whole block: waits until every block has arrived.  Global loads issued
+  // between arrive() and wait() stay in flight across the wait.  Returns
+  // false if the grid is aborting.
+  __device__ __forceinline__ bool wait(int32_t* status, int* flag) {
+    if (threadIdx.x == 0) {
+      const uint32_t* top = base;
+      uint32_t* abort = base + 32 * (1 + kGroups);
       const uint32_t target = epoch * (uint32_t)ngroups;
       int ok = 1;
       for (int spins = 0; ld_agent(top) < target; ++spins) {
@@ -80,20 +88,71 @@ struct GridBarrier {
       }
       *flag = ok;
     }
-    __syncthreads();
+    block_sync_lds();
     return *flag != 0;
+  }
+
+  // Whole block: drain, arrive, wait.
+  __device__ __forceinline__ bool sync(int32_t* status, int* flag) {
+    drain_memory();
+    __syncthreads();
+    arrive();
+    return wait(status, flag);
   }
 };
 
+// ------------------------------------------------------------ tagged words
+// A value handed from one block to the others travels as one 64-bit word:
+// the payload in the low half, the tag of the layer that wrote it in the
+// high half.  Readers poll the word until the tag they expect shows up, so
+// the word is its own flag and no fence or grid barrier sits between the
+// writer and its readers.  Each word has one writing block for the whole
+// launch, and a block writes layer l+1's value only after every block has
+// read layer l's (each layer's three handoffs form a chain), so a reader
+// never sees a tag newer than the one it waits for.
+__device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t payload, uint32_t tag) {
+  st_agent(p, ((uint64_t)tag << 32) | payload);
+}
+
+// Polls the words base[idx(i)] for the bits i set in `valid` until each
+// carries `tag`; payloads land in out[i].  Bounded: gives up (and raises
+// the grid's abort flag) after kSpinLimit polls, or when another block has
+// raised it.
+template <int N, typename Idx>
+__device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
+                                            uint32_t (&out)[N], uint32_t* abort, int32_t* status) {
+  uint32_t pending = valid;
+  for (int spins = 0;; ++spins) {
+    uint64_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = ((pending >> i) & 1) ? ld_agent(base + idx(i)) : 0ull;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (((pending >> i) & 1) && (uint32_t)(v[i] >> 32) == tag) {
+        out[i] = (uint32_t)v[i];
+        pending &= ~(1u << i);
+      }
+    }
+    if (pending == 0) return true;
+    if ((spins & 15) == 15 && ld_agent(abort) != 0u) return false;
+    if (spins > kSpinLimit) {
+      set_status(status, kStatusTimeout);
+      st_agent(abort, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // ------------------------------------------------------------------ layout
 struct StackLds {
-  int hs, xp, xs, ap, as, gres, dres, lg, tbl, total;
+  int hs, xp, xs, ap, as, gres, dres, lg, tbl, clk, total;
 };
 
 __host__ __device__ inline int al16(int v) { return (v + 15) & ~15; }
 
 __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S, int KS, int PC,
-                                                     int RG, int RD) {
+                                                     int RG, int RD, int clk_entries) {
   StackLds L;
   L.hs = 0;
   L.xp = al16(L.hs + 4 * H);
@@ -104,7 +163,8 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S,
   L.dres = al16(L.gres + 4 * KS * 2 * RG);
   L.lg = al16(L.dres + 4 * KS * RD);
   L.tbl = al16(L.lg + 8 * E);
-  L.total = al16(L.tbl + 8 * (E + S));
+  L.clk = al16(L.tbl + 8 * (E + S));
+  L.total = al16(L.clk + 8 * clk_entries);
   return L;
 }
 
@@ -143,20 +203,25 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ uint32_t amax[kMaxKS];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
+  __shared__ int64_t candk[kWaves * MOEQ_MAX_TOPK];
+  __shared__ int candi[kWaves * MOEQ_MAX_TOPK];
   __shared__ float selw[MOEQ_MAX_TOPK];
   __shared__ const uint8_t* eblob[kMaxKS];
   __shared__ const uint16_t* rtr[kMaxLayers];
   __shared__ const uint8_t* shp[kMaxLayers];
   __shared__ float undo_x;
   __shared__ int bar_flag;
+  __shared__ int fail_flag;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int NB = gridDim.x, b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NB = gridDim.x;
+  int b = blockIdx.x;   // re-derived opaquely each layer (see the layer loop)
   const int H = a.H, I = a.I, E = a.E, K = a.K, S = a.S, KS = K + S, L = a.L;
   const int nchG = H / PC, nchD = I / PC;
   const int RG = (I + NB - 1) / NB, RD = (H + NB - 1) / NB;
 
-  const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD);
+  const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD, a.clocks ? L * kStackClockEvents : 0);
   float* hs = reinterpret_cast<float*>(smem + LL.hs);               // [H]
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem + LL.xp);         // [H/2]
   float* xs = reinterpret_cast<float*>(smem + LL.xs);               // [H/PC]
@@ -166,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   float* dres = reinterpret_cast<float*>(smem + LL.dres);           // [KS][RD]
   double* lg = reinterpret_cast<double*>(smem + LL.lg);             // [E]
   const uint8_t** tbl = reinterpret_cast<const uint8_t**>(smem + LL.tbl);  // [E + S], this layer
+  int64_t* clk = reinterpret_cast<int64_t*>(smem + LL.clk);         // [L][kStackClockEvents] if timed
 
   GridBarrier bar;
   bar.base = a.bar;
@@ -188,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t sg[RPWG][CPLG];
   u32x4 qd[STEPSD][CPLD];
   uint32_t sd[STEPSD][CPLD];
-  const uint8_t* tnext[kTblPer];   // next layer's pointer-table row, in flight
+  const uint8_t* tnext[kTblPer];   // this layer's pointer-table row, in flight to LDS
 
   auto gu_task = [&](int m, int& j, int& sec, int& row) -> bool {
     const int t = wave * RPWG + m;
@@ -197,37 +263,50 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     row = b + NB * (t % RG);
     return j < KS && row < I;
   };
-  auto load_router = [&](int li) {
-    const bool ok = r_row < E;
-    const uint16_t* w = ok ? rtr[li] + (int64_t)r_row * H + (int64_t)r_seg * seg_len : nullptr;
+  // Loads are planned (every LDS read they need) before any is issued: an
+  // LDS read between loads makes the compiler wait for the loads in flight.
+  const uint16_t* rplan = nullptr;          // this wave's router row segment
+  auto plan_router = [&](int li) {
+    rplan = r_row < E ? uniform_ptr(rtr[li]) + (int64_t)r_row * H + (int64_t)r_seg * seg_len : nullptr;
+  };
+  auto issue_router = [&]() {
 #pragma unroll
     for (int c = 0; c < CPLR; ++c) {
       const int cc = lane + 64 * c;
-      wr[c] = (ok && cc < seg_ch) ? load_stream(reinterpret_cast<const u32x4*>(w) + cc)
-                                  : u32x4{0u, 0u, 0u, 0u};
+      // no default for skipped lanes: zeroing a register that a load may
+      // still target also makes the compiler wait for the loads in flight
+      if (rplan != nullptr && cc < seg_ch) wr[c] = load_stream(reinterpret_cast<const u32x4*>(rplan) + cc);
     }
   };
-  // gate/up rows of the tasks whose slot is in [jlo, jhi)
-  auto load_gu = [&](int jlo, int jhi) {
+  // gate/up rows of the tasks whose slot is in [jlo, jhi); gu_task is
+  // uniform over a wave, so the row addresses are scalar
+  const uint8_t* gq[RPWG];       // quantized row, or null: no task
+  const uint32_t* gs[RPWG];      // the row's scale/bias words
+  auto plan_gu = [&](int jlo, int jhi) {
     const int64_t row_bytes = (int64_t)H * BITS / 8;
     const int gpr = H / 64;
 #pragma unroll
     for (int m = 0; m < RPWG; ++m) {
       int j, sec, row;
       const bool ok = gu_task(m, j, sec, row);
-      if (!(ok && j >= jlo && j < jhi)) continue;
-      const uint8_t* blob = eblob[j];
+      const uint8_t* blob = (ok && j >= jlo && j < jhi) ? uniform_ptr(eblob[j]) : nullptr;
       const int r = sec * I + row;   // row of [gate; up]
+      gq[m] = blob != nullptr ? blob + (int64_t)r * row_bytes : nullptr;
+      gs[m] = blob != nullptr ? reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8) +
+                                    (int64_t)r * gpr
+                              : nullptr;
+    }
+  };
+  auto issue_gu = [&]() {
+#pragma unroll
+    for (int m = 0; m < RPWG; ++m) {
+      if (gq[m] == nullptr) continue;   // gu_dots skips it too
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
         const int cc = lane + 64 * c;
-        if (blob != nullptr && cc < nchG) {
-          const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8);
-          qg[m][c] = load_stream(reinterpret_cast<const u32x4*>(blob + r * row_bytes) + cc);
-          sg[m][c] = load_stream(sb + (int64_t)r * gpr + (cc * PC) / 64);
-        } else {
-          qg[m][c] = u32x4{0u, 0u, 0u, 0u};
-          sg[m][c] = 0u;
+        if (cc < nchG) {
+          qg[m][c] = load_stream(reinterpret_cast<const u32x4*>(gq[m]) + cc);
+          sg[m][c] = load_stream(gs[m] + (cc * PC) / 64);
         }
       }
     }
@@ -239,38 +318,50 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       int j, sec, row;
       const bool ok = gu_task(m, j, sec, row);
       if (!(ok && j >= jlo && j < jhi)) continue;
+      const bool have = gq[m] != nullptr;
       float part = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
         const int cc = lane + 64 * c;
-        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
+        if (have && cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
       }
       const float v = wave_sum_dpp(part) * ux;
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
     }
   };
-  auto load_down = [&]() {
+  // down rows: step s of a wave covers RPSD rows, LPRD lanes each
+  const uint8_t* dblob[STEPSD];  // this lane's expert for step s, or null
+  auto down_row = [&](int s, int& j, int& row) {
+    const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
+    j = u / RD;
+    row = b + NB * (u % RD);
+  };
+  auto plan_down = [&]() {
+#pragma unroll
+    for (int s = 0; s < STEPSD; ++s) {
+      int j, row;
+      down_row(s, j, row);
+      dblob[s] = (j < KS && row < H) ? eblob[j] : nullptr;
+    }
+  };
+  auto issue_down = [&]() {
     const int64_t row_bytes = (int64_t)I * BITS / 8;
     const int gpr = I / 64;
     const int sub = lane % LPRD;
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
-      const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
-      const int j = u / RD, row = b + NB * (u % RD);
-      const uint8_t* blob = j < KS ? eblob[j] : nullptr;
-      const bool ok = j < KS && row < H && blob != nullptr;
+      int j, row;
+      down_row(s, j, row);
+      const uint8_t* blob = dblob[s];
+      const uint8_t* q = blob + 2 * (int64_t)H * I * BITS / 8 + (int64_t)row * row_bytes;
+      const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8 +
+                                                             2 * (int64_t)H * I / 64 * 4) + (int64_t)row * gpr;
 #pragma unroll
       for (int c = 0; c < CPLD; ++c) {
         const int cc = sub + LPRD * c;
-        if (ok && cc < nchD) {
-          const int64_t qoff = 2 * (int64_t)H * I * BITS / 8;
-          const uint32_t* sb = reinterpret_cast<const uint32_t*>(
-              blob + 3 * (int64_t)H * I * BITS / 8 + 2 * (int64_t)H * I / 64 * 4);
-          qd[s][c] = load_stream(reinterpret_cast<const u32x4*>(blob + qoff + row * row_bytes) + cc);
-          sd[s][c] = load_stream(sb + (int64_t)row * gpr + (cc * PC) / 64);
-        } else {
-          qd[s][c] = u32x4{0u, 0u, 0u, 0u};
-          sd[s][c] = 0u;
+        if (blob != nullptr && cc < nchD) {   // the down dots skip what is not loaded here
+          qd[s][c] = load_stream(reinterpret_cast<const u32x4*>(q) + cc);
+          sd[s][c] = load_stream(sb + (cc * PC) / 64);
         }
       }
     }
@@ -293,13 +384,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   // diagnostic phase stamps (block 0, after a block-wide barrier)
   auto stamp = [&](int li, int ev) {
     if (a.clocks && b == 0) {
-      __syncthreads();
-      if (tid == 0) a.clocks[(int64_t)li * kStackClockEvents + ev] = (int64_t)wall_clock64();
+      block_sync_lds();
+      if (tid == 0) clk[li * kStackClockEvents + ev] = (int64_t)wall_clock64();
     }
   };
   // diagnostic stamps from wave 0 alone (no block barrier)
   auto stamp0 = [&](int li, int ev) {
-    if (a.clocks && b == 0 && tid == 0) a.clocks[(int64_t)li * kStackClockEvents + ev] = (int64_t)wall_clock64();
+    if (a.clocks && b == 0 && tid == 0) clk[li * kStackClockEvents + ev] = (int64_t)wall_clock64();
   };
 
   // prologue: router and shared-expert pointers of every layer, first rows
@@ -307,26 +398,71 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     rtr[li] = a.routers[a.layer0 + li];
     shp[li] = S > 0 ? static_cast<const uint8_t*>(a.blobs[(int64_t)(a.layer0 + li) * tbl_n + E]) : nullptr;
   }
-  load_tbl_row(a.layer0);
-  __syncthreads();
+  if (tid == 0) fail_flag = 0;
+  // this block's tagged words start at tag 0 (no layer's); one grid
+  // barrier puts every clear before any layer's write
+  for (int j = tid; j < RW; j += kThreads) {
+    const int r = b + NB * j;
+    if (r < E) { st_agent(a.lwords + 2 * r, uint64_t{0}); st_agent(a.lwords + 2 * r + 1, uint64_t{0}); }
+  }
+  for (int t = tid; t < KS * RG; t += kThreads) {
+    const int j = t / RG, row = b + NB * (t - j * RG);
+    if (row < I) st_agent(a.awords + (int64_t)j * I + row, uint64_t{0});
+  }
+  for (int i = tid; i < RD; i += kThreads) {
+    const int row = b + NB * i;
+    if (row < H) st_agent(a.hwords + row, uint64_t{0});
+  }
   if (tid < S) eblob[K + tid] = shp[0];
-  __syncthreads();
-  load_router(0);
-  load_gu(K, KS);
+  if (!bar.sync(a.status, &bar_flag)) return;
+  block_sync_lds();
+  plan_router(0);
+  plan_gu(K, KS);
+  issue_router();
+  issue_gu();
+  uint32_t* const abort_word = a.bar + 32 * (1 + kGroups);
+  auto block_failed = [&](bool ok) -> bool {   // whole block
+    if (!ok) fail_flag = 1;
+    block_sync_lds();
+    return fail_flag != 0;
+  };
 
   for (int li = 0; li < L; ++li) {
+    // Row offsets and addresses derived from the block index are cheap to
+    // recompute; hoisted out of the loop they stay live across all phases
+    // and push registers into scratch, whose reloads are memory round trips.
+    {
+      int zero;
+      asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+      b = (int)blockIdx.x + zero;
+    }
     stamp(li, 0);
     // ------------------------------------------------------------ phase R
     // h -> LDS with sum of squares (fp64) and max |h|
     {
       uint64_t hv[HW];
-      const uint64_t* src = reinterpret_cast<const uint64_t*>(a.h);
+      bool ok = true;
+      if (li == 0) {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.h);
 #pragma unroll
-      for (int i = 0; i < HW; ++i) {
-        const int p = tid + i * kThreads;
-        hv[i] = (2 * p < H) ? ld_agent(src + p) : 0ull;
+        for (int i = 0; i < HW; ++i) {
+          const int p = tid + i * kThreads;
+          hv[i] = (2 * p < H) ? ld_agent(src + p) : 0ull;
+        }
+      } else {
+        uint32_t hw[2 * HW];
+        uint32_t valid = 0;
+#pragma unroll
+        for (int i = 0; i < HW; ++i) {
+          hw[2 * i] = hw[2 * i + 1] = 0u;
+          if (2 * (tid + i * kThreads) < H) valid |= 3u << (2 * i);
+        }
+        ok = take_tagged<2 * HW>(a.hwords, [&](int i) { return 2 * (tid + (i >> 1) * kThreads) + (i & 1); },
+                                 valid, (uint32_t)li, hw, abort_word, a.status);
+#pragma unroll
+        for (int i = 0; i < HW; ++i) hv[i] = ((uint64_t)hw[2 * i + 1] << 32) | hw[2 * i];
       }
-      store_tbl_row();
+      if (block_failed(ok)) return;
       double ss = 0.0;
       float mx = 0.0f;
 #pragma unroll
@@ -400,37 +536,38 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
     }
     __syncthreads();
+    const uint32_t tag = (uint32_t)li + 1u;
     if (lane == 0 && r_seg == 0 && r_row < E) {
       double d = 0.0;
       for (int sgi = 0; sgi < NSEG; ++sgi) d += rpart[wave + sgi];
-      st_agent(a.logits + r_row, d * inv);
+      const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
+      put_tagged(a.lwords + 2 * r_row, (uint32_t)bits, tag);
+      put_tagged(a.lwords + 2 * r_row + 1, (uint32_t)(bits >> 32), tag);
     }
     stamp(li, 2);
     gu_dots(K, KS);                 // the shared expert's rows are already here
     stamp(li, 3);
-    if (!bar.sync(a.status, &bar_flag)) return;
     stamp(li, 4);
 
     // ------------------------------------------------------------ phase G
+    // this layer's pointer-table row lands while the logits are polled
+    load_tbl_row(a.layer0 + li);
+    for (int e0 = 0; e0 < E; e0 += kThreads) {   // one logit (two words) per thread per pass
+      const int e = e0 + tid;
+      uint32_t w[2] = {0u, 0u};
+      const bool ok = take_tagged<2>(a.lwords + 2 * e, [](int i) { return i; }, e < E ? 3u : 0u, tag, w,
+                                     abort_word, a.status);
+      if (e < E) lg[e] = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
+      if (block_failed(ok)) return;
+    }
+    store_tbl_row();
+    __syncthreads();
+    stamp0(li, 12);
+    if (E <= kThreads) block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
+    else block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
     if (wave == 0) {
-      for (int base = 0; base < E; base += 64 * 8) {
-        double v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = base + 64 * i + lane;
-          v[i] = e < E ? ld_agent(a.logits + e) : 0.0;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = base + 64 * i + lane;
-          if (e < E) lg[e] = v[i];
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      stamp0(li, 12);
-      wave_topk_dpp(lg, E, K, sel, selv);
-      stamp0(li, 13);
-      const float w = wave_softmax_weight(lg, E, K, selv, a.no_renorm != 0);
+      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
+                                  : wave_softmax_selected(selv, K);
       stamp0(li, 14);
       if (lane < K) {
         selw[lane] = w;
@@ -443,20 +580,23 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     if (tid < KS) amax[tid] = 0u;
     __syncthreads();
     stamp(li, 5);
-    load_gu(0, K);                   // routed gate/up rows
+    plan_gu(0, K);                   // routed gate/up rows
+    issue_gu();
+    stamp0(li, 15);
+    plan_down();                     // LDS reads, placed where the gate/up data is awaited anyway
     gu_dots(0, K);
-    load_down();                     // down rows of every slot, used after barrier C
+    stamp0(li, 13);
     __syncthreads();
     stamp(li, 6);
     for (int t = tid; t < KS * RG; t += kThreads) {
       const int j = t / RG, i = t - j * RG, row = b + NB * i;
       if (row < I) {
         const float g = gres[(j * 2) * RG + i], u = gres[(j * 2 + 1) * RG + i];
-        st_agent(a.abuf + (int64_t)j * I + row, g / (1.0f + __expf(-g)) * u);
+        put_tagged(a.awords + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
       }
     }
-    stamp(li, 7);
-    if (!bar.sync(a.status, &bar_flag)) return;
+    issue_down();                    // down rows of every slot, in flight while the activations arrive
+    stamp0(li, 7);
     stamp(li, 8);
 
     // ------------------------------------------------------------ phase D
@@ -469,21 +609,24 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         const bool ok = t < total;
         const int m = ok ? t / nwa : 0, w = ok ? t - m * nwa : 0;
         float v[PW];
-        if (ok) {
-          const uint64_t* src = reinterpret_cast<const uint64_t*>(a.abuf + (int64_t)m * I + (int64_t)w * PW);
-          uint64_t raw[PW / 2];
+        uint32_t raw[PW];
 #pragma unroll
-          for (int j = 0; j < PW / 2; ++j) raw[j] = ld_agent(src + j);
+        for (int j = 0; j < PW; ++j) raw[j] = 0u;
+        const uint64_t* src = a.awords + (int64_t)m * I + (int64_t)w * PW;
+        const bool got = take_tagged<PW>(src, [](int j) { return j; }, ok ? (uint32_t)((1ull << PW) - 1) : 0u,
+                                         tag, raw, abort_word, a.status);
+        if (ok) {
           float lm = 0.0f;
 #pragma unroll
-          for (int j = 0; j < PW / 2; ++j) {
-            v[2 * j] = __uint_as_float((uint32_t)raw[j]);
-            v[2 * j + 1] = __uint_as_float((uint32_t)(raw[j] >> 32));
-            lm = fmaxf(lm, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+          for (int j = 0; j < PW; ++j) {
+            v[j] = __uint_as_float(raw[j]);
+            lm = fmaxf(lm, fabsf(v[j]));
           }
           atomicMax(&amax[m], __float_as_uint(lm));   // non-negative floats order as integers
         }
-        __syncthreads();
+        stamp0(li, 16);
+        if (block_failed(got)) return;
+        stamp0(li, 17);
         float s = 0.0f;
         if (ok) {
           const float p = pow2_stage_factor(__uint_as_float(amax[m]));
@@ -504,11 +647,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         const int j = u / RD, i = u % RD;
         const bool ok = j < KS && b + NB * i < H;
         const int jj = ok ? j : 0;
+        const bool have = dblob[s] != nullptr;
         float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPLD; ++c) {
           const int cc = sub + LPRD * c;
-          if (ok && cc < nchD)
+          if (have && cc < nchD)
             part += chunk_affine(chunk_dot<BITS>(qd[s][c], ap + (int64_t)jj * (I / 2) + cc * PPC), sd[s][c],
                                  as[jj * nchD + cc]);
         }
@@ -517,6 +661,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         if (ok && sub == 0) dres[j * RD + i] = d;
       }
     }
+    stamp0(li, 18);
     __syncthreads();
     for (int i = tid; i < RD; i += kThreads) {
       const int row = b + NB * i;
@@ -525,19 +670,25 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         for (int j = 0; j < K; ++j) acc = fmaf(selw[j], dres[j * RD + i], acc);
         for (int j = K; j < KS; ++j) acc = fmaf(1.0f, dres[j * RD + i], acc);
         if (a.h_trace) a.h_trace[(int64_t)li * H + row] = hs[row];
-        st_agent(a.h + row, acc);
+        if (li + 1 == L) a.h[row] = acc;   // complete when the launch ends
+        else put_tagged(a.hwords + row, __float_as_uint(acc), tag);
       }
     }
     stamp(li, 10);
-    if (li + 1 == L) break;   // the last layer's h is complete when the launch ends
-    // next layer: router rows, shared-expert gate/up rows, pointer-table row
+    if (li + 1 == L) break;
+    // next layer: router rows, shared-expert gate/up rows, pointer-table row,
+    // in flight while h arrives
     if (tid < S) eblob[K + tid] = shp[li + 1];
-    __syncthreads();
-    load_router(li + 1);
-    load_gu(K, KS);
-    load_tbl_row(a.layer0 + li + 1);
-    stamp(li, 11);
-    if (!bar.sync(a.status, &bar_flag)) return;
+    block_sync_lds();
+    plan_router(li + 1);
+    plan_gu(K, KS);
+    issue_router();
+    issue_gu();
+    stamp0(li, 11);
+  }
+  if (a.clocks && b == 0) {   // stamps were kept in LDS so taking them adds no memory traffic
+    block_sync_lds();
+    for (int i = tid; i < L * kStackClockEvents; i += kThreads) a.clocks[i] = clk[i];
   }
 }
 
@@ -606,7 +757,8 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   a.router_rows = rw;
   const int PC = 128 / a.bits;
   const int RG = (a.I + nb - 1) / nb, RD = (a.H + nb - 1) / nb;
-  const size_t lds = (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD).total;
+  const size_t lds =
+      (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD, a.clocks ? a.L * kStackClockEvents : 0).total;
   if (lds > 96 * 1024) return hipErrorNotSupported;
   const Geometry g{nb, rw, a.H, a.I, a.E, a.S, KS, a.bits};
   // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,
