@@ -174,12 +174,13 @@ int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts
  *   topk_trace  device [L][T][k] int32 out, or NULL
  *   h_trace     device [L][T][H] f32 out (the input of each layer), or NULL
  *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE
- * T == 1 runs one persistent cooperative launch for all L layers (grid
- * barriers between the dependent steps, no host involvement) when the
- * shape has a persistent instantiation; otherwise, or with
+ * T == 1 runs one persistent cooperative launch for all L layers (no host
+ * involvement: the workgroups hand the logits, the activations and the
+ * hidden state to each other through tagged words in the workspace) when
+ * the shape has a persistent instantiation; otherwise, or with
  * MOEQ_F_STACK_LAYERWISE or T > 1, it enqueues the three per-layer calls
- * for each layer.  A grid barrier that waits too long sets status bit 2
- * (see moe_read_device_status) and the launch ends early. */
+ * for each layer.  A wait between workgroups that lasts too long sets
+ * status bit 2 (see moe_read_device_status) and the launch ends early. */
 int moe_expert_stack_decode(const moeq_shape* shape, const moeq_experts* experts,
                             const uint16_t* const* w_router, int layer0, int L, int T, int k,
                             uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
@@ -192,13 +193,79 @@ int moeq_last_stack_path(void);
 /* Diagnostic: the next persistent moe_expert_stack_decode launch writes
  * wall-clock stamps (100 MHz device counter) of its phase boundaries, as
  * seen by workgroup 0, to the device array `clocks` [L][n] where n is the
- * return value (12).  The pointer is consumed by that launch. */
+ * return value (24).  The pointer is consumed by that launch. */
 int moeq_stack_clock_trace(int64_t* clocks);
 
 /* Synchronise `stream` and read the workspace status word: 0 = clean,
- * else a bitmask (1 = an expert id outside [0, E) was seen, 2 = a grid
- * barrier of the persistent stack kernel timed out).  Clears it. */
+ * else a bitmask (1 = an expert id outside [0, E) or a NULL blob pointer
+ * was seen, 2 = a wait between workgroups of the persistent stack kernel
+ * timed out).  Clears it. */
 int moe_read_device_status(void* workspace, void* stream, int32_t* status);
+
+/* ------------------------------------------------------------------ pool
+ * Expert slot pool (openclawradar.com/fr, Flash-MoE write-up: experts kept
+ * in a bounded number of resident slots and loaded when the router asks for
+ * them; fr.news.hada.io, Flash-MoE, "SSD Expert Streaming": one contiguous
+ * 6.75 MiB read per expert).  The pool owns the placement of experts in a
+ * caller-provided device arena of n_slots slots and writes the device
+ * pointer table that the expert calls read (entries of non-resident experts
+ * are NULL).  Misses are copied from a pinned host image of every blob by
+ * hipMemcpyAsync on `copy_stream`; the compute stream is made to wait on an
+ * event, so no kernel reads a slot before its copy lands.  The least
+ * recently acquired unpinned slot is evicted first, and only after the
+ * last layer that used it was released (its release event is awaited on
+ * the copy stream).  A pool is used from one host thread. */
+typedef struct moeq_pool moeq_pool;
+
+/*   n_layers     layers in the host image and the table
+ *   arena        device, n_slots * slot_bytes bytes, 256-byte aligned
+ *   slot_bytes   multiple of 256, >= moeq_expert_bytes(shape)
+ *   host_src     pinned host memory (hipHostMalloc), n_layers * (E + S)
+ *                blobs, blob (l, e) at byte (l * (E + S) + e) * slot_bytes
+ *   table        device array [n_layers][E + S] of pointers, set to NULL here
+ *   copy_stream  stream for the copies and table edits (caller-owned)
+ * The arena, host image, table and stream stay caller-owned and must
+ * outlive the pool.  The pool allocates its host metadata and events. */
+int moe_pool_create(const moeq_shape* shape, int n_layers, void* arena, int64_t n_slots, int64_t slot_bytes,
+                    const void* host_src, const void** table, void* copy_stream, moeq_pool** out);
+
+/* Every expert resident, blob i in slot i (needs n_slots >= n_layers*(E+S));
+ * `stream` waits for the copy. */
+int moe_pool_make_resident(moeq_pool* pool, void* stream);
+
+/* Makes the experts `ids` (host int32 [n], duplicates allowed, the shared
+ * expert is id E) of `layer` resident and pins them until moe_pool_release
+ * for the layer.  Queues the copies of the misses; `compute_stream` waits
+ * for them.  `view` receives the table to pass to the expert calls.
+ * MOEQ_E_POOL_EXHAUSTED (nothing changed) when the misses need more slots
+ * than are unpinned; MOEQ_E_INVALID for a bad id or a layer acquired twice
+ * without a release. */
+int moe_pool_acquire(moeq_pool* pool, int layer, const int32_t* ids, int n, void* compute_stream,
+                     moeq_experts* view);
+
+/* Unpins the layer's slots once the work queued so far on compute_stream is
+ * done (an event is recorded there). */
+int moe_pool_release(moeq_pool* pool, int layer, void* compute_stream);
+
+/* out[4]: hits, misses, bytes copied, evictions. */
+int moe_pool_stats(const moeq_pool* pool, int64_t* out);
+
+/* Synchronises the copy stream and frees the pool's host state. */
+void moe_pool_destroy(moeq_pool* pool);
+
+/* The pool's placement and eviction decisions alone, with no device: same
+ * policy object as moe_pool_*, for host-side checks.  acquire writes, for
+ * each distinct id in first-appearance order, its slot, the entry
+ * (layer * per_layer + expert) it evicted or -1, and 1 if it missed;
+ * n_out = number of distinct ids.  stats: hits, misses, 0, evictions. */
+typedef struct moeq_poolsim moeq_poolsim;
+int moeq_poolsim_create(int n_layers, int per_layer, int64_t n_slots, moeq_poolsim** out);
+int moeq_poolsim_make_resident(moeq_poolsim* pool);
+int moeq_poolsim_acquire(moeq_poolsim* pool, int layer, const int32_t* ids, int n, int32_t* slots,
+                         int32_t* evicted, int32_t* missed, int32_t* n_out);
+int moeq_poolsim_release(moeq_poolsim* pool, int layer);
+int moeq_poolsim_stats(const moeq_poolsim* pool, int64_t* out);
+void moeq_poolsim_destroy(moeq_poolsim* pool);
 
 #ifdef __cplusplus
 }

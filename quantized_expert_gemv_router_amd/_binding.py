@@ -73,6 +73,22 @@ def lib() -> ctypes.CDLL:
         L.moeq_stack_clock_trace.argtypes = [_P]
         L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                               _P, _P]
+        H = ctypes.POINTER(ctypes.c_void_p)
+        I64 = ctypes.c_int64
+        L.moe_pool_create.argtypes = [S, _I, _P, I64, I64, _P, _P, _P, H]
+        L.moe_pool_make_resident.argtypes = [_P, _P]
+        L.moe_pool_acquire.argtypes = [_P, _I, _P, _I, _P, X]
+        L.moe_pool_release.argtypes = [_P, _I, _P]
+        L.moe_pool_stats.argtypes = [_P, ctypes.POINTER(I64)]
+        L.moe_pool_destroy.argtypes = [_P]
+        L.moe_pool_destroy.restype = None
+        L.moeq_poolsim_create.argtypes = [_I, _I, I64, H]
+        L.moeq_poolsim_make_resident.argtypes = [_P]
+        L.moeq_poolsim_acquire.argtypes = [_P, _I, _P, _I, _P, _P, _P, ctypes.POINTER(ctypes.c_int32)]
+        L.moeq_poolsim_release.argtypes = [_P, _I]
+        L.moeq_poolsim_stats.argtypes = [_P, ctypes.POINTER(I64)]
+        L.moeq_poolsim_destroy.argtypes = [_P]
+        L.moeq_poolsim_destroy.restype = None
         _lib = L
     return _lib
 
@@ -250,7 +266,7 @@ def moeq_last_stack_path() -> int:
 
 
 def moeq_stack_clock_trace(clocks: torch.Tensor) -> int:
-    """Arm the diagnostic phase clock trace (int64 device tensor [L, 12])."""
+    """Arm the diagnostic phase clock trace (int64 device tensor [L, 24])."""
     return lib().moeq_stack_clock_trace(_ptr(clocks))
 
 
@@ -273,3 +289,105 @@ def moe_layer(shape: Shape, experts: ExpertTable, layer: int, x: torch.Tensor,
     out = moe_swiglu_down_combine(shape, experts, layer, gu, idx, w,
                                   sw if shape.n_shared else None, x, k, workspace, stream=stream)
     return dict(idx=idx, w=w, shared_w=sw, logits=logits, gate_up=gu, y=out)
+
+
+_STATS = ("hits", "misses", "bytes_copied", "evictions")
+
+
+def _int32_host(ids) -> ctypes.Array:
+    vals = [int(v) for v in ids]
+    return (ctypes.c_int32 * max(len(vals), 1))(*vals)
+
+
+class PoolView:
+    """The moeq_experts view a pool acquire returns (the pool's pointer table)."""
+
+    def __init__(self, ex: _Experts, pool):
+        self._ex = ex
+        self.pool = pool
+        self.n_layers = ex.n_layers
+
+    def view(self):
+        return ctypes.byref(self._ex)
+
+
+class Pool:
+    """moe_pool_*: expert slots in a device arena, filled from a pinned host
+    image of every (layer, expert) blob on demand, least recently used slot
+    evicted.  `host_src` is a pinned uint8 CPU tensor laid out blob (l, e) at
+    (l * (E + S) + e) * slot_bytes; `table` an int64 device tensor of
+    n_layers * (E + S) entries (the pointer table the pool writes)."""
+
+    def __init__(self, shape: Shape, n_layers: int, arena: torch.Tensor, n_slots: int, slot_bytes: int,
+                 host_src: torch.Tensor, table: torch.Tensor, copy_stream=None):
+        self._h = ctypes.c_void_p()
+        self.shape, self.arena, self.host_src, self.table = shape, arena, host_src, table
+        self.copy_stream = copy_stream
+        _check(lib().moe_pool_create(ctypes.byref(shape), n_layers, _ptr(arena), n_slots, slot_bytes,
+                                     host_src.data_ptr(), _ptr(table), _stream(copy_stream),
+                                     ctypes.byref(self._h)))
+
+    def make_resident(self, stream=None):
+        _check(lib().moe_pool_make_resident(self._h, _stream(stream)))
+
+    def acquire(self, layer: int, ids, stream=None) -> PoolView:
+        arr = _int32_host(ids)
+        ex = _Experts()
+        _check(lib().moe_pool_acquire(self._h, layer, ctypes.cast(arr, _P), len(ids), _stream(stream),
+                                      ctypes.byref(ex)))
+        return PoolView(ex, self)
+
+    def release(self, layer: int, stream=None):
+        _check(lib().moe_pool_release(self._h, layer, _stream(stream)))
+
+    def stats(self) -> dict:
+        out = (ctypes.c_int64 * 4)()
+        _check(lib().moe_pool_stats(self._h, out))
+        return dict(zip(_STATS, list(out)))
+
+    def destroy(self):
+        if self._h:
+            lib().moe_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+class PoolSim:
+    """moeq_poolsim_*: the pool's placement and eviction decisions alone."""
+
+    def __init__(self, n_layers: int, per_layer: int, n_slots: int):
+        self._h = ctypes.c_void_p()
+        _check(lib().moeq_poolsim_create(n_layers, per_layer, n_slots, ctypes.byref(self._h)))
+
+    def make_resident(self):
+        _check(lib().moeq_poolsim_make_resident(self._h))
+
+    def acquire(self, layer: int, ids) -> list:
+        """[(slot, evicted entry or -1, missed)] per distinct id, first-appearance order."""
+        n = len(ids)
+        arr = _int32_host(ids)
+        slots, ev, miss = ((ctypes.c_int32 * max(n, 1))() for _ in range(3))
+        n_out = ctypes.c_int32()
+        _check(lib().moeq_poolsim_acquire(self._h, layer, ctypes.cast(arr, _P), n, slots, ev, miss,
+                                          ctypes.byref(n_out)))
+        return [(slots[i], ev[i], bool(miss[i])) for i in range(n_out.value)]
+
+    def release(self, layer: int):
+        _check(lib().moeq_poolsim_release(self._h, layer))
+
+    def stats(self) -> dict:
+        out = (ctypes.c_int64 * 4)()
+        _check(lib().moeq_poolsim_stats(self._h, out))
+        return dict(zip(_STATS, list(out)))
+
+    def __del__(self):
+        try:
+            if self._h:
+                lib().moeq_poolsim_destroy(self._h)
+        except Exception:
+            pass

@@ -13,10 +13,10 @@ namespace moeq {
 int down_row_blocks(int H);
 
 namespace {
-
 thread_local std::string g_last_error;
 thread_local int g_last_stack_path = 0;
 int64_t* g_stack_clocks = nullptr;   // diagnostic phase stamps for the next persistent launch
+}  // namespace
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -57,6 +57,8 @@ int check_shape(const moeq_shape* s) {
     return fail(MOEQ_E_UNSUPPORTED, "n_shared=%d: at most one shared expert", s->n_shared);
   return MOEQ_OK;
 }
+
+namespace {
 
 int check_tk(const moeq_shape* s, int T, int k) {
   if (T < 0) return fail(MOEQ_E_INVALID, "T=%d is negative", T);

@@ -9,6 +9,13 @@
 
 namespace moeq {
 
+// Error reporting shared by the entry points: fail() records the message
+// returned by moeq_last_error() and returns `code`; ok() clears it.
+int fail(int code, const char* fmt, ...);
+int ok();
+int hip_fail(hipError_t e, const char* what);
+int check_shape(const moeq_shape* s);
+
 constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -17,8 +24,9 @@ inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; 
 //                    [64 .. 64 + n_rowblocks) down-combine row-block counters
 //   logits           f64 [T][E + 1]   (last column: shared-gate logit)
 //   dbuf             f32 [T][k + S][H] per-slot down outputs (multi-token)
-//   stack area       barrier words, fp64 logits [E], activations
-//                    [k + S][I], and the per-layer path's routing
+//   stack area       barrier words, tagged words (fp64 logit halves [E][2],
+//                    activations [k + S][I], hidden state [H]), and the
+//                    per-layer path's routing
 //                    (idx [T][k], w [T][k], shared w [T]) and gate_up
 //                    [T][k + S][2][I]
 struct WorkspaceLayout {
@@ -38,7 +46,7 @@ struct WorkspaceLayout {
 
 constexpr int kCounterRouter = 0;
 constexpr int kCounterStatus = 1;
-constexpr int32_t kStatusTimeout = 2;   // a grid barrier gave up waiting
+constexpr int32_t kStatusTimeout = 2;   // a grid barrier or handoff wait gave up
 constexpr int kCounterRowBlocks = 64;
 constexpr int kMaxRowBlockCounters = 1024 - kCounterRowBlocks;
 
