@@ -186,6 +186,29 @@ int moe_expert_stack_decode(const moeq_shape* shape, const moeq_experts* experts
                             uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
                             void* workspace, void* stream);
 
+/* Prefill: T tokens (any T >= 1; the configured workload is 2048) through
+ * the stacked layers [layer0, layer0 + L) on the fp32 residual stream h
+ * [T][H], in place; per layer and token the same computation as
+ * moe_expert_stack_decode (unit-weight RMS norm, router, top-k + softmax,
+ * experts, combine).  Flash-MoE (fr.news.hada.io), "Architecture du
+ * modèle"; openclawradar.com/fr (top-10 over 512 experts).  Tokens are
+ * grouped by expert so each expert's weights are streamed once per layer
+ * (per 64 tokens routed to it) into dequantise-on-load MFMA GEMMs with fp16
+ * operands and fp32 accumulation; the router stays fp64.
+ *   topk_trace  device [L][T][k] int32 out, or NULL
+ *   flags       MOEQ_F_NO_RENORM
+ *   workspace   moeq_prefill_workspace_bytes(shape, T, k) bytes
+ * 4-bit experts only; hidden and inter multiples of 128; scales and biases
+ * must be representable in fp16 (they are converted from bf16 for the
+ * MFMA operands). */
+int moe_expert_stack_prefill(const moeq_shape* shape, const moeq_experts* experts,
+                             const uint16_t* const* w_router, int layer0, int L, int T, int k,
+                             uint32_t flags, float* h, int32_t* topk_trace, void* workspace, void* stream);
+
+/* Workspace bytes of moe_expert_stack_prefill for T tokens and top-k
+ * (about 440 MB at T=2048, k=10, hidden 4096, inter 1024, 512+1 experts). */
+int moeq_prefill_workspace_bytes(const moeq_shape* shape, int T, int k, int64_t* bytes);
+
 /* Which path the last successful moe_expert_stack_decode on this thread
  * took: 1 = persistent launch, 2 = per-layer launches, 0 = none yet. */
 int moeq_last_stack_path(void);

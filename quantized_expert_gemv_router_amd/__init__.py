@@ -15,4 +15,5 @@ from ._binding import (  # noqa: F401
     moe_router_topk, moe_q4_expert_gemv, moe_swiglu_down_combine, moe_read_device_status,
     moe_expert_stack_decode, moeq_last_stack_path, moeq_stack_clock_trace,
     new_workspace, moe_layer, Pool, PoolSim, PoolView,
+    moe_expert_stack_prefill, moeq_prefill_workspace_bytes, new_prefill_workspace,
 )

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moeq_stack_clock_trace.argtypes = [_P]
         L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                               _P, _P]
+        L.moe_expert_stack_prefill.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P, _P]
+        L.moeq_prefill_workspace_bytes.argtypes = [S, _I, _I, ctypes.POINTER(ctypes.c_int64)]
         H = ctypes.POINTER(ctypes.c_void_p)
         I64 = ctypes.c_int64
         L.moe_pool_create.argtypes = [S, _I, _P, I64, I64, _P, _P, _P, H]
@@ -258,6 +260,34 @@ def moe_expert_stack_decode(shape: Shape, experts: ExpertTable, routers: RouterT
                                          k, flags, _ptr(h), _ptr(tk), _ptr(hk), _ptr(workspace),
                                          _stream(stream)))
     return (tk, hk) if trace else None
+
+
+def moeq_prefill_workspace_bytes(shape: Shape, T: int, k: int) -> int:
+    out = ctypes.c_int64()
+    _check(lib().moeq_prefill_workspace_bytes(ctypes.byref(shape), T, k, ctypes.byref(out)))
+    return out.value
+
+
+def new_prefill_workspace(shape: Shape, T: int, k: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace of moeq_prefill_workspace_bytes(shape, T, k) bytes."""
+    return torch.zeros(moeq_prefill_workspace_bytes(shape, T, k), dtype=torch.uint8, device=device)
+
+
+def moe_expert_stack_prefill(shape: Shape, experts, routers: RouterTable, h: torch.Tensor, k: int,
+                             layer0: int = 0, L: int | None = None, flags: int = 0,
+                             workspace: torch.Tensor | None = None, trace: bool = False, stream=None):
+    """Prefill layers [layer0, layer0 + L) in place on h (f32 [T, H]).
+    Returns topk_trace int32 [L, T, k] when trace, else None."""
+    T = h.shape[0]
+    L = experts.n_layers - layer0 if L is None else L
+    if h.dtype != torch.float32:
+        raise ValueError("the stack runs on an fp32 residual stream")
+    if workspace is None:
+        workspace = new_prefill_workspace(shape, T, k, h.device)
+    tk = torch.empty((L, T, k), dtype=torch.int32, device=h.device) if trace else None
+    _check(lib().moe_expert_stack_prefill(ctypes.byref(shape), experts.view(), routers.ptr(), layer0, L, T, k,
+                                          flags, _ptr(h), _ptr(tk), _ptr(workspace), _stream(stream)))
+    return tk
 
 
 def moeq_last_stack_path() -> int:

@@ -1,0 +1,623 @@
+// Prefill: T tokens through L stacked MoE layers at once (the same layer as
+// decode, token by token; tokens are independent, there is no attention).
+// fr.news.hada.io, Flash-MoE, "Architecture du modèle" (512 experts, K
+// routed + one shared per token, 60 layers), "Noyau de déquantification
+// optimisé FMA" (w = value * scale + bias), "Shaders de calcul Metal"
+// (dequantised mat-vec, SwiGLU, combine + residual); openclawradar.com/fr
+// (top-10 routing over 512 experts).
+//
+// Per layer, all on the device:
+//   norm     x = h / sqrt(mean(h^2) + 1e-6) -> fp16, stored permuted
+//   router   logits[t][e] = (Wr[e] . h[t]) / rms[t] in fp64 (tiled GEMM)
+//   top-K    per token, ties to the lower index, softmax of the selection
+//   group    (token, slot) pairs sorted by expert, token order kept
+//   gate/up  per expert: [pairs x H] fp16 times the dequantised [2I x H]
+//            weights on MFMA (fp16 in, fp32 accumulation), SwiGLU fused,
+//            activations stored fp16
+//   down     per expert: [pairs x I] times the dequantised [H x I] weights
+//            -> per-pair fp32 rows
+//   combine  h[t] += sum_s w[t][s] d[t][s] + d[t][shared], in slot order
+//
+// Weights are dequantised in registers to fp16 (exact nibble, one fp16
+// rounding of s*q + b) just before they enter the MFMA; each expert's rows
+// are streamed from memory once per tile of up to 64 pairs.  Within an MFMA
+// the K order of a lane's eight values is the nibble order of a packed word
+// (0,4,1,5,2,6,3,7); the activations are stored in that order so both
+// operands agree.  The results do not depend on the launch geometry (no
+// atomics on floating-point values; grouping keeps token order).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "moeq.h"
+#include "moeq_device.hpp"
+#include "moeq_internal.hpp"
+#include "topk.hpp"
+
+namespace moeq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPThreads = 256;          // four waves
+constexpr int kMB = 4;                  // row blocks of 16 per tile
+constexpr int kMT = 16 * kMB;           // pairs per tile
+constexpr int kNBW = 2;                 // blocks of 16 weight rows per wave
+constexpr int kNT = 4 * 16 * kNBW;      // weight rows per tile
+constexpr int kKC = 128;                // K per chunk (two groups of 64)
+constexpr int kPitch = kKC + 8;         // LDS row pitch in halves (bank spread)
+
+// position of value j of a packed word in the stored (MFMA) order
+__device__ __forceinline__ int perm_pos(int r) {
+  const int j = r & 7;
+  return (r & ~7) | (j < 4 ? 2 * j : 2 * (j - 4) + 1);
+}
+
+// ------------------------------------------------------------------ norm
+// One block per token: fp64 sum of squares, 1/rms, and x in fp16 (permuted
+// within each 8-block).  Block 0 also clears the per-expert counters.
+__global__ __launch_bounds__(kPThreads) void norm_kernel(const float* __restrict__ h, int H,
+                                                          double* __restrict__ inv_rms,
+                                                          _Float16* __restrict__ xh, int32_t* counts,
+                                                          int n_counts) {
+  __shared__ double part[kPThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (t == 0)
+    for (int i = tid; i < n_counts; i += kPThreads) counts[i] = 0;
+  const float* row = h + (int64_t)t * H;
+  double ss = 0.0;
+  for (int j = tid; j < H; j += kPThreads) ss = fma((double)row[j], (double)row[j], ss);
+  ss = wave_sum_f64_dpp(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kPThreads / 64; ++w) tot += part[w];
+  const double inv = 1.0 / sqrt(tot / (double)H + 1e-6);
+  if (tid == 0) inv_rms[t] = inv;
+  for (int b = tid; b < H / 8; b += kPThreads) {
+    const float4 v0 = *reinterpret_cast<const float4*>(row + 8 * b);
+    const float4 v1 = *reinterpret_cast<const float4*>(row + 8 * b + 4);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    half8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j < 4 ? 2 * j : 2 * (j - 4) + 1] = (_Float16)(float)((double)v[j] * inv);
+    *reinterpret_cast<half8*>(xh + (int64_t)t * H + 8 * b) = o;
+  }
+}
+
+// ---------------------------------------------------------------- router
+// logits[t][e] = (sum_j Wr[e][j] h[t][j]) * inv_rms[t], fp64 throughout
+// (bf16 and fp32 inputs are exact in fp64).  64 x 64 tile per block, 4 x 4
+// per thread, K in chunks of 16 staged in LDS.
+constexpr int kRT = 64, kRK = 16;
+
+__global__ __launch_bounds__(kPThreads) void router_kernel(const float* __restrict__ h,
+                                                            const uint16_t* const* __restrict__ routers,
+                                                            int layer, int T, int H, int E,
+                                                            const double* __restrict__ inv_rms,
+                                                            double* __restrict__ logits) {
+  __shared__ double As[kRK][kRT + 1];
+  __shared__ double Bs[kRK][kRT + 1];
+  const uint16_t* wr = uniform_ptr(routers[layer]);
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRT;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < H; k0 += kRK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + kPThreads * i, r = idx / kRK, kk = idx % kRK;
+      const int t = t0 + r, e = e0 + r;
+      As[kk][r] = t < T ? (double)h[(int64_t)t * H + k0 + kk] : 0.0;
+      Bs[kk][r] = e < E ? (double)__uint_as_float((uint32_t)wr[(int64_t)e * H + k0 + kk] << 16) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kRK; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = As[kk][ty + 16 * i];
+        b[i] = Bs[kk][tx + 16 * i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty + 16 * i;
+    if (t >= T) continue;
+    const double inv = inv_rms[t];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx + 16 * j;
+      if (e < E) logits[(int64_t)t * E + e] = acc[i][j] * inv;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- top-K
+template <int M>
+__global__ __launch_bounds__(kPThreads) void topk_kernel(const double* __restrict__ logits, int E, int K,
+                                                          int no_renorm, int32_t* __restrict__ idx,
+                                                          float* __restrict__ w, int32_t* trace) {
+  __shared__ double lg[64 * 4 * M];
+  __shared__ int64_t ck[64];
+  __shared__ int ci[64];
+  __shared__ int sel[MOEQ_MAX_TOPK];
+  __shared__ double selv[MOEQ_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPThreads) lg[e] = logits[(int64_t)t * E + e];
+  __syncthreads();
+  block_topk_keys<4, M, 1>(lg, E, K, ck, ci, sel, selv);
+  if (tid < 64) {
+    const float wt = no_renorm ? wave_softmax_weight(lg, E, K, selv, true) : wave_softmax_selected(selv, K);
+    if (tid < K) {
+      idx[(int64_t)t * K + tid] = sel[tid];
+      w[(int64_t)t * K + tid] = wt;
+      if (trace) trace[(int64_t)t * K + tid] = sel[tid];
+    }
+  }
+}
+
+// -------------------------------------------------------------- grouping
+__global__ void count_kernel(const int32_t* __restrict__ idx, int n, int E, int32_t* counts, int32_t* status) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= n) return;
+  const int e = idx[p];
+  if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+  else set_status(status, 1);
+}
+
+// One block: offsets of each expert's pair list (shared experts hold every
+// token) and the prefix of its tile count.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int E, int S, int T,
+                                                     int32_t* __restrict__ offs, int32_t* __restrict__ mtoff) {
+  __shared__ int32_t sc[1024], sm[1024];
+  const int n = E + S, tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  int c_sum = 0, m_sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < n) {
+      const int c = e < E ? counts[e] : T;
+      c_sum += c;
+      m_sum += (c + kMT - 1) / kMT;
+    }
+  }
+  sc[tid] = c_sum;
+  sm[tid] = m_sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan (Hillis-Steele)
+    const int a = tid >= o ? sc[tid - o] : 0, b = tid >= o ? sm[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += a;
+    sm[tid] += b;
+    __syncthreads();
+  }
+  int co = sc[tid] - c_sum, mo = sm[tid] - m_sum;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < n) {
+      const int c = e < E ? counts[e] : T;
+      offs[e] = co;
+      mtoff[e] = mo;
+      co += c;
+      mo += (c + kMT - 1) / kMT;
+    }
+  }
+  if (tid == 1023) {
+    offs[n] = sc[1023];
+    mtoff[n] = sm[1023];
+  }
+}
+
+// One block per expert: its pairs in token order (p = t*K + slot ascending),
+// stored as row ids t*(K+S) + slot.
+__global__ __launch_bounds__(kPThreads) void compact_kernel(const int32_t* __restrict__ idx, int T, int K, int S,
+                                                             int E, const int32_t* __restrict__ offs,
+                                                             int32_t* __restrict__ lists) {
+  __shared__ int wc[kPThreads / 64];
+  __shared__ int running;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = offs[e], KS = K + S;
+  if (e >= E) {
+    for (int t = tid; t < T; t += kPThreads) lists[base + t] = t * KS + K + (e - E);
+    return;
+  }
+  if (tid == 0) running = 0;
+  __syncthreads();
+  const int n = T * K;
+  for (int p0 = 0; p0 < n; p0 += kPThreads) {
+    const int p = p0 + tid;
+    const bool hit = p < n && idx[p] == e;
+    const uint64_t mask = __ballot(hit);
+    if (lane == 0) wc[wave] = __popcll(mask);
+    __syncthreads();
+    int before = running;
+    for (int w2 = 0; w2 < wave; ++w2) before += wc[w2];
+    if (hit) {
+      const int r = before + __popcll(mask & ((1ull << lane) - 1));
+      lists[base + r] = (p / K) * KS + p % K;
+    }
+    __syncthreads();
+    if (tid == 0)
+      for (int w2 = 0; w2 < kPThreads / 64; ++w2) running += wc[w2];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------- expert GEMMs
+struct GemmArgs {
+  const void* const* blobs;   // this layer's table row [E + S]
+  int E, S, K, H, I;
+  const int32_t* offs;        // [E + S + 1]
+  const int32_t* mtoff;       // [E + S + 1]
+  const int32_t* lists;       // pair rows grouped by expert
+  const _Float16* xh;         // [T][H] permuted fp16 (gate/up input)
+  _Float16* abuf;             // [T*(K+S)][I] permuted fp16 (gate/up out, down in)
+  float* dbuf;                // [T*(K+S)][H] fp32 (down out)
+  int32_t* status;
+};
+
+// Eight fp16 weights of one packed word, dequantised: w = q*s + b.
+__device__ __forceinline__ half8 dequant_word(uint32_t word, half2v s2, half2v b2) {
+  const half2v m2 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;   // (1024 + q_i, 1024 + q_{i+4})
+    const half2v q = __builtin_bit_cast(half2v, t) + m2;
+    const half2v v = q * s2 + b2;
+    r[2 * i] = v[0];
+    r[2 * i + 1] = v[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ void sb_halves(uint32_t sb, half2v& s2, half2v& b2) {
+  const _Float16 s = (_Float16)__uint_as_float(sb << 16), b = (_Float16)__uint_as_float(sb & 0xFFFF0000u);
+  s2 = half2v{s, s};
+  b2 = half2v{b, b};
+}
+
+// GU: gate and up rows (2 matrices), SwiGLU into abuf.  Otherwise down rows
+// into dbuf.  NPF chunks of weights are in flight per wave; it divides the
+// chunk count.
+template <bool GU, int NPF>
+__global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
+  constexpr int NMAT = GU ? 2 : 1;
+  __shared__ __align__(16) _Float16 As[2][kMT * kPitch];
+  __shared__ int32_t src_row[kMT], dst_row[kMT];
+  __shared__ int s_e, s_row0, s_n;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = a.E, S = a.S, KS = a.K + S;
+  const int KD = GU ? a.H : a.I;            // reduction length
+  const int NR = GU ? a.I : a.H;            // weight rows per matrix
+  const int NC = KD / kKC;                  // chunks
+  const int NT = NR / kNT;                  // tiles along the weight rows
+  const int n_mt = a.mtoff[E + S];
+  const int total = (n_mt + 7) / 8 * 8 * NT;
+  const int64_t qsec = (int64_t)a.H * a.I / 2;   // bytes of one q section
+  const int64_t ssec = (int64_t)a.H * a.I / 64 * 4;
+
+  for (int wi = blockIdx.x; wi < total; wi += gridDim.x) {
+    // the NT tiles of one row tile land on one XCD (wi mod 8)
+    const int grp = wi / (8 * NT), r8 = wi % (8 * NT);
+    const int nt = r8 / 8, mt = grp * 8 + r8 % 8;
+    if (mt >= n_mt) continue;   // uniform over the block
+    if (tid == 0) {
+      int lo = 0, hi = E + S;   // last e with mtoff[e] <= mt
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (a.mtoff[mid] <= mt) lo = mid; else hi = mid;
+      }
+      const int mi = mt - a.mtoff[lo];
+      const int cnt = a.offs[lo + 1] - a.offs[lo];
+      s_e = lo;
+      s_row0 = a.offs[lo] + mi * kMT;
+      s_n = min(kMT, cnt - mi * kMT);
+    }
+    __syncthreads();
+    const int e = s_e, nrows = s_n;
+    if (tid < kMT) {
+      const int p = a.lists[s_row0 + min(tid, nrows - 1)];   // padding rows repeat a real row
+      src_row[tid] = GU ? p / KS : p;
+      dst_row[tid] = p;
+    }
+    const uint8_t* blob = uniform_ptr(static_cast<const uint8_t*>(a.blobs[e]));
+    __syncthreads();
+    if (blob == nullptr) {   // missing expert: flag it, leave its outputs unwritten
+      if (tid == 0) set_status(a.status, 1);
+      continue;
+    }
+    const int nmb = (nrows + 15) / 16;
+
+    // this lane's weight rows, matrices and packed-word offsets
+    const int q4 = lane >> 4;                     // k quarter of the MFMA operand
+    const uint32_t* qrow[NMAT][kNBW];
+    const uint32_t* srow[NMAT][kNBW];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int nb = 0; nb < kNBW; ++nb) {
+        const int n = nt * kNT + wave * (16 * kNBW) + nb * 16 + (lane & 15);
+        const int sec = GU ? m : 2;
+        qrow[m][nb] = reinterpret_cast<const uint32_t*>(blob + sec * qsec + (int64_t)n * (KD / 2)) + 2 * q4;
+        srow[m][nb] = reinterpret_cast<const uint32_t*>(blob + 3 * qsec + sec * ssec) + (int64_t)n * (KD / 64);
+      }
+
+    // activation rows: thread -> (row, quarter of a 128-K chunk)
+    const int arow = tid >> 2, apart = tid & 3;
+    const _Float16* asrc = GU ? a.xh + (int64_t)src_row[arow] * KD : a.abuf + (int64_t)src_row[arow] * KD;
+    auto load_a = [&](int c, u32x4 (&v)[4]) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(asrc + c * kKC + apart * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = load_stream(p + i);
+    };
+    auto store_a = [&](int buf, const u32x4 (&v)[4]) {
+      u32x4* d = reinterpret_cast<u32x4*>(&As[buf][arow * kPitch + apart * 32]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = v[i];
+    };
+
+    // raw weights of one chunk: [matrix][n block][group] two words + scale/bias
+    struct Raw {
+      uint32_t q[NMAT][kNBW][2][2];
+      uint32_t sb[NMAT][kNBW][2];
+    };
+    Raw raw[NPF];
+    auto load_w = [&](int c, Raw& r) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int nb = 0; nb < kNBW; ++nb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int grp64 = 2 * c + g;
+            const u32x2 w2 = load_stream(reinterpret_cast<const u32x2*>(qrow[m][nb] + 8 * grp64));
+            r.q[m][nb][g][0] = w2.x;
+            r.q[m][nb][g][1] = w2.y;
+            r.sb[m][nb][g] = load_stream(srow[m][nb] + grp64);
+          }
+    };
+
+    float4v acc[NMAT][kNBW][kMB];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int nb = 0; nb < kNBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) acc[m][nb][mb] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: NPF chunks of weights in flight, chunk 0 of activations in LDS
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) load_w(min(j, NC - 1), raw[j]);
+    {
+      u32x4 v[4];
+      load_a(0, v);
+      store_a(0, v);
+    }
+    block_sync_lds();
+
+    for (int c0 = 0; c0 < NC; c0 += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        const int c = c0 + j;
+        const int buf = c & 1;
+        u32x4 an[4];
+        load_a(min(c + 1, NC - 1), an);   // next chunk's activations
+        const _Float16* A = &As[buf][0];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          half8 bw[NMAT][kNBW][2];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int nb = 0; nb < kNBW; ++nb) {
+              half2v s2, b2;
+              sb_halves(raw[j].sb[m][nb][g], s2, b2);
+#pragma unroll
+              for (int hk = 0; hk < 2; ++hk) bw[m][nb][hk] = dequant_word(raw[j].q[m][nb][g][hk], s2, b2);
+            }
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb) {
+            if (mb < nmb) {   // uniform over the block
+#pragma unroll
+              for (int hk = 0; hk < 2; ++hk) {
+                const half8 af = *reinterpret_cast<const half8*>(
+                    A + (mb * 16 + (lane & 15)) * kPitch + g * 64 + 8 * (2 * q4 + hk));
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                  for (int nb = 0; nb < kNBW; ++nb)
+                    acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[m][nb][hk], acc[m][nb][mb], 0, 0, 0);
+              }
+            }
+          }
+        }
+        load_w(min(c + NPF, NC - 1), raw[j]);
+        store_a(buf ^ 1, an);
+        block_sync_lds();
+      }
+    }
+
+    // epilogue: lane holds weight row n = ... + (lane & 15), rows 4*(lane>>4)+i of each block
+#pragma unroll
+    for (int nb = 0; nb < kNBW; ++nb) {
+      const int n = nt * kNT + wave * (16 * kNBW) + nb * 16 + (lane & 15);
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mb * 16 + 4 * q4 + i;
+          if (r < nrows) {
+            const int p = dst_row[r];
+            if constexpr (GU) {
+              const float gv = acc[0][nb][mb][i], uv = acc[1 % NMAT][nb][mb][i];
+              a.abuf[(int64_t)p * a.I + perm_pos(n)] = (_Float16)(gv / (1.0f + __expf(-gv)) * uv);
+            } else {
+              a.dbuf[(int64_t)p * a.H + n] = acc[0][nb][mb][i];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // row tables and LDS reused by the next tile
+  }
+}
+
+// --------------------------------------------------------------- combine
+// h[t][i] += sum_{s<K} w[t][s] d[t][s][i] + sum_shared d[t][K+j][i], in
+// slot order, one fma per term.
+__global__ __launch_bounds__(kPThreads) void combine_kernel(float* __restrict__ h, const float* __restrict__ dbuf,
+                                                             const float* __restrict__ w, int K, int S, int H) {
+  const int t = blockIdx.x, KS = K + S;
+  const float* d = dbuf + (int64_t)t * KS * H;
+  for (int i = threadIdx.x; i < H; i += kPThreads) {
+    float acc = h[(int64_t)t * H + i];
+    for (int s = 0; s < K; ++s) acc = fmaf(w[(int64_t)t * K + s], d[(int64_t)s * H + i], acc);
+    for (int s = K; s < KS; ++s) acc = fmaf(1.0f, d[(int64_t)s * H + i], acc);
+    h[(int64_t)t * H + i] = acc;
+  }
+}
+
+template <bool GU>
+hipError_t launch_gemm(const GemmArgs& g, int nc, int grid, hipStream_t st) {
+  if (!GU && nc % 4 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 4>), dim3(grid), dim3(kPThreads), 0, st, g);
+  else if (nc % 2 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 2>), dim3(grid), dim3(kPThreads), 0, st, g);
+  else hipLaunchKernelGGL((gemm_kernel<GU, 1>), dim3(grid), dim3(kPThreads), 0, st, g);
+  return hipGetLastError();
+}
+
+int device_cus_prefill() {
+  static int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+  }();
+  return n;
+}
+
+}  // namespace
+
+PrefillLayout prefill_layout(const moeq_shape& s, int T, int k) {
+  PrefillLayout p;
+  const int64_t KS = (int64_t)k + s.n_shared, P = (int64_t)T * KS, n = s.n_experts + s.n_shared;
+  p.status = 0;
+  p.inv = 256;
+  p.xh = p.inv + align_up((int64_t)T * 8);
+  p.logits = p.xh + align_up((int64_t)T * s.hidden * 2);
+  p.idx = p.logits + align_up((int64_t)T * s.n_experts * 8);
+  p.w = p.idx + align_up((int64_t)T * k * 4);
+  p.counts = p.w + align_up((int64_t)T * k * 4);
+  p.offs = p.counts + align_up(n * 4);
+  p.mtoff = p.offs + align_up((n + 1) * 4);
+  p.lists = p.mtoff + align_up((n + 1) * 4);
+  p.abuf = p.lists + align_up(P * 4);
+  p.dbuf = p.abuf + align_up(P * s.inter * 2);
+  p.total = p.dbuf + align_up(P * s.hidden * 4);
+  return p;
+}
+
+hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, const uint16_t* const* routers,
+                                int layer, int T, int k, uint32_t flags, float* h, int32_t* trace,
+                                char* ws, hipStream_t st) {
+  const PrefillLayout W = prefill_layout(s, T, k);
+  const int E = s.n_experts, S = s.n_shared, H = s.hidden, I = s.inter, KS = k + S;
+  double* inv = reinterpret_cast<double*>(ws + W.inv);
+  _Float16* xh = reinterpret_cast<_Float16*>(ws + W.xh);
+  double* logits = reinterpret_cast<double*>(ws + W.logits);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + W.idx);
+  float* w = reinterpret_cast<float*>(ws + W.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + W.counts);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + W.offs);
+  int32_t* mtoff = reinterpret_cast<int32_t*>(ws + W.mtoff);
+  int32_t* lists = reinterpret_cast<int32_t*>(ws + W.lists);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + W.status);
+
+  hipLaunchKernelGGL(norm_kernel, dim3(T), dim3(kPThreads), 0, st, h, H, inv, xh, counts, E);
+  hipLaunchKernelGGL(router_kernel, dim3((T + kRT - 1) / kRT, (E + kRT - 1) / kRT), dim3(kPThreads), 0, st, h,
+                     routers, layer, T, H, E, inv, logits);
+  const int nr = (flags & MOEQ_F_NO_RENORM) ? 1 : 0;
+  if (E <= 512)
+    hipLaunchKernelGGL(topk_kernel<2>, dim3(T), dim3(kPThreads), 0, st, logits, E, k, nr, idx, w, trace);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, dim3(T), dim3(kPThreads), 0, st, logits, E, k, nr, idx, w, trace);
+  hipLaunchKernelGGL(count_kernel, dim3((T * k + 255) / 256), dim3(256), 0, st, idx, T * k, E, counts, status);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, E, S, T, offs, mtoff);
+  hipLaunchKernelGGL(compact_kernel, dim3(E + S), dim3(kPThreads), 0, st, idx, T, k, S, E, offs, lists);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  GemmArgs g{};
+  g.blobs = blobs + (int64_t)layer * (E + S);
+  g.E = E; g.S = S; g.K = k; g.H = H; g.I = I;
+  g.offs = offs; g.mtoff = mtoff; g.lists = lists;
+  g.xh = xh;
+  g.abuf = reinterpret_cast<_Float16*>(ws + W.abuf);
+  g.dbuf = reinterpret_cast<float*>(ws + W.dbuf);
+  g.status = status;
+  const int grid = 2 * max(8, device_cus_prefill() / 8 * 8);
+  if ((e = launch_gemm<true>(g, H / kKC, grid, st)) != hipSuccess) return e;
+  if ((e = launch_gemm<false>(g, I / kKC, grid, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kPThreads), 0, st, h, g.dbuf, w, k, S, H);
+  (void)KS;
+  return hipGetLastError();
+}
+
+}  // namespace moeq
+
+using namespace moeq;
+
+extern "C" {
+
+int moeq_prefill_workspace_bytes(const moeq_shape* s, int T, int k, int64_t* bytes) {
+  if (int rc = check_shape(s)) return rc;
+  if (!bytes) return fail(MOEQ_E_INVALID, "bytes is NULL");
+  if (T < 0 || k < 0) return fail(MOEQ_E_INVALID, "T=%d k=%d must be non-negative", T, k);
+  *bytes = prefill_layout(*s, T, k).total;
+  return ok();
+}
+
+int moe_expert_stack_prefill(const moeq_shape* s, const moeq_experts* ex, const uint16_t* const* w_router,
+                             int layer0, int L, int T, int k, uint32_t flags, float* h, int32_t* topk_trace,
+                             void* workspace, void* stream) {
+  if (int rc = check_shape(s)) return rc;
+  if (s->bits != 4) return fail(MOEQ_E_UNSUPPORTED, "prefill is implemented for 4-bit experts (bits=%d)", s->bits);
+  if (s->hidden % kKC || s->inter % kNT || s->hidden % kNT)
+    return fail(MOEQ_E_UNSUPPORTED, "prefill needs hidden and inter multiples of %d (hidden=%d inter=%d)", kNT,
+                s->hidden, s->inter);
+  if (T < 0 || L < 0 || layer0 < 0) return fail(MOEQ_E_INVALID, "T=%d L=%d layer0=%d must be >= 0", T, L, layer0);
+  if (k < 1 || k > s->n_experts || k > MOEQ_MAX_TOPK)
+    return fail(k > MOEQ_MAX_TOPK ? MOEQ_E_UNSUPPORTED : MOEQ_E_INVALID, "k=%d outside [1, min(E, %d)]", k,
+                MOEQ_MAX_TOPK);
+  if ((int64_t)T * (k + s->n_shared) > INT_MAX / 2 || (int64_t)T * s->n_experts > INT_MAX / 2)
+    return fail(MOEQ_E_UNSUPPORTED, "T=%d too large", T);
+  if (flags & ~(uint32_t)MOEQ_F_NO_RENORM) return fail(MOEQ_E_UNSUPPORTED, "flags 0x%x: only MOEQ_F_NO_RENORM", flags);
+  if (T == 0 || L == 0) return ok();
+  if (!ex || !ex->blobs || !w_router || !h || !workspace)
+    return fail(MOEQ_E_INVALID, "experts, w_router, h and workspace must be non-NULL");
+  if (layer0 + L > ex->n_layers)
+    return fail(MOEQ_E_INVALID, "layers [%d, %d) exceed the table's %d", layer0, layer0 + L, ex->n_layers);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < L; ++l) {
+    int32_t* tr = topk_trace ? topk_trace + (int64_t)l * T * k : nullptr;
+    const hipError_t e = launch_prefill_layer(*s, ex->blobs, w_router, layer0 + l, T, k, flags, h, tr,
+                                              static_cast<char*>(workspace), st);
+    if (e != hipSuccess) return hip_fail(e, "prefill layer launch");
+  }
+  return ok();
+}
+
+}  // extern "C"
