@@ -13,7 +13,9 @@ expert bytes come from HBM (the set is far larger than the caches).
 
 Other workloads (--workload): decode_4bit, decode_2bit, batch16_top10 --
 one layer per step, rotating over --instances resident layer instances so
-every expert byte is read from HBM.
+every expert byte is read from HBM; stack60_prefill -- 2048 tokens through
+the same 60 resident layers per step (top-10 + shared, grouped
+dequant-GEMMs on MFMA).
 
 Inputs are seeded synthetic data (SplitMix64 streams); no trained weights
 or prompts.  Prints ONE JSON line on stdout; progress goes to stderr.
@@ -45,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=64)
     p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--workload", default="stack60_decode",
-                   choices=["stack60_decode", "decode_4bit", "decode_2bit", "batch16_top10"])
+                   choices=["stack60_decode", "decode_4bit", "decode_2bit", "batch16_top10", "stack60_prefill"])
     p.add_argument("--layerwise", action="store_true",
                    help="stack60_decode: per-layer launches instead of the persistent kernel")
     p.add_argument("--instances", type=int, default=8, help="layer instances for cold rotation")
@@ -222,6 +224,82 @@ def run_stack(args, cfg, dev, stream):
     return rec
 
 
+def run_prefill(args, cfg, dev, stream):
+    """T-token prefill through all resident layers per step (grouped
+    dequant-GEMMs on MFMA); per-kernel times from HIP events on the stream."""
+    import torch
+    import quantized_expert_gemv_router_amd as q
+    import synth
+
+    shape, table, routers, _ = setup_layers(cfg, cfg.layers, dev, stream)
+    rt = q.RouterTable(routers, device=dev)
+    T, K = cfg.tokens, cfg.top_k
+    total = args.warmup + args.steps
+    sets = [torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, 3000 + i, T)).astype(np.float32)).to(dev)
+            for i in range(min(total, 4))]
+    hs = [sets[s % len(sets)].clone() for s in range(total)]
+    ws = q.new_prefill_workspace(shape, T, K, dev)
+    tk = torch.empty((cfg.layers, T, K), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(s, trace=None):
+        import ctypes
+        rc = q.lib().moe_expert_stack_prefill(ctypes.byref(shape), table.view(), rt.ptr(), 0, cfg.layers, T, K,
+                                              0, hs[s].data_ptr(), None if trace is None else trace.data_ptr(),
+                                              ws.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(q.moeq_last_error())
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            step(s, tk if s == args.warmup - 1 else None)
+        torch.cuda.synchronize()
+        q.moeq_prefill_timing(True)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    kt = q.moeq_prefill_timing_read()
+    q.moeq_prefill_timing(False)
+    status = q.moe_read_device_status(ws, stream)
+    if status != 0:
+        raise RuntimeError(f"device status {status} after the timed region")
+    elapsed_ms = start.elapsed_time(end)
+    idx = tk.cpu().numpy()
+    touched = np.array([np.count_nonzero(np.bincount(idx[l].ravel(), minlength=cfg.n_experts))
+                        for l in range(cfg.layers)]) + cfg.n_shared
+    expert_bytes = int(touched.sum()) * cfg.expert_bytes          # per step (the warm-up's routing)
+    router_bytes = cfg.layers * cfg.n_experts * cfg.hidden * 2
+    sec = elapsed_ms / 1e3
+    # dominant kernel: the gate/up GEMM (2/3 of the weight bytes)
+    gu_ms, gu_n = kt["gate_up"]
+    gu_bytes = expert_bytes * 2 // 3 // cfg.layers               # per launch (one layer)
+    gu_gbs = gu_bytes / (gu_ms / gu_n / 1e3) / 1e9
+    pairs = T * (K + cfg.n_shared)
+    gu_flop = 2.0 * pairs * 2 * cfg.inter * cfg.hidden            # per launch
+    rec = base_record(args, cfg, steps_tokens=args.steps * T, elapsed_ms=elapsed_ms, wall=wall)
+    rec.update({
+        "gbps_expert": round(expert_bytes * args.steps / sec / 1e9, 1),
+        "gbps_all_bytes": round((expert_bytes + router_bytes) * args.steps / sec / 1e9, 1),
+        "frac_hbm_peak": round(expert_bytes * args.steps / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "expert_layers_per_s": round(args.steps * T * cfg.layers / sec, 1),
+        "kernel_ms_per_layer": {k: round(v[0] / max(v[1], 1), 4) for k, v in kt.items()},
+        "roofline": {"kernel": "gemm_kernel<gate/up> (grouped dequant-GEMM, fp16 MFMA)", "bound": "hbm",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(gu_ms / gu_n * 1e3, 2), "bytes_per_launch": int(gu_bytes),
+                     "mfma_tflops": round(gu_flop / (gu_ms / gu_n / 1e3) / 1e12, 1),
+                     "mfma_peak_tflops": 2500.0},
+    })
+    rec["config"].update(layers_per_step=cfg.layers, experts_touched_per_layer=float(touched.mean()),
+                         resident_gb=round(cfg.layers * cfg.n_slots * cfg.expert_bytes / 1e9, 1))
+    return rec
+
+
 def run_layer_workload(args, cfg, dev, stream):
     import torch
     import quantized_expert_gemv_router_amd as q
@@ -342,7 +420,9 @@ def main():
         return
     cfg = synth.CONFIGS[args.workload]
     stream = torch.cuda.Stream(device=dev)
-    if cfg.layers > 1:
+    if cfg.layers > 1 and cfg.tokens > 1:
+        rec = run_prefill(args, cfg, dev, stream)
+    elif cfg.layers > 1:
         rec = run_stack(args, cfg, dev, stream)
     else:
         rec = run_layer_workload(args, cfg, dev, stream)

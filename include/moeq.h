@@ -209,6 +209,16 @@ int moe_expert_stack_prefill(const moeq_shape* shape, const moeq_experts* expert
  * (about 440 MB at T=2048, k=10, hidden 4096, inter 1024, 512+1 experts). */
 int moeq_prefill_workspace_bytes(const moeq_shape* shape, int T, int k, int64_t* bytes);
 
+/* Diagnostic timing of the prefill kernels: with enable != 0, every later
+ * moe_expert_stack_prefill layer records HIP events on its stream around
+ * each kernel class (0 norm, 1 router, 2 top-K, 3 grouping, 4 gate/up GEMM,
+ * 5 down GEMM, 6 combine).  moeq_prefill_timing_read waits for them and
+ * returns, per class, the summed milliseconds ms[7] and the number of
+ * timed launches launches[7], then discards the events; timing stays on
+ * until moeq_prefill_timing(0). */
+int moeq_prefill_timing(int enable);
+int moeq_prefill_timing_read(double* ms, int32_t* launches);
+
 /* Which path the last successful moe_expert_stack_decode on this thread
  * took: 1 = persistent launch, 2 = per-layer launches, 0 = none yet. */
 int moeq_last_stack_path(void);

@@ -16,4 +16,5 @@ from ._binding import (  # noqa: F401
     moe_expert_stack_decode, moeq_last_stack_path, moeq_stack_clock_trace,
     new_workspace, moe_layer, Pool, PoolSim, PoolView,
     moe_expert_stack_prefill, moeq_prefill_workspace_bytes, new_prefill_workspace,
+    moeq_prefill_timing, moeq_prefill_timing_read, PREFILL_KERNELS,
 )

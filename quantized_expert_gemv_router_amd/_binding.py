@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
                                               _P, _P]
         L.moe_expert_stack_prefill.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P, _P]
         L.moeq_prefill_workspace_bytes.argtypes = [S, _I, _I, ctypes.POINTER(ctypes.c_int64)]
+        L.moeq_prefill_timing.argtypes = [_I]
+        L.moeq_prefill_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
         H = ctypes.POINTER(ctypes.c_void_p)
         I64 = ctypes.c_int64
         L.moe_pool_create.argtypes = [S, _I, _P, I64, I64, _P, _P, _P, H]
@@ -288,6 +290,21 @@ def moe_expert_stack_prefill(shape: Shape, experts, routers: RouterTable, h: tor
     _check(lib().moe_expert_stack_prefill(ctypes.byref(shape), experts.view(), routers.ptr(), layer0, L, T, k,
                                           flags, _ptr(h), _ptr(tk), _ptr(workspace), _stream(stream)))
     return tk
+
+
+PREFILL_KERNELS = ("norm", "router", "topk", "group", "gate_up", "down", "combine")
+
+
+def moeq_prefill_timing(enable: bool = True):
+    _check(lib().moeq_prefill_timing(int(enable)))
+
+
+def moeq_prefill_timing_read() -> dict:
+    """{class: (summed ms, launches)} of the prefill kernels timed so far."""
+    ms = (ctypes.c_double * 7)()
+    n = (ctypes.c_int32 * 7)()
+    _check(lib().moeq_prefill_timing_read(ms, n))
+    return {k: (ms[i], n[i]) for i, k in enumerate(PREFILL_KERNELS)}
 
 
 def moeq_last_stack_path() -> int:

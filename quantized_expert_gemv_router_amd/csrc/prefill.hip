@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <vector>
 
 #include "moeq.h"
 #include "moeq_device.hpp"
@@ -40,7 +41,6 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPThreads = 256;          // four waves
 constexpr int kMB = 4;                  // row blocks of 16 per tile
@@ -49,6 +49,7 @@ constexpr int kNBW = 2;                 // blocks of 16 weight rows per wave
 constexpr int kNT = 4 * 16 * kNBW;      // weight rows per tile
 constexpr int kKC = 128;                // K per chunk (two groups of 64)
 constexpr int kPitch = kKC + 8;         // LDS row pitch in halves (bank spread)
+constexpr int kSbWin = 8;               // chunks per scale/bias window (16 groups)
 
 // position of value j of a packed word in the stored (MFMA) order
 __device__ __forceinline__ int perm_pos(int r) {
@@ -295,6 +296,9 @@ template <bool GU, int NPF>
 __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
   constexpr int NMAT = GU ? 2 : 1;
   __shared__ __align__(16) _Float16 As[2][kMT * kPitch];
+  // scale/bias words of the tile's rows, windows of 2*kSbWin groups,
+  // double-buffered: [buffer][matrix][row][group in window]
+  __shared__ __align__(16) uint32_t Sb[2][NMAT][kNT][2 * kSbWin];
   __shared__ int32_t src_row[kMT], dst_row[kMT];
   __shared__ int s_e, s_row0, s_n;
 
@@ -345,16 +349,36 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
     // this lane's weight rows, matrices and packed-word offsets
     const int q4 = lane >> 4;                     // k quarter of the MFMA operand
     const uint32_t* qrow[NMAT][kNBW];
-    const uint32_t* srow[NMAT][kNBW];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int nb = 0; nb < kNBW; ++nb) {
         const int n = nt * kNT + wave * (16 * kNBW) + nb * 16 + (lane & 15);
         const int sec = GU ? m : 2;
-        qrow[m][nb] = reinterpret_cast<const uint32_t*>(blob + sec * qsec + (int64_t)n * (KD / 2)) + 2 * q4;
-        srow[m][nb] = reinterpret_cast<const uint32_t*>(blob + 3 * qsec + sec * ssec) + (int64_t)n * (KD / 64);
+        qrow[m][nb] = reinterpret_cast<const uint32_t*>(blob + sec * qsec + (int64_t)n * (KD / 2)) + 4 * q4;
       }
+    // scale/bias windows: thread -> (matrix, row, quarter of the window's 16
+    // words); piece p of NPIECE covers rows [p*PR, (p+1)*PR) of every matrix
+    const int gpr = KD / 64;
+    constexpr int PR = kPThreads / 4 / NMAT;       // rows per piece and matrix
+    constexpr int NPIECE = kNT / PR;               // pieces per window
+    const int sb_m = tid / (kPThreads / NMAT), sb_r = (tid / 4) % PR, sb_qt = tid & 3;
+    const uint32_t* sb_src = reinterpret_cast<const uint32_t*>(blob + 3 * qsec + (GU ? sb_m : 2) * ssec) +
+                             (int64_t)(nt * kNT + sb_r) * gpr + 4 * sb_qt;
+    auto load_sb = [&](int win, int piece) -> u32x4 {   // window win, piece piece
+      const int w = min(win, (NC - 1) / kSbWin);
+      const int g0 = w * 2 * kSbWin + 4 * sb_qt;          // first group of this thread's four
+      const uint32_t* p = sb_src + (int64_t)piece * PR * gpr + w * 2 * kSbWin;
+      if (g0 + 4 <= gpr) return load_stream(reinterpret_cast<const u32x4*>(p));
+      u32x4 v = {0u, 0u, 0u, 0u};                          // rows shorter than a window
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (g0 + e < gpr) v[e] = load_stream(p + e);
+      return v;
+    };
+    auto store_sb = [&](int buf, int piece, u32x4 v) {
+      *reinterpret_cast<u32x4*>(&Sb[buf][sb_m][piece * PR + sb_r][4 * sb_qt]) = v;
+    };
 
     // activation rows: thread -> (row, quarter of a 128-K chunk)
     const int arow = tid >> 2, apart = tid & 3;
@@ -370,25 +394,19 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i) d[i] = v[i];
     };
 
-    // raw weights of one chunk: [matrix][n block][group] two words + scale/bias
+    // raw weights of one chunk: lane quarter q4 holds the four contiguous
+    // words 4*q4 .. 4*q4+3 of the chunk's 16 (all in group 2c + q4/2, so one
+    // scale/bias pair); MFMA k-step h takes word 4*q4 + h.  The weights are
+    // fully dequantised, so a k-step may span two groups.
     struct Raw {
-      uint32_t q[NMAT][kNBW][2][2];
-      uint32_t sb[NMAT][kNBW][2];
+      u32x4 q[NMAT][kNBW];
     };
     Raw raw[NPF];
     auto load_w = [&](int c, Raw& r) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int nb = 0; nb < kNBW; ++nb)
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const int grp64 = 2 * c + g;
-            const u32x2 w2 = load_stream(reinterpret_cast<const u32x2*>(qrow[m][nb] + 8 * grp64));
-            r.q[m][nb][g][0] = w2.x;
-            r.q[m][nb][g][1] = w2.y;
-            r.sb[m][nb][g] = load_stream(srow[m][nb] + grp64);
-          }
+        for (int nb = 0; nb < kNBW; ++nb) r.q[m][nb] = load_stream(reinterpret_cast<const u32x4*>(qrow[m][nb] + 16 * c));
     };
 
     float4v acc[NMAT][kNBW][kMB];
@@ -399,54 +417,70 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) acc[m][nb][mb] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: NPF chunks of weights in flight, chunk 0 of activations in LDS
+    // prologue: NPF chunks of weights and two chunks of activations in
+    // flight, chunk 0 of activations in LDS.  Activations of chunk c+1 are
+    // loaded a full chunk before they are stored, so waiting for them never
+    // waits for the weight loads issued after them (loads complete in order).
+    u32x4 an[2][4];
 #pragma unroll
     for (int j = 0; j < NPF; ++j) load_w(min(j, NC - 1), raw[j]);
+    load_a(0, an[0]);
+    load_a(min(1, NC - 1), an[1]);
     {
-      u32x4 v[4];
-      load_a(0, v);
-      store_a(0, v);
+      u32x4 v[NPIECE];
+#pragma unroll
+      for (int p = 0; p < NPIECE; ++p) v[p] = load_sb(0, p);
+#pragma unroll
+      for (int p = 0; p < NPIECE; ++p) store_sb(0, p, v[p]);
     }
+    store_a(0, an[0]);
     block_sync_lds();
+    // the next window's pieces are loaded one per chunk (piece = chunk mod
+    // NPIECE) and stored one chunk later; every piece is in place before
+    // the window starts
+    u32x4 sbn = load_sb(1, 0);
 
     for (int c0 = 0; c0 < NC; c0 += NPF) {
 #pragma unroll
       for (int j = 0; j < NPF; ++j) {
         const int c = c0 + j;
         const int buf = c & 1;
-        u32x4 an[4];
-        load_a(min(c + 1, NC - 1), an);   // next chunk's activations
+        if (NPF % 2 == 0 ? (j & 1) == 0 : buf == 0) load_a(min(c + 2, NC - 1), an[0]);
+        else load_a(min(c + 2, NC - 1), an[1]);
         const _Float16* A = &As[buf][0];
+        const int wbuf = (c / kSbWin) & 1, wg = (2 * c + (q4 >> 1)) % (2 * kSbWin);
+        half2v s2[NMAT][kNBW], b2[NMAT][kNBW];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          half8 bw[NMAT][kNBW][2];
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int nb = 0; nb < kNBW; ++nb)
+            sb_halves(Sb[wbuf][m][wave * (16 * kNBW) + nb * 16 + (lane & 15)][wg], s2[m][nb], b2[m][nb]);
+        // dequantise one k-step at a time (fewer live registers)
+#pragma unroll
+        for (int hk = 0; hk < 4; ++hk) {
+          half8 bw[NMAT][kNBW];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int nb = 0; nb < kNBW; ++nb) {
-              half2v s2, b2;
-              sb_halves(raw[j].sb[m][nb][g], s2, b2);
-#pragma unroll
-              for (int hk = 0; hk < 2; ++hk) bw[m][nb][hk] = dequant_word(raw[j].q[m][nb][g][hk], s2, b2);
-            }
+            for (int nb = 0; nb < kNBW; ++nb) bw[m][nb] = dequant_word(raw[j].q[m][nb][hk], s2[m][nb], b2[m][nb]);
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) {
             if (mb < nmb) {   // uniform over the block
+              const half8 af = *reinterpret_cast<const half8*>(A + (mb * 16 + (lane & 15)) * kPitch + 8 * (4 * q4 + hk));
 #pragma unroll
-              for (int hk = 0; hk < 2; ++hk) {
-                const half8 af = *reinterpret_cast<const half8*>(
-                    A + (mb * 16 + (lane & 15)) * kPitch + g * 64 + 8 * (2 * q4 + hk));
+              for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                  for (int nb = 0; nb < kNBW; ++nb)
-                    acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[m][nb][hk], acc[m][nb][mb], 0, 0, 0);
-              }
+                for (int nb = 0; nb < kNBW; ++nb)
+                  acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[m][nb], acc[m][nb][mb], 0, 0, 0);
             }
           }
         }
         load_w(min(c + NPF, NC - 1), raw[j]);
-        store_a(buf ^ 1, an);
+        // scale/bias: store the piece loaded last chunk, load the next one
+        store_sb(((c / kSbWin) + 1) & 1, c % NPIECE, sbn);
+        sbn = load_sb((c + 1) / kSbWin + 1, (c + 1) % NPIECE);
+        if (NPF % 2 == 0 ? (j & 1) == 0 : buf == 0) store_a(buf ^ 1, an[1]);
+        else store_a(buf ^ 1, an[0]);
         block_sync_lds();
       }
     }
@@ -493,8 +527,15 @@ __global__ __launch_bounds__(kPThreads) void combine_kernel(float* __restrict__ 
 
 template <bool GU>
 hipError_t launch_gemm(const GemmArgs& g, int nc, int grid, hipStream_t st) {
-  if (!GU && nc % 4 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 4>), dim3(grid), dim3(kPThreads), 0, st, g);
-  else if (nc % 2 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 2>), dim3(grid), dim3(kPThreads), 0, st, g);
+  // gate/up holds two matrices' weights per chunk: two chunks in flight fit
+  // its registers, the down GEMM keeps four
+  if constexpr (!GU) {
+    if (nc % 4 == 0) {
+      hipLaunchKernelGGL((gemm_kernel<GU, 4>), dim3(grid), dim3(kPThreads), 0, st, g);
+      return hipGetLastError();
+    }
+  }
+  if (nc % 2 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 2>), dim3(grid), dim3(kPThreads), 0, st, g);
   else hipLaunchKernelGGL((gemm_kernel<GU, 1>), dim3(grid), dim3(kPThreads), 0, st, g);
   return hipGetLastError();
 }
@@ -508,6 +549,35 @@ int device_cus_prefill() {
   }();
   return n;
 }
+
+// Optional per-kernel-class event pairs on the launch stream (diagnostic
+// timing of the prefill kernels).
+enum { kTNorm, kTRouter, kTTopk, kTGroup, kTGateUp, kTDown, kTCombine, kTClasses };
+struct PrefillTimer {
+  bool on = false;
+  std::vector<hipEvent_t> start[kTClasses], stop[kTClasses];
+  void mark(std::vector<hipEvent_t>* v, hipStream_t st) {
+    if (!on) return;
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventRecord(e, st) != hipSuccess) {
+      (void)hipEventDestroy(e);
+      return;
+    }
+    v->push_back(e);
+  }
+  void begin(int c, hipStream_t st) { mark(&start[c], st); }
+  void end(int c, hipStream_t st) { mark(&stop[c], st); }
+  void clear() {
+    for (int c = 0; c < kTClasses; ++c) {
+      for (hipEvent_t e : start[c]) (void)hipEventDestroy(e);
+      for (hipEvent_t e : stop[c]) (void)hipEventDestroy(e);
+      start[c].clear();
+      stop[c].clear();
+    }
+  }
+};
+PrefillTimer g_timer;
 
 }  // namespace
 
@@ -546,17 +616,26 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   int32_t* lists = reinterpret_cast<int32_t*>(ws + W.lists);
   int32_t* status = reinterpret_cast<int32_t*>(ws + W.status);
 
+  PrefillTimer& tm = g_timer;
+  tm.begin(kTNorm, st);
   hipLaunchKernelGGL(norm_kernel, dim3(T), dim3(kPThreads), 0, st, h, H, inv, xh, counts, E);
+  tm.end(kTNorm, st);
+  tm.begin(kTRouter, st);
   hipLaunchKernelGGL(router_kernel, dim3((T + kRT - 1) / kRT, (E + kRT - 1) / kRT), dim3(kPThreads), 0, st, h,
                      routers, layer, T, H, E, inv, logits);
+  tm.end(kTRouter, st);
   const int nr = (flags & MOEQ_F_NO_RENORM) ? 1 : 0;
+  tm.begin(kTTopk, st);
   if (E <= 512)
     hipLaunchKernelGGL(topk_kernel<2>, dim3(T), dim3(kPThreads), 0, st, logits, E, k, nr, idx, w, trace);
   else
     hipLaunchKernelGGL(topk_kernel<16>, dim3(T), dim3(kPThreads), 0, st, logits, E, k, nr, idx, w, trace);
+  tm.end(kTTopk, st);
+  tm.begin(kTGroup, st);
   hipLaunchKernelGGL(count_kernel, dim3((T * k + 255) / 256), dim3(256), 0, st, idx, T * k, E, counts, status);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, E, S, T, offs, mtoff);
   hipLaunchKernelGGL(compact_kernel, dim3(E + S), dim3(kPThreads), 0, st, idx, T, k, S, E, offs, lists);
+  tm.end(kTGroup, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -569,9 +648,15 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   g.dbuf = reinterpret_cast<float*>(ws + W.dbuf);
   g.status = status;
   const int grid = 2 * max(8, device_cus_prefill() / 8 * 8);
+  tm.begin(kTGateUp, st);
   if ((e = launch_gemm<true>(g, H / kKC, grid, st)) != hipSuccess) return e;
+  tm.end(kTGateUp, st);
+  tm.begin(kTDown, st);
   if ((e = launch_gemm<false>(g, I / kKC, grid, st)) != hipSuccess) return e;
+  tm.end(kTDown, st);
+  tm.begin(kTCombine, st);
   hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kPThreads), 0, st, h, g.dbuf, w, k, S, H);
+  tm.end(kTCombine, st);
   (void)KS;
   return hipGetLastError();
 }
@@ -581,6 +666,33 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
 using namespace moeq;
 
 extern "C" {
+
+int moeq_prefill_timing(int enable) {
+  g_timer.clear();
+  g_timer.on = enable != 0;
+  return ok();
+}
+
+int moeq_prefill_timing_read(double* ms, int32_t* launches) {
+  if (!ms || !launches) return fail(MOEQ_E_INVALID, "ms and launches must be non-NULL");
+  for (int c = 0; c < kTClasses; ++c) {
+    ms[c] = 0.0;
+    launches[c] = 0;
+    const size_t n = g_timer.start[c].size() < g_timer.stop[c].size() ? g_timer.start[c].size()
+                                                                        : g_timer.stop[c].size();
+    for (size_t i = 0; i < n; ++i) {
+      hipError_t e = hipEventSynchronize(g_timer.stop[c][i]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (prefill timing)");
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, g_timer.start[c][i], g_timer.stop[c][i]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime (prefill timing)");
+      ms[c] += t;
+      ++launches[c];
+    }
+  }
+  g_timer.clear();
+  return ok();
+}
 
 int moeq_prefill_workspace_bytes(const moeq_shape* s, int T, int k, int64_t* bytes) {
   if (int rc = check_shape(s)) return rc;
