@@ -127,6 +127,28 @@ def cpu_baseline_stack(cfg, seconds: float):
 
 # -------------------------------------------------------------- workloads
 
+def recorded_stack_traffic():
+    """HBM bytes per launch of the persistent stack kernel from the committed
+    rocprofv3 counter summary, or None when the kernel's sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "stack_kernel_stack60_decode_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("stack_decode.hip", "moeq_device.hpp", "topk.hpp", "moeq_internal.hpp"):
+        with open(os.path.join(ROOT, "quantized_expert_gemv_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256_16") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def setup_layers(cfg, n_layers, dev, stream):
     import torch
     import quantized_expert_gemv_router_amd as q
@@ -215,7 +237,8 @@ def run_stack(args, cfg, dev, stream):
                      "bound": "hbm", "achieved": round(per_launch / (launch_ms / 1e3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(per_launch / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 2),
+                     "traffic": recorded_stack_traffic() if q.moeq_last_stack_path() == 1 else None,
+                     "avg_launch_us": round(launch_ms * 1e3, 2),
                      "bytes_per_launch": int(per_launch),
                      "router_bytes_per_launch": router_bytes},
     })
