@@ -49,6 +49,7 @@ constexpr int kMaxKS = 8;                  // selected + shared experts per laye
 constexpr int kMaxLayers = 128;            // per persistent launch
 constexpr int kTblPer = 8;                 // pointer-table entries per thread (E + S <= 4096)
 static_assert(kWaves * MOEQ_MAX_TOPK <= 64 * 2, "top-K merge holds two candidates per lane");
+static_assert(2 * kWaves >= MOEQ_MAX_TOPK && kWaves * MOEQ_MAX_TOPK >= 64, "threshold top-K sizes");
 
 // ------------------------------------------------------------------ barrier
 struct GridBarrier {
@@ -205,6 +206,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ double selv[MOEQ_MAX_TOPK];
   __shared__ int64_t candk[kWaves * MOEQ_MAX_TOPK];
   __shared__ int candi[kWaves * MOEQ_MAX_TOPK];
+  __shared__ int64_t sample_k[2 * kWaves], cand_tau;
+  __shared__ int cand_n;
   __shared__ float selw[MOEQ_MAX_TOPK];
   __shared__ const uint8_t* eblob[kMaxKS];
   __shared__ const uint16_t* rtr[kMaxLayers];
@@ -256,12 +259,17 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t sd[STEPSD][CPLD];
   const uint8_t* tnext[kTblPer];   // this layer's pointer-table row, in flight to LDS
 
+  // gate/up rows: task t = m * kWaves + wave, the shared experts' rows first,
+  // then the routed ones, so every wave takes part in both phases
   auto gu_task = [&](int m, int& j, int& sec, int& row) -> bool {
-    const int t = wave * RPWG + m;
-    j = t / (2 * RG);
-    sec = (t / RG) % 2;
-    row = b + NB * (t % RG);
-    return j < KS && row < I;
+    const int t = m * kWaves + wave, nsh = S * 2 * RG;
+    const bool shared = t < nsh;
+    const int u = shared ? t : t - nsh;
+    j = (shared ? K : 0) + u / (2 * RG);
+    const int tj = u % (2 * RG);
+    sec = tj / RG;
+    row = b + NB * (tj % RG);
+    return (shared ? j < KS : j < K) && row < I;
   };
   // Loads are planned (every LDS read they need) before any is issued: an
   // LDS read between loads makes the compiler wait for the loads in flight.
@@ -563,8 +571,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     store_tbl_row();
     __syncthreads();
     stamp0(li, 12);
-    if (E <= kThreads) block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
-    else block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
+    if (E <= kThreads) {
+      if (!block_topk_sample<kWaves>(lg, E, K, sample_k, candk, candi, &cand_n, &cand_tau, sel, selv))
+        block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
+    } else {
+      block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
+    }
     if (wave == 0) {
       const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
                                   : wave_softmax_selected(selv, K);

@@ -208,6 +208,70 @@ __device__ __forceinline__ void block_topk_keys(const double* lg, int E, int K, 
   __syncthreads();
 }
 
+// All NW waves, one logit per thread (E <= 64*NW), K <= 2*NW: top-K by a
+// threshold.  Each wave publishes its P = ceil(K/NW) largest keys; tau, the
+// K-th largest of those NW*P samples, is at most the K-th largest key of all
+// E, so every element of the true top-K has a key >= tau, and at least K
+// elements do.  Those candidates are compacted into LDS and ranked by
+// (key desc, index asc) in wave 0.  Returns false (nothing written, block
+// uniform) when more than 64 candidates pass, e.g. under massive ties; the
+// caller then runs block_topk_keys.  Scratch: wk [2*NW], ck/ci [64], cnt,
+// tau.  Ends with a block barrier.
+template <int NW>
+__device__ __forceinline__ bool block_topk_sample(const double* lg, int E, int K, int64_t* wk, int64_t* ck,
+                                                  int* ci, int* cnt, int64_t* tau, int* sel, double* selv) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int P = (K + NW - 1) / NW;
+  const int64_t key = tid < E ? order_key(lg[tid]) : kNoKey;
+  const int64_t m1 = wave_max_key(key);
+  int64_t m2 = kNoKey;
+  if (P > 1) {   // second largest: drop one lane holding the maximum
+    const uint64_t mask = __ballot(key == m1);
+    m2 = wave_max_key(lane == __builtin_ctzll(mask) ? kNoKey : key);
+  }
+  if (lane == 0) {
+    wk[w * P] = m1;
+    if (P > 1) wk[w * P + 1] = m2;
+  }
+  if (tid == 0) *cnt = 0;
+  __syncthreads();
+  if (tid < NW * P) {   // the sample of rank K-1 (ties by sample position)
+    const int64_t v = wk[tid];
+    int r = 0;
+    for (int s = 0; s < NW * P; ++s) {
+      const int64_t o = wk[s];
+      r += (o > v || (o == v && s < tid)) ? 1 : 0;
+    }
+    if (r == K - 1) *tau = v;
+  }
+  __syncthreads();
+  if (tid < E && key >= *tau) {
+    const int slot = atomicAdd(cnt, 1);
+    if (slot < 64) {
+      ck[slot] = key;
+      ci[slot] = tid;
+    }
+  }
+  __syncthreads();
+  const int C = *cnt;
+  if (C > 64) return false;
+  if (tid < C) {
+    const int64_t v = ck[tid];
+    const int vi = ci[tid];
+    int r = 0;
+    for (int c = 0; c < C; ++c) {
+      const int64_t o = ck[c];
+      r += (o > v || (o == v && ci[c] < vi)) ? 1 : 0;
+    }
+    if (r < K) {
+      sel[r] = vi;
+      selv[r] = lg[vi];
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
 // One wave, K <= 64: softmax weights over the K selected logits (fp64,
 // rounded to fp32), one exponential per lane.  Returns lane's weight.
 __device__ __forceinline__ float wave_softmax_selected(const double* selv, int K) {
