@@ -292,13 +292,15 @@ __device__ __forceinline__ void sb_halves(uint32_t sb, half2v& s2, half2v& b2) {
 // GU: gate and up rows (2 matrices), SwiGLU into abuf.  Otherwise down rows
 // into dbuf.  NPF chunks of weights are in flight per wave; it divides the
 // chunk count.
-template <bool GU, int NPF>
-__global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
+template <bool GU, int NPF, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs a) {
   constexpr int NMAT = GU ? 2 : 1;
+  constexpr int NTH = 64 * NW;              // threads
+  constexpr int NTR = NW * 16 * kNBW;       // weight rows per tile
   __shared__ __align__(16) _Float16 As[2][kMT * kPitch];
   // scale/bias words of the tile's rows, windows of 2*kSbWin groups,
   // double-buffered: [buffer][matrix][row][group in window]
-  __shared__ __align__(16) uint32_t Sb[2][NMAT][kNT][2 * kSbWin];
+  __shared__ __align__(16) uint32_t Sb[2][NMAT][NTR][2 * kSbWin];
   __shared__ int32_t src_row[kMT], dst_row[kMT];
   __shared__ int s_e, s_row0, s_n;
 
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
   const int KD = GU ? a.H : a.I;            // reduction length
   const int NR = GU ? a.I : a.H;            // weight rows per matrix
   const int NC = KD / kKC;                  // chunks
-  const int NT = NR / kNT;                  // tiles along the weight rows
+  const int NT = NR / NTR;                  // tiles along the weight rows
   const int n_mt = a.mtoff[E + S];
   const int total = (n_mt + 7) / 8 * 8 * NT;
   const int64_t qsec = (int64_t)a.H * a.I / 2;   // bytes of one q section
@@ -353,18 +355,18 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int nb = 0; nb < kNBW; ++nb) {
-        const int n = nt * kNT + wave * (16 * kNBW) + nb * 16 + (lane & 15);
+        const int n = nt * NTR + wave * (16 * kNBW) + nb * 16 + (lane & 15);
         const int sec = GU ? m : 2;
         qrow[m][nb] = reinterpret_cast<const uint32_t*>(blob + sec * qsec + (int64_t)n * (KD / 2)) + 4 * q4;
       }
     // scale/bias windows: thread -> (matrix, row, quarter of the window's 16
     // words); piece p of NPIECE covers rows [p*PR, (p+1)*PR) of every matrix
     const int gpr = KD / 64;
-    constexpr int PR = kPThreads / 4 / NMAT;       // rows per piece and matrix
-    constexpr int NPIECE = kNT / PR;               // pieces per window
-    const int sb_m = tid / (kPThreads / NMAT), sb_r = (tid / 4) % PR, sb_qt = tid & 3;
+    constexpr int PR = NTH / 4 / NMAT;             // rows per piece and matrix
+    constexpr int NPIECE = NTR / PR;               // pieces per window
+    const int sb_m = tid / (NTH / NMAT), sb_r = (tid / 4) % PR, sb_qt = tid & 3;
     const uint32_t* sb_src = reinterpret_cast<const uint32_t*>(blob + 3 * qsec + (GU ? sb_m : 2) * ssec) +
-                             (int64_t)(nt * kNT + sb_r) * gpr + 4 * sb_qt;
+                             (int64_t)(nt * NTR + sb_r) * gpr + 4 * sb_qt;
     auto load_sb = [&](int win, int piece) -> u32x4 {   // window win, piece piece
       const int w = min(win, (NC - 1) / kSbWin);
       const int g0 = w * 2 * kSbWin + 4 * sb_qt;          // first group of this thread's four
@@ -380,18 +382,20 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
       *reinterpret_cast<u32x4*>(&Sb[buf][sb_m][piece * PR + sb_r][4 * sb_qt]) = v;
     };
 
-    // activation rows: thread -> (row, quarter of a 128-K chunk)
-    const int arow = tid >> 2, apart = tid & 3;
+    // activation rows: thread -> (row, part of a 128-K chunk)
+    constexpr int APR = NTH / kMT;                 // threads per row
+    constexpr int AV = kKC / APR / 8;              // 16-byte vectors per thread
+    const int arow = tid / APR, apart = tid % APR;
     const _Float16* asrc = GU ? a.xh + (int64_t)src_row[arow] * KD : a.abuf + (int64_t)src_row[arow] * KD;
-    auto load_a = [&](int c, u32x4 (&v)[4]) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(asrc + c * kKC + apart * 32);
+    auto load_a = [&](int c, u32x4 (&v)[AV]) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(asrc + c * kKC + apart * (8 * AV));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = load_stream(p + i);
+      for (int i = 0; i < AV; ++i) v[i] = load_stream(p + i);
     };
-    auto store_a = [&](int buf, const u32x4 (&v)[4]) {
-      u32x4* d = reinterpret_cast<u32x4*>(&As[buf][arow * kPitch + apart * 32]);
+    auto store_a = [&](int buf, const u32x4 (&v)[AV]) {
+      u32x4* d = reinterpret_cast<u32x4*>(&As[buf][arow * kPitch + apart * (8 * AV)]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = v[i];
+      for (int i = 0; i < AV; ++i) d[i] = v[i];
     };
 
     // raw weights of one chunk: lane quarter q4 holds the four contiguous
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
     // flight, chunk 0 of activations in LDS.  Activations of chunk c+1 are
     // loaded a full chunk before they are stored, so waiting for them never
     // waits for the weight loads issued after them (loads complete in order).
-    u32x4 an[2][4];
+    u32x4 an[2][AV];
 #pragma unroll
     for (int j = 0; j < NPF; ++j) load_w(min(j, NC - 1), raw[j]);
     load_a(0, an[0]);
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(kPThreads, 2) void gemm_kernel(GemmArgs a) {
     // epilogue: lane holds weight row n = ... + (lane & 15), rows 4*(lane>>4)+i of each block
 #pragma unroll
     for (int nb = 0; nb < kNBW; ++nb) {
-      const int n = nt * kNT + wave * (16 * kNBW) + nb * 16 + (lane & 15);
+      const int n = nt * NTR + wave * (16 * kNBW) + nb * 16 + (lane & 15);
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
 #pragma unroll
@@ -525,18 +529,24 @@ __global__ __launch_bounds__(kPThreads) void combine_kernel(float* __restrict__ 
   }
 }
 
+// Tiles of 256 weight rows (eight waves) when the rows divide into them: one
+// activation chunk then feeds twice the weights.  Gate/up keeps two chunks
+// of weights in flight (it holds two matrices per chunk), down four.
+template <bool GU, int NW>
+void launch_gemm_w(const GemmArgs& g, int nc, int grid, hipStream_t st) {
+  constexpr int NPF_MAX = GU ? 2 : 4;
+  if (NPF_MAX >= 4 && nc % 4 == 0)
+    hipLaunchKernelGGL((gemm_kernel<GU, NPF_MAX, NW>), dim3(grid), dim3(64 * NW), 0, st, g);
+  else if (nc % 2 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 2, NW>), dim3(grid), dim3(64 * NW), 0, st, g);
+  else hipLaunchKernelGGL((gemm_kernel<GU, 1, NW>), dim3(grid), dim3(64 * NW), 0, st, g);
+}
+
 template <bool GU>
-hipError_t launch_gemm(const GemmArgs& g, int nc, int grid, hipStream_t st) {
-  // gate/up holds two matrices' weights per chunk: two chunks in flight fit
-  // its registers, the down GEMM keeps four
-  if constexpr (!GU) {
-    if (nc % 4 == 0) {
-      hipLaunchKernelGGL((gemm_kernel<GU, 4>), dim3(grid), dim3(kPThreads), 0, st, g);
-      return hipGetLastError();
-    }
-  }
-  if (nc % 2 == 0) hipLaunchKernelGGL((gemm_kernel<GU, 2>), dim3(grid), dim3(kPThreads), 0, st, g);
-  else hipLaunchKernelGGL((gemm_kernel<GU, 1>), dim3(grid), dim3(kPThreads), 0, st, g);
+hipError_t launch_gemm(const GemmArgs& g, int nc, int cus, hipStream_t st) {
+  const int nr = GU ? g.I : g.H;
+  const int xcd_cus = max(8, cus / 8 * 8);
+  if (nr % (8 * 16 * kNBW) == 0) launch_gemm_w<GU, 8>(g, nc, xcd_cus, st);
+  else launch_gemm_w<GU, 4>(g, nc, 2 * xcd_cus, st);
   return hipGetLastError();
 }
 
@@ -647,12 +657,12 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   g.abuf = reinterpret_cast<_Float16*>(ws + W.abuf);
   g.dbuf = reinterpret_cast<float*>(ws + W.dbuf);
   g.status = status;
-  const int grid = 2 * max(8, device_cus_prefill() / 8 * 8);
+  const int cus = device_cus_prefill();
   tm.begin(kTGateUp, st);
-  if ((e = launch_gemm<true>(g, H / kKC, grid, st)) != hipSuccess) return e;
+  if ((e = launch_gemm<true>(g, H / kKC, cus, st)) != hipSuccess) return e;
   tm.end(kTGateUp, st);
   tm.begin(kTDown, st);
-  if ((e = launch_gemm<false>(g, I / kKC, grid, st)) != hipSuccess) return e;
+  if ((e = launch_gemm<false>(g, I / kKC, cus, st)) != hipSuccess) return e;
   tm.end(kTDown, st);
   tm.begin(kTCombine, st);
   hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kPThreads), 0, st, h, g.dbuf, w, k, S, H);
