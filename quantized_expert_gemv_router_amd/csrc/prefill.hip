@@ -91,57 +91,83 @@ __global__ __launch_bounds__(kPThreads) void norm_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------- router
-// logits[t][e] = (sum_j Wr[e][j] h[t][j]) * inv_rms[t], fp64 throughout
-// (bf16 and fp32 inputs are exact in fp64).  64 x 64 tile per block, 4 x 4
-// per thread, K in chunks of 16 staged in LDS.
+// logits[t][e] = (sum_j Wr[e][j] h[t][j]) * inv_rms[t] in fp64 (bf16 and
+// fp32 inputs are exact in fp64) on fp64 MFMA (16x16x4).  A block computes a
+// 64-token x 64-expert tile, each wave a 32 x 32 quarter (2 x 2 MFMA
+// blocks); K advances in chunks of 16 staged in LDS as fp64, the next
+// chunk's inputs loaded into registers while the current one is consumed.
+// Lane layout of v_mfma_f64_16x16x4_f64: A lane l = (row l%16, k l/16),
+// B lane l = (k l/16, col l%16), D element i of lane l = (row 4i + l/16,
+// col l%16).
 constexpr int kRT = 64, kRK = 16;
+typedef double double4v __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kPThreads) void router_kernel(const float* __restrict__ h,
                                                             const uint16_t* const* __restrict__ routers,
                                                             int layer, int T, int H, int E,
                                                             const double* __restrict__ inv_rms,
                                                             double* __restrict__ logits) {
-  __shared__ double As[kRK][kRT + 1];
-  __shared__ double Bs[kRK][kRT + 1];
+  __shared__ double As[kRK][kRT + 2];
+  __shared__ double Bs[kRK][kRT + 2];
   const uint16_t* wr = uniform_ptr(routers[layer]);
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
   const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRT;
-  double acc[4][4] = {};
+  // staging: thread -> (row r, four consecutive k)
+  const int sr = tid / 4, sk = (tid % 4) * 4;
+  const bool tok_ok = t0 + sr < T, exp_ok = e0 + sr < E;
+  const float* hrow = h + (int64_t)(tok_ok ? t0 + sr : 0) * H + sk;
+  const uint16_t* wrow = wr + (int64_t)(exp_ok ? e0 + sr : 0) * H + sk;
+  float4 hv = tok_ok ? *reinterpret_cast<const float4*>(hrow) : make_float4(0.f, 0.f, 0.f, 0.f);
+  uint2 wv = exp_ok ? *reinterpret_cast<const uint2*>(wrow) : make_uint2(0u, 0u);
+  double4v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = double4v{0.0, 0.0, 0.0, 0.0};
   for (int k0 = 0; k0 < H; k0 += kRK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + kPThreads * i, r = idx / kRK, kk = idx % kRK;
-      const int t = t0 + r, e = e0 + r;
-      As[kk][r] = t < T ? (double)h[(int64_t)t * H + k0 + kk] : 0.0;
-      Bs[kk][r] = e < E ? (double)__uint_as_float((uint32_t)wr[(int64_t)e * H + k0 + kk] << 16) : 0.0;
-    }
+    As[sk + 0][sr] = hv.x;
+    As[sk + 1][sr] = hv.y;
+    As[sk + 2][sr] = hv.z;
+    As[sk + 3][sr] = hv.w;
+    Bs[sk + 0][sr] = (double)__uint_as_float(wv.x << 16);
+    Bs[sk + 1][sr] = (double)__uint_as_float(wv.x & 0xFFFF0000u);
+    Bs[sk + 2][sr] = (double)__uint_as_float(wv.y << 16);
+    Bs[sk + 3][sr] = (double)__uint_as_float(wv.y & 0xFFFF0000u);
     __syncthreads();
+    if (k0 + kRK < H) {   // uniform: next chunk's inputs in flight during the MFMAs
+      hv = tok_ok ? *reinterpret_cast<const float4*>(hrow + k0 + kRK) : make_float4(0.f, 0.f, 0.f, 0.f);
+      wv = exp_ok ? *reinterpret_cast<const uint2*>(wrow + k0 + kRK) : make_uint2(0u, 0u);
+    }
 #pragma unroll
-    for (int kk = 0; kk < kRK; ++kk) {
-      double a[4], b[4];
+    for (int ks = 0; ks < kRK / 4; ++ks) {
+      const int kk = ks * 4 + (lane >> 4);
+      double a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = As[kk][ty + 16 * i];
-        b[i] = Bs[kk][tx + 16 * i];
+      for (int i = 0; i < 2; ++i) {
+        a[i] = As[kk][wm * 32 + i * 16 + (lane & 15)];
+        b[i] = Bs[kk][wn * 32 + i * 16 + (lane & 15)];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty + 16 * i;
-    if (t >= T) continue;
-    const double inv = inv_rms[t];
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx + 16 * j;
-      if (e < E) logits[(int64_t)t * E + e] = acc[i][j] * inv;
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + wm * 32 + i * 16 + 4 * r + (lane >> 4);
+      if (t >= T) continue;
+      const double inv = inv_rms[t];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = e0 + wn * 32 + j * 16 + (lane & 15);
+        if (e < E) logits[(int64_t)t * E + e] = acc[i][j][r] * inv;
+      }
     }
-  }
 }
 
 // ----------------------------------------------------------------- top-K
