@@ -105,11 +105,12 @@ hipError_t launch_down_combine(const DownArgs& a, hipStream_t stream);
 // ------------------------------------------------------------- prefill
 // Prefill workspace (offsets in bytes): status word, 1/rms [T] f64, x fp16
 // [T][H] (permuted), logits [T][E] f64, idx [T][k] i32, w [T][k] f32,
-// per-expert counts / list offsets / tile offsets, pair lists [T*(k+S)],
+// per-expert counts / list offsets / tile offsets, the row-tile table,
+// pair lists [T*(k+S)],
 // activations fp16 [T*(k+S)][I], per-pair down rows f32 [T*(k+S)][H].
 struct PrefillLayout {
   int64_t status = 0, inv = 0, xh = 0, logits = 0, idx = 0, w = 0, counts = 0, offs = 0, mtoff = 0,
-          lists = 0, abuf = 0, dbuf = 0, total = 0;
+          tiles = 0, lists = 0, abuf = 0, dbuf = 0, total = 0;
 };
 PrefillLayout prefill_layout(const moeq_shape& s, int T, int k);
 

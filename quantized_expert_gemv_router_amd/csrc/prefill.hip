@@ -204,9 +204,11 @@ __global__ void count_kernel(const int32_t* __restrict__ idx, int n, int E, int3
 }
 
 // One block: offsets of each expert's pair list (shared experts hold every
-// token) and the prefix of its tile count.
+// token), the prefix of its tile count, and per row tile (expert, first
+// list entry, rows).
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int E, int S, int T,
-                                                     int32_t* __restrict__ offs, int32_t* __restrict__ mtoff) {
+                                                     int32_t* __restrict__ offs, int32_t* __restrict__ mtoff,
+                                                     int4* __restrict__ tiles) {
   __shared__ int32_t sc[1024], sm[1024];
   const int n = E + S, tid = threadIdx.x;
   const int per = (n + 1023) / 1024;
@@ -236,6 +238,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
       const int c = e < E ? counts[e] : T;
       offs[e] = co;
       mtoff[e] = mo;
+      for (int mi = 0; mi * kMT < c; ++mi)   // the expert's row tiles
+        tiles[mo + mi] = make_int4(e, co + mi * kMT, min(kMT, c - mi * kMT), 0);
       co += c;
       mo += (c + kMT - 1) / kMT;
     }
@@ -287,6 +291,7 @@ struct GemmArgs {
   int E, S, K, H, I;
   const int32_t* offs;        // [E + S + 1]
   const int32_t* mtoff;       // [E + S + 1]
+  const int4* tiles;          // per row tile: expert, first list entry, rows
   const int32_t* lists;       // pair rows grouped by expert
   const _Float16* xh;         // [T][H] permuted fp16 (gate/up input)
   _Float16* abuf;             // [T*(K+S)][I] permuted fp16 (gate/up out, down in)
@@ -348,16 +353,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
     const int nt = r8 / 8, mt = grp * 8 + r8 % 8;
     if (mt >= n_mt) continue;   // uniform over the block
     if (tid == 0) {
-      int lo = 0, hi = E + S;   // last e with mtoff[e] <= mt
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) / 2;
-        if (a.mtoff[mid] <= mt) lo = mid; else hi = mid;
-      }
-      const int mi = mt - a.mtoff[lo];
-      const int cnt = a.offs[lo + 1] - a.offs[lo];
-      s_e = lo;
-      s_row0 = a.offs[lo] + mi * kMT;
-      s_n = min(kMT, cnt - mi * kMT);
+      const int4 tl = a.tiles[mt];
+      s_e = tl.x;
+      s_row0 = tl.y;
+      s_n = tl.z;
     }
     __syncthreads();
     const int e = s_e, nrows = s_n;
@@ -629,7 +628,8 @@ PrefillLayout prefill_layout(const moeq_shape& s, int T, int k) {
   p.counts = p.w + align_up((int64_t)T * k * 4);
   p.offs = p.counts + align_up(n * 4);
   p.mtoff = p.offs + align_up((n + 1) * 4);
-  p.lists = p.mtoff + align_up((n + 1) * 4);
+  p.tiles = p.mtoff + align_up((n + 1) * 4);
+  p.lists = p.tiles + align_up((P / kMT + n + 1) * 16);
   p.abuf = p.lists + align_up(P * 4);
   p.dbuf = p.abuf + align_up(P * s.inter * 2);
   p.total = p.dbuf + align_up(P * s.hidden * 4);
@@ -649,6 +649,7 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   int32_t* counts = reinterpret_cast<int32_t*>(ws + W.counts);
   int32_t* offs = reinterpret_cast<int32_t*>(ws + W.offs);
   int32_t* mtoff = reinterpret_cast<int32_t*>(ws + W.mtoff);
+  int4* tiles = reinterpret_cast<int4*>(ws + W.tiles);
   int32_t* lists = reinterpret_cast<int32_t*>(ws + W.lists);
   int32_t* status = reinterpret_cast<int32_t*>(ws + W.status);
 
@@ -669,7 +670,7 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   tm.end(kTTopk, st);
   tm.begin(kTGroup, st);
   hipLaunchKernelGGL(count_kernel, dim3((T * k + 255) / 256), dim3(256), 0, st, idx, T * k, E, counts, status);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, E, S, T, offs, mtoff);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, E, S, T, offs, mtoff, tiles);
   hipLaunchKernelGGL(compact_kernel, dim3(E + S), dim3(kPThreads), 0, st, idx, T, k, S, E, offs, lists);
   tm.end(kTGroup, st);
   hipError_t e = hipGetLastError();
@@ -678,7 +679,7 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   GemmArgs g{};
   g.blobs = blobs + (int64_t)layer * (E + S);
   g.E = E; g.S = S; g.K = k; g.H = H; g.I = I;
-  g.offs = offs; g.mtoff = mtoff; g.lists = lists;
+  g.offs = offs; g.mtoff = mtoff; g.tiles = tiles; g.lists = lists;
   g.xh = xh;
   g.abuf = reinterpret_cast<_Float16*>(ws + W.abuf);
   g.dbuf = reinterpret_cast<float*>(ws + W.dbuf);
