@@ -164,6 +164,29 @@ __device__ __forceinline__ T load_stream(const T* p) {
   return __builtin_nontemporal_load((GlobalT*)p);
 }
 
+// Range-checked streaming loads through a buffer resource (base address in
+// scalar registers, byte size).  A load whose offset lies outside [0, size)
+// returns zeros without touching memory, so a wave can issue its loads
+// unconditionally and let the range check drop the ones it does not need.
+// Loads issued under a branch are a poor fit for the compiler's wait-count
+// placement: the first use of any of them then waits for every load in
+// flight.  `base` and `bytes` must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // 32-bit data format, untyped access
+constexpr int kCpolNonTemporal = 2;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 load_rsrc_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolNonTemporal));
+}
+__device__ __forceinline__ uint32_t load_rsrc_b32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCpolNonTemporal);
+}
+// Keeps the compiler from sinking loads issued above it into the branches
+// that use them (no wait is implied).
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
 // Cross-workgroup hand-off without cache-wide flushes.  Data that another
 // workgroup (possibly on another XCD, with its own L2) will read is written
 // with agent-scope atomic stores (write-through) and read with agent-scope

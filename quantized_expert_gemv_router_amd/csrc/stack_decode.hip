@@ -273,51 +273,52 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   };
   // Loads are planned (every LDS read they need) before any is issued: an
   // LDS read between loads makes the compiler wait for the loads in flight.
-  const uint16_t* rplan = nullptr;          // this wave's router row segment
+  // Every lane issues its loads unconditionally; what a lane does not need
+  // is outside its buffer range (zeros, no memory access) or re-reads a
+  // valid address, and the dot products skip it.
+  rsrc_t rplan;                    // this wave's router row segment
   auto plan_router = [&](int li) {
-    rplan = r_row < E ? uniform_ptr(rtr[li]) + (int64_t)r_row * H + (int64_t)r_seg * seg_len : nullptr;
+    const bool have = r_row < E;
+    const uint16_t* base = uniform_ptr(rtr[li]) + (int64_t)(have ? r_row : 0) * H + (int64_t)r_seg * seg_len;
+    rplan = make_rsrc(base, have ? (uint32_t)seg_ch * 16u : 0u);
   };
   auto issue_router = [&]() {
 #pragma unroll
-    for (int c = 0; c < CPLR; ++c) {
-      const int cc = lane + 64 * c;
-      // no default for skipped lanes: zeroing a register that a load may
-      // still target also makes the compiler wait for the loads in flight
-      if (rplan != nullptr && cc < seg_ch) wr[c] = load_stream(reinterpret_cast<const u32x4*>(rplan) + cc);
-    }
+    for (int c = 0; c < CPLR; ++c) wr[c] = load_rsrc_b128(rplan, (uint32_t)(lane + 64 * c) * 16u);
   };
   // gate/up rows of the tasks whose slot is in [jlo, jhi); gu_task is
-  // uniform over a wave, so the row addresses are scalar
-  const uint8_t* gq[RPWG];       // quantized row, or null: no task
-  const uint32_t* gs[RPWG];      // the row's scale/bias words
+  // uniform over a wave, so each row is one scalar buffer resource
+  rsrc_t gq[RPWG];               // the task's expert blob, or an empty range: no task
+  uint32_t gqo[RPWG], gso[RPWG]; // byte offsets of its quantized row and scale/bias words
+  bool ghave[RPWG];
   auto plan_gu = [&](int jlo, int jhi) {
-    const int64_t row_bytes = (int64_t)H * BITS / 8;
-    const int gpr = H / 64;
+    const uint32_t row_bytes = (uint32_t)H * BITS / 8;
+    const uint32_t gpr = H / 64;
+    const uint32_t sb_off = 3u * (uint32_t)H * I * BITS / 8;
+    const uint32_t blob_bytes = sb_off + 3u * (uint32_t)(H / 64) * I * 4u;
 #pragma unroll
     for (int m = 0; m < RPWG; ++m) {
       int j, sec, row;
       const bool ok = gu_task(m, j, sec, row);
-      const uint8_t* blob = (ok && j >= jlo && j < jhi) ? uniform_ptr(eblob[j]) : nullptr;
-      const int r = sec * I + row;   // row of [gate; up]
-      gq[m] = blob != nullptr ? blob + (int64_t)r * row_bytes : nullptr;
-      gs[m] = blob != nullptr ? reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8) +
-                                    (int64_t)r * gpr
-                              : nullptr;
+      ghave[m] = ok && j >= jlo && j < jhi;
+      const uint8_t* blob = uniform_ptr(eblob[ghave[m] ? j : 0]);
+      const uint32_t r = ghave[m] ? (uint32_t)(sec * I + row) : 0u;   // row of [gate; up]
+      gq[m] = make_rsrc(blob, ghave[m] ? blob_bytes : 0u);
+      gqo[m] = r * row_bytes;
+      gso[m] = sb_off + r * gpr * 4u;
     }
   };
   auto issue_gu = [&]() {
 #pragma unroll
     for (int m = 0; m < RPWG; ++m) {
-      if (gq[m] == nullptr) continue;   // gu_dots skips it too
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
-        const int cc = lane + 64 * c;
-        if (cc < nchG) {
-          qg[m][c] = load_stream(reinterpret_cast<const u32x4*>(gq[m]) + cc);
-          sg[m][c] = load_stream(gs[m] + (cc * PC) / 64);
-        }
+        const int cc = min(lane + 64 * c, nchG - 1);   // past the row: the dots skip it
+        qg[m][c] = load_rsrc_b128(gq[m], gqo[m] + (uint32_t)cc * 16u);
+        sg[m][c] = load_rsrc_b32(gq[m], gso[m] + (uint32_t)(cc * PC / 64) * 4u);
       }
     }
+    issue_fence();
   };
   auto gu_dots = [&](int jlo, int jhi) {
     const float ux = undo_x;
@@ -326,19 +327,18 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       int j, sec, row;
       const bool ok = gu_task(m, j, sec, row);
       if (!(ok && j >= jlo && j < jhi)) continue;
-      const bool have = gq[m] != nullptr;
       float part = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
         const int cc = lane + 64 * c;
-        if (have && cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
+        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
       }
       const float v = wave_sum_dpp(part) * ux;
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
     }
   };
   // down rows: step s of a wave covers RPSD rows, LPRD lanes each
-  const uint8_t* dblob[STEPSD];  // this lane's expert for step s, or null
+  const uint8_t* dblob[STEPSD];  // this lane's expert for step s (slot 0's for a padding lane)
   auto down_row = [&](int s, int& j, int& row) {
     const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
     j = u / RD;
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int s = 0; s < STEPSD; ++s) {
       int j, row;
       down_row(s, j, row);
-      dblob[s] = (j < KS && row < H) ? eblob[j] : nullptr;
+      dblob[s] = (j < KS && row < H) ? eblob[j] : eblob[0];
     }
   };
   auto issue_down = [&]() {
@@ -360,19 +360,19 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int s = 0; s < STEPSD; ++s) {
       int j, row;
       down_row(s, j, row);
+      if (!(j < KS && row < H)) row = 0;   // padding lane: re-reads a valid row, skipped by the dots
       const uint8_t* blob = dblob[s];
       const uint8_t* q = blob + 2 * (int64_t)H * I * BITS / 8 + (int64_t)row * row_bytes;
       const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8 +
                                                              2 * (int64_t)H * I / 64 * 4) + (int64_t)row * gpr;
 #pragma unroll
       for (int c = 0; c < CPLD; ++c) {
-        const int cc = sub + LPRD * c;
-        if (blob != nullptr && cc < nchD) {   // the down dots skip what is not loaded here
-          qd[s][c] = load_stream(reinterpret_cast<const u32x4*>(q) + cc);
-          sd[s][c] = load_stream(sb + (cc * PC) / 64);
-        }
+        const int cc = min(sub + LPRD * c, nchD - 1);
+        qd[s][c] = load_stream(reinterpret_cast<const u32x4*>(q) + cc);
+        sd[s][c] = load_stream(sb + (cc * PC) / 64);
       }
     }
+    issue_fence();
   };
   auto load_tbl_row = [&](int layer) {   // into registers; stored to LDS after the next barrier
     const void* const* row = a.blobs + (int64_t)layer * tbl_n;
@@ -593,9 +593,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     __syncthreads();
     stamp(li, 5);
     plan_gu(0, K);                   // routed gate/up rows
+    plan_down();                     // every slot's down rows (LDS reads before any load)
     issue_gu();
     stamp0(li, 15);
-    plan_down();                     // LDS reads, placed where the gate/up data is awaited anyway
     gu_dots(0, K);
     stamp0(li, 13);
     __syncthreads();
@@ -607,7 +607,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         put_tagged(a.awords + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
       }
     }
-    issue_down();                    // down rows of every slot, in flight while the activations arrive
+    // down rows of every slot, in flight while the activations arrive (not
+    // earlier: they would share the memory system with the gate/up rows
+    // every block is waiting for)
+    issue_down();
     stamp0(li, 7);
     stamp(li, 8);
 
@@ -659,12 +662,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         const int j = u / RD, i = u % RD;
         const bool ok = j < KS && b + NB * i < H;
         const int jj = ok ? j : 0;
-        const bool have = dblob[s] != nullptr;
         float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPLD; ++c) {
           const int cc = sub + LPRD * c;
-          if (have && cc < nchD)
+          if (ok && cc < nchD)
             part += chunk_affine(chunk_dot<BITS>(qd[s][c], ap + (int64_t)jj * (I / 2) + cc * PPC), sd[s][c],
                                  as[jj * nchD + cc]);
         }
@@ -734,6 +736,8 @@ struct Geometry {
   int nb, rw, H, I, E, S, KS, bits;
   bool fits(int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW) const {
     if (bits != BITS) return false;
+    // expert blobs are addressed with 32-bit byte offsets
+    if ((int64_t)3 * H * I * BITS / 8 + (int64_t)3 * (H / 64) * I * 4 >= (int64_t{1} << 31)) return false;
     const int PC = 128 / BITS;
     const int seg = H / (kWaves / rw);
     if (seg % 8 || seg / 8 > 64 * CPLR) return false;
