@@ -80,7 +80,7 @@ struct DownTile {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int cc = sub + LPR * c;
-      if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[s][c], xp + cc * PPC), sbw[s][c], xs[cc]);
+      if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[s][c], xp + cc * PPC), sbw[s][c], xs + kChunkSums * cc);
     }
     return group_sum(part, LPR) * undo;
   }
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void down_grouped_kernel(DownArgs a, int 
   const int nch = I / Tile::PC;
   uint32_t* pairs = smem;
   float* xsum = reinterpret_cast<float*>(pairs + kTokensPerStage * (I / 2));
-  uint32_t* list = reinterpret_cast<uint32_t*>(xsum + kTokensPerStage * nch);
+  uint32_t* list = reinterpret_cast<uint32_t*>(xsum + kTokensPerStage * kChunkSums * nch);
   int* ids = reinterpret_cast<int*>(list + list_words);
   const uint8_t** ptrs = reinterpret_cast<const uint8_t**>(ids + list_words);
 
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void down_grouped_kernel(DownArgs a, int 
         const int rr = s * Tile::RPS + rsub, r = wrow0 + rr;
         const bool row_ok = rr < ROWS && r < H;
         for (int m = 0; m < nv; ++m) {
-          const float d = tile.dot(s, pairs + (int64_t)m * (I / 2), xsum + (int64_t)m * nch, undo[m], I, lane);
+          const float d = tile.dot(s, pairs + (int64_t)m * (I / 2), xsum + (int64_t)m * kChunkSums * nch, undo[m], I,
+                                   lane);
           if (sub == 0 && row_ok) {
             const uint32_t e = list[m0 + m];
             const int t = (int)(e >> 8), slot = (int)(e & 255u);
@@ -235,7 +236,8 @@ __global__ __launch_bounds__(kThreads) void down_fused_kernel(DownArgs a) {
       if (p < NP) {
         const int t = p / KS, slot = p - t * KS;
         if (slot == 0) acc = row_ok ? residual_at(a, (int64_t)t * H + r) : 0.0f;
-        const float d = tile[p].dot(s, pairs + (int64_t)p * (I / 2), xsum + (int64_t)p * nch, undo[p], I, lane);
+        const float d = tile[p].dot(s, pairs + (int64_t)p * (I / 2), xsum + (int64_t)p * kChunkSums * nch, undo[p],
+                                      I, lane);
         if (blob_of[p] != nullptr && coef[p] != 0.0f) acc = fmaf(coef[p], d, acc);
         if (slot == KS - 1 && sub == 0 && row_ok) a.out[(int64_t)t * H + r] = acc;
       }
@@ -250,7 +252,8 @@ hipError_t launch_t(const DownArgs& a, hipStream_t stream) {
   using FusedTile = DownTile<BITS, LPR, CPL, kFusedRows / kWaves>;
   if (NP <= kFusedPairs && FusedTile::STEPS * CPL <= 2) {
     const int grid = (a.H + kFusedRows - 1) / kFusedRows;
-    const size_t lds = sizeof(uint32_t) * ((size_t)kFusedPairs * (a.I / 2) + (size_t)kFusedPairs * nch);
+    const size_t lds =
+        sizeof(uint32_t) * ((size_t)kFusedPairs * (a.I / 2) + (size_t)kFusedPairs * kChunkSums * nch);
     hipLaunchKernelGGL((down_fused_kernel<BITS, LPR, CPL, WMAX>), dim3(grid), dim3(kThreads), lds,
                        stream, a);
     return hipGetLastError();
@@ -258,7 +261,8 @@ hipError_t launch_t(const DownArgs& a, hipStream_t stream) {
   const int n_rb = (a.H + kGroupedRows - 1) / kGroupedRows;
   const int items = min(a.E, a.T * a.k) + a.S;
   const int list_words = (max(a.T * a.k, a.T) + 3) & ~3;
-  const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.I / 2) + (size_t)kTokensPerStage * nch +
+  const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.I / 2) +
+                                         (size_t)kTokensPerStage * kChunkSums * nch +
                                          2 * (size_t)list_words) +
                      sizeof(void*) * (size_t)list_words;
   hipLaunchKernelGGL((down_grouped_kernel<BITS, LPR, CPL, WMAX>), dim3(items * n_rb), dim3(kThreads),

@@ -39,10 +39,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
   const int H = a.H, I = a.I, KS = a.k + a.S;
   const int nch = H / PC;
   const int P = a.T * a.k;
-  // dynamic LDS: pairs [4][H/2] | xsum [4][nch] | list | ids | ptrs
+  // dynamic LDS: pairs [4][H/2] | xsum [4][kChunkSums * nch] | list | ids | ptrs
   uint32_t* pairs = smem;
   float* xsum = reinterpret_cast<float*>(pairs + kTokensPerStage * (H / 2));
-  uint32_t* list = reinterpret_cast<uint32_t*>(xsum + kTokensPerStage * nch);
+  uint32_t* list = reinterpret_cast<uint32_t*>(xsum + kTokensPerStage * kChunkSums * nch);
   int* ids = reinterpret_cast<int*>(list + list_words);
   const uint8_t** ptrs = reinterpret_cast<const uint8_t**>(ids + list_words);
 
@@ -87,12 +87,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
       if (r >= 2 * I) break;
       for (int m = 0; m < nv; ++m) {
         const uint32_t* xp = pairs + (int64_t)m * (H / 2);
-        const float* xs = xsum + (int64_t)m * nch;
+        const float* xs = xsum + (int64_t)m * kChunkSums * nch;
         float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int cc = lane + 64 * c;
-          if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[i][c], xp + cc * PPC), sbw[i][c], xs[cc]);
+          if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[i][c], xp + cc * PPC), sbw[i][c], xs + kChunkSums * cc);
         }
         const float v = wave_sum(part) * undo[m];
         if (lane == 0) {
@@ -123,7 +123,8 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t stream) {
   const int items = min(a.E, a.T * a.k) + a.S;
   const int list_words = (max(a.T * a.k, a.T) + 3) & ~3;
   const int nch = a.H / Pack<BITS>::kPerChunk;
-  const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.H / 2) + (size_t)kTokensPerStage * nch +
+  const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.H / 2) +
+                                         (size_t)kTokensPerStage * kChunkSums * nch +
                                          2 * (size_t)list_words) +
                      sizeof(void*) * (size_t)list_words;
   if (a.T == 1)

@@ -1,17 +1,23 @@
 // Device building blocks shared by the moeq kernels (gfx950, wave64).
 //
-// Dequantised dot products use the fp16 "magic exponent" form: a packed
-// unsigned value q (< 1024) OR-ed into the mantissa of fp16 1024.0 is the
-// fp16 number 1024 + q exactly, so one v_and_or per pair of values and one
-// v_dot2_f32_f16 per pair give sum_j (1024 + q_j) x_j in fp32.  Per chunk
-// of consecutive inputs sharing a scale s and bias b (Flash-MoE,
-// "Noyau de déquantification optimisé FMA": w = q*s + b):
-//     sum_j (q_j s + b) x_j = s * dot + (b - 1024 s) * X,   X = sum_j x_j
-// with dot the magic-exponent sum and X precomputed once per input vector
-// in LDS.  Activations are staged in LDS as fp16 pairs laid out to match
-// the pair order the masks produce, after a power-of-two rescale per
-// vector (exact) that puts max|x| in [2^14, 2^15) so no input overflows or
-// loses precision to fp16 subnormals.
+// Dequantised dot products use the fp16 "magic exponent" form.  A packed
+// unsigned field q placed at mantissa bit 2^k of fp16 1024.0 (k = 0 for a
+// nibble at bits 0-3, k = 4 at bits 4-7; for 2-bit fields k = 0, 2, .., 8)
+// reads as the fp16 number 1024 + 2^k q exactly.  So each pair of values
+// costs one v_and_or (mask the two fields of a 32-bit word in place and OR
+// in the exponent) and one v_dot2_f32_f16, with one shift per word to bring
+// the upper fields into the mantissa.  The activation staged for a field
+// at 2^k is pre-divided by 2^k (exact), so the product is (1024 + 2^k q)
+// x / 2^k = 1024 x' + q x, with x' the stored value.  Per chunk of
+// consecutive inputs sharing a scale s and bias b (Flash-MoE, "Noyau de
+// déquantification optimisé FMA": w = q*s + b):
+//     sum_j (q_j s + b) x_j = s * (dot - 1024 X') + b * X
+// with dot the magic-exponent sum, X the sum of the chunk's inputs and X'
+// the sum of the stored (pre-divided) values, both precomputed once per
+// input vector in LDS.  Activations are staged in LDS as fp16 pairs laid
+// out to match the pair order the masks produce, after a power-of-two
+// rescale per vector (exact) that puts max|x| in [2^14, 2^15) so no input
+// overflows or loses precision to fp16 subnormals.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,7 +30,6 @@ namespace moeq {
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kMagicPair = 0x64006400u;   // two fp16 1024.0
 constexpr float kMagic = 1024.0f;
 
 // status bits written to the workspace status word
@@ -88,13 +93,30 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 
 // ----------------------------------------------------------- packed layout
 
-// Values per u32 word, fp16 pairs per word, u32x4 chunks per row.
-template <int BITS> struct Pack {
-  static constexpr int kPerWord = 32 / BITS;          // 8 or 16
-  static constexpr int kPairsPerWord = kPerWord / 2;  // 4 or 8
-  static constexpr int kPerChunk = 4 * kPerWord;      // values per 16-byte chunk: 32 or 64
-  static constexpr uint32_t kPairMask = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+// Values per u32 word, fp16 pairs per word, values per 16-byte chunk.
+// Pair slot m of a word holds values (m, m + kPerWord/2) of the word, one
+// in each 16-bit half; kSlotDiv[m] is the power of two its field sits at
+// once masked (the staged activation is divided by it).
+template <int BITS> struct Pack;
+template <> struct Pack<4> {
+  static constexpr int kPerWord = 8, kPairsPerWord = 4, kPerChunk = 32;
+  static constexpr float kSlotDiv[4] = {1.0f, 16.0f, 1.0f, 16.0f};
 };
+template <> struct Pack<2> {
+  static constexpr int kPerWord = 16, kPairsPerWord = 8, kPerChunk = 64;
+  static constexpr float kSlotDiv[8] = {1.0f, 4.0f, 16.0f, 64.0f, 256.0f, 1.0f, 4.0f, 16.0f};
+};
+// Floats of precomputed sums per staged chunk: X and 1024 * X'.
+constexpr int kChunkSums = 2;
+
+// Two fp16 1024.0 in a vector register: as an operand of v_and_or_b32 it
+// cannot be a literal, and a register keeps the compiler from splitting the
+// and/or pair.
+__device__ __forceinline__ uint32_t magic_pair() {
+  uint32_t m;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
 
 // Magic-exponent dot of one 16-byte chunk of packed values against the
 // staged fp16 pairs of the same chunk (xp points at the chunk's first pair).
@@ -102,48 +124,72 @@ template <int BITS>
 __device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* __restrict__ xp) {
   float acc = 0.0f;
   const uint4* xv = reinterpret_cast<const uint4*>(xp);
-  constexpr uint32_t M = Pack<BITS>::kPairMask;
+  const uint32_t mg = magic_pair();
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 x = xv[i];
-      uint32_t w = q[i];
-      acc = dot2(kMagicPair | (w & M), x.x, acc);
-      acc = dot2(kMagicPair | ((w >> 4) & M), x.y, acc);
-      acc = dot2(kMagicPair | ((w >> 8) & M), x.z, acc);
-      acc = dot2(kMagicPair | ((w >> 12) & M), x.w, acc);
+      const uint4 x = xv[i];
+      const uint32_t w = q[i], t = w >> 8;
+      acc = dot2((w & 0x000F000Fu) | mg, x.x, acc);
+      acc = dot2((w & 0x00F000F0u) | mg, x.y, acc);
+      acc = dot2((t & 0x000F000Fu) | mg, x.z, acc);
+      acc = dot2((t & 0x00F000F0u) | mg, x.w, acc);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 xa = xv[2 * i];
-      uint4 xb = xv[2 * i + 1];
-      uint32_t w = q[i];
-      acc = dot2(kMagicPair | (w & M), xa.x, acc);
-      acc = dot2(kMagicPair | ((w >> 2) & M), xa.y, acc);
-      acc = dot2(kMagicPair | ((w >> 4) & M), xa.z, acc);
-      acc = dot2(kMagicPair | ((w >> 6) & M), xa.w, acc);
-      acc = dot2(kMagicPair | ((w >> 8) & M), xb.x, acc);
-      acc = dot2(kMagicPair | ((w >> 10) & M), xb.y, acc);
-      acc = dot2(kMagicPair | ((w >> 12) & M), xb.z, acc);
-      acc = dot2(kMagicPair | ((w >> 14) & M), xb.w, acc);
+      const uint4 xa = xv[2 * i], xb = xv[2 * i + 1];
+      const uint32_t w = q[i], t = w >> 10;
+      acc = dot2((w & 0x00030003u) | mg, xa.x, acc);
+      acc = dot2((w & 0x000C000Cu) | mg, xa.y, acc);
+      acc = dot2((w & 0x00300030u) | mg, xa.z, acc);
+      acc = dot2((w & 0x00C000C0u) | mg, xa.w, acc);
+      acc = dot2((w & 0x03000300u) | mg, xb.x, acc);
+      acc = dot2((t & 0x00030003u) | mg, xb.y, acc);
+      acc = dot2((t & 0x000C000Cu) | mg, xb.z, acc);
+      acc = dot2((t & 0x00300030u) | mg, xb.w, acc);
     }
   }
   return acc;
 }
 
-// One chunk's contribution: s * dot + (b - 1024 s) * X_chunk.
-__device__ __forceinline__ float chunk_affine(float dot, uint32_t sb, float xsum) {
-  float s = bf16_lo(sb);
-  float b = bf16_hi(sb);
-  return fmaf(s, dot, fmaf(-kMagic, s, b) * xsum);
+// One chunk's contribution: s * (dot - 1024 X') + b * X, with xs the
+// chunk's two precomputed sums {X, 1024 X'}.
+__device__ __forceinline__ float chunk_affine(float dot, uint32_t sb, const float* xs) {
+  const float2 x = *reinterpret_cast<const float2*>(xs);
+  return fmaf(bf16_lo(sb), dot - x.y, bf16_hi(sb) * x.x);
+}
+
+// Rounds the PW values v[] * f to fp16, divides each pair slot by its
+// power of two (exact) and packs the pairs into pr[]; adds the chunk
+// sums' share of this word to X (the rounded values) and Xs (1024 times
+// the stored values).  The fp32 products and packed pairs are pinned so the
+// sums add exactly the values the dot products read: the 1024 X' term
+// must cancel the magic offsets inside the dot.
+template <int BITS>
+__device__ __forceinline__ void pack_word(const float* v, float f, uint32_t* pr, float& X, float& Xs) {
+  constexpr int HP = Pack<BITS>::kPairsPerWord;
+#pragma unroll
+  for (int j = 0; j < HP; ++j) {
+    float lo = v[j] * f, hi = v[j + HP] * f;
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    const float d = Pack<BITS>::kSlotDiv[j];
+    // round to fp16 first, then the exact division by a power of two
+    const float lr = (float)(_Float16)lo, hr = (float)(_Float16)hi;
+    pr[j] = pack_half2(lr * (1.0f / d), hr * (1.0f / d));
+    asm volatile("" : "+v"(pr[j]));
+    const float sl = half_lo(pr[j]), sh = half_hi(pr[j]);
+    Xs += (sl + sh) * kMagic;
+    X += (sl + sh) * d;
+  }
 }
 
 // ------------------------------------------------------------- LDS staging
 //
 // A staged vector of n values (n a multiple of 64) occupies
-//   pairs : n/2 u32   (pair m of word w = (v[w*PW + m], v[w*PW + m + PW/2]))
-//   xsum  : n/kPerChunk floats (sum of the fp16-rounded values per chunk)
+//   pairs : n/2 u32   (pair m of word w = (v[w*PW + m], v[w*PW + m + PW/2]),
+//                      each divided by the slot's power of two)
+//   sums  : kChunkSums * n/kPerChunk floats ({X, 1024 X'} per chunk)
 // plus one float per vector: the power of two that undoes the rescale.
 
 // Power-of-two factor p with max_abs * p in [2^14, 2^15) (1 if max_abs == 0

@@ -158,9 +158,9 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S,
   L.hs = 0;
   L.xp = al16(L.hs + 4 * H);
   L.xs = al16(L.xp + 2 * H);
-  L.ap = al16(L.xs + 4 * (H / PC));
+  L.ap = al16(L.xs + 4 * kChunkSums * (H / PC));
   L.as = al16(L.ap + KS * 2 * I);
-  L.gres = al16(L.as + 4 * KS * (I / PC));
+  L.gres = al16(L.as + 4 * kChunkSums * KS * (I / PC));
   L.dres = al16(L.gres + 4 * KS * 2 * RG);
   L.lg = al16(L.dres + 4 * KS * RD);
   L.tbl = al16(L.lg + 8 * E);
@@ -169,28 +169,28 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S,
   return L;
 }
 
-// Stage one word (PW values) into fp16 pairs at pairs + w*PW/2 and return
-// the sum of the rounded values (the caller folds the four words of a
-// chunk with lane shuffles).  The fp32 products and the packed pairs are
-// pinned so the sum adds exactly the stored fp16 values (the bias term
-// b*X of the magic-exponent dot cancels 1024*X).
+// Stage one word (PW values, scaled by f) into fp16 pairs at pairs +
+// w*PW/2; returns the word's share of the chunk sums {X, 1024 X'} (the
+// caller folds the four words of a chunk with lane shuffles).
+// Sum over the four lanes of a quad (the four words of a chunk).
+__device__ __forceinline__ float2 quad_sum(float2 s) {
+  s.x += __shfl_xor(s.x, 1, 64);
+  s.y += __shfl_xor(s.y, 1, 64);
+  s.x += __shfl_xor(s.x, 2, 64);
+  s.y += __shfl_xor(s.y, 2, 64);
+  return s;
+}
+
 template <int BITS>
-__device__ __forceinline__ float stage_word(const float* v, float f, uint32_t* pairs, int w) {
-  constexpr int PW = Pack<BITS>::kPerWord, HP = PW / 2;
+__device__ __forceinline__ float2 stage_word(const float* v, float f, uint32_t* pairs, int w) {
+  constexpr int HP = Pack<BITS>::kPairsPerWord;
   uint32_t pr[HP];
-  float s = 0.0f;
-#pragma unroll
-  for (int j = 0; j < HP; ++j) {
-    float lo = v[j] * f, hi = v[j + HP] * f;
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    pr[j] = pack_half2(lo, hi);
-    asm volatile("" : "+v"(pr[j]));
-    s += half_lo(pr[j]) + half_hi(pr[j]);
-  }
+  float X = 0.0f, Xs = 0.0f;
+  pack_word<BITS>(v, f, pr, X, Xs);
   uint4* dst = reinterpret_cast<uint4*>(pairs + (int64_t)w * HP);
 #pragma unroll
   for (int j = 0; j < HP / 4; ++j) dst[j] = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
-  return s;
+  return make_float2(X, Xs);
 }
 
 template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW>
@@ -227,9 +227,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD, a.clocks ? L * kStackClockEvents : 0);
   float* hs = reinterpret_cast<float*>(smem + LL.hs);               // [H]
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem + LL.xp);         // [H/2]
-  float* xs = reinterpret_cast<float*>(smem + LL.xs);               // [H/PC]
+  float* xs = reinterpret_cast<float*>(smem + LL.xs);               // [H/PC][kChunkSums]
   uint32_t* ap = reinterpret_cast<uint32_t*>(smem + LL.ap);         // [KS][I/2]
-  float* as = reinterpret_cast<float*>(smem + LL.as);               // [KS][I/PC]
+  float* as = reinterpret_cast<float*>(smem + LL.as);               // [KS][I/PC][kChunkSums]
   float* gres = reinterpret_cast<float*>(smem + LL.gres);           // [KS][2][RG]
   float* dres = reinterpret_cast<float*>(smem + LL.dres);           // [KS][RD]
   double* lg = reinterpret_cast<double*>(smem + LL.lg);             // [E]
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
         const int cc = lane + 64 * c;
-        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs[cc]);
+        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs + kChunkSums * cc);
       }
       const float v = wave_sum_dpp(part) * ux;
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
@@ -531,16 +531,15 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       const int nw = H / PW;
       for (int w0 = 0; w0 < nw; w0 += kThreads) {
         const int w = w0 + tid;
-        float s = 0.0f;
+        float2 s = make_float2(0.0f, 0.0f);
         if (w < nw) {
           float v[PW];
 #pragma unroll
           for (int j = 0; j < PW; ++j) v[j] = hs[w * PW + j];
           s = stage_word<BITS>(v, f, xp, w);
         }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if ((tid & 3) == 0 && w < nw) xs[w >> 2] = s;
+        s = quad_sum(s);
+        if ((tid & 3) == 0 && w < nw) *reinterpret_cast<float2*>(xs + kChunkSums * (w >> 2)) = s;
       }
     }
     __syncthreads();
@@ -642,14 +641,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         stamp0(li, 16);
         if (block_failed(got)) return;
         stamp0(li, 17);
-        float s = 0.0f;
+        float2 s = make_float2(0.0f, 0.0f);
         if (ok) {
           const float p = pow2_stage_factor(__uint_as_float(amax[m]));
           s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w);
         }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if (ok && (tid & 3) == 0) as[m * nchD + (w >> 2)] = s;
+        s = quad_sum(s);
+        if (ok && (tid & 3) == 0) *reinterpret_cast<float2*>(as + kChunkSums * (m * nchD + (w >> 2))) = s;
       }
     }
     __syncthreads();
@@ -668,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           const int cc = sub + LPRD * c;
           if (ok && cc < nchD)
             part += chunk_affine(chunk_dot<BITS>(qd[s][c], ap + (int64_t)jj * (I / 2) + cc * PPC), sd[s][c],
-                                 as[jj * nchD + cc]);
+                                 as + kChunkSums * (jj * nchD + cc));
         }
         const float undo = 1.0f / pow2_stage_factor(__uint_as_float(amax[jj]));
         const float d = group_sum(part, LPRD) * undo;

@@ -57,10 +57,11 @@ __device__ __forceinline__ void load_swiglu(const float* gu, int I, int64_t o, f
 // WMAX * blockDim).  load(m, o, v) fills v[0..PW) with values o..o+PW of
 // vector m.  With `rmsnorm` each vector is scaled by 1/sqrt(mean(v^2)+1e-6)
 // first.  Then each vector is rescaled by a power of two p (max|v| * p in
-// [2^14, 2^15)), rounded to fp16 pairs and summed per 16-byte chunk.
-// pairs: [nvec][n/2] u32 (16-byte aligned), xsum: [nvec][n / chunk] f32,
-// undo: [nvec] f32 (= 1/p), red: 2 * MMAX * nwaves floats.
-// Whole block; returns after a barrier.
+// [2^14, 2^15)), rounded to fp16 pairs in the slot layout chunk_dot reads,
+// and summed per 16-byte chunk.
+// pairs: [nvec][n/2] u32 (16-byte aligned), xsum: [nvec][kChunkSums * n /
+// chunk] f32 (8-byte aligned), undo: [nvec] f32 (= 1/p), red: 2 * MMAX *
+// nwaves floats.  Whole block; returns after a barrier.
 template <int BITS, int WMAX, int MMAX, class Loader>
 __device__ __forceinline__ void stage_batch(int nvec, int n, Loader load, bool rmsnorm,
                                             uint32_t* __restrict__ pairs,
@@ -118,32 +119,23 @@ __device__ __forceinline__ void stage_batch(int nvec, int n, Loader load, bool r
 #pragma unroll
       for (int i = 0; i < WMAX; ++i) {
         const int w = tid + i * blockDim.x;
-        float s = 0.0f;
+        float X = 0.0f, Xs = 0.0f;
         if (w < nwords) {
           uint32_t pr[HP];
-#pragma unroll
-          for (int j = 0; j < HP; ++j) {
-            // The chunk sum must add exactly the fp16 values stored: the
-            // bias term b*X cancels 1024*X inside the magic-exponent dot.
-            // Pin the fp32 product and the packed pair so the compiler
-            // cannot re-derive the fp16 values with a differently rounded
-            // fused multiply-convert (which it does when f is not a power
-            // of two).
-            float lo = v[m][i][j] * f, hi = v[m][i][j + HP] * f;
-            asm volatile("" : "+v"(lo), "+v"(hi));
-            pr[j] = pack_half2(lo, hi);
-            asm volatile("" : "+v"(pr[j]));
-            s += half_lo(pr[j]) + half_hi(pr[j]);
-          }
+          pack_word<BITS>(v[m][i], f, pr, X, Xs);
           uint4* dst = reinterpret_cast<uint4*>(pairs + (int64_t)m * np + (int64_t)w * HP);
 #pragma unroll
           for (int j = 0; j < HP / 4; ++j)
             dst[j] = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
         }
         // words 4c..4c+3 of chunk c sit in four consecutive lanes
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if ((tid & 3) == 0 && w < nwords) xsum[(int64_t)m * nch + (w >> 2)] = s;
+        X += __shfl_xor(X, 1, 64);
+        X += __shfl_xor(X, 2, 64);
+        Xs += __shfl_xor(Xs, 1, 64);
+        Xs += __shfl_xor(Xs, 2, 64);
+        if ((tid & 3) == 0 && w < nwords)
+          *reinterpret_cast<float2*>(xsum + (int64_t)m * kChunkSums * nch + kChunkSums * (w >> 2)) =
+              make_float2(X, Xs);
       }
     }
   }

@@ -1,16 +1,15 @@
 """GPU parity of the stacked decode path (persistent launch and per-layer
 launches) against the fp64 oracle.
 
-Free-running: the oracle and the GPU each run all layers from the same
-token; top-K must be bit-exact at every layer and the final residual stream
-within max|gpu - oracle| <= 2e-3 * max|oracle|.  The GPU carries the
-residual stream in fp32, so its normalised input at layer l differs from the
-oracle's by some dx; a logit can then move by at most
-delta_l = max_e |Wr_e|_2 * |dx|_2 (Cauchy-Schwarz).  Where the oracle's gap
-between its K-th and (K+1)-th logits exceeds 2*delta_l the selection is
-unique and must match exactly; where it does not, any selection whose
-oracle logits are within 2*delta_l of the oracle's K-th is valid, the
-trajectories may then part, and later layers are not compared.
+Free-running: the GPU runs all layers from a token, recording each layer's
+input h_l and top-K.  The gate is teacher forcing along the GPU's own
+trajectory: at every layer the oracle runs the layer on the GPU's input h_l
+(fp32, exact in fp64), the GPU's top-K must equal the oracle's exactly and
+its h_{l+1} must be within max|gpu - oracle| <= 2e-3 * max|oracle|.  The
+distance of the GPU trajectory from the oracle's own free-running one is
+reported, not gated: it accumulates every layer's rounding (the activations
+are fp16) and, where a logit margin is small, can take another valid
+selection.
 Oracle-fed: the oracle's h_l is given to the GPU for one layer, and top-K
 and h_{l+1} are compared with the oracle's layer on the same input.
 """
@@ -42,31 +41,27 @@ def build_stack(cfg, L):
 
 def compare_free_running(cfg, L, token_set, traces, gpu_h):
     tk, hk = traces
-    x64 = synth.bf16_to_f64(synth.tokens(cfg, token_set, 1))
-    ref = oracle.run_stack(cfg, x64, layers=L)
     idx = tk.cpu().numpy()[:, 0, :]
     hs = hk.cpu().numpy()[:, 0, :].astype(np.float64)
+    outs = [hs[l + 1] for l in range(L - 1)] + [np.asarray(gpu_h, dtype=np.float64)]
     K = cfg.top_k
+    worst, min_gap = 0.0, np.inf
     for l in range(L):
-        assert_close(hs[l], ref["h"][l, 0], f"h input of layer {l}")
-        wr = synth.bf16_to_f64(synth.router(cfg, l))
-        dx = oracle.rmsnorm(hs[l]) - oracle.rmsnorm(ref["h"][l, 0])
-        delta = np.sqrt((wr * wr).sum(axis=1)).max() * np.sqrt((dx * dx).sum())
-        logits = oracle.router_logits(oracle.shape_of(cfg), synth.router(cfg, l), oracle.rmsnorm(ref["h"][l, 0]))
-        kth = np.sort(logits)[::-1][K - 1]
-        if ref["margin"][l, 0] > 2 * delta:
-            assert np.array_equal(idx[l], ref["idx"][l, 0]), (l, idx[l], ref["idx"][l, 0], delta)
-            continue
-        # several selections are valid: each chosen expert must be within 2*delta of the K-th
-        assert np.all(logits[idx[l]] >= kth - 2 * delta), (l, idx[l], logits[idx[l]], kth, delta)
-        if not np.array_equal(idx[l], ref["idx"][l, 0]):
-            say(f"  token set {token_set}: layer {l} gap {ref['margin'][l, 0]:.2e} <= 2*delta "
-                f"{2 * delta:.2e}; valid different selection {idx[l]} vs {ref['idx'][l, 0]}; "
-                f"compared layers <= {l}")
-            return
-    e = assert_close(gpu_h, ref["h"][L, 0], "final h")
-    say(f"  token set {token_set}: {L} layers exact top-K, final h rel err {e:.2e}, "
-        f"min gap {ref['margin'].min():.3e}")
+        exp = oracle.run_layer(cfg, l, hs[l][None, :], want_intermediates=False)
+        srt = -np.sort(-exp["logits"][0])
+        min_gap = min(min_gap, srt[K - 1] - srt[K])
+        assert np.array_equal(idx[l], exp["idx"][0]), (l, idx[l], exp["idx"][0], srt[K - 1] - srt[K])
+        worst = max(worst, assert_close(outs[l], exp["y"][0], f"layer {l} output (GPU input)"))
+    # drift from the oracle's own trajectory, for the record
+    ref = oracle.run_stack(cfg, synth.bf16_to_f64(synth.tokens(cfg, token_set, 1)), layers=L)
+    same = 0
+    while same < L and np.array_equal(idx[same], ref["idx"][same, 0]):
+        same += 1
+    last = min(same, L - 1)
+    drift = np.abs(hs[last] - ref["h"][last, 0]).max() / np.abs(ref["h"][last, 0]).max()
+    say(f"  token set {token_set}: {L} layers, exact top-K on the GPU's inputs (min gap {min_gap:.2e}), "
+        f"worst layer output rel err {worst:.2e}; same selections as the free-running oracle for "
+        f"{same} layers, h drift at layer {last} {drift:.2e}")
 
 
 @pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
