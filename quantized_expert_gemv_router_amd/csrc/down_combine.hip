@@ -41,7 +41,6 @@ __device__ __forceinline__ float residual_at(const DownArgs& a, int64_t i) {
 template <int BITS, int LPR, int CPL, int ROWS>
 struct DownTile {
   static constexpr int PC = Pack<BITS>::kPerChunk;
-  static constexpr int PPC = PC / 2;
   static constexpr int RPS = 64 / LPR;
   static constexpr int STEPS = (ROWS + RPS - 1) / RPS;
   u32x4 q[STEPS][CPL];
@@ -72,7 +71,7 @@ struct DownTile {
     }
   }
 
-  // d for step s against one staged vector; valid in every lane of the row group.
+  // d for step s against one staged vector; valid in lane LPR - 1 of the row group.
   __device__ __forceinline__ float dot(int s, const uint32_t* xp, const float* xs, float undo,
                                        int I, int lane) const {
     const int sub = lane % LPR, nch = I / PC;
@@ -80,9 +79,9 @@ struct DownTile {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int cc = sub + LPR * c;
-      if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[s][c], xp + cc * PPC), sbw[s][c], xs + kChunkSums * cc);
+      if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[s][c], xp, cc, nch), sbw[s][c], xs + kChunkSums * cc);
     }
-    return group_sum(part, LPR) * undo;
+    return group_sum_dpp<LPR>(part) * undo;
   }
 };
 
@@ -129,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void down_grouped_kernel(DownArgs a, int 
         for (int m = 0; m < nv; ++m) {
           const float d = tile.dot(s, pairs + (int64_t)m * (I / 2), xsum + (int64_t)m * kChunkSums * nch, undo[m], I,
                                    lane);
-          if (sub == 0 && row_ok) {
+          if (sub == LPR - 1 && row_ok) {
             const uint32_t e = list[m0 + m];
             const int t = (int)(e >> 8), slot = (int)(e & 255u);
             st_agent(a.dbuf + ((int64_t)t * KS + slot) * H + r, d);
@@ -239,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void down_fused_kernel(DownArgs a) {
         const float d = tile[p].dot(s, pairs + (int64_t)p * (I / 2), xsum + (int64_t)p * kChunkSums * nch, undo[p],
                                       I, lane);
         if (blob_of[p] != nullptr && coef[p] != 0.0f) acc = fmaf(coef[p], d, acc);
-        if (slot == KS - 1 && sub == 0 && row_ok) a.out[(int64_t)t * H + r] = acc;
+        if (slot == KS - 1 && sub == LPR - 1 && row_ok) a.out[(int64_t)t * H + r] = acc;
       }
     }
   }

@@ -32,7 +32,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
   __shared__ float red[2 * kTokensPerStage * kWaves];
   __shared__ float undo[kTokensPerStage];
   constexpr int PC = Pack<BITS>::kPerChunk;
-  constexpr int PPC = PC / 2;
   constexpr int RPB = kWaves * RPW;
   const int item = blockIdx.x / n_rb, rb = blockIdx.x - item * n_rb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -92,9 +91,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int cc = lane + 64 * c;
-          if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[i][c], xp + cc * PPC), sbw[i][c], xs + kChunkSums * cc);
+          if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[i][c], xp, cc, nch), sbw[i][c], xs + kChunkSums * cc);
         }
-        const float v = wave_sum(part) * undo[m];
+        const float v = wave_sum_dpp(part) * undo[m];
         if (lane == 0) {
           const uint32_t e = list[m0 + m];
           const int t = (int)(e >> 8), slot = (int)(e & 255u);

@@ -99,11 +99,11 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 // once masked (the staged activation is divided by it).
 template <int BITS> struct Pack;
 template <> struct Pack<4> {
-  static constexpr int kPerWord = 8, kPairsPerWord = 4, kPerChunk = 32;
+  static constexpr int kPerWord = 8, kPairsPerWord = 4, kPerChunk = 32, kUnitsPerChunk = 4;
   static constexpr float kSlotDiv[4] = {1.0f, 16.0f, 1.0f, 16.0f};
 };
 template <> struct Pack<2> {
-  static constexpr int kPerWord = 16, kPairsPerWord = 8, kPerChunk = 64;
+  static constexpr int kPerWord = 16, kPairsPerWord = 8, kPerChunk = 64, kUnitsPerChunk = 8;
   static constexpr float kSlotDiv[8] = {1.0f, 4.0f, 16.0f, 64.0f, 256.0f, 1.0f, 4.0f, 16.0f};
 };
 // Floats of precomputed sums per staged chunk: X and 1024 * X'.
@@ -118,27 +118,41 @@ __device__ __forceinline__ uint32_t magic_pair() {
   return m;
 }
 
-// Magic-exponent dot of one 16-byte chunk of packed values against the
-// staged fp16 pairs of the same chunk (xp points at the chunk's first pair).
+// The staged fp16 pairs of one chunk, in registers.
+template <int BITS> struct XChunk {
+  uint4 u[Pack<BITS>::kUnitsPerChunk];
+};
+
+// Chunk cc of a staged vector (vec, nch chunks: the stride between a
+// chunk's 16-byte units).
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* __restrict__ xp) {
+__device__ __forceinline__ XChunk<BITS> load_xchunk(const uint32_t* __restrict__ vec, int cc, int nch) {
+  XChunk<BITS> x;
+  const uint4* xv = reinterpret_cast<const uint4*>(vec) + cc;
+#pragma unroll
+  for (int u = 0; u < Pack<BITS>::kUnitsPerChunk; ++u) x.u[u] = xv[u * nch];
+  return x;
+}
+
+// Magic-exponent dot of one 16-byte chunk of packed values against the
+// staged fp16 pairs of the same chunk.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(u32x4 q, const XChunk<BITS>& x) {
   float acc = 0.0f;
-  const uint4* xv = reinterpret_cast<const uint4*>(xp);
   const uint32_t mg = magic_pair();
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 x = xv[i];
       const uint32_t w = q[i], t = w >> 8;
-      acc = dot2((w & 0x000F000Fu) | mg, x.x, acc);
-      acc = dot2((w & 0x00F000F0u) | mg, x.y, acc);
-      acc = dot2((t & 0x000F000Fu) | mg, x.z, acc);
-      acc = dot2((t & 0x00F000F0u) | mg, x.w, acc);
+      acc = dot2((w & 0x000F000Fu) | mg, x.u[i].x, acc);
+      acc = dot2((w & 0x00F000F0u) | mg, x.u[i].y, acc);
+      acc = dot2((t & 0x000F000Fu) | mg, x.u[i].z, acc);
+      acc = dot2((t & 0x00F000F0u) | mg, x.u[i].w, acc);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 xa = xv[2 * i], xb = xv[2 * i + 1];
+      const uint4 xa = x.u[2 * i], xb = x.u[2 * i + 1];
       const uint32_t w = q[i], t = w >> 10;
       acc = dot2((w & 0x00030003u) | mg, xa.x, acc);
       acc = dot2((w & 0x000C000Cu) | mg, xa.y, acc);
@@ -153,11 +167,18 @@ __device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* __restrict__
   return acc;
 }
 
-// One chunk's contribution: s * (dot - 1024 X') + b * X, with xs the
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* __restrict__ vec, int cc, int nch) {
+  return chunk_dot<BITS>(q, load_xchunk<BITS>(vec, cc, nch));
+}
+
+// One chunk's contribution: s * (dot - 1024 X') + b * X, with x the
 // chunk's two precomputed sums {X, 1024 X'}.
-__device__ __forceinline__ float chunk_affine(float dot, uint32_t sb, const float* xs) {
-  const float2 x = *reinterpret_cast<const float2*>(xs);
+__device__ __forceinline__ float chunk_affine(float dot, uint32_t sb, float2 x) {
   return fmaf(bf16_lo(sb), dot - x.y, bf16_hi(sb) * x.x);
+}
+__device__ __forceinline__ float chunk_affine(float dot, uint32_t sb, const float* xs) {
+  return chunk_affine(dot, sb, *reinterpret_cast<const float2*>(xs));
 }
 
 // Rounds the PW values v[] * f to fp16, divides each pair slot by its
@@ -186,11 +207,27 @@ __device__ __forceinline__ void pack_word(const float* v, float f, uint32_t* pr,
 
 // ------------------------------------------------------------- LDS staging
 //
-// A staged vector of n values (n a multiple of 64) occupies
-//   pairs : n/2 u32   (pair m of word w = (v[w*PW + m], v[w*PW + m + PW/2]),
-//                      each divided by the slot's power of two)
-//   sums  : kChunkSums * n/kPerChunk floats ({X, 1024 X'} per chunk)
+// A staged vector of n values (n a multiple of 64, nch = n / kPerChunk
+// chunks) occupies
+//   pairs : n/2 u32, in 16-byte units: unit u of chunk c at unit index
+//           u * nch + c, so lanes reading consecutive chunks read
+//           consecutive LDS addresses (no bank conflicts).  Word i of a
+//           chunk fills units kUnitsPerChunk/4 * i ..; pair m of a word
+//           = (v[w*PW + m], v[w*PW + m + PW/2]), each divided by the slot's
+//           power of two.
+//   sums  : kChunkSums * nch floats ({X, 1024 X'} per chunk)
 // plus one float per vector: the power of two that undoes the rescale.
+
+// Writes the pr[] pairs of word w of a staged vector (base vec, nch chunks).
+template <int BITS>
+__device__ __forceinline__ void store_word(uint32_t* vec, int w, int nch, const uint32_t* pr) {
+  constexpr int UPW = Pack<BITS>::kUnitsPerChunk / 4;   // 16-byte units per word
+  uint4* dst = reinterpret_cast<uint4*>(vec);
+  const int c = w >> 2, i = w & 3;
+#pragma unroll
+  for (int u = 0; u < UPW; ++u)
+    dst[(UPW * i + u) * nch + c] = make_uint4(pr[4 * u], pr[4 * u + 1], pr[4 * u + 2], pr[4 * u + 3]);
+}
 
 // Power-of-two factor p with max_abs * p in [2^14, 2^15) (1 if max_abs == 0
 // or not finite).
@@ -340,6 +377,21 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += __int_as_float(dpp_move<kDppBcast15, 0xA>(0, __float_as_int(v)));
   v += __int_as_float(dpp_move<kDppBcast31, 0xC>(0, __float_as_int(v)));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64) with DPP lane
+// moves, no LDS crossbar round trips.  The sum is valid in lane W - 1 of
+// each group (in every lane of the group for W <= 16).
+template <int W>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) v += __int_as_float(dpp_move<kDppQuadXor1>(0, __float_as_int(v)));
+  if constexpr (W >= 4) v += __int_as_float(dpp_move<kDppQuadXor2>(0, __float_as_int(v)));
+  if constexpr (W >= 8) v += __int_as_float(dpp_move<kDppHalfMirror>(0, __float_as_int(v)));
+  if constexpr (W >= 16) v += __int_as_float(dpp_move<kDppMirror>(0, __float_as_int(v)));
+  if constexpr (W >= 32) v += __int_as_float(dpp_move<kDppBcast15, 0xA>(0, __float_as_int(v)));
+  if constexpr (W >= 64) v += __int_as_float(dpp_move<kDppBcast31, 0xC>(0, __float_as_int(v)));
+  return v;
 }
 
 __device__ __forceinline__ float wave_max_dpp(float v) {

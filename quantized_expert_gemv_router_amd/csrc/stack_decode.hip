@@ -169,8 +169,8 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S,
   return L;
 }
 
-// Stage one word (PW values, scaled by f) into fp16 pairs at pairs +
-// w*PW/2; returns the word's share of the chunk sums {X, 1024 X'} (the
+// Stage word w (PW values, scaled by f) of a vector of nch chunks into its
+// fp16 pairs; returns the word's share of the chunk sums {X, 1024 X'} (the
 // caller folds the four words of a chunk with lane shuffles).
 // Sum over the four lanes of a quad (the four words of a chunk).
 __device__ __forceinline__ float2 quad_sum(float2 s) {
@@ -182,26 +182,25 @@ __device__ __forceinline__ float2 quad_sum(float2 s) {
 }
 
 template <int BITS>
-__device__ __forceinline__ float2 stage_word(const float* v, float f, uint32_t* pairs, int w) {
+__device__ __forceinline__ float2 stage_word(const float* v, float f, uint32_t* vec, int w, int nch) {
   constexpr int HP = Pack<BITS>::kPairsPerWord;
   uint32_t pr[HP];
   float X = 0.0f, Xs = 0.0f;
   pack_word<BITS>(v, f, pr, X, Xs);
-  uint4* dst = reinterpret_cast<uint4*>(pairs + (int64_t)w * HP);
-#pragma unroll
-  for (int j = 0; j < HP / 4; ++j) dst[j] = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
+  store_word<BITS>(vec, w, nch, pr);
   return make_float2(X, Xs);
 }
 
 template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW>
 __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
-  constexpr int PC = Pack<BITS>::kPerChunk, PPC = PC / 2, PW = Pack<BITS>::kPerWord;
+  constexpr int PC = Pack<BITS>::kPerChunk, PW = Pack<BITS>::kPerWord;
   constexpr int RPSD = 64 / LPRD;          // down rows per wave step
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ double rpart[kWaves];
   __shared__ double ssum[kWaves];
   __shared__ float hmax[kWaves];
   __shared__ uint32_t amax[kMaxKS];
+  __shared__ float aundo[kMaxKS];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
   __shared__ int64_t candk[kWaves * MOEQ_MAX_TOPK];
@@ -331,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 #pragma unroll
       for (int c = 0; c < CPLG; ++c) {
         const int cc = lane + 64 * c;
-        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp + cc * PPC), sg[m][c], xs + kChunkSums * cc);
+        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp, cc, nchG), sg[m][c], xs + kChunkSums * cc);
       }
       const float v = wave_sum_dpp(part) * ux;
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
@@ -536,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           float v[PW];
 #pragma unroll
           for (int j = 0; j < PW; ++j) v[j] = hs[w * PW + j];
-          s = stage_word<BITS>(v, f, xp, w);
+          s = stage_word<BITS>(v, f, xp, w, nchG);
         }
         s = quad_sum(s);
         if ((tid & 3) == 0 && w < nw) *reinterpret_cast<float2*>(xs + kChunkSums * (w >> 2)) = s;
@@ -644,7 +643,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         float2 s = make_float2(0.0f, 0.0f);
         if (ok) {
           const float p = pow2_stage_factor(__uint_as_float(amax[m]));
-          s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w);
+          s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w, nchD);
+          if (w == 0) aundo[m] = 1.0f / p;
         }
         s = quad_sum(s);
         if (ok && (tid & 3) == 0) *reinterpret_cast<float2*>(as + kChunkSums * (m * nchD + (w >> 2))) = s;
@@ -653,24 +653,37 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     __syncthreads();
     stamp(li, 9);
     {
+      // A wave's rows mostly share one slot: its activation chunks are read
+      // from LDS once per slot, not once per row.
       const int sub = lane % LPRD;
+      XChunk<BITS> xa[CPLD];
+      float2 xsm[CPLD];
+      float undo = 0.0f;
+      int jcur = -1;
 #pragma unroll
       for (int s = 0; s < STEPSD; ++s) {
         const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
         const int j = u / RD, i = u % RD;
         const bool ok = j < KS && b + NB * i < H;
         const int jj = ok ? j : 0;
+        if (jj != jcur) {
+#pragma unroll
+          for (int c = 0; c < CPLD; ++c) {
+            const int cc = min(sub + LPRD * c, nchD - 1);
+            xa[c] = load_xchunk<BITS>(ap + (int64_t)jj * (I / 2), cc, nchD);
+            xsm[c] = *reinterpret_cast<const float2*>(as + kChunkSums * (jj * nchD + cc));
+          }
+          undo = aundo[jj];
+          jcur = jj;
+        }
         float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPLD; ++c) {
           const int cc = sub + LPRD * c;
-          if (ok && cc < nchD)
-            part += chunk_affine(chunk_dot<BITS>(qd[s][c], ap + (int64_t)jj * (I / 2) + cc * PPC), sd[s][c],
-                                 as + kChunkSums * (jj * nchD + cc));
+          if (ok && cc < nchD) part += chunk_affine(chunk_dot<BITS>(qd[s][c], xa[c]), sd[s][c], xsm[c]);
         }
-        const float undo = 1.0f / pow2_stage_factor(__uint_as_float(amax[jj]));
-        const float d = group_sum(part, LPRD) * undo;
-        if (ok && sub == 0) dres[j * RD + i] = d;
+        const float d = group_sum_dpp<LPRD>(part) * undo;
+        if (ok && sub == LPRD - 1) dres[j * RD + i] = d;
       }
     }
     stamp0(li, 18);

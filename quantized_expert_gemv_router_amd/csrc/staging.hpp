@@ -123,10 +123,7 @@ __device__ __forceinline__ void stage_batch(int nvec, int n, Loader load, bool r
         if (w < nwords) {
           uint32_t pr[HP];
           pack_word<BITS>(v[m][i], f, pr, X, Xs);
-          uint4* dst = reinterpret_cast<uint4*>(pairs + (int64_t)m * np + (int64_t)w * HP);
-#pragma unroll
-          for (int j = 0; j < HP / 4; ++j)
-            dst[j] = make_uint4(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]);
+          store_word<BITS>(pairs + (int64_t)m * np, w, nch, pr);
         }
         // words 4c..4c+3 of chunk c sit in four consecutive lanes
         X += __shfl_xor(X, 1, 64);
