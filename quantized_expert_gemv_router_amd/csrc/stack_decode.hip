@@ -307,12 +307,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       gso[m] = sb_off + r * gpr * 4u;
     }
   };
+  // chunk-major: the dots take one staged x chunk at a time against every
+  // row of the wave, so each chunk is read from LDS once
   auto issue_gu = [&]() {
 #pragma unroll
-    for (int m = 0; m < RPWG; ++m) {
+    for (int c = 0; c < CPLG; ++c) {
+      const int cc = min(lane + 64 * c, nchG - 1);   // past the row: the dots skip it
 #pragma unroll
-      for (int c = 0; c < CPLG; ++c) {
-        const int cc = min(lane + 64 * c, nchG - 1);   // past the row: the dots skip it
+      for (int m = 0; m < RPWG; ++m) {
         qg[m][c] = load_rsrc_b128(gq[m], gqo[m] + (uint32_t)cc * 16u);
         sg[m][c] = load_rsrc_b32(gq[m], gso[m] + (uint32_t)(cc * PC / 64) * 4u);
       }
@@ -320,19 +322,35 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     issue_fence();
   };
   auto gu_dots = [&](int jlo, int jhi) {
-    const float ux = undo_x;
+    bool live[RPWG];
+    bool any = false;
 #pragma unroll
     for (int m = 0; m < RPWG; ++m) {
       int j, sec, row;
-      const bool ok = gu_task(m, j, sec, row);
-      if (!(ok && j >= jlo && j < jhi)) continue;
-      float part = 0.0f;
+      live[m] = gu_task(m, j, sec, row) && j >= jlo && j < jhi;
+      any = any || live[m];
+    }
+    if (!any) return;
+    float part[RPWG];
 #pragma unroll
-      for (int c = 0; c < CPLG; ++c) {
-        const int cc = lane + 64 * c;
-        if (cc < nchG) part += chunk_affine(chunk_dot<BITS>(qg[m][c], xp, cc, nchG), sg[m][c], xs + kChunkSums * cc);
-      }
-      const float v = wave_sum_dpp(part) * ux;
+    for (int m = 0; m < RPWG; ++m) part[m] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPLG; ++c) {
+      const int cc = lane + 64 * c;
+      const int ccl = min(cc, nchG - 1);
+      const XChunk<BITS> x = load_xchunk<BITS>(xp, ccl, nchG);
+      const float2 xsum = *reinterpret_cast<const float2*>(xs + kChunkSums * ccl);
+#pragma unroll
+      for (int m = 0; m < RPWG; ++m)
+        if (live[m] && cc < nchG) part[m] += chunk_affine(chunk_dot<BITS>(qg[m][c], x), sg[m][c], xsum);
+    }
+    const float ux = undo_x;
+#pragma unroll
+    for (int m = 0; m < RPWG; ++m) {
+      if (!live[m]) continue;
+      int j, sec, row;
+      gu_task(m, j, sec, row);
+      const float v = wave_sum_dpp(part[m]) * ux;
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
     }
   };
