@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ int bar_flag;
   __shared__ int fail_flag;
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  int tid = threadIdx.x, lane = tid & 63;   // re-derived opaquely each layer, as b
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NB = gridDim.x;
   int b = blockIdx.x;   // re-derived opaquely each layer (see the layer loop)
@@ -453,13 +453,16 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   };
 
   for (int li = 0; li < L; ++li) {
-    // Row offsets and addresses derived from the block index are cheap to
-    // recompute; hoisted out of the loop they stay live across all phases
-    // and push registers into scratch, whose reloads are memory round trips.
+    // Row offsets and addresses derived from the block and thread indices
+    // are cheap to recompute; hoisted out of the loop they stay live across
+    // all phases and push registers into scratch, whose reloads are memory
+    // round trips.
     {
       int zero;
       asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
       b = (int)blockIdx.x + zero;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+      lane = tid & 63;
     }
     stamp(li, 0);
     // ------------------------------------------------------------ phase R
@@ -721,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     if (li + 1 == L) break;
     // next layer: router rows, shared-expert gate/up rows, pointer-table row,
     // in flight while h arrives
-    if (tid < S) eblob[K + tid] = shp[li + 1];
+    if (S > 0 && tid == 0) eblob[K] = shp[li + 1];   // at most one shared expert
     block_sync_lds();
     plan_router(li + 1);
     plan_gu(K, KS);
