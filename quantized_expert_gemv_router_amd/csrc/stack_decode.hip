@@ -196,17 +196,18 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   constexpr int PC = Pack<BITS>::kPerChunk, PW = Pack<BITS>::kPerWord;
   constexpr int RPSD = 64 / LPRD;          // down rows per wave step
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ double rpart[kWaves];
+  __shared__ double rpart[CPLR * kWaves];
   __shared__ double ssum[kWaves];
   __shared__ float hmax[kWaves];
   __shared__ uint32_t amax[kMaxKS];
   __shared__ float aundo[kMaxKS];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
-  __shared__ int64_t candk[kWaves * MOEQ_MAX_TOPK];
-  __shared__ int candi[kWaves * MOEQ_MAX_TOPK];
-  __shared__ int64_t sample_k[2 * kWaves], cand_tau;
-  __shared__ int cand_n;
+  __shared__ int64_t candk[kWaves * 64];
+  __shared__ int candi[kWaves * 64];
+  __shared__ int sample_k[2 * kWaves];
+  __shared__ int cand_cnt[kWaves];
+  __shared__ int wsel[kWaves][MOEQ_MAX_TOPK];   // each wave's copy of the selection
   __shared__ float selw[MOEQ_MAX_TOPK];
   __shared__ const uint8_t* eblob[kMaxKS];
   __shared__ const uint16_t* rtr[kMaxLayers];
@@ -242,16 +243,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   bar.gsize = (NB - bar.group + bar.ngroups - 1) / bar.ngroups;
   bar.epoch = 0;
 
-  // router geometry: RW rows per block, 8/RW segments per row
+  // router: RW (<= CPLR) rows per block, rows b + NB*k; each thread takes
+  // the columns of the h values it polls (2p, 2p+1 for p = tid + i*kThreads)
   const int RW = a.router_rows;
-  const int NSEG = kWaves / RW;
-  const int r_row = b + NB * (wave / NSEG);
-  const int r_seg = wave % NSEG;
-  const int seg_len = H / NSEG;
-  const int seg_ch = seg_len / 8;
   const int tbl_n = E + S;
 
-  u32x4 wr[CPLR];
+  uint32_t wr[CPLR][HW];
   u32x4 qg[RPWG][CPLG];
   uint32_t sg[RPWG][CPLG];
   u32x4 qd[STEPSD][CPLD];
@@ -275,15 +272,21 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   // Every lane issues its loads unconditionally; what a lane does not need
   // is outside its buffer range (zeros, no memory access) or re-reads a
   // valid address, and the dot products skip it.
-  rsrc_t rplan;                    // this wave's router row segment
+  rsrc_t rplan[CPLR];              // this block's router rows (empty range: no row)
   auto plan_router = [&](int li) {
-    const bool have = r_row < E;
-    const uint16_t* base = uniform_ptr(rtr[li]) + (int64_t)(have ? r_row : 0) * H + (int64_t)r_seg * seg_len;
-    rplan = make_rsrc(base, have ? (uint32_t)seg_ch * 16u : 0u);
+    const uint16_t* base = uniform_ptr(rtr[li]);
+#pragma unroll
+    for (int k = 0; k < CPLR; ++k) {
+      const int r = b + NB * k;
+      const bool have = k < RW && r < E;
+      rplan[k] = make_rsrc(base + (int64_t)(have ? r : 0) * H, have ? (uint32_t)H * 2u : 0u);
+    }
   };
   auto issue_router = [&]() {
 #pragma unroll
-    for (int c = 0; c < CPLR; ++c) wr[c] = load_rsrc_b128(rplan, (uint32_t)(lane + 64 * c) * 16u);
+    for (int k = 0; k < CPLR; ++k)
+#pragma unroll
+      for (int i = 0; i < HW; ++i) wr[k][i] = load_rsrc_b32(rplan[k], (uint32_t)(tid + i * kThreads) * 4u);
   };
   // gate/up rows of the tasks whose slot is in [jlo, jhi); gu_task is
   // uniform over a wave, so each row is one scalar buffer resource
@@ -300,9 +303,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       int j, sec, row;
       const bool ok = gu_task(m, j, sec, row);
       ghave[m] = ok && j >= jlo && j < jhi;
-      const uint8_t* blob = uniform_ptr(eblob[ghave[m] ? j : 0]);
+      // routed slots: this wave's own copy of the selection; the shared one
+      // from eblob.  A missing expert (null) loads nothing.
+      const int jj = ghave[m] ? j : K;
+      const int e = jj < K ? wsel[wave][jj] : 0;
+      const uint8_t* blob = uniform_ptr(jj < K ? ((unsigned)e < (unsigned)E ? tbl[e] : nullptr)
+                                               : eblob[min(jj, KS - 1)]);
       const uint32_t r = ghave[m] ? (uint32_t)(sec * I + row) : 0u;   // row of [gate; up]
-      gq[m] = make_rsrc(blob, ghave[m] ? blob_bytes : 0u);
+      gq[m] = make_rsrc(blob, ghave[m] && blob != nullptr ? blob_bytes : 0u);
       gqo[m] = r * row_bytes;
       gso[m] = sb_off + r * gpr * 4u;
     }
@@ -354,39 +362,39 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
     }
   };
-  // down rows: step s of a wave covers RPSD rows, LPRD lanes each
-  const uint8_t* dblob[STEPSD];  // this lane's expert for step s (slot 0's for a padding lane)
+  // down rows: step s of a wave covers RPSD rows, LPRD lanes each; RPSD
+  // divides RD, so a step's rows belong to one slot
+  rsrc_t dsrc[STEPSD];       // the step's expert blob, or an empty range
   auto down_row = [&](int s, int& j, int& row) {
     const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
     j = u / RD;
     row = b + NB * (u % RD);
   };
   auto plan_down = [&]() {
+    const uint32_t blob_bytes = 3u * (uint32_t)H * I * BITS / 8 + 3u * (uint32_t)(H / 64) * I * 4u;
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
-      int j, row;
-      down_row(s, j, row);
-      dblob[s] = (j < KS && row < H) ? eblob[j] : eblob[0];
+      const int j = __builtin_amdgcn_readfirstlane(((wave * STEPSD + s) * RPSD) / RD);
+      const uint8_t* blob = j < KS ? uniform_ptr(eblob[j]) : nullptr;
+      dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes : 0u);
     }
   };
   auto issue_down = [&]() {
-    const int64_t row_bytes = (int64_t)I * BITS / 8;
-    const int gpr = I / 64;
+    const uint32_t row_bytes = (uint32_t)I * BITS / 8;
+    const uint32_t gpr = I / 64;
+    const uint32_t q_off = 2u * (uint32_t)H * I * BITS / 8;
+    const uint32_t sb_off = 3u * (uint32_t)H * I * BITS / 8 + 2u * (uint32_t)H * (I / 64) * 4u;
     const int sub = lane % LPRD;
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
       int j, row;
       down_row(s, j, row);
-      if (!(j < KS && row < H)) row = 0;   // padding lane: re-reads a valid row, skipped by the dots
-      const uint8_t* blob = dblob[s];
-      const uint8_t* q = blob + 2 * (int64_t)H * I * BITS / 8 + (int64_t)row * row_bytes;
-      const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + 3 * (int64_t)H * I * BITS / 8 +
-                                                             2 * (int64_t)H * I / 64 * 4) + (int64_t)row * gpr;
+      if (row >= H) row = 0;   // padding lane: re-reads a valid row, skipped by the dots
 #pragma unroll
       for (int c = 0; c < CPLD; ++c) {
         const int cc = min(sub + LPRD * c, nchD - 1);
-        qd[s][c] = load_stream(reinterpret_cast<const u32x4*>(q) + cc);
-        sd[s][c] = load_stream(sb + (cc * PC) / 64);
+        qd[s][c] = load_rsrc_b128(dsrc[s], q_off + (uint32_t)row * row_bytes + (uint32_t)cc * 16u);
+        sd[s][c] = load_rsrc_b32(dsrc[s], sb_off + ((uint32_t)row * gpr + (uint32_t)(cc * PC / 64)) * 4u);
       }
     }
     issue_fence();
@@ -491,22 +499,40 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         for (int i = 0; i < HW; ++i) hv[i] = ((uint64_t)hw[2 * i + 1] << 32) | hw[2 * i];
       }
       if (block_failed(ok)) return;
+      // sum of squares and max |h| (for the norm and the fp16 rescale) and
+      // this thread's share of the router rows' dot products, from the
+      // polled registers: one barrier then completes the logits
       double ss = 0.0;
+      double racc[CPLR];
+#pragma unroll
+      for (int k = 0; k < CPLR; ++k) racc[k] = 0.0;
       float mx = 0.0f;
 #pragma unroll
       for (int i = 0; i < HW; ++i) {
         const int p = tid + i * kThreads;
+        const float lo = __uint_as_float((uint32_t)hv[i]), hi = __uint_as_float((uint32_t)(hv[i] >> 32));
         if (2 * p < H) {
-          const float lo = __uint_as_float((uint32_t)hv[i]), hi = __uint_as_float((uint32_t)(hv[i] >> 32));
           *reinterpret_cast<float2*>(hs + 2 * p) = make_float2(lo, hi);
           ss = fma((double)lo, (double)lo, ss);
           ss = fma((double)hi, (double)hi, ss);
           mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
         }
+#pragma unroll
+        for (int k = 0; k < CPLR; ++k) {   // zeros past the row (buffer range)
+          racc[k] = fma((double)bf16_lo(wr[k][i]), (double)lo, racc[k]);
+          racc[k] = fma((double)bf16_hi(wr[k][i]), (double)hi, racc[k]);
+        }
       }
       ss = wave_sum_f64_dpp(ss);
       mx = wave_max_dpp(mx);
-      if (lane == 0) { ssum[wave] = ss; hmax[wave] = mx; }
+#pragma unroll
+      for (int k = 0; k < CPLR; ++k) racc[k] = wave_sum_f64_dpp(racc[k]);
+      if (lane == 0) {
+        ssum[wave] = ss;
+        hmax[wave] = mx;
+#pragma unroll
+        for (int k = 0; k < CPLR; ++k) rpart[k * kWaves + wave] = racc[k];
+      }
     }
     __syncthreads();
     stamp(li, 1);
@@ -515,31 +541,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) { ss += ssum[i]; mx = fmaxf(mx, hmax[i]); }
     const double inv = 1.0 / sqrt(ss / (double)H + 1e-6);
-
-    // router: fp64 partial dot of this wave's segment
-    {
-      double acc = 0.0;
-      if (r_row < E) {
-#pragma unroll
-        for (int c = 0; c < CPLR; ++c) {
-          const int cc = lane + 64 * c;
-          if (cc < seg_ch) {
-            const float* hp = hs + r_seg * seg_len + 8 * cc;
-            const float4 x0 = *reinterpret_cast<const float4*>(hp);
-            const float4 x1 = *reinterpret_cast<const float4*>(hp + 4);
-            acc = fma((double)bf16_lo(wr[c][0]), (double)x0.x, acc);
-            acc = fma((double)bf16_hi(wr[c][0]), (double)x0.y, acc);
-            acc = fma((double)bf16_lo(wr[c][1]), (double)x0.z, acc);
-            acc = fma((double)bf16_hi(wr[c][1]), (double)x0.w, acc);
-            acc = fma((double)bf16_lo(wr[c][2]), (double)x1.x, acc);
-            acc = fma((double)bf16_hi(wr[c][2]), (double)x1.y, acc);
-            acc = fma((double)bf16_lo(wr[c][3]), (double)x1.z, acc);
-            acc = fma((double)bf16_hi(wr[c][3]), (double)x1.w, acc);
-          }
-        }
-      }
-      acc = wave_sum_f64_dpp(acc);
-      if (lane == 0) rpart[wave] = acc;
+    const uint32_t tag = (uint32_t)li + 1u;
+    if (tid < RW && b + NB * tid < E) {   // logits of this block's router rows
+      double d = 0.0;
+      for (int w = 0; w < kWaves; ++w) d += rpart[tid * kWaves + w];
+      const int r = b + NB * tid;
+      const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
+      put_tagged(a.lwords + 2 * r, (uint32_t)bits, tag);
+      put_tagged(a.lwords + 2 * r + 1, (uint32_t)(bits >> 32), tag);
     }
     // xhat -> fp16 pairs, one packed word per thread; the norm and the
     // rescale come from the h pass above, so no further reductions
@@ -563,14 +572,6 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
     }
     __syncthreads();
-    const uint32_t tag = (uint32_t)li + 1u;
-    if (lane == 0 && r_seg == 0 && r_row < E) {
-      double d = 0.0;
-      for (int sgi = 0; sgi < NSEG; ++sgi) d += rpart[wave + sgi];
-      const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
-      put_tagged(a.lwords + 2 * r_row, (uint32_t)bits, tag);
-      put_tagged(a.lwords + 2 * r_row + 1, (uint32_t)(bits >> 32), tag);
-    }
     stamp(li, 2);
     gu_dots(K, KS);                 // the shared expert's rows are already here
     stamp(li, 3);
@@ -579,46 +580,63 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // ------------------------------------------------------------ phase G
     // this layer's pointer-table row lands while the logits are polled
     load_tbl_row(a.layer0 + li);
+    int64_t key = kNoKey;   // this thread's logit (E <= kThreads)
     for (int e0 = 0; e0 < E; e0 += kThreads) {   // one logit (two words) per thread per pass
       const int e = e0 + tid;
       uint32_t w[2] = {0u, 0u};
       const bool ok = take_tagged<2>(a.lwords + 2 * e, [](int i) { return i; }, e < E ? 3u : 0u, tag, w,
                                      abort_word, a.status);
-      if (e < E) lg[e] = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
+      if (e < E) {
+        const double v = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
+        lg[e] = v;
+        key = order_key(v);
+      }
+      if (E <= kThreads) topk_samples<kWaves>(key, K, sample_k);
       if (block_failed(ok)) return;
     }
     store_tbl_row();
-    __syncthreads();
+    if (tid < KS) amax[tid] = 0u;
     stamp0(li, 12);
+    // top-K: every wave ends with its own copy of the selection, so the
+    // gate/up rows are requested without another block barrier
+    bool fast = false;
     if (E <= kThreads) {
-      if (!block_topk_sample<kWaves>(lg, E, K, sample_k, candk, candi, &cand_n, &cand_tau, sel, selv))
-        block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
+      topk_candidates<kWaves>(key, tid, K, sample_k, candk, candi, cand_cnt);
+      __syncthreads();
+      fast = topk_select<kWaves>(K, candk, candi, cand_cnt, [&](int r, int win) { wsel[wave][r] = win; });
     } else {
-      block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
+      __syncthreads();
     }
+    if (!fast) {   // block-uniform
+      if (E <= kThreads) block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
+      else block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
+      if (lane < K) wsel[wave][lane] = sel[lane];
+    }
+    stamp0(li, 14);
+    plan_gu(0, K);                   // routed gate/up rows
+    issue_gu();
+    stamp0(li, 5);
+    // while they arrive: wave 0 takes the softmax weights and the blob
+    // pointers the down rows use (read after the next block barrier)
     if (wave == 0) {
+      if (lane < K) selv[lane] = (unsigned)wsel[0][lane] < (unsigned)E ? lg[wsel[0][lane]] : -INFINITY;
       const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
                                   : wave_softmax_selected(selv, K);
-      stamp0(li, 14);
       if (lane < K) {
         selw[lane] = w;
-        const uint8_t* bp = tbl[sel[lane]];
+        const int e = wsel[0][lane];
+        const uint8_t* bp = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
         eblob[lane] = bp;
         if (bp == nullptr) set_status(a.status, kStatusBadExpert);
-        if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = sel[lane];
+        if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
       }
     }
-    if (tid < KS) amax[tid] = 0u;
-    __syncthreads();
-    stamp(li, 5);
-    plan_gu(0, K);                   // routed gate/up rows
-    plan_down();                     // every slot's down rows (LDS reads before any load)
-    issue_gu();
     stamp0(li, 15);
     gu_dots(0, K);
     stamp0(li, 13);
     __syncthreads();
     stamp(li, 6);
+    plan_down();                     // every slot's down rows (eblob is complete now)
     for (int t = tid; t < KS * RG; t += kThreads) {
       const int j = t / RG, i = t - j * RG, row = b + NB * i;
       if (row < I) {
@@ -771,8 +789,7 @@ struct Geometry {
     // expert blobs are addressed with 32-bit byte offsets
     if ((int64_t)3 * H * I * BITS / 8 + (int64_t)3 * (H / 64) * I * 4 >= (int64_t{1} << 31)) return false;
     const int PC = 128 / BITS;
-    const int seg = H / (kWaves / rw);
-    if (seg % 8 || seg / 8 > 64 * CPLR) return false;
+    if (rw > CPLR) return false;
     if (H / PC > 64 * CPLG) return false;
     const int RG = (I + nb - 1) / nb, RD = (H + nb - 1) / nb;
     if (KS * 2 * RG > kWaves * RPWG) return false;
@@ -780,6 +797,7 @@ struct Geometry {
     if (nchd > LPRD * CPLD) return false;
     if (KS * (I * BITS / 32) > kThreads) return false;   // one activation word per thread
     if (KS * RD > kWaves * STEPSD * (64 / LPRD)) return false;
+    if (RD % (64 / LPRD) != 0) return false;   // a down step's rows share one slot
     if (H > 2 * kThreads * HW) return false;
     if (E + S > kTblPer * kThreads) return false;
     return true;
@@ -813,7 +831,7 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
   if (g.fits(4, 2, 2, 4, 32, 1, 4, 4)) return launch_t<4, 2, 2, 4, 32, 1, 4, 4>(a, nb, lds, stream);
   if (g.fits(2, 2, 1, 5, 16, 1, 3, 4)) return launch_t<2, 2, 1, 5, 16, 1, 3, 4>(a, nb, lds, stream);
-  if (g.fits(4, 1, 1, 1, 4, 1, 1, 1)) return launch_t<4, 1, 1, 1, 4, 1, 1, 1>(a, nb, lds, stream);
+  if (g.fits(4, 1, 1, 1, 64, 1, 1, 1)) return launch_t<4, 1, 1, 1, 64, 1, 1, 1>(a, nb, lds, stream);
   return hipErrorNotSupported;
 }
 

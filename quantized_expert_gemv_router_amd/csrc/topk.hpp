@@ -208,67 +208,94 @@ __device__ __forceinline__ void block_topk_keys(const double* lg, int E, int K, 
   __syncthreads();
 }
 
-// All NW waves, one logit per thread (E <= 64*NW), K <= 2*NW: top-K by a
-// threshold.  Each wave publishes its P = ceil(K/NW) largest keys; tau, the
-// K-th largest of those NW*P samples, is at most the K-th largest key of all
-// E, so every element of the true top-K has a key >= tau, and at least K
-// elements do.  Those candidates are compacted into LDS and ranked by
-// (key desc, index asc) in wave 0.  Returns false (nothing written, block
-// uniform) when more than 64 candidates pass, e.g. under massive ties; the
-// caller then runs block_topk_keys.  Scratch: wk [2*NW], ck/ci [64], cnt,
-// tau.  Ends with a block barrier.
+// Threshold top-K over NW waves, one key per thread (E <= 64*NW, K <= 2*NW),
+// in three steps separated by block barriers, after which EVERY wave holds
+// the selection (no barrier is needed between the selection and its use).
+// The threshold works on the keys' high words h = key >> 32 (a monotone
+// map, so ties only add candidates): each wave publishes its P =
+// ceil(K/NW) largest h; tau, the K-th largest of those NW*P samples, is at
+// most the high word of the K-th largest key, so every element of the true
+// top-K has h >= tau, and at least K elements do.  Those candidates are
+// compacted per wave and ranked on their full keys (key desc, index asc).
+//
+// Step 1 (each wave, then a block barrier): samples into wk[w*P ..].
 template <int NW>
-__device__ __forceinline__ bool block_topk_sample(const double* lg, int E, int K, int64_t* wk, int64_t* ck,
-                                                  int* ci, int* cnt, int64_t* tau, int* sel, double* selv) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__device__ __forceinline__ void topk_samples(int64_t key, int K, int* wk) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int P = (K + NW - 1) / NW;
-  const int64_t key = tid < E ? order_key(lg[tid]) : kNoKey;
-  const int64_t m1 = wave_max_key(key);
-  int64_t m2 = kNoKey;
+  const int h = (int)(key >> 32);
+  const int m1 = wave_max_i32(h);
+  int m2 = INT_MIN;
   if (P > 1) {   // second largest: drop one lane holding the maximum
-    const uint64_t mask = __ballot(key == m1);
-    m2 = wave_max_key(lane == __builtin_ctzll(mask) ? kNoKey : key);
+    const uint64_t mask = __ballot(h == m1);
+    m2 = wave_max_i32(lane == __builtin_ctzll(mask) ? INT_MIN : h);
   }
   if (lane == 0) {
     wk[w * P] = m1;
     if (P > 1) wk[w * P + 1] = m2;
   }
-  if (tid == 0) *cnt = 0;
-  __syncthreads();
-  if (tid < NW * P) {   // the sample of rank K-1 (ties by sample position)
-    const int64_t v = wk[tid];
-    int r = 0;
-    for (int s = 0; s < NW * P; ++s) {
-      const int64_t o = wk[s];
-      r += (o > v || (o == v && s < tid)) ? 1 : 0;
-    }
-    if (r == K - 1) *tau = v;
+}
+
+// Step 2 (every wave, then a block barrier): tau from the samples (each
+// wave computes it), then this wave's candidates (h >= tau; element index
+// e) into ck/ci[w*64 ..] and their number into cnt[w].
+template <int NW>
+__device__ __forceinline__ void topk_candidates(int64_t key, int e, int K, const int* wk, int64_t* ck,
+                                                int* ci, int* cnt) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int NS = NW * ((K + NW - 1) / NW);
+  // the sample of rank K-1 (ties by sample position): lane s < NS ranks
+  // sample s by counting
+  const int v = lane < NS ? wk[lane] : INT_MIN;
+  int r = 0;
+#pragma unroll
+  for (int s = 0; s < 2 * NW; ++s) {
+    const int o = __builtin_amdgcn_readlane(v, s);
+    r += (s < NS && (o > v || (o == v && s < lane))) ? 1 : 0;
   }
-  __syncthreads();
-  if (tid < E && key >= *tau) {
-    const int slot = atomicAdd(cnt, 1);
-    if (slot < 64) {
-      ck[slot] = key;
-      ci[slot] = tid;
-    }
+  const uint64_t at = __ballot(lane < NS && r == K - 1);
+  const int tau = __builtin_amdgcn_readlane(v, __builtin_ctzll(at));
+  const bool pass = key != kNoKey && (int)(key >> 32) >= tau;
+  const uint64_t mask = __ballot(pass);
+  if (pass) {
+    const int pos = __builtin_popcountll(mask & ((1ull << lane) - 1ull));
+    ck[w * 64 + pos] = key;
+    ci[w * 64 + pos] = e;
   }
-  __syncthreads();
-  const int C = *cnt;
+  if (lane == 0) cnt[w] = __builtin_popcountll(mask);
+}
+
+// Step 3 (every wave): the K best candidates in rank order through
+// emit(r, index) on the lane holding rank r.  Returns false (the same in
+// every wave) when more than 64 candidates passed; the caller then falls
+// back to block_topk_keys.
+template <int NW, typename Emit>
+__device__ __forceinline__ bool topk_select(int K, const int64_t* ck, const int* ci, const int* cnt, Emit emit) {
+  const int lane = threadIdx.x & 63;
+  int pre[NW + 1];
+  pre[0] = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) pre[w + 1] = pre[w] + __builtin_amdgcn_readfirstlane(cnt[w]);
+  const int C = pre[NW];
   if (C > 64) return false;
-  if (tid < C) {
-    const int64_t v = ck[tid];
-    const int vi = ci[tid];
-    int r = 0;
-    for (int c = 0; c < C; ++c) {
-      const int64_t o = ck[c];
-      r += (o > v || (o == v && ci[c] < vi)) ? 1 : 0;
-    }
-    if (r < K) {
-      sel[r] = vi;
-      selv[r] = lg[vi];
+  int64_t k = kNoKey;
+  int id = kTopkNone;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (lane >= pre[w] && lane < pre[w + 1]) {
+      k = ck[w * 64 + lane - pre[w]];
+      id = ci[w * 64 + lane - pre[w]];
     }
   }
-  __syncthreads();
+  // rank by counting over the C candidates (few: about K)
+  int r = 0;
+  for (int c = 0; c < C; ++c) {
+    const int64_t o = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(k >> 32), c) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, c));
+    const int oi = __builtin_amdgcn_readlane(id, c);
+    r += (o > k || (o == k && oi < id)) ? 1 : 0;
+  }
+  if (lane < C && r < K) emit(r, id);
   return true;
 }
 
