@@ -12,27 +12,37 @@
 //   a = silu(g) u, d = Wd a;  h <- h + sum_k w_k d_k + d_shared
 //
 // Grid: one workgroup of 8 waves per CU, all co-resident (cooperative
-// launch).  Three grid barriers per layer separate the all-to-all steps:
-//   A: h complete      -> each block reads h, router rows, xhat staging
-//   B: logits complete -> top-K (every block, redundantly), gate/up
-//   C: activations a   -> down rows and the combine
-// Loads are issued as early as their addresses are known: the router and
-// shared-expert pointers of every layer are cached in LDS at start, the next
-// layer's router rows, shared-expert gate/up rows and pointer-table row are
-// requested before barrier A, and the shared expert's gate/up is computed
-// before barrier B, so after top-K only the routed experts' rows remain on
-// the critical path (their down rows are requested right after their
-// gate/up rows).  Each block owns fixed rows of every matrix:
-//   router rows  e = b + NB*i, split into 8/RW segments across waves;
+// launch).  Three all-to-all steps per layer, each a handoff of tagged
+// words (payload + layer tag in one 64-bit word, polled by the readers; no
+// grid barrier or fence between the phases):
+//   h:       each block publishes its rows of h_{l+1}; every block polls all
+//            of h, takes sum(h^2), max|h| and its router rows' partial dot
+//            products from the polled registers, and after one block
+//            barrier publishes its logits
+//   logits:  every block polls all E logits and selects top-K itself
+//            (threshold on the keys' high words, every wave keeps its own
+//            copy of the selection), then streams its gate/up rows
+//   a:       each block publishes silu(g)*u for its gate/up rows; every block
+//            polls all activations of the K + S slots, then its down rows
+//            and the combine with the residual.
+// Loads are issued as early as their addresses are known and their data
+// does not compete with loads on the critical path: the router and
+// shared-expert pointers of every layer are cached in LDS at start; the
+// next layer's router rows and shared-expert gate/up rows are requested
+// right after h is published, and the shared expert's gate/up is computed
+// while the logits travel; the down rows are requested once the gate/up
+// rows are consumed.  A poll's loads complete after every load the wave
+// issued before them (the vector memory counter is in order), which is why
+// nothing large is requested just before a poll that is on the critical
+// path.  Each block owns fixed rows of every matrix:
+//   router rows  e = b + NB*k (every thread takes the columns of the h
+//   values it polls);
 //   gate/up rows r = b + NB*i of every selected expert (a = silu(g)*u is
 //   formed locally);
 //   down rows    r = b + NB*i of every selected expert (the combine is a
 //   per-row sum in slot order, no atomics).
-// Cross-block data (logits, activations, h) moves with agent-scope
-// write-through stores and loads; each barrier waits for the caller's
-// stores to complete before arriving.  Barriers are two-level counter
-// trees with bounded spins: on time-out a block sets the status word and
-// an abort flag, and every block leaves the kernel.
+// Every wait is bounded: on time-out a block sets the status word and an
+// abort flag, and every block leaves the kernel.
 #include "moeq_device.hpp"
 #include "moeq_internal.hpp"
 #include "topk.hpp"
