@@ -282,7 +282,9 @@ def run_prefill(args, cfg, dev, stream):
         t0 = time.perf_counter()
         start.record(stream)
         for i in range(args.steps):
-            step(args.warmup + i)
+            # the routing of the last warm-up step gives the bytes per step; with
+            # no warm-up, the first timed step records it (80 KB per layer)
+            step(args.warmup + i, tk if (args.warmup == 0 and i == 0) else None)
         end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
