@@ -56,6 +56,7 @@ constexpr int kGroups = 8;                 // barrier tree: groups of blocks
 constexpr int kBarWords = 32 * (kGroups + 2);
 constexpr int kSpinLimit = 1 << 18;        // polls before a barrier gives up
 constexpr int kMaxKS = 8;                  // selected + shared experts per layer
+constexpr int kActSums = 4;                // per staged activation chunk: X, 1024 X', undo, pad
 constexpr int kMaxLayers = 128;            // per persistent launch
 constexpr int kTblPer = 8;                 // pointer-table entries per thread (E + S <= 4096)
 static_assert(kWaves * MOEQ_MAX_TOPK <= 64 * 2, "top-K merge holds two candidates per lane");
@@ -170,7 +171,7 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S,
   L.xs = al16(L.xp + 2 * H);
   L.ap = al16(L.xs + 4 * kChunkSums * (H / PC));
   L.as = al16(L.ap + KS * 2 * I);
-  L.gres = al16(L.as + 4 * kChunkSums * KS * (I / PC));
+  L.gres = al16(L.as + 4 * kActSums * KS * (I / PC));
   L.dres = al16(L.gres + 4 * KS * 2 * RG);
   L.lg = al16(L.dres + 4 * KS * RD);
   L.tbl = al16(L.lg + 8 * E);
@@ -209,8 +210,6 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ double rpart[CPLR * kWaves];
   __shared__ double ssum[kWaves];
   __shared__ float hmax[kWaves];
-  __shared__ uint32_t amax[kMaxKS];
-  __shared__ float aundo[kMaxKS];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
   __shared__ int64_t candk[kWaves * 64];
@@ -239,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem + LL.xp);         // [H/2]
   float* xs = reinterpret_cast<float*>(smem + LL.xs);               // [H/PC][kChunkSums]
   uint32_t* ap = reinterpret_cast<uint32_t*>(smem + LL.ap);         // [KS][I/2]
-  float* as = reinterpret_cast<float*>(smem + LL.as);               // [KS][I/PC][kChunkSums]
+  float* as = reinterpret_cast<float*>(smem + LL.as);               // [KS][I/PC][kActSums]
   float* gres = reinterpret_cast<float*>(smem + LL.gres);           // [KS][2][RG]
   float* dres = reinterpret_cast<float*>(smem + LL.dres);           // [KS][RD]
   double* lg = reinterpret_cast<double*>(smem + LL.lg);             // [E]
@@ -605,7 +604,6 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (block_failed(ok)) return;
     }
     store_tbl_row();
-    if (tid < KS) amax[tid] = 0u;
     stamp0(li, 12);
     // top-K: every wave ends with its own copy of the selection, so the
     // gate/up rows are requested without another block barrier
@@ -662,10 +660,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     stamp(li, 8);
 
     // ------------------------------------------------------------ phase D
-    // activations: one packed word of one slot per thread
+    // activations: one packed word of one slot per thread, staged with a
+    // power-of-two scale per 16-byte chunk (the four threads of a chunk
+    // agree on it with two lane shuffles), so staging needs no block-wide
+    // maximum; the one block barrier below also settles a failed poll
     {
       const int nwa = I / PW;
       const int total = KS * nwa;
+      bool got_all = true;
       for (int t0 = 0; t0 < total; t0 += kThreads) {
         const int t = t0 + tid;
         const bool ok = t < total;
@@ -677,37 +679,33 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         const uint64_t* src = a.awords + (int64_t)m * I + (int64_t)w * PW;
         const bool got = take_tagged<PW>(src, [](int j) { return j; }, ok ? (uint32_t)((1ull << PW) - 1) : 0u,
                                          tag, raw, abort_word, a.status);
-        if (ok) {
-          float lm = 0.0f;
-#pragma unroll
-          for (int j = 0; j < PW; ++j) {
-            v[j] = __uint_as_float(raw[j]);
-            lm = fmaxf(lm, fabsf(v[j]));
-          }
-          atomicMax(&amax[m], __float_as_uint(lm));   // non-negative floats order as integers
-        }
+        got_all = got_all && got;
         stamp0(li, 16);
-        if (block_failed(got)) return;
-        stamp0(li, 17);
-        float2 s = make_float2(0.0f, 0.0f);
-        if (ok) {
-          const float p = pow2_stage_factor(__uint_as_float(amax[m]));
-          s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w, nchD);
-          if (w == 0) aundo[m] = 1.0f / p;
+        float lm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PW; ++j) {
+          v[j] = __uint_as_float(raw[j]);
+          lm = fmaxf(lm, fabsf(v[j]));
         }
+        lm = fmaxf(lm, __shfl_xor(lm, 1, 64));
+        lm = fmaxf(lm, __shfl_xor(lm, 2, 64));
+        const float p = pow2_stage_factor(lm);
+        float2 s = make_float2(0.0f, 0.0f);
+        if (ok) s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w, nchD);
         s = quad_sum(s);
-        if (ok && (tid & 3) == 0) *reinterpret_cast<float2*>(as + kChunkSums * (m * nchD + (w >> 2))) = s;
+        if (ok && (tid & 3) == 0)
+          *reinterpret_cast<float4*>(as + kActSums * (m * nchD + (w >> 2))) = make_float4(s.x, s.y, 1.0f / p, 0.0f);
       }
+      if (block_failed(got_all)) return;
+      stamp0(li, 17);
     }
-    __syncthreads();
     stamp(li, 9);
     {
       // A wave's rows mostly share one slot: its activation chunks are read
       // from LDS once per slot, not once per row.
       const int sub = lane % LPRD;
       XChunk<BITS> xa[CPLD];
-      float2 xsm[CPLD];
-      float undo = 0.0f;
+      float4 xsm[CPLD];   // chunk sums {X, 1024 X'} and the chunk's undo factor
       int jcur = -1;
 #pragma unroll
       for (int s = 0; s < STEPSD; ++s) {
@@ -720,18 +718,19 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           for (int c = 0; c < CPLD; ++c) {
             const int cc = min(sub + LPRD * c, nchD - 1);
             xa[c] = load_xchunk<BITS>(ap + (int64_t)jj * (I / 2), cc, nchD);
-            xsm[c] = *reinterpret_cast<const float2*>(as + kChunkSums * (jj * nchD + cc));
+            xsm[c] = *reinterpret_cast<const float4*>(as + kActSums * (jj * nchD + cc));
           }
-          undo = aundo[jj];
           jcur = jj;
         }
         float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPLD; ++c) {
           const int cc = sub + LPRD * c;
-          if (ok && cc < nchD) part += chunk_affine(chunk_dot<BITS>(qd[s][c], xa[c]), sd[s][c], xsm[c]);
+          if (ok && cc < nchD)
+            part += chunk_affine(chunk_dot<BITS>(qd[s][c], xa[c]), sd[s][c], make_float2(xsm[c].x, xsm[c].y)) *
+                    xsm[c].z;
         }
-        const float d = group_sum_dpp<LPRD>(part) * undo;
+        const float d = group_sum_dpp<LPRD>(part);
         if (ok && sub == LPRD - 1) dres[j * RD + i] = d;
       }
     }
