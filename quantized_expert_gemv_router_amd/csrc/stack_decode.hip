@@ -158,7 +158,7 @@ __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint3
 
 // ------------------------------------------------------------------ layout
 struct StackLds {
-  int hs, xp, xs, ap, as, gres, dres, lg, tbl, clk, total;
+  int hs, xp, xs, ap, as, gres, lg, tbl, clk, total;
 };
 
 __host__ __device__ inline int al16(int v) { return (v + 15) & ~15; }
@@ -172,8 +172,7 @@ __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S,
   L.ap = al16(L.xs + 4 * kChunkSums * (H / PC));
   L.as = al16(L.ap + KS * 2 * I);
   L.gres = al16(L.as + 4 * kActSums * KS * (I / PC));
-  L.dres = al16(L.gres + 4 * KS * 2 * RG);
-  L.lg = al16(L.dres + 4 * KS * RD);
+  L.lg = al16(L.gres + 4 * KS * 2 * RG);
   L.tbl = al16(L.lg + 8 * E);
   L.clk = al16(L.tbl + 8 * (E + S));
   L.total = al16(L.clk + 8 * clk_entries);
@@ -240,7 +239,6 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t* ap = reinterpret_cast<uint32_t*>(smem + LL.ap);         // [KS][I/2]
   float* as = reinterpret_cast<float*>(smem + LL.as);               // [KS][I/PC][kActSums]
   float* gres = reinterpret_cast<float*>(smem + LL.gres);           // [KS][2][RG]
-  float* dres = reinterpret_cast<float*>(smem + LL.dres);           // [KS][RD]
   double* lg = reinterpret_cast<double*>(smem + LL.lg);             // [E]
   const uint8_t** tbl = reinterpret_cast<const uint8_t**>(smem + LL.tbl);  // [E + S], this layer
   int64_t* clk = reinterpret_cast<int64_t*>(smem + LL.clk);         // [L][kStackClockEvents] if timed
@@ -371,20 +369,20 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
     }
   };
-  // down rows: step s of a wave covers RPSD rows, LPRD lanes each; RPSD
-  // divides RD, so a step's rows belong to one slot
-  rsrc_t dsrc[STEPSD];       // the step's expert blob, or an empty range
+  // down rows: a wave owns RPSD of the block's output rows (LPRD lanes
+  // each), for every slot: step s is slot s, so the combine of a row stays
+  // in the wave
+  rsrc_t dsrc[STEPSD];       // slot s's expert blob, or an empty range
   auto down_row = [&](int s, int& j, int& row) {
-    const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
-    j = u / RD;
-    row = b + NB * (u % RD);
+    j = s;
+    const int i = wave * RPSD + lane / LPRD;
+    row = i < RD ? b + NB * i : H;   // H: no row
   };
   auto plan_down = [&]() {
     const uint32_t blob_bytes = 3u * (uint32_t)H * I * BITS / 8 + 3u * (uint32_t)(H / 64) * I * 4u;
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
-      const int j = __builtin_amdgcn_readfirstlane(((wave * STEPSD + s) * RPSD) / RD);
-      const uint8_t* blob = j < KS ? uniform_ptr(eblob[j]) : nullptr;
+      const uint8_t* blob = s < KS ? uniform_ptr(eblob[s]) : nullptr;
       dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes : 0u);
     }
   };
@@ -701,47 +699,30 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     }
     stamp(li, 9);
     {
-      // A wave's rows mostly share one slot: its activation chunks are read
-      // from LDS once per slot, not once per row.
+      // down rows of every slot and the combine, in registers: lane LPRD-1
+      // of each row group ends with the row's h
       const int sub = lane % LPRD;
-      XChunk<BITS> xa[CPLD];
-      float4 xsm[CPLD];   // chunk sums {X, 1024 X'} and the chunk's undo factor
-      int jcur = -1;
+      const int i = wave * RPSD + lane / LPRD;
+      const int row = b + NB * i;
+      const bool ok = i < RD && row < H;
+      float acc = ok ? hs[row] : 0.0f;
 #pragma unroll
       for (int s = 0; s < STEPSD; ++s) {
-        const int u = (wave * STEPSD + s) * RPSD + lane / LPRD;
-        const int j = u / RD, i = u % RD;
-        const bool ok = j < KS && b + NB * i < H;
-        const int jj = ok ? j : 0;
-        if (jj != jcur) {
-#pragma unroll
-          for (int c = 0; c < CPLD; ++c) {
-            const int cc = min(sub + LPRD * c, nchD - 1);
-            xa[c] = load_xchunk<BITS>(ap + (int64_t)jj * (I / 2), cc, nchD);
-            xsm[c] = *reinterpret_cast<const float4*>(as + kActSums * (jj * nchD + cc));
-          }
-          jcur = jj;
-        }
+        if (s >= KS) break;
         float part = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPLD; ++c) {
-          const int cc = sub + LPRD * c;
-          if (ok && cc < nchD)
-            part += chunk_affine(chunk_dot<BITS>(qd[s][c], xa[c]), sd[s][c], make_float2(xsm[c].x, xsm[c].y)) *
-                    xsm[c].z;
+          const int cc = min(sub + LPRD * c, nchD - 1);
+          const XChunk<BITS> x = load_xchunk<BITS>(ap + (int64_t)s * (I / 2), cc, nchD);
+          const float4 xsm = *reinterpret_cast<const float4*>(as + kActSums * (s * nchD + cc));
+          if (ok && sub + LPRD * c < nchD)
+            part += chunk_affine(chunk_dot<BITS>(qd[s][c], x), sd[s][c], make_float2(xsm.x, xsm.y)) * xsm.z;
         }
         const float d = group_sum_dpp<LPRD>(part);
-        if (ok && sub == LPRD - 1) dres[j * RD + i] = d;
+        acc = fmaf(s < K ? selw[s] : 1.0f, d, acc);   // slot order: routed, then shared
       }
-    }
-    stamp0(li, 18);
-    __syncthreads();
-    for (int i = tid; i < RD; i += kThreads) {
-      const int row = b + NB * i;
-      if (row < H) {
-        float acc = hs[row];
-        for (int j = 0; j < K; ++j) acc = fmaf(selw[j], dres[j * RD + i], acc);
-        for (int j = K; j < KS; ++j) acc = fmaf(1.0f, dres[j * RD + i], acc);
+      stamp0(li, 18);
+      if (ok && sub == LPRD - 1) {
         if (a.h_trace) a.h_trace[(int64_t)li * H + row] = hs[row];
         if (li + 1 == L) a.h[row] = acc;   // complete when the launch ends
         else put_tagged(a.hwords + row, __float_as_uint(acc), tag);
@@ -805,8 +786,8 @@ struct Geometry {
     const int nchd = I / PC;
     if (nchd > LPRD * CPLD) return false;
     if (KS * (I * BITS / 32) > kThreads) return false;   // one activation word per thread
-    if (KS * RD > kWaves * STEPSD * (64 / LPRD)) return false;
-    if (RD % (64 / LPRD) != 0) return false;   // a down step's rows share one slot
+    if (KS > STEPSD) return false;                 // one down step per slot
+    if (RD > kWaves * (64 / LPRD)) return false;   // every output row owned by a wave
     if (H > 2 * kThreads * HW) return false;
     if (E + S > kTblPer * kThreads) return false;
     return true;
@@ -839,8 +820,8 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,
   // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
   if (g.fits(4, 2, 2, 4, 32, 1, 4, 4)) return launch_t<4, 2, 2, 4, 32, 1, 4, 4>(a, nb, lds, stream);
-  if (g.fits(2, 2, 1, 5, 16, 1, 3, 4)) return launch_t<2, 2, 1, 5, 16, 1, 3, 4>(a, nb, lds, stream);
-  if (g.fits(4, 1, 1, 1, 64, 1, 1, 1)) return launch_t<4, 1, 1, 1, 64, 1, 1, 1>(a, nb, lds, stream);
+  if (g.fits(2, 2, 1, 5, 32, 1, 5, 4)) return launch_t<2, 2, 1, 5, 32, 1, 5, 4>(a, nb, lds, stream);
+  if (g.fits(4, 1, 1, 1, 64, 1, 3, 1)) return launch_t<4, 1, 1, 1, 64, 1, 3, 1>(a, nb, lds, stream);
   return hipErrorNotSupported;
 }
 
