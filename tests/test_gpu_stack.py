@@ -80,6 +80,32 @@ def test_stack_small_shape(flags):
         compare_free_running(cfg, cfg.layers, ts, traces, h.cpu().numpy()[0])
 
 
+@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
+def test_stack_all_logits_tied(flags):
+    """A zero router ties all 128 logits: more candidates pass the top-K
+    threshold than one wave ranks, so the persistent kernel takes its
+    block-wide selection; ties go to the lower index (experts 0..K-1,
+    weights 1/K)."""
+    cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_ties", hidden=256, inter=128,
+                             n_experts=128, top_k=2, layers=3)
+    shape, ex, _ = build_stack(cfg, cfg.layers)
+    zero = np.zeros((cfg.n_experts, cfg.hidden), dtype=np.uint16)
+    rt = q.RouterTable([bf16_dev(zero) for _ in range(cfg.layers)])
+    h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, 4, 1)).astype(np.float32)).cuda()
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    tk, hk = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws, trace=True)
+    assert q.moeq_last_stack_path() == (2 if flags else 1)
+    assert q.moe_read_device_status(ws) == 0
+    idx = tk.cpu().numpy()[:, 0, :]
+    hs = hk.cpu().numpy()[:, 0, :].astype(np.float64)
+    outs = [hs[l + 1] for l in range(cfg.layers - 1)] + [h.cpu().numpy()[0].astype(np.float64)]
+    for l in range(cfg.layers):
+        assert np.array_equal(idx[l], np.arange(cfg.top_k)), (l, idx[l])
+        exp = oracle.run_layer(cfg, l, hs[l][None, :], want_intermediates=False, wr=zero)
+        assert np.array_equal(exp["idx"][0], np.arange(cfg.top_k))
+        assert_close(outs[l], exp["y"][0], f"tied layer {l} output")
+
+
 @pytest.fixture(scope="module")
 def stack60():
     cfg = synth.CONFIGS["stack60_decode"]
