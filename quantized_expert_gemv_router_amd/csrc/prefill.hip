@@ -299,14 +299,23 @@ struct GemmArgs {
   int32_t* status;
 };
 
-// Eight fp16 weights of one packed word, dequantised: w = q*s + b.
+// Eight fp16 weights of one packed word, dequantised: w = q*s + b.  Each
+// pair (q_i, q_{i+4}) is masked in place and OR-ed into an fp16 exponent
+// whose mantissa unit is the field's own: a nibble at bits 0-3 of a half
+// reads as 1024 + q, one at bits 4-7 as 64 + q (one v_and_or per pair,
+// one shift per word), then the exact subtract and one fma.
 __device__ __forceinline__ half8 dequant_word(uint32_t word, half2v s2, half2v b2) {
-  const half2v m2 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  uint32_t m1024, m64;   // in registers: v_and_or_b32 takes no literal
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(m1024));
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(m64));
+  const half2v k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f}, k64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const uint32_t hi = word >> 8;
+  const uint32_t t[4] = {(word & 0x000F000Fu) | m1024, (word & 0x00F000F0u) | m64, (hi & 0x000F000Fu) | m1024,
+                         (hi & 0x00F000F0u) | m64};
   half8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;   // (1024 + q_i, 1024 + q_{i+4})
-    const half2v q = __builtin_bit_cast(half2v, t) + m2;
+    const half2v q = __builtin_bit_cast(half2v, t[i]) + ((i & 1) ? k64 : k1024);
     const half2v v = q * s2 + b2;
     r[2 * i] = v[0];
     r[2 * i + 1] = v[1];
@@ -371,7 +380,6 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
       if (tid == 0) set_status(a.status, 1);
       continue;
     }
-    const int nmb = (nrows + 15) / 16;
 
     // this lane's weight rows, matrices and packed-word offsets
     const int q4 = lane >> 4;                     // k quarter of the MFMA operand
@@ -492,16 +500,20 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int nb = 0; nb < kNBW; ++nb) bw[m][nb] = dequant_word(raw[j].q[m][nb][hk], s2[m][nb], b2[m][nb]);
+          // every row block, padding rows included (they repeat a real
+          // row and are not stored): no branch between the MFMAs, so the
+          // independent accumulators hide each other's latency
+          half8 af[kMB];   // all row blocks' fragments read before the first MFMA
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+            af[mb] = *reinterpret_cast<const half8*>(A + (mb * 16 + (lane & 15)) * kPitch + 8 * (4 * q4 + hk));
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) {
-            if (mb < nmb) {   // uniform over the block
-              const half8 af = *reinterpret_cast<const half8*>(A + (mb * 16 + (lane & 15)) * kPitch + 8 * (4 * q4 + hk));
 #pragma unroll
-              for (int m = 0; m < NMAT; ++m)
+            for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int nb = 0; nb < kNBW; ++nb)
-                  acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[m][nb], acc[m][nb][mb], 0, 0, 0);
-            }
+              for (int nb = 0; nb < kNBW; ++nb)
+                acc[m][nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bw[m][nb], acc[m][nb][mb], 0, 0, 0);
           }
         }
         load_w(min(c + NPF, NC - 1), raw[j]);
@@ -539,6 +551,156 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
   }
 }
 
+// ------------------------------------------------- down GEMM, resident A
+// The down GEMM with the pairs' activation tile resident in LDS: a block
+// takes one row tile (up to 64 pairs of one expert) and a run of TG weight
+// tiles of 256 rows; the tile's activations (64 x I fp16) are read once and
+// every weight tile of the run streams against them, with no block barrier
+// in the K loop.  Weights and their scale/bias words are prefetched NPF
+// chunks ahead, across the weight tiles of the run.  I <= kResMaxI.
+constexpr int kResMaxI = 1024;
+constexpr int kResThreads = 512;
+constexpr int kResUnits = kMT * kResMaxI / 8 / kResThreads;   // 16-byte activation units per thread
+
+template <int NPF, int TG>
+__global__ __launch_bounds__(kResThreads, 1) void down_resident_kernel(GemmArgs a) {
+  constexpr int NTR = (kResThreads / 64) * 16 * kNBW;   // weight rows per tile: 256
+  extern __shared__ __align__(16) _Float16 Ar[];        // [kMT][I + 8]
+  __shared__ int32_t src_row[kMT];
+  __shared__ int s_e, s_row0, s_n;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4;
+  const int E = a.E, S = a.S, H = a.H, I = a.I;
+  const int pitch = I + 8;
+  const int NC = I / kKC;                  // chunks per weight tile
+  const int NT = H / NTR;                  // weight tiles
+  const int NG = (NT + TG - 1) / TG;       // runs per row tile
+  const int n_mt = a.mtoff[E + S];
+  const int total = n_mt * NG;
+  const int64_t qsec = (int64_t)H * I / 2, ssec = (int64_t)H * I / 64 * 4;
+
+  for (int wi = blockIdx.x; wi < total; wi += gridDim.x) {
+    const int mt = wi / NG, nt0 = (wi % NG) * TG;
+    const int ntn = min(TG, NT - nt0);
+    if (tid == 0) {
+      const int4 tl = a.tiles[mt];
+      s_e = tl.x;
+      s_row0 = tl.y;
+      s_n = tl.z;
+    }
+    __syncthreads();
+    const int e = s_e, nrows = s_n, row0 = s_row0;
+    if (tid < kMT) src_row[tid] = a.lists[row0 + min(tid, nrows - 1)];   // padding rows repeat a real row
+    const uint8_t* blob = uniform_ptr(static_cast<const uint8_t*>(a.blobs[e]));
+    __syncthreads();
+    if (blob == nullptr) {   // missing expert: flag it, leave its outputs unwritten
+      if (tid == 0) set_status(a.status, 1);
+      continue;
+    }
+    // activation tile: every 16-byte unit requested before any is stored
+    const int upr = I / 8;   // units per row
+    u32x4 av[kResUnits];
+#pragma unroll
+    for (int i = 0; i < kResUnits; ++i) {
+      const int x = min(tid + i * kResThreads, kMT * upr - 1);
+      const int r = x / upr, u = x - r * upr;
+      av[i] = load_stream(reinterpret_cast<const u32x4*>(a.abuf + (int64_t)src_row[r] * I) + u);
+    }
+
+    // weights: flat chunk f = t * NC + c over the run's tiles; lane quarter
+    // q4 holds words 4*q4 .. 4*q4+3 of the chunk's 16 (group 2c + q4/2)
+    struct Raw {
+      u32x4 q[kNBW];
+      uint32_t sb[kNBW];
+    };
+    Raw raw[NPF];
+    const int nf = ntn * NC;
+    const uint8_t* dq = blob + 2 * qsec;
+    const uint32_t* dsb = reinterpret_cast<const uint32_t*>(blob + 3 * qsec + 2 * ssec);
+    auto load_w = [&](int f, Raw& r) {
+      f = min(f, nf - 1);
+      const int t = f / NC, c = f - t * NC;
+#pragma unroll
+      for (int nb = 0; nb < kNBW; ++nb) {
+        const int n = (nt0 + t) * NTR + wave * (16 * kNBW) + nb * 16 + (lane & 15);
+        r.q[nb] = load_stream(reinterpret_cast<const u32x4*>(dq + (int64_t)n * (I / 2)) + 4 * c + q4);
+        r.sb[nb] = load_stream(dsb + (int64_t)n * (I / 64) + 2 * c + (q4 >> 1));
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) load_w(j, raw[j]);
+#pragma unroll
+    for (int i = 0; i < kResUnits; ++i) {
+      const int x = tid + i * kResThreads;
+      if (x < kMT * upr) {
+        const int r = x / upr, u = x - r * upr;
+        *reinterpret_cast<u32x4*>(&Ar[r * pitch + 8 * u]) = av[i];
+      }
+    }
+    block_sync_lds();
+
+    float4v acc[kNBW][kMB];
+#pragma unroll
+    for (int nb = 0; nb < kNBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) acc[nb][mb] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int f0 = 0; f0 < nf; f0 += NPF) {   // NPF divides NC
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        const int f = f0 + j;
+        const int t = f / NC, c = f - t * NC;
+        half2v s2[kNBW], b2[kNBW];
+#pragma unroll
+        for (int nb = 0; nb < kNBW; ++nb) sb_halves(raw[j].sb[nb], s2[nb], b2[nb]);
+        // activation fragments of every row block (see gemm_kernel), one
+        // k-step ahead: the reads of step hk+1 are in flight while step hk's
+        // MFMAs run, and one wait covers a step's four reads
+        const _Float16* arow = &Ar[(lane & 15) * pitch + c * kKC + 8 * (4 * q4)];
+        half8 af[2][kMB];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) af[0][mb] = *reinterpret_cast<const half8*>(arow + mb * 16 * pitch);
+#pragma unroll
+        for (int hk = 0; hk < 4; ++hk) {
+          if (hk < 3) {
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb)
+              af[(hk + 1) & 1][mb] = *reinterpret_cast<const half8*>(arow + mb * 16 * pitch + 8 * (hk + 1));
+          }
+          half8 bw[kNBW];
+#pragma unroll
+          for (int nb = 0; nb < kNBW; ++nb) bw[nb] = dequant_word(raw[j].q[nb][hk], s2[nb], b2[nb]);
+          const half8 (&cur)[kMB] = af[hk & 1];
+          asm volatile("" ::"v"(cur[0]), "v"(cur[1]), "v"(cur[2]), "v"(cur[3]) : "memory");
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < kNBW; ++nb)
+              acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mb], bw[nb], acc[nb][mb], 0, 0, 0);
+        }
+        load_w(f + NPF, raw[j]);
+        if (c == NC - 1) {   // tile t done: lane holds weight row n, pairs 4*(lane>>4)+i of each block
+#pragma unroll
+          for (int nb = 0; nb < kNBW; ++nb) {
+            const int n = (nt0 + t) * NTR + wave * (16 * kNBW) + nb * 16 + (lane & 15);
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = mb * 16 + 4 * q4 + i;
+                if (r < nrows) a.dbuf[(int64_t)src_row[r] * H + n] = acc[nb][mb][i];
+              }
+              acc[nb][mb] = float4v{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // row table and LDS reused by the next item
+  }
+}
+
 // --------------------------------------------------------------- combine
 // h[t][i] += sum_{s<K} w[t][s] d[t][s][i] + sum_shared d[t][K+j][i], in
 // slot order, one fma per term.
@@ -573,6 +735,26 @@ hipError_t launch_gemm(const GemmArgs& g, int nc, int cus, hipStream_t st) {
   if (nr % (8 * 16 * kNBW) == 0) launch_gemm_w<GU, 8>(g, nc, xcd_cus, st);
   else launch_gemm_w<GU, 4>(g, nc, 2 * xcd_cus, st);
   return hipGetLastError();
+}
+
+// Down GEMM: resident activation tiles where the tile fits in LDS and the
+// weight rows divide into 256-row tiles; otherwise the streamed form.
+hipError_t launch_down(const GemmArgs& g, int cus, hipStream_t st) {
+  constexpr int TG = 4, NPF = 4;
+  const int NC = g.I / kKC;
+  if (g.I <= kResMaxI && g.H % 256 == 0 && NC % NPF == 0) {
+    const size_t lds = sizeof(_Float16) * (size_t)kMT * (g.I + 8);
+    static const bool lds_ok =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&down_resident_kernel<NPF, TG>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(sizeof(_Float16) * kMT * (kResMaxI + 8))) == hipSuccess;
+    if (lds_ok) {
+      hipLaunchKernelGGL((down_resident_kernel<NPF, TG>), dim3(max(1, cus)), dim3(kResThreads), lds, st, g);
+      return hipGetLastError();
+    }
+    (void)hipGetLastError();
+  }
+  return launch_gemm<false>(g, NC, cus, st);
 }
 
 int device_cus_prefill() {
@@ -689,7 +871,7 @@ hipError_t launch_prefill_layer(const moeq_shape& s, const void* const* blobs, c
   if ((e = launch_gemm<true>(g, H / kKC, cus, st)) != hipSuccess) return e;
   tm.end(kTGateUp, st);
   tm.begin(kTDown, st);
-  if ((e = launch_gemm<false>(g, I / kKC, cus, st)) != hipSuccess) return e;
+  if ((e = launch_down(g, cus, st)) != hipSuccess) return e;
   tm.end(kTDown, st);
   tm.begin(kTCombine, st);
   hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kPThreads), 0, st, h, g.dbuf, w, k, S, H);

@@ -146,26 +146,6 @@ __device__ __forceinline__ void wave_select(int64_t (&k)[M], const int (&id)[M],
   }
 }
 
-// One wave: top-K of lg[0..E) (LDS, E <= 64*M), ties to the lower index.
-// sel/selv (LDS) receive the indices and logits in rank order.
-template <int M>
-__device__ __forceinline__ void wave_topk_keys(const double* lg, int E, int K, int* sel, double* selv) {
-  const int lane = threadIdx.x & 63;
-  int64_t k[M];
-  int id[M];
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    const int e = lane + 64 * i;
-    k[i] = e < E ? order_key(lg[e]) : kNoKey;
-    id[i] = e < E ? e : kTopkNone;
-  }
-  wave_select<M, true>(k, id, K, [&](int r, int64_t, int win) {
-    sel[r] = win;
-    selv[r] = win != kTopkNone ? lg[win] : -INFINITY;
-  });
-  __builtin_amdgcn_wave_barrier();
-}
-
 // All NW waves of a block: top-K (K <= 64*MC/NW) of lg[0..E) (LDS, E <= 64*NW*M).
 // Wave w selects the K best of its elements w*64 + lane + 64*NW*i into
 // ck/ci[w*K + r]; wave 0 then selects the K best of those NW*K candidates
