@@ -106,6 +106,21 @@ def test_stack_all_logits_tied(flags):
         assert_close(outs[l], exp["y"][0], f"tied layer {l} output")
 
 
+def test_stack_2bit_full_width():
+    """The 2-bit persistent instantiation (hidden 4096, 512 experts, top-4 +
+    1 shared) on three layers, gated per layer along its own trajectory."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_2bit"], name="stack_2bit", layers=3, rmsnorm=True)
+    say("[stack] 2-bit, 3 layers at full width")
+    shape, ex, rt = build_stack(cfg, cfg.layers)
+    for ts in (0, 1):
+        h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+        ws = q.new_workspace(shape, 1, cfg.top_k)
+        traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == 1
+        assert q.moe_read_device_status(ws) == 0
+        compare_free_running(cfg, cfg.layers, ts, traces, h.cpu().numpy()[0])
+
+
 @pytest.fixture(scope="module")
 def stack60():
     cfg = synth.CONFIGS["stack60_decode"]
