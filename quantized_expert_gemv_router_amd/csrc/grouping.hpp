@@ -29,7 +29,8 @@ struct GroupLds {
 };
 
 // LDS scratch the caller provides: list [max(T*k, T)] u32, ids [T*k] int,
-// ptrs [T*k] pointers.  list entries: token << 8 | slot.  Whole block.
+// ptrs [T*k] pointers.  list entries: token << 8 | slot.  A negative item
+// -1 - s names shared expert s directly.  Whole block.
 __device__ __forceinline__ void group_item(int item, const int32_t* __restrict__ topk_idx,
                                            const void* const* __restrict__ blobs, int T, int k,
                                            int E, int S, GroupLds& g, uint32_t* __restrict__ list,
@@ -62,7 +63,9 @@ __device__ __forceinline__ void group_item(int item, const int32_t* __restrict__
     const int excl = incl - c;
     const int total = __shfl(incl, 63, 64);
     int e = -1;
-    if (item < total) {
+    if (item < 0) {
+      if (-1 - item < S) e = E + (-1 - item);
+    } else if (item < total) {
       // the owner lane finds the item-th set bit; broadcast it
       int mine = -1;
       if (item >= excl && item < incl) {
@@ -104,7 +107,7 @@ __device__ __forceinline__ void group_item(int item, const int32_t* __restrict__
     }
     if (lane == 0) {
       g.n_distinct = total;
-      g.in_range = item < total + S;
+      g.in_range = item < 0 ? (-1 - item < S) : (item < total + S);
       g.expert = (blob != nullptr && cnt > 0) ? e : -1;
       g.blob = blob;
       g.count = cnt;

@@ -10,7 +10,6 @@
 #include "moeq_internal.hpp"
 
 namespace moeq {
-int down_row_blocks(int H);
 
 namespace {
 thread_local std::string g_last_error;
@@ -203,8 +202,6 @@ int moe_swiglu_down_combine(const moeq_shape* s, const moeq_experts* ex, int lay
   if (T == 0) return ok();
   if (!gate_up || !residual || !out || !workspace || (k > 0 && (!topk_idx || !topk_w)))
     return fail(MOEQ_E_INVALID, "gate_up, topk_idx, topk_w, residual, out and workspace must be non-NULL");
-  if (moeq::down_row_blocks(s->hidden) > kMaxRowBlockCounters)
-    return fail(MOEQ_E_UNSUPPORTED, "hidden=%d needs too many row blocks", s->hidden);
   if (k + s->n_shared == 0) {
     return fail(MOEQ_E_UNSUPPORTED, "k == 0 without a shared expert: the layer is the identity");
   }
