@@ -223,13 +223,15 @@ __device__ __forceinline__ void apply_down_tile(const DownRows<BITS, LPR, CPL>& 
   }
 }
 
-// Grid: chunk-major over NTC token chunks (entries 4c..4c+3 of an item's
-// list, the last chunk first), then the n_routed routed items and the S shared experts, then NS
-// row ranges.  Workgroups whose item does not exist in this batch, or holds
-// no more than 4c entries, exit after the grouping.  Writes d for every
-// (token, slot, row) of its items into dbuf [T][k + S][H].
+// Grid, NS row ranges per unit: first the n_extra units that may hold a
+// later chunk of an item's (token, slot) list (entries 4c.., c >= 1;
+// group_extra finds which, the rest exit), then chunk 0 of the n_routed
+// routed items and the S shared experts (items missing from this batch
+// exit).  Writes d for every (token, slot, row) of its items into dbuf
+// [T][k + S][H].
 template <int BITS, int LPR, int CPL, int WMAX>
-__global__ __launch_bounds__(kThreads) void down_batch_kernel(DownArgs a, int NS, int n_routed, int list_words) {
+__global__ __launch_bounds__(kThreads) void down_batch_kernel(DownArgs a, int NS, int n_routed, int n_extra,
+                                                                                       int list_words) {
   using T = DownRows<BITS, LPR, CPL>;
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ GroupLds g;
@@ -245,15 +247,21 @@ __global__ __launch_bounds__(kThreads) void down_batch_kernel(DownArgs a, int NS
   int* ids = reinterpret_cast<int*>(list + list_words);
   const uint8_t** ptrs = reinterpret_cast<const uint8_t**>(ids + list_words);
 
-  const int per_chunk = (n_routed + a.S) * NS;
-  const int rev = blockIdx.x / per_chunk;   // the last chunks first: they run long where they exist
-  const int chunk = (a.T + MMAX - 1) / MMAX - 1 - rev;
-  const int rem = blockIdx.x - rev * per_chunk;
-  const int it = rem / NS, split = rem - it * NS;
-  const int item = it < n_routed ? it : -1 - (it - n_routed);
-  group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ptrs + list_words);
+  int split;
+  if ((int)blockIdx.x < n_extra * NS) {   // later token chunks first: they run long
+    const int u = blockIdx.x / NS;
+    split = blockIdx.x - u * NS;
+    group_extra<MMAX>(u, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, hist, a.status);
+  } else {
+    const int b = blockIdx.x - n_extra * NS;
+    const int it = b / NS;
+    split = b - it * NS;
+    const int item = it < n_routed ? it : -1 - (it - n_routed);
+    group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
+  }
   if (g.expert < 0) return;
-  const int m0 = chunk * MMAX;
+  const int m0 = g.chunk * MMAX;
   if (m0 >= g.count) return;
   const int nv = min(MMAX, g.count - m0);
 
@@ -419,17 +427,18 @@ hipError_t launch_t(const DownArgs& a, hipStream_t stream) {
   const int n_items = n_routed + a.S;
   const int list_words = (max(a.T * a.k, a.T) + 3) & ~3;
   const int ntiles = (a.H + DownRows<BITS, LPR, CPL>::TR - 1) / DownRows<BITS, LPR, CPL>::TR;
-  // about four workgroups per CU over the items' first token chunks
-  const int NS = max(1, min((4 * cu_count() + n_items - 1) / max(n_items, 1), ntiles));
+  // about eight workgroups per CU over the items' first token chunks
+  const int NS = max(1, min((8 * cu_count() + n_items - 1) / max(n_items, 1), ntiles));
   const int NTC = (a.T + kTokensPerStage - 1) / kTokensPerStage;
-  const int64_t grid = (int64_t)NTC * n_items * NS;
+  const int n_extra = a.T * a.k / kTokensPerStage + a.S * (NTC - 1);   // bound on later token chunks
+  const int64_t grid = (int64_t)(n_extra + n_items) * NS;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.I / 2) +
                                          (size_t)kTokensPerStage * kChunkSums * nch +
-                                         2 * (size_t)list_words) +
+                                         2 * (size_t)list_words + (size_t)a.E) +
                      sizeof(void*) * (size_t)list_words;
   hipLaunchKernelGGL((down_batch_kernel<BITS, LPR, CPL, WMAX>), dim3((unsigned)grid), dim3(kThreads), lds, stream,
-                     a, NS, n_routed, list_words);
+                     a, NS, n_routed, n_extra, list_words);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t cgrid = ((int64_t)a.T * a.H + kThreads - 1) / kThreads;

@@ -265,13 +265,13 @@ __device__ __forceinline__ void apply_gu_tile(const GuTile<BITS, CPL>& t, const 
   }
 }
 
-// Grid: chunk-major over NTC token chunks (tokens 4c..4c+3 of an item's
-// list, the last chunk first), then the n_routed routed items and the S shared experts, then NS
-// row ranges: b = (c * (n_routed + S) + item) * NS + range.  Workgroups
-// whose item does not exist in this batch, or holds no more than 4c tokens,
-// exit after the grouping.
+// Grid, NS row ranges per unit: first the n_extra units that may hold a
+// later token chunk (tokens 4c.. of an item's list, c >= 1; group_extra
+// finds which, the rest exit), then chunk 0 of the n_routed routed items
+// and the S shared experts (items missing from this batch exit).
 template <int BITS, int CPL, int WMAX>
-__global__ __launch_bounds__(kThreads) void gemv_batch_kernel(GemvArgs a, int NS, int n_routed, int list_words) {
+__global__ __launch_bounds__(kThreads) void gemv_batch_kernel(GemvArgs a, int NS, int n_routed, int n_extra,
+                                                                                     int list_words) {
   extern __shared__ __align__(16) uint32_t smem[];
   __shared__ GroupLds g;
   __shared__ float red[2 * kTokensPerStage * kWaves];
@@ -286,15 +286,21 @@ __global__ __launch_bounds__(kThreads) void gemv_batch_kernel(GemvArgs a, int NS
   int* ids = reinterpret_cast<int*>(list + list_words);
   const uint8_t** ptrs = reinterpret_cast<const uint8_t**>(ids + list_words);
 
-  const int per_chunk = (n_routed + a.S) * NS;
-  const int rev = blockIdx.x / per_chunk;   // the last chunks first: they run long where they exist
-  const int chunk = (a.T + MMAX - 1) / MMAX - 1 - rev;
-  const int rem = blockIdx.x - rev * per_chunk;
-  const int it = rem / NS, split = rem - it * NS;
-  const int item = it < n_routed ? it : -1 - (it - n_routed);
-  group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ptrs + list_words);
+  int split;
+  if ((int)blockIdx.x < n_extra * NS) {   // later token chunks first: they run long
+    const int u = blockIdx.x / NS;
+    split = blockIdx.x - u * NS;
+    group_extra<MMAX>(u, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, hist, a.status);
+  } else {
+    const int b = blockIdx.x - n_extra * NS;
+    const int it = b / NS;
+    split = b - it * NS;
+    const int item = it < n_routed ? it : -1 - (it - n_routed);
+    group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
+  }
   if (g.expert < 0) return;
-  const int m0 = chunk * MMAX;
+  const int m0 = g.chunk * MMAX;
   if (m0 >= g.count) return;
   const int nv = min(MMAX, g.count - m0);
 
@@ -336,18 +342,19 @@ hipError_t launch_batch(const GemvArgs& a, hipStream_t stream, int cus) {
   const int list_words = (max(a.T * a.k, a.T) + 3) & ~3;
   const int nch = a.H / Pack<BITS>::kPerChunk;
   const int ntiles = (2 * a.I + kTileRows - 1) / kTileRows;
-  // about four workgroups per CU over the items' first token chunks
+  // about eight workgroups per CU over the items' first token chunks
   const int n_items = n_routed + a.S;
-  const int NS = max(1, min((4 * cus + n_items - 1) / max(n_items, 1), ntiles));
+  const int NS = max(1, min((8 * cus + n_items - 1) / max(n_items, 1), ntiles));
   const int NTC = (a.T + kTokensPerStage - 1) / kTokensPerStage;
+  const int n_extra = a.T * a.k / kTokensPerStage + a.S * (NTC - 1);   // bound on later token chunks
   const size_t lds = sizeof(uint32_t) * ((size_t)kTokensPerStage * (a.H / 2) +
                                          (size_t)kTokensPerStage * kChunkSums * nch +
-                                         2 * (size_t)list_words) +
+                                         2 * (size_t)list_words + (size_t)a.E) +
                      sizeof(void*) * (size_t)list_words;
-  const int64_t grid = (int64_t)NTC * n_items * NS;
+  const int64_t grid = (int64_t)(n_extra + n_items) * NS;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((gemv_batch_kernel<BITS, CPL, WMAX>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
-                     NS, n_routed, list_words);
+                     NS, n_routed, n_extra, list_words);
   return hipGetLastError();
 }
 

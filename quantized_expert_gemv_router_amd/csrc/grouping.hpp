@@ -26,7 +26,42 @@ struct GroupLds {
   int count;             // (token, slot) pairs in `list`
   int n_distinct;
   int in_range;          // item < n_distinct + S (the item exists in this batch)
+  int chunk;             // token chunk of the item this workgroup takes (group_extra)
 };
+
+// Wave 0: the (token, slot) list of item expert e (routed id, or E + s for
+// shared expert s) into list, in pair order; returns its length and sets
+// blob.  ids/ptrs hold the routed ids and their blobs (from the scan).
+__device__ __forceinline__ int collect_item(int e, int lane, int T, int k, int E, int P,
+                                            const void* const* __restrict__ blobs, const GroupLds& g,
+                                            uint32_t* __restrict__ list, const int* __restrict__ ids,
+                                            const uint8_t* const* __restrict__ ptrs, const uint8_t*& blob) {
+  int cnt = 0;
+  blob = nullptr;
+  if (e >= 0 && e < E) {
+    for (int base = 0; base < P; base += 64) {
+      const int p = base + lane;
+      const bool hit = p < P && ids[p] == e;
+      const uint64_t m = __ballot(hit);
+      if (hit) {
+        const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+        const int t = p / k;
+        list[pos] = ((uint32_t)t << 8) | (uint32_t)(p - t * k);
+        if (pos == 0) blob = ptrs[p];
+      }
+      cnt += __popcll(m);
+    }
+    const uint64_t hb = __ballot(blob != nullptr);
+    if (hb) blob = reinterpret_cast<const uint8_t*>(
+                __shfl((long long)(uintptr_t)blob, (int)__builtin_ctzll(hb), 64));
+  } else if (e >= E) {
+    const int slot = k + (e - E);
+    for (int t = lane; t < T; t += 64) list[t] = ((uint32_t)t << 8) | (uint32_t)slot;
+    cnt = T;
+    blob = (e == E) ? g.shared_blob : static_cast<const uint8_t*>(blobs[e]);
+  }
+  return cnt;
+}
 
 // LDS scratch the caller provides: list [max(T*k, T)] u32, ids [T*k] int,
 // ptrs [T*k] pointers.  list entries: token << 8 | slot.  A negative item
@@ -81,36 +116,92 @@ __device__ __forceinline__ void group_item(int item, const int32_t* __restrict__
     } else if (item < total + S) {
       e = E + (item - total);
     }
-    int cnt = 0;
-    const uint8_t* blob = nullptr;
-    if (e >= 0 && e < E) {
-      for (int base = 0; base < P; base += 64) {
-        const int p = base + lane;
-        const bool hit = p < P && ids[p] == e;
-        const uint64_t m = __ballot(hit);
-        if (hit) {
-          const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
-          const int t = p / k;
-          list[pos] = ((uint32_t)t << 8) | (uint32_t)(p - t * k);
-          if (pos == 0) blob = ptrs[p];
-        }
-        cnt += __popcll(m);
-      }
-      const uint64_t hb = __ballot(blob != nullptr);
-      if (hb) blob = reinterpret_cast<const uint8_t*>(
-                  __shfl((long long)(uintptr_t)blob, (int)__builtin_ctzll(hb), 64));
-    } else if (e >= E) {
-      const int slot = k + (e - E);
-      for (int t = lane; t < T; t += 64) list[t] = ((uint32_t)t << 8) | (uint32_t)slot;
-      cnt = T;
-      blob = (e == E) ? g.shared_blob : static_cast<const uint8_t*>(blobs[e]);
-    }
+    const uint8_t* blob;
+    const int cnt = collect_item(e, lane, T, k, E, P, blobs, g, list, ids, ptrs, blob);
     if (lane == 0) {
       g.n_distinct = total;
       g.in_range = item < 0 ? (-1 - item < S) : (item < total + S);
       g.expert = (blob != nullptr && cnt > 0) ? e : -1;
       g.blob = blob;
       g.count = cnt;
+      g.chunk = 0;
+    }
+  }
+  __syncthreads();
+}
+
+// Later token chunks.  An item with n (token, slot) pairs has ceil(n / C)
+// chunks of C; chunks 1.. of all items, numbered in item order (routed
+// experts by id, then the shared experts), are the batch's extra chunks,
+// at most floor(T*k / C) + S * (ceil(T / C) - 1) of them.  Fills g and list
+// as group_item does for the item holding extra chunk u, with g.chunk its
+// chunk number (>= 1); g.expert = -1 past the last one.  hist: LDS [E] u32.
+// Whole block.
+template <int C>
+__device__ __forceinline__ void group_extra(int u, const int32_t* __restrict__ topk_idx,
+                                            const void* const* __restrict__ blobs, int T, int k, int E,
+                                            int S, GroupLds& g, uint32_t* __restrict__ list,
+                                            int* __restrict__ ids, const uint8_t** __restrict__ ptrs,
+                                            uint32_t* __restrict__ hist, int32_t* status) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int P = T * k;
+  for (int i = tid; i < E; i += blockDim.x) hist[i] = 0u;
+  if (tid == 0) g.shared_blob = S > 0 ? static_cast<const uint8_t*>(blobs[E]) : nullptr;
+  __syncthreads();
+  for (int p = tid; p < P; p += blockDim.x) {
+    const int e = topk_idx[p];
+    const bool ok = e >= 0 && e < E;
+    ids[p] = ok ? e : -1;
+    ptrs[p] = ok ? static_cast<const uint8_t*>(blobs[e]) : nullptr;
+    if (ok) atomicAdd(&hist[e], 1u);
+    else set_status(status, kStatusBadExpert);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // lane l owns experts [l * per, (l + 1) * per)
+    const int per = (E + 63) / 64;
+    const int lo = lane * per, hi = min(E, lo + per);
+    int c = 0;
+    for (int e = lo; e < hi; ++e) c += hist[e] > 0 ? (int)((hist[e] - 1) / C) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - c;
+    const int total = __shfl(incl, 63, 64);
+    int e = -1, chunk = 0;
+    if (u < total) {
+      int mine = -1, mc = 0;
+      if (u >= excl && u < incl) {
+        int r = u - excl;
+        for (int x = lo; x < hi; ++x) {
+          const int n = hist[x] > 0 ? (int)((hist[x] - 1) / C) : 0;
+          if (r < n) { mine = x; mc = 1 + r; break; }
+          r -= n;
+        }
+      }
+      const uint64_t owner = __ballot(mine >= 0);
+      const int ol = (int)__builtin_ctzll(owner);
+      e = __shfl(mine, ol, 64);
+      chunk = __shfl(mc, ol, 64);
+    } else {
+      const int per_s = (T + C - 1) / C - 1;
+      const int v = u - total;
+      if (per_s > 0 && v / per_s < S) {
+        e = E + v / per_s;
+        chunk = 1 + v % per_s;
+      }
+    }
+    const uint8_t* blob;
+    const int cnt = collect_item(e, lane, T, k, E, P, blobs, g, list, ids, ptrs, blob);
+    if (lane == 0) {
+      g.in_range = e >= 0;
+      g.expert = (blob != nullptr && cnt > chunk * C) ? e : -1;
+      g.blob = blob;
+      g.count = cnt;
+      g.chunk = chunk;
     }
   }
   __syncthreads();
