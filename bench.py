@@ -384,7 +384,8 @@ def run_layer_workload(args, cfg, dev, stream):
         "frac_hbm_peak": round(expert_bytes.sum() / sec / 1e9 / HBM_PEAK_GBS, 4),
         "expert_layers_per_s": round(args.steps * T / sec, 1),
         "distinct_experts_per_step": round(float(np.mean(distinct)), 2),
-        "roofline": {"kernel": "gemv_kernel (gate/up dequant GEMV)", "bound": "hbm",
+        "roofline": {"kernel": ("gemv_kernel (gate/up dequant GEMV, one token)" if T == 1 else
+                                "gemv_batch_kernel (gate/up dequant GEMV, several tokens)"), "bound": "hbm",
                      "achieved": round(gemv_bytes / (gemv_ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_bytes / (gemv_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None, "avg_launch_us": round(gemv_ms * 1e3, 3),
