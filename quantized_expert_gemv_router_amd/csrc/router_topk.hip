@@ -9,15 +9,18 @@
 //
 // One wave per router row: the row (bf16, H/8 16-byte chunks) is loaded
 // once into registers and dotted with every token in fp64 (bf16 x bf16 and
-// bf16 x fp32 products are exact in fp64).  Tokens are staged into LDS as
-// fp32 a group at a time; the dots of a group's tokens are interleaved and
-// their wave sums are DPP reductions, so one token's latency hides behind
-// the next.  With RMS norm, sum(x^2) of each token is accumulated (fp64)
-// while it is staged, and the logit is inv_rms * sum(W x).  Logits are
-// written with agent-scope write-through stores; the last workgroup to bump
-// the arrival counter selects top-K for every token, one token per wave at a
-// time (keys in registers for E <= 512, else the logits staged in LDS), and
-// writes indices, weights and the shared expert's weight.
+// bf16 x fp32 products are exact in fp64).  Up to 16 tokens are copied into
+// LDS in their own type (bf16 or fp32) per pass; the dots of four tokens
+// at a time are interleaved and their wave sums are DPP reductions, so one
+// token's latency hides behind the next.  With RMS norm, sum(x^2) of each
+// staged token is taken once (fp64, one wave per token) and the logit is
+// inv_rms * sum(W x).  Logits are
+// written with agent-scope write-through stores.  Up to 8 tokens, the last
+// workgroup to bump the arrival counter selects top-K for every token, one
+// token per wave; more tokens, a second launch selects with one wave per
+// token, all at once.  Either way the logits are held as keys in registers
+// for E <= 512 (else staged in LDS), and the indices, weights and the
+// shared expert's weight are written.
 #include "moeq_device.hpp"
 #include "moeq_internal.hpp"
 #include "topk.hpp"
@@ -27,72 +30,95 @@ namespace {
 
 constexpr int kWaves = 8;            // router rows per workgroup (one per wave)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTokenGroup = 4;       // tokens per staging pass (upper bound)
-constexpr int kStageVec = 4;         // 16-byte loads in flight per thread while staging x
+constexpr int kTokenGroup = 4;       // tokens whose dots are interleaved
+constexpr int kMaxStaged = 16;       // tokens per staging pass (upper bound)
+constexpr int kStageVec = 8;         // 16-byte loads in flight per thread while staging x
 constexpr int kLdsWaves = 2;         // waves that select from LDS when E > 64 * kKeySlots
 constexpr int kKeySlots = 8;         // logits per lane in the register selection
+constexpr int kStageBudget = 128 * 1024;   // LDS bytes for staged tokens and LDS selection
 
-__host__ __device__ inline int token_group(int H) {
-  const int tg = 16384 / H;
-  return tg < 1 ? 1 : (tg > kTokenGroup ? kTokenGroup : tg);
+// Tokens staged per pass: x in its own type (esz bytes per value), within
+// the LDS budget left after the LDS selection's logits.
+__host__ __device__ inline int token_group(int H, int esz, int E) {
+  const int budget = kStageBudget - (E > 64 * kKeySlots ? kLdsWaves * E * 8 : 0);
+  const int tg = budget / (H * esz);
+  return tg < 1 ? 1 : (tg > kMaxStaged ? kMaxStaged : tg);
 }
 
-// Selection for token t by one wave, E <= 64 * M: lane l holds logits
-// l, l + 64, ... as order keys (ascending slot = ascending id).
-template <int M>
-__device__ void select_token_keys(const RouterArgs& a, int t, int* sel) {
-  const int lane = threadIdx.x & 63;
-  const int E = a.E, K = a.k;
-  const double* src = a.logits + (int64_t)t * (E + 1);
-  double v[M];
-  int64_t key[M];
-  int id[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = lane + 64 * m;
-    v[m] = e < E ? ld_agent(src + e) : 0.0;
-  }
-  const double sg = (lane == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) : 0.0;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = lane + 64 * m;
-    key[m] = e < E ? order_key(v[m]) : kNoKey;
-    id[m] = e;
-    if (a.logits_out && e < E) a.logits_out[(int64_t)t * E + e] = v[m];
-  }
-  wave_select<M, true>(key, id, K, [&](int r, int64_t, int win) {
-    sel[r] = win;
-  });
-  __builtin_amdgcn_wave_barrier();
-  // the selected logits, read back from the registers of their owner lanes
-  const int mine = lane < K ? sel[lane] : -1;
-  double sv = 0.0;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    // lane l fetches logit `mine` = owner (mine & 63), slot (mine >> 6)
-    const int2 p = __builtin_bit_cast(int2, v[m]);
-    const double got = __builtin_bit_cast(
-        double, make_int2(__shfl(p.x, mine & 63, 64), __shfl(p.y, mine & 63, 64)));
-    if (mine >= 0 && (mine >> 6) == m) sv = got;
-  }
-  const double top = readlane_f64(sv, 0);   // rank 0 is the maximum
-  double z;
-  if (a.no_renorm) {
-    double part = 0.0;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (lane + 64 * m < E) part += exp(v[m] - top);
-    z = wave_sum_f64_dpp(part);
+// 8 consecutive staged values of x as fp64 (bf16 or fp32 in LDS).
+__device__ __forceinline__ void staged_x8(const unsigned char* xs, int x_f32, int64_t elem, double* xv) {
+  if (x_f32) {
+    const float4* p = reinterpret_cast<const float4*>(xs + elem * 4);
+    const float4 xa = p[0], xb = p[1];
+    xv[0] = xa.x; xv[1] = xa.y; xv[2] = xa.z; xv[3] = xa.w;
+    xv[4] = xb.x; xv[5] = xb.y; xv[6] = xb.z; xv[7] = xb.w;
   } else {
-    z = wave_sum_f64_dpp(lane < K ? exp(sv - top) : 0.0);
+    const uint4 u = *reinterpret_cast<const uint4*>(xs + elem * 2);
+    xv[0] = bf16_lo(u.x); xv[1] = bf16_hi(u.x); xv[2] = bf16_lo(u.y); xv[3] = bf16_hi(u.y);
+    xv[4] = bf16_lo(u.z); xv[5] = bf16_hi(u.z); xv[6] = bf16_lo(u.w); xv[7] = bf16_hi(u.w);
   }
-  if (lane < K) {
-    a.topk_idx[(int64_t)t * K + lane] = mine;
-    a.topk_w[(int64_t)t * K + lane] = (float)(exp(sv - top) / z);
+}
+
+// Selection for tokens t0, t0 + step, ... by one wave, E <= 64 * M: lane l
+// holds logits l, l + 64, ... as order keys (ascending slot = ascending
+// id).  The next token's logits are requested before the current one is
+// selected.  sel/selv (this wave's LDS) receive the ranked ids and logits.
+template <int M>
+__device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* sel, double* selv) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, K = a.k, T = a.T;
+  auto fetch = [&](int t, double (&d)[M], double& g) {
+    const double* src = a.logits + (int64_t)t * (E + 1);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int e = lane + 64 * m;
+      d[m] = (t < T && e < E) ? ld_agent(src + e) : 0.0;
+    }
+    g = (t < T && lane == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) : 0.0;
+  };
+  double v[M], sg;
+  fetch(t0, v, sg);
+  for (int t = t0; t < T; t += step) {
+    double nv[M], nsg;
+    fetch(t + step, nv, nsg);
+    int64_t key[M];
+    int id[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int e = lane + 64 * m;
+      key[m] = e < E ? order_key(v[m]) : kNoKey;
+      id[m] = e;
+      if (a.logits_out && e < E) a.logits_out[(int64_t)t * E + e] = v[m];
+    }
+    wave_select<M, true>(key, id, K, [&](int r, int64_t kk, int win) {
+      sel[r] = win;
+      // the logit back from its key (a -0 logit comes back as +0)
+      selv[r] = __longlong_as_double(kk >= 0 ? kk : (kk ^ 0x7FFFFFFFFFFFFFFFll));
+    });
+    __builtin_amdgcn_wave_barrier();
+    const double top = selv[0];   // rank 0 is the maximum
+    const double ex = lane < K ? exp(selv[lane] - top) : 0.0;
+    double z;
+    if (a.no_renorm) {
+      double part = 0.0;
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (lane + 64 * m < E) part += exp(v[m] - top);
+      z = wave_sum_f64_dpp(part);
+    } else {
+      z = wave_sum_f64_dpp(ex);
+    }
+    if (lane < K) {
+      a.topk_idx[(int64_t)t * K + lane] = sel[lane];
+      a.topk_w[(int64_t)t * K + lane] = (float)(ex / z);
+    }
+    if (lane == 0 && a.shared_w)
+      a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-sg))) : 1.0f;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] = nv[m];
+    sg = nsg;
   }
-  if (lane == 0 && a.shared_w)
-    a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-sg))) : 1.0f;
-  __builtin_amdgcn_wave_barrier();
 }
 
 // Selection for token t by one wave from the logits staged in LDS (any E).
@@ -129,18 +155,22 @@ __device__ void select_token_lds(const RouterArgs& a, int t, double* lg, int* se
 }
 
 // One wave per router row (rows E.. hold the optional shared-gate vector).
-template <int CPL>
+// SELECT: the last workgroup to arrive selects for every token (small
+// batches); otherwise select_kernel does, one wave per token, in a second
+// launch.
+template <int CPL, bool SELECT>
 __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int sel[kWaves][MOEQ_MAX_TOPK];
   __shared__ double selv[kWaves][MOEQ_MAX_TOPK];
-  __shared__ double red[kTokenGroup][kWaves];
+  __shared__ double inv_rms[kMaxStaged];
   __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, E = a.E;
-  const int TG = token_group(H);
-  float* xs = reinterpret_cast<float*>(smem_raw);                                      // [TG][H]
-  double* lds_lg = reinterpret_cast<double*>(smem_raw + sizeof(float) * (size_t)TG * H);  // [kLdsWaves][E]
+  const int esz = a.x_f32 ? 4 : 2;
+  const int TG = token_group(H, esz, E);
+  unsigned char* xs = smem_raw;                                                      // [TG][H] x
+  double* lds_lg = reinterpret_cast<double*>(smem_raw + (size_t)TG * H * esz);       // [kLdsWaves][E]
   const int rows = E + (a.shared_gate ? 1 : 0);
   const int row = blockIdx.x * kWaves + wave;
   const bool has_row = row < rows;
@@ -158,17 +188,15 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
     }
   }
 
-  const int esz = a.x_f32 ? 4 : 2;
-  const int per16 = 16 / esz;            // elements per 16-byte load
   for (int t0 = 0; t0 < a.T; t0 += TG) {
     const int nt = min(TG, a.T - t0);
-    // stage nt tokens (contiguous rows of x) into xs as fp32
-    const int n16 = nt * H / per16;
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.x) + (int64_t)t0 * H * esz);
-    double ss[kTokenGroup] = {};
+    // copy nt tokens (contiguous rows of x) into LDS as they are
+    const int n16 = nt * H * esz / 16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + (int64_t)t0 * H * esz);
+    u32x4* dst = reinterpret_cast<u32x4*>(xs);
     __syncthreads();
     for (int base = 0; base < n16; base += kThreads * kStageVec) {
-      uint4 buf[kStageVec];
+      u32x4 buf[kStageVec];
 #pragma unroll
       for (int i = 0; i < kStageVec; ++i) {
         const int v = base + i * kThreads + tid;
@@ -177,83 +205,63 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 #pragma unroll
       for (int i = 0; i < kStageVec; ++i) {
         const int v = base + i * kThreads + tid;
-        if (v < n16) {
-          float f[8];
-          float4* d = reinterpret_cast<float4*>(xs);
-          const uint4 u = buf[i];
-          double part = 0.0;
-          if (a.x_f32) {
-            f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
-            f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
-            d[v] = make_float4(f[0], f[1], f[2], f[3]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) part = fma((double)f[j], (double)f[j], part);
-          } else {
-            f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-            f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
-            d[2 * v] = make_float4(f[0], f[1], f[2], f[3]);
-            d[2 * v + 1] = make_float4(f[4], f[5], f[6], f[7]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) part = fma((double)f[j], (double)f[j], part);
-          }
-          if (a.rmsnorm) {
-            const int ti = v * per16 / H;
-#pragma unroll
-            for (int j = 0; j < kTokenGroup; ++j)
-              if (j == ti) ss[j] += part;
-          }
-        }
-      }
-    }
-    if (a.rmsnorm) {
-#pragma unroll
-      for (int j = 0; j < kTokenGroup; ++j) {
-        const double s2 = wave_sum_f64_dpp(ss[j]);
-        if (lane == 0) red[j][wave] = s2;
+        if (v < n16) dst[v] = buf[i];
       }
     }
     __syncthreads();
+    if (a.rmsnorm) {
+      // sum(x^2) per token (fp64), one wave per token
+      for (int i = wave; i < nt; i += kWaves) {
+        double ss = 0.0;
+        for (int c = lane; c < nch; c += 64) {
+          double xv[8];
+          staged_x8(xs, a.x_f32, (int64_t)i * H + 8 * c, xv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ss = fma(xv[j], xv[j], ss);
+        }
+        ss = wave_sum_f64_dpp(ss);
+        if (lane == 0) inv_rms[i] = 1.0 / sqrt(ss / (double)H + 1e-6);
+      }
+      __syncthreads();
+    }
     if (has_row) {
-      double acc[kTokenGroup] = {};
+      for (int g0 = 0; g0 < nt; g0 += kTokenGroup) {
+        double acc[kTokenGroup] = {};
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int cc = lane + 64 * c;
-        if (cc < nch) {
-          const double w[8] = {bf16_lo(wv[c][0]), bf16_hi(wv[c][0]), bf16_lo(wv[c][1]),
-                               bf16_hi(wv[c][1]), bf16_lo(wv[c][2]), bf16_hi(wv[c][2]),
-                               bf16_lo(wv[c][3]), bf16_hi(wv[c][3])};
+        for (int c = 0; c < CPL; ++c) {
+          const int cc = lane + 64 * c;
+          if (cc < nch) {
+            const double w[8] = {bf16_lo(wv[c][0]), bf16_hi(wv[c][0]), bf16_lo(wv[c][1]),
+                                 bf16_hi(wv[c][1]), bf16_lo(wv[c][2]), bf16_hi(wv[c][2]),
+                                 bf16_lo(wv[c][3]), bf16_hi(wv[c][3])};
 #pragma unroll
-          for (int i = 0; i < kTokenGroup; ++i) {
-            if (i < nt) {
-              const float4* xt = reinterpret_cast<const float4*>(xs + (int64_t)i * H);
-              const float4 xa = xt[2 * cc], xb = xt[2 * cc + 1];
-              const double xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            for (int i = 0; i < kTokenGroup; ++i) {
+              if (g0 + i < nt) {
+                double xv[8];
+                staged_x8(xs, a.x_f32, (int64_t)(g0 + i) * H + 8 * cc, xv);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) acc[i] = fma(w[j], xv[j], acc[i]);
+                for (int j = 0; j < 8; ++j) acc[i] = fma(w[j], xv[j], acc[i]);
+              }
             }
           }
         }
-      }
-      double d[kTokenGroup];
+        double d[kTokenGroup];
 #pragma unroll
-      for (int i = 0; i < kTokenGroup; ++i) d[i] = wave_sum_f64_dpp(acc[i]);
-      if (lane == 0) {
+        for (int i = 0; i < kTokenGroup; ++i) d[i] = wave_sum_f64_dpp(acc[i]);
+        if (lane == 0) {
 #pragma unroll
-        for (int i = 0; i < kTokenGroup; ++i) {
-          if (i < nt) {
-            double di = d[i];
-            if (a.rmsnorm) {
-              double s2 = 0.0;
-              for (int w = 0; w < kWaves; ++w) s2 += red[i][w];
-              di = di * (1.0 / sqrt(s2 / (double)H + 1e-6));
+          for (int i = 0; i < kTokenGroup; ++i) {
+            if (g0 + i < nt) {
+              const double di = a.rmsnorm ? d[i] * inv_rms[g0 + i] : d[i];
+              st_agent(a.logits + (int64_t)(t0 + g0 + i) * (E + 1) + row, di);
             }
-            st_agent(a.logits + (int64_t)(t0 + i) * (E + 1) + row, di);
           }
         }
       }
     }
   }
 
+  if constexpr (!SELECT) return;
   // the last workgroup to arrive selects top-K for every token
   drain_memory();
   __syncthreads();
@@ -262,17 +270,53 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   if (!is_last) return;
   if (tid == 0) st_agent(a.counter, 0u);
   if (E <= 64) {
-    for (int t = wave; t < a.T; t += kWaves) select_token_keys<1>(a, t, sel[wave]);
+    select_tokens_keys<1>(a, wave, kWaves, sel[wave], selv[wave]);
   } else if (E <= 128) {
-    for (int t = wave; t < a.T; t += kWaves) select_token_keys<2>(a, t, sel[wave]);
+    select_tokens_keys<2>(a, wave, kWaves, sel[wave], selv[wave]);
   } else if (E <= 256) {
-    for (int t = wave; t < a.T; t += kWaves) select_token_keys<4>(a, t, sel[wave]);
+    select_tokens_keys<4>(a, wave, kWaves, sel[wave], selv[wave]);
   } else if (E <= 64 * kKeySlots) {
-    for (int t = wave; t < a.T; t += kWaves) select_token_keys<kKeySlots>(a, t, sel[wave]);
+    select_tokens_keys<kKeySlots>(a, wave, kWaves, sel[wave], selv[wave]);
   } else if (wave < kLdsWaves) {
     for (int t = wave; t < a.T; t += kLdsWaves)
       select_token_lds(a, t, lds_lg + (int64_t)wave * E, sel[wave], selv[wave]);
   }
+}
+
+// One wave per token (token blockIdx.x): top-K, softmax weights, shared
+// weight, from the logits the router kernel wrote.
+__global__ __launch_bounds__(64) void select_kernel(RouterArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int sel[MOEQ_MAX_TOPK];
+  __shared__ double selv[MOEQ_MAX_TOPK];
+  const int t = blockIdx.x, E = a.E;
+  if (E <= 64) select_tokens_keys<1>(a, t, a.T, sel, selv);
+  else if (E <= 128) select_tokens_keys<2>(a, t, a.T, sel, selv);
+  else if (E <= 256) select_tokens_keys<4>(a, t, a.T, sel, selv);
+  else if (E <= 64 * kKeySlots) select_tokens_keys<kKeySlots>(a, t, a.T, sel, selv);
+  else select_token_lds(a, t, reinterpret_cast<double*>(smem_raw), sel, selv);
+}
+
+template <int CPL>
+hipError_t launch_cpl(const RouterArgs& a, hipStream_t stream, int grid, size_t lds) {
+  const bool split = a.T > kWaves;   // more tokens than the last workgroup has waves
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<CPL, false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kStageBudget) == hipSuccess
+          ? hipFuncSetAttribute(reinterpret_cast<const void*>(&router_kernel<CPL, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kStageBudget)
+          : hipErrorInvalidValue;
+  if (attr != hipSuccess) return attr;
+  if (!split) {
+    hipLaunchKernelGGL((router_kernel<CPL, true>), dim3(grid), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((router_kernel<CPL, false>), dim3(grid), dim3(kThreads), lds, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t sel_lds = a.E > 64 * kKeySlots ? sizeof(double) * (size_t)a.E : 0;
+  hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -280,20 +324,15 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
 hipError_t launch_router_topk(const RouterArgs& a, hipStream_t stream) {
   const int rows = a.E + (a.shared_gate ? 1 : 0);
   const int grid = (rows + kWaves - 1) / kWaves;
-  const size_t lds = sizeof(float) * (size_t)token_group(a.H) * a.H +
+  const int esz = a.x_f32 ? 4 : 2;
+  const size_t lds = (size_t)token_group(a.H, esz, a.E) * a.H * esz +
                      (a.E > 64 * kKeySlots ? sizeof(double) * (size_t)kLdsWaves * (size_t)a.E : 0);
   const int cpl = (a.H / 8 + 63) / 64;
-  if (cpl <= 1)
-    hipLaunchKernelGGL(router_kernel<1>, dim3(grid), dim3(kThreads), lds, stream, a);
-  else if (cpl <= 2)
-    hipLaunchKernelGGL(router_kernel<2>, dim3(grid), dim3(kThreads), lds, stream, a);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL(router_kernel<4>, dim3(grid), dim3(kThreads), lds, stream, a);
-  else if (cpl <= 8)
-    hipLaunchKernelGGL(router_kernel<8>, dim3(grid), dim3(kThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL(router_kernel<16>, dim3(grid), dim3(kThreads), lds, stream, a);
-  return hipGetLastError();
+  if (cpl <= 1) return launch_cpl<1>(a, stream, grid, lds);
+  if (cpl <= 2) return launch_cpl<2>(a, stream, grid, lds);
+  if (cpl <= 4) return launch_cpl<4>(a, stream, grid, lds);
+  if (cpl <= 8) return launch_cpl<8>(a, stream, grid, lds);
+  return launch_cpl<16>(a, stream, grid, lds);
 }
 
 }  // namespace moeq
