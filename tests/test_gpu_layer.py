@@ -97,6 +97,24 @@ def test_rmsnorm_fp32_input():
     run_and_check(cfg, flags=q.F_RMSNORM, x_dev=x)
 
 
+def test_max_decode_batch_many_chunks():
+    """64 tokens (the decode maximum) over 8 experts, top-2: every expert holds
+    about 16 (token, slot) pairs, so the batched kernels run several token
+    chunks per expert, and the router stages its tokens in several passes."""
+    cfg = synth.with_changes(synth.CONFIGS["tiny"], name="t64", tokens=64)
+    run_and_check(cfg)
+
+
+def test_many_tokens_fp32_rmsnorm_gated():
+    """20 fp32 tokens with RMS norm, the shared-expert gate and full softmax:
+    more tokens than the router stages in one pass at this width (8 fp32
+    tokens of 4096), and selection in its own launch."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_4bit"], name="rms20", tokens=20)
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(20, cfg.hidden, generator=g, dtype=torch.float32) * 11.0).cuda()
+    run_and_check(cfg, flags=q.F_RMSNORM | q.F_NO_RENORM, shared_gate=synth.shared_gate_vector(cfg, 0), x_dev=x)
+
+
 def test_empty_batch_is_noop():
     cfg = synth.CONFIGS["tiny"]
     shape, ex = experts_for(cfg)
