@@ -7,9 +7,10 @@
 // Gate rows and up rows are contiguous in the blob, so the [gate; up] block
 // is addressed as 2I rows of one matrix.  Every selected expert of the batch
 // and the shared expert are handled in one launch; two grid shapes:
-//  - one token: one workgroup per (expert item, block of 4*RPW rows).  Each
-//    wave requests its RPW rows with 16-byte non-temporal loads into
-//    registers as soon as its expert is known, stages the token into LDS as
+//  - one token: one workgroup per (slot, block of 4*RPW rows).  Each wave
+//    requests its RPW rows with 16-byte non-temporal loads into registers
+//    as soon as its slot's expert is known (no grouping: one token's slots
+//    are separate outputs), stages the token into LDS as
 //    fp16 pairs while those loads are in flight, then produces one
 //    wave-wide sum per row;
 //  - several tokens: one workgroup per (chunk of 4 of the expert's tokens,
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
   int* ids = reinterpret_cast<int*>(list + list_words);
   const uint8_t** ptrs = reinterpret_cast<const uint8_t**>(ids + list_words);
 
-  group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
+  if constexpr (MMAX == 1) group_single(item, a.topk_idx, a.blobs, a.k, a.E, a.S, g, list, a.status);
+  else group_item(item, a.topk_idx, a.blobs, a.T, a.k, a.E, a.S, g, list, ids, ptrs, a.status);
   if (g.expert < 0) return;
   const uint8_t* blob = g.blob;
   (void)P;
@@ -388,12 +390,8 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t stream) {
                                          (size_t)kTokensPerStage * kChunkSums * nch +
                                          2 * (size_t)list_words) +
                      sizeof(void*) * (size_t)list_words;
-  if (a.T == 1)
-    hipLaunchKernelGGL((gemv_kernel<BITS, CPL, RPW, WMAX, 1>), dim3(items * n_rb), dim3(kThreads), lds,
-                       stream, a, n_rb, list_words);
-  else
-    hipLaunchKernelGGL((gemv_kernel<BITS, CPL, RPW, WMAX, kTokensPerStage>), dim3(items * n_rb),
-                       dim3(kThreads), lds, stream, a, n_rb, list_words);
+  hipLaunchKernelGGL((gemv_kernel<BITS, CPL, RPW, WMAX, 1>), dim3(items * n_rb), dim3(kThreads), lds, stream, a,
+                     n_rb, list_words);
   return hipGetLastError();
 }
 

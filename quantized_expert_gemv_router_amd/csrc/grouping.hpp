@@ -130,6 +130,34 @@ __device__ __forceinline__ void group_item(int item, const int32_t* __restrict__
   __syncthreads();
 }
 
+// One token: item i is slot i (the k routed slots, then the S shared
+// experts).  A token's slots are separate outputs, so no grouping is
+// needed; an out-of-range id is flagged and its item does nothing.  Whole
+// block.
+__device__ __forceinline__ void group_single(int item, const int32_t* __restrict__ topk_idx,
+                                             const void* const* __restrict__ blobs, int k, int E, int S,
+                                             GroupLds& g, uint32_t* __restrict__ list, int32_t* status) {
+  if (threadIdx.x == 0) {
+    int e = -1;
+    if (item < k) {
+      const int id = topk_idx[item];
+      if (id >= 0 && id < E) e = id;
+      else set_status(status, kStatusBadExpert);
+    } else if (item < k + S) {
+      e = E + (item - k);
+    }
+    const uint8_t* blob = e >= 0 ? static_cast<const uint8_t*>(blobs[e]) : nullptr;
+    g.expert = blob != nullptr ? e : -1;
+    g.blob = blob;
+    g.count = 1;
+    g.chunk = 0;
+    g.n_distinct = k;
+    g.in_range = item < k + S;
+    list[0] = (uint32_t)item;   // token 0, slot `item`
+  }
+  __syncthreads();
+}
+
 // Later token chunks.  An item with n (token, slot) pairs has ceil(n / C)
 // chunks of C; chunks 1.. of all items, numbered in item order (routed
 // experts by id, then the shared experts), are the batch's extra chunks,
