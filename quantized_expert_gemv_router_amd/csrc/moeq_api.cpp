@@ -219,7 +219,6 @@ int moe_swiglu_down_combine(const moeq_shape* s, const moeq_experts* ex, int lay
   a.T = T; a.k = k; a.bits = s->bits;
   a.out = out;
   a.dbuf = reinterpret_cast<float*>(ws + L.dbuf);
-  a.rb_counters = reinterpret_cast<uint32_t*>(ws + L.counters) + kCounterRowBlocks;
   a.status = reinterpret_cast<int32_t*>(ws + L.counters) + kCounterStatus;
   hipError_t e = launch_down_combine(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "down/combine kernel launch");

@@ -20,8 +20,7 @@ constexpr int64_t kAlign = 256;
 inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout (offsets in bytes from the workspace base):
-//   [0, 4096)        u32 words: [0] router arrival counter, [1] status word,
-//                    [64 .. 64 + n_rowblocks) down-combine row-block counters
+//   [0, 4096)        u32 words: [0] router arrival counter, [1] status word
 //   logits           f64 [T][E + 1]   (last column: shared-gate logit)
 //   dbuf             f32 [T][k + S][H] per-slot down outputs (multi-token)
 //   stack area       barrier words, tagged words (fp64 logit halves [E][2],
@@ -47,8 +46,6 @@ struct WorkspaceLayout {
 constexpr int kCounterRouter = 0;
 constexpr int kCounterStatus = 1;
 constexpr int32_t kStatusTimeout = 2;   // a grid barrier or handoff wait gave up
-constexpr int kCounterRowBlocks = 64;
-constexpr int kMaxRowBlockCounters = 1024 - kCounterRowBlocks;
 
 WorkspaceLayout workspace_layout(const moeq_shape& s, int T, int k);
 
@@ -96,8 +93,7 @@ struct DownArgs {
   const void* const* blobs;
   int H, I, E, S, T, k, bits;
   float* out;
-  float* dbuf;
-  uint32_t* rb_counters;
+  float* dbuf;         // [T][k + S][H] per-slot rows (batches)
   int32_t* status;
 };
 hipError_t launch_down_combine(const DownArgs& a, hipStream_t stream);
