@@ -136,7 +136,9 @@ int moe_router_topk(const moeq_shape* shape, const void* x, int x_dtype, uint32_
 /* Gate and up projections of every selected expert and the shared expert
  * (Flash-MoE, "Noyau de déquantification optimisé FMA" and "Shaders de
  * calcul Metal": dequantised 4-bit / 2-bit mat-vec).  Each expert's rows
- * are streamed once per call and applied to every token routed to it.
+ * are streamed once per call for every 4 of the (token, slot) pairs routed
+ * to it (once, for most experts of a decode batch) and applied to those
+ * tokens.
  *   x         device [T][H] in x_dtype; with MOEQ_F_RMSNORM normalised first
  *   topk_idx  device [T][k] int32 (ids outside [0, E) are skipped, their
  *             outputs left unwritten, and the workspace status word is set)
