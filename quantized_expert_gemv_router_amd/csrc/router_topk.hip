@@ -60,11 +60,12 @@ __device__ __forceinline__ void staged_x8(const unsigned char* xs, int x_f32, in
 }
 
 // Selection for tokens t0, t0 + step, ... by one wave, E <= 64 * M: lane l
-// holds logits l, l + 64, ... as order keys (ascending slot = ascending
-// id).  The next token's logits are requested before the current one is
+// holds logits l, l + 64, ... (times `scale`) as order keys (ascending
+// slot = ascending id).  The next token's logits are requested before the current one is
 // selected.  sel/selv (this wave's LDS) receive the ranked ids and logits.
 template <int M>
-__device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* sel, double* selv) {
+__device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* sel, double* selv,
+                                   double scale = 1.0) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.k, T = a.T;
   auto fetch = [&](int t, double (&d)[M], double& g) {
@@ -72,9 +73,9 @@ __device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* s
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int e = lane + 64 * m;
-      d[m] = (t < T && e < E) ? ld_agent(src + e) : 0.0;
+      d[m] = (t < T && e < E) ? ld_agent(src + e) * scale : 0.0;
     }
-    g = (t < T && lane == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) : 0.0;
+    g = (t < T && lane == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) * scale : 0.0;
   };
   double v[M], sg;
   fetch(t0, v, sg);
@@ -283,17 +284,129 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   }
 }
 
+// ------------------------------------------------ batches on the fp64 MFMA
+// Unscaled logits sum_j W[e,j] x[t,j] of a tile of 16 tokens x 16 router
+// rows on v_mfma_f64_16x16x4f64, whose lane layout is: A lane l = (row
+// l%16, k slot l/16), B lane l = (k slot l/16, column l%16), D element i of
+// lane l = (row 4i + l/16, column l%16); rows are tokens, columns router
+// rows.  H is cut into 32-value chunks, wave w taking an eighth of them.
+// In a chunk, lane (r, q) holds values 8q .. 8q+7 of its token and of its
+// router row (one 16-byte load each), and MFMA j pairs value 8q + j of
+// both, so the four k slots of MFMA j are 8 apart and the chunk's 8 MFMAs
+// cover its 32 values.  All of a wave's chunks are requested before the
+// first MFMA.  The eight waves' tiles are summed in wave order through LDS.
+// bf16 x bf16 and bf16 x fp32 products are exact in fp64, as in the
+// vector kernel; only the order of the fp64 sum differs.
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaChunks = 16;   // chunks per wave: H <= 32 * 8 * 16 = 4096
+typedef double double4v __attribute__((ext_vector_type(4)));
+
+template <bool F32>
+__global__ __launch_bounds__(64 * kMfmaWaves) void router_mfma_kernel(RouterArgs a) {
+  __shared__ double part[kMfmaWaves][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, E = a.E, T = a.T;
+  const int rows = E + (a.shared_gate ? 1 : 0);
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int r = lane & 15, q = lane >> 4;
+  const uint16_t* wmat = a.w_table ? a.w_table[a.w_layer] : a.w_router;
+  const int e = e0 + r, t = t0 + r;
+  const uint16_t* wrow = e < E ? wmat + (int64_t)e * H : (e < rows ? a.shared_gate : nullptr);
+  const bool tok_ok = t < T;
+  const int nch = H / 32;
+  const int c_lo = nch * wave / kMfmaWaves, c_hi = nch * (wave + 1) / kMfmaWaves;
+  u32x4 wq[kMfmaChunks], xq[kMfmaChunks][F32 ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < kMfmaChunks; ++i) {
+    const int c = c_lo + i;
+    const int k = c * 32 + q * 8;
+    const bool ok = c < c_hi;
+    wq[i] = (ok && wrow) ? load_stream(reinterpret_cast<const u32x4*>(wrow + k)) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (F32) {
+      const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.x) + (int64_t)t * H + k);
+      xq[i][0] = (ok && tok_ok) ? xp[0] : u32x4{0u, 0u, 0u, 0u};
+      xq[i][1] = (ok && tok_ok) ? xp[1] : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const u32x4* xp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + (int64_t)t * H + k);
+      xq[i][0] = (ok && tok_ok) ? xp[0] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  double4v acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < kMfmaChunks; ++i) {
+    if (c_lo + i < c_hi) {
+      double wv[8], xv[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wv[2 * j] = bf16_lo(wq[i][j]);
+        wv[2 * j + 1] = bf16_hi(wq[i][j]);
+      }
+      if constexpr (F32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xv[j] = __uint_as_float(xq[i][0][j]);
+          xv[4 + j] = __uint_as_float(xq[i][1][j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xv[2 * j] = bf16_lo(xq[i][0][j]);
+          xv[2 * j + 1] = bf16_hi(xq[i][0][j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[j], wv[j], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv[j + 1], wv[j + 1], acc1, 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][4 * i + q][r] = acc0[i] + acc1[i];
+  __syncthreads();
+  if (tid < 256) {
+    const int tt = tid >> 4, rr = tid & 15;
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) sum += part[w][tt][rr];
+    if (t0 + tt < T && e0 + rr < rows) a.logits[(int64_t)(t0 + tt) * (E + 1) + e0 + rr] = sum;
+  }
+}
+
 // One wave per token (token blockIdx.x): top-K, softmax weights, shared
-// weight, from the logits the router kernel wrote.
-__global__ __launch_bounds__(64) void select_kernel(RouterArgs a) {
+// weight, from the logits the router kernel wrote.  `raw`: the logits are
+// unscaled sums, and with RMS norm this wave takes the token's 1/rms first.
+__global__ __launch_bounds__(64) void select_kernel(RouterArgs a, int raw) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
-  const int t = blockIdx.x, E = a.E;
-  if (E <= 64) select_tokens_keys<1>(a, t, a.T, sel, selv);
-  else if (E <= 128) select_tokens_keys<2>(a, t, a.T, sel, selv);
-  else if (E <= 256) select_tokens_keys<4>(a, t, a.T, sel, selv);
-  else if (E <= 64 * kKeySlots) select_tokens_keys<kKeySlots>(a, t, a.T, sel, selv);
+  const int t = blockIdx.x, E = a.E, lane = threadIdx.x;
+  double scale = 1.0;
+  if (raw && a.rmsnorm) {
+    const int H = a.H;
+    double ss = 0.0;
+    for (int c = lane; c < H / 8; c += 64) {
+      double xv[8];
+      if (a.x_f32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (int64_t)t * H + 8 * c);
+        const float4 u0 = p[0], u1 = p[1];
+        xv[0] = u0.x; xv[1] = u0.y; xv[2] = u0.z; xv[3] = u0.w;
+        xv[4] = u1.x; xv[5] = u1.y; xv[6] = u1.z; xv[7] = u1.w;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (int64_t)t * H + 8 * c);
+        xv[0] = bf16_lo(u.x); xv[1] = bf16_hi(u.x); xv[2] = bf16_lo(u.y); xv[3] = bf16_hi(u.y);
+        xv[4] = bf16_lo(u.z); xv[5] = bf16_hi(u.z); xv[6] = bf16_lo(u.w); xv[7] = bf16_hi(u.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fma(xv[j], xv[j], ss);
+    }
+    ss = wave_sum_f64_dpp(ss);
+    scale = 1.0 / sqrt(ss / (double)H + 1e-6);
+  }
+  if (E <= 64) select_tokens_keys<1>(a, t, a.T, sel, selv, scale);
+  else if (E <= 128) select_tokens_keys<2>(a, t, a.T, sel, selv, scale);
+  else if (E <= 256) select_tokens_keys<4>(a, t, a.T, sel, selv, scale);
+  else if (E <= 64 * kKeySlots) select_tokens_keys<kKeySlots>(a, t, a.T, sel, selv, scale);
   else select_token_lds(a, t, reinterpret_cast<double*>(smem_raw), sel, selv);
 }
 
@@ -311,11 +424,22 @@ hipError_t launch_cpl(const RouterArgs& a, hipStream_t stream, int grid, size_t 
     hipLaunchKernelGGL((router_kernel<CPL, true>), dim3(grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((router_kernel<CPL, false>), dim3(grid), dim3(kThreads), lds, stream, a);
+  // logits on the fp64 MFMA where a wave's share of H fits its registers
+  // and the selection reads them in registers (E <= 512), else the vector
+  // kernel
+  const int rows = a.E + (a.shared_gate ? 1 : 0);
+  const bool mfma = a.H % 32 == 0 && a.H / 32 <= kMfmaWaves * kMfmaChunks && a.E <= 64 * kKeySlots;
+  if (mfma) {
+    const dim3 g((rows + 15) / 16, (a.T + 15) / 16);
+    if (a.x_f32) hipLaunchKernelGGL(router_mfma_kernel<true>, g, dim3(64 * kMfmaWaves), 0, stream, a);
+    else hipLaunchKernelGGL(router_mfma_kernel<false>, g, dim3(64 * kMfmaWaves), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((router_kernel<CPL, false>), dim3(grid), dim3(kThreads), lds, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t sel_lds = a.E > 64 * kKeySlots ? sizeof(double) * (size_t)a.E : 0;
-  hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a);
+  hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a, mfma ? 1 : 0);
   return hipGetLastError();
 }
 
