@@ -7,20 +7,25 @@
 // the K largest logits, ties to the lower expert index, and the weights are
 // the softmax of the selected logits.
 //
-// One wave per router row: the row (bf16, H/8 16-byte chunks) is loaded
-// once into registers and dotted with every token in fp64 (bf16 x bf16 and
-// bf16 x fp32 products are exact in fp64).  Up to 16 tokens are copied into
-// LDS in their own type (bf16 or fp32) per pass; the dots of four tokens
-// at a time are interleaved and their wave sums are DPP reductions, so one
-// token's latency hides behind the next.  With RMS norm, sum(x^2) of each
-// staged token is taken once (fp64, one wave per token) and the logit is
-// inv_rms * sum(W x).  Logits are
-// written with agent-scope write-through stores.  Up to 8 tokens, the last
-// workgroup to bump the arrival counter selects top-K for every token, one
-// token per wave; more tokens, a second launch selects with one wave per
-// token, all at once.  Either way the logits are held as keys in registers
-// for E <= 512 (else staged in LDS), and the indices, weights and the
-// shared expert's weight are written.
+// Up to 8 tokens (router_kernel): one wave per router row.  The row (bf16,
+// H/8 16-byte chunks) is loaded once into registers and dotted with every
+// token in fp64 (bf16 x bf16 and bf16 x fp32 products are exact in fp64).
+// Up to 16 tokens are copied into LDS in their own type (bf16 or fp32) per
+// pass; the dots of four tokens at a time are interleaved and their wave
+// sums are DPP reductions, so one token's latency hides behind the next.
+// With RMS norm, sum(x^2) of each staged token is taken once (fp64, one
+// wave per token) and the logit is inv_rms * sum(W x).  Logits are written
+// with agent-scope write-through stores, and the last workgroup to bump the
+// arrival counter selects top-K for every token, one token per wave.
+//
+// More tokens: the logits of 16 tokens x 16 rows per workgroup on the fp64
+// MFMA (router_mfma_kernel, unscaled; H <= 4096 and E <= 512, else the
+// vector kernel without its selection), then a second launch selects with
+// one wave per token, all at once, applying 1/rms itself.
+//
+// Either way the logits are held as keys in registers for E <= 512 (else
+// staged in LDS), and the indices, weights and the shared expert's weight
+// are written.
 #include "moeq_device.hpp"
 #include "moeq_internal.hpp"
 #include "topk.hpp"
