@@ -79,6 +79,15 @@ def test_topk_edges(k, E):
     run_and_check(cfg)
 
 
+@pytest.mark.parametrize("T", [2, 12])
+def test_many_experts_lds_selection(T):
+    """1024 experts, top-16: more logits than the register selection holds
+    (8 per lane), so top-K runs from LDS -- in the last router workgroup
+    (2 tokens) or in the separate selection launch (12 tokens)."""
+    cfg = synth.with_changes(synth.CONFIGS["tiny"], name=f"e1024t{T}", n_experts=1024, top_k=16, tokens=T)
+    run_and_check(cfg)
+
+
 def test_without_shared_expert():
     cfg = synth.with_changes(synth.CONFIGS["tiny"], name="noshared", n_shared=0, tokens=3)
     run_and_check(cfg)
