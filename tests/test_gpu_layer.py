@@ -73,6 +73,15 @@ def test_largest_supported_rows(bits, H, I):
     run_and_check(cfg)
 
 
+def test_wide_rows_many_tokens():
+    """hidden 8192 with 10 tokens: wider than the MFMA router takes, so the
+    vector logits kernel runs without its selection tail and the selection
+    launch reads logits it already scaled."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_4bit"], name="max4t10", hidden=8192, inter=4096,
+                             n_experts=6, top_k=2, tokens=10)
+    run_and_check(cfg)
+
+
 @pytest.mark.parametrize("k,E", [(1, 8), (8, 8), (16, 64)])
 def test_topk_edges(k, E):
     cfg = synth.with_changes(synth.CONFIGS["tiny"], name=f"k{k}E{E}", n_experts=E, top_k=k, tokens=2)
