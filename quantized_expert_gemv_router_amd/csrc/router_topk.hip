@@ -20,8 +20,10 @@
 //
 // More tokens: the logits of 16 tokens x 16 rows per workgroup on the fp64
 // MFMA (router_mfma_kernel, unscaled; H <= 4096 and E <= 512, else the
-// vector kernel without its selection), then a second launch selects with
-// one wave per token, all at once, applying 1/rms itself.
+// vector kernel without its selection), then a second launch selects for
+// all tokens at once, applying 1/rms itself: one workgroup per token with
+// the threshold top-K over one logit per thread (E <= 512), else one wave
+// per token.
 //
 // Either way the logits are held as keys in registers for E <= 512 (else
 // staged in LDS), and the indices, weights and the shared expert's weight
@@ -415,6 +417,88 @@ __global__ __launch_bounds__(64) void select_kernel(RouterArgs a, int raw) {
   else select_token_lds(a, t, reinterpret_cast<double*>(smem_raw), sel, selv);
 }
 
+// One workgroup of kWaves waves per token (token blockIdx.x), E <= 64 *
+// kWaves: each thread holds one logit as an order key, the threshold top-K
+// over the workgroup (samples, candidates, ranking by counting; the
+// two-level wave selection when more than 64 candidates pass), then wave 0
+// takes the softmax weights.  `raw`: as select_kernel.
+__global__ __launch_bounds__(kThreads) void select_block_kernel(RouterArgs a, int raw) {
+  __shared__ double lg[64 * kWaves];
+  __shared__ double red[kWaves];
+  __shared__ int wk[2 * kWaves];
+  __shared__ int64_t ck[64 * kWaves];
+  __shared__ int ci[64 * kWaves];
+  __shared__ int cnt[kWaves];
+  __shared__ int sel[MOEQ_MAX_TOPK];
+  __shared__ double selv[MOEQ_MAX_TOPK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x, E = a.E, K = a.k, H = a.H;
+  const double* src = a.logits + (int64_t)t * (E + 1);
+  // the logit first: its load is in flight during the sum of squares
+  const double raw_v = tid < E ? ld_agent(src + tid) : 0.0;
+  const double raw_g = (tid == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) : 0.0;
+  double scale = 1.0;
+  if (raw && a.rmsnorm) {
+    double ss = 0.0;
+    for (int c = tid; c < H / 8; c += kThreads) {
+      double xv[8];
+      if (a.x_f32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (int64_t)t * H + 8 * c);
+        const float4 u0 = p[0], u1 = p[1];
+        xv[0] = u0.x; xv[1] = u0.y; xv[2] = u0.z; xv[3] = u0.w;
+        xv[4] = u1.x; xv[5] = u1.y; xv[6] = u1.z; xv[7] = u1.w;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (int64_t)t * H + 8 * c);
+        xv[0] = bf16_lo(u.x); xv[1] = bf16_hi(u.x); xv[2] = bf16_lo(u.y); xv[3] = bf16_hi(u.y);
+        xv[4] = bf16_lo(u.z); xv[5] = bf16_hi(u.z); xv[6] = bf16_lo(u.w); xv[7] = bf16_hi(u.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fma(xv[j], xv[j], ss);
+    }
+    ss = wave_sum_f64_dpp(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += red[w];
+    scale = 1.0 / sqrt(tot / (double)H + 1e-6);
+  }
+  const double v = raw_v * scale;
+  const int64_t key = tid < E ? order_key(v) : kNoKey;
+  if (tid < E) {
+    lg[tid] = v;
+    if (a.logits_out) a.logits_out[(int64_t)t * E + tid] = v;
+  }
+  topk_samples<kWaves>(key, K, wk);
+  __syncthreads();
+  topk_candidates<kWaves>(key, tid, K, wk, ck, ci, cnt);
+  __syncthreads();
+  const bool fast = topk_select<kWaves>(K, ck, ci, cnt, [&](int r, int win) {
+    if (wave == 0) sel[r] = win;
+  });
+  if (!fast) block_topk_keys<kWaves, 1, 2>(lg, E, K, ck, ci, sel, selv);   // block-uniform
+  __syncthreads();
+  if (wave == 0) {
+    const int mine = lane < K ? sel[lane] : 0;
+    const double top = lg[sel[0]];   // rank 0 is the maximum
+    const double ex = lane < K ? exp(lg[mine] - top) : 0.0;
+    double z;
+    if (a.no_renorm) {
+      double part = 0.0;
+      for (int e = lane; e < E; e += 64) part += exp(lg[e] - top);
+      z = wave_sum_f64_dpp(part);
+    } else {
+      z = wave_sum_f64_dpp(ex);
+    }
+    if (lane < K) {
+      a.topk_idx[(int64_t)t * K + lane] = mine;
+      a.topk_w[(int64_t)t * K + lane] = (float)(ex / z);
+    }
+    if (lane == 0 && a.shared_w)
+      a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-raw_g * scale))) : 1.0f;
+  }
+}
+
 template <int CPL>
 hipError_t launch_cpl(const RouterArgs& a, hipStream_t stream, int grid, size_t lds) {
   const bool split = a.T > kWaves;   // more tokens than the last workgroup has waves
@@ -443,8 +527,12 @@ hipError_t launch_cpl(const RouterArgs& a, hipStream_t stream, int grid, size_t 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t sel_lds = a.E > 64 * kKeySlots ? sizeof(double) * (size_t)a.E : 0;
-  hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a, mfma ? 1 : 0);
+  if (a.E <= 64 * kWaves) {
+    hipLaunchKernelGGL(select_block_kernel, dim3(a.T), dim3(kThreads), 0, stream, a, mfma ? 1 : 0);
+  } else {
+    const size_t sel_lds = sizeof(double) * (size_t)a.E;
+    hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a, mfma ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
