@@ -67,12 +67,10 @@ __device__ __forceinline__ void staged_x8(const unsigned char* xs, int x_f32, in
 }
 
 // Selection for tokens t0, t0 + step, ... by one wave, E <= 64 * M: lane l
-// holds logits l, l + 64, ... (times `scale`) as order keys (ascending
-// slot = ascending id).  The next token's logits are requested before the current one is
+// holds logits l, l + 64, ... as order keys (ascending slot = ascending id).  The next token's logits are requested before the current one is
 // selected.  sel/selv (this wave's LDS) receive the ranked ids and logits.
 template <int M>
-__device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* sel, double* selv,
-                                   double scale = 1.0) {
+__device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* sel, double* selv) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.k, T = a.T;
   auto fetch = [&](int t, double (&d)[M], double& g) {
@@ -80,9 +78,9 @@ __device__ void select_tokens_keys(const RouterArgs& a, int t0, int step, int* s
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int e = lane + 64 * m;
-      d[m] = (t < T && e < E) ? ld_agent(src + e) * scale : 0.0;
+      d[m] = (t < T && e < E) ? ld_agent(src + e) : 0.0;
     }
-    g = (t < T && lane == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) * scale : 0.0;
+    g = (t < T && lane == 0 && a.shared_w && a.shared_gate) ? ld_agent(src + E) : 0.0;
   };
   double v[M], sg;
   fetch(t0, v, sg);
@@ -380,48 +378,21 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void router_mfma_kernel(RouterArgs
   }
 }
 
-// One wave per token (token blockIdx.x): top-K, softmax weights, shared
-// weight, from the logits the router kernel wrote.  `raw`: the logits are
-// unscaled sums, and with RMS norm this wave takes the token's 1/rms first.
-__global__ __launch_bounds__(64) void select_kernel(RouterArgs a, int raw) {
+// One wave per token (token blockIdx.x), E > 64 * kWaves: top-K from the
+// (scaled) logits staged in LDS, softmax weights, shared weight.
+__global__ __launch_bounds__(64) void select_kernel(RouterArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int sel[MOEQ_MAX_TOPK];
   __shared__ double selv[MOEQ_MAX_TOPK];
-  const int t = blockIdx.x, E = a.E, lane = threadIdx.x;
-  double scale = 1.0;
-  if (raw && a.rmsnorm) {
-    const int H = a.H;
-    double ss = 0.0;
-    for (int c = lane; c < H / 8; c += 64) {
-      double xv[8];
-      if (a.x_f32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (int64_t)t * H + 8 * c);
-        const float4 u0 = p[0], u1 = p[1];
-        xv[0] = u0.x; xv[1] = u0.y; xv[2] = u0.z; xv[3] = u0.w;
-        xv[4] = u1.x; xv[5] = u1.y; xv[6] = u1.z; xv[7] = u1.w;
-      } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (int64_t)t * H + 8 * c);
-        xv[0] = bf16_lo(u.x); xv[1] = bf16_hi(u.x); xv[2] = bf16_lo(u.y); xv[3] = bf16_hi(u.y);
-        xv[4] = bf16_lo(u.z); xv[5] = bf16_hi(u.z); xv[6] = bf16_lo(u.w); xv[7] = bf16_hi(u.w);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fma(xv[j], xv[j], ss);
-    }
-    ss = wave_sum_f64_dpp(ss);
-    scale = 1.0 / sqrt(ss / (double)H + 1e-6);
-  }
-  if (E <= 64) select_tokens_keys<1>(a, t, a.T, sel, selv, scale);
-  else if (E <= 128) select_tokens_keys<2>(a, t, a.T, sel, selv, scale);
-  else if (E <= 256) select_tokens_keys<4>(a, t, a.T, sel, selv, scale);
-  else if (E <= 64 * kKeySlots) select_tokens_keys<kKeySlots>(a, t, a.T, sel, selv, scale);
-  else select_token_lds(a, t, reinterpret_cast<double*>(smem_raw), sel, selv);
+  select_token_lds(a, blockIdx.x, reinterpret_cast<double*>(smem_raw), sel, selv);
 }
 
 // One workgroup of kWaves waves per token (token blockIdx.x), E <= 64 *
 // kWaves: each thread holds one logit as an order key, the threshold top-K
 // over the workgroup (samples, candidates, ranking by counting; the
 // two-level wave selection when more than 64 candidates pass), then wave 0
-// takes the softmax weights.  `raw`: as select_kernel.
+// takes the softmax weights.  `raw`: the logits are unscaled sums, and with
+// RMS norm the workgroup takes the token's 1/rms first.
 __global__ __launch_bounds__(kThreads) void select_block_kernel(RouterArgs a, int raw) {
   __shared__ double lg[64 * kWaves];
   __shared__ double red[kWaves];
@@ -529,9 +500,9 @@ hipError_t launch_cpl(const RouterArgs& a, hipStream_t stream, int grid, size_t 
   if (e != hipSuccess) return e;
   if (a.E <= 64 * kWaves) {
     hipLaunchKernelGGL(select_block_kernel, dim3(a.T), dim3(kThreads), 0, stream, a, mfma ? 1 : 0);
-  } else {
+  } else {   // the vector kernel wrote scaled logits (mfma needs E <= 512)
     const size_t sel_lds = sizeof(double) * (size_t)a.E;
-    hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a, mfma ? 1 : 0);
+    hipLaunchKernelGGL(select_kernel, dim3(a.T), dim3(64), sel_lds, stream, a);
   }
   return hipGetLastError();
 }
