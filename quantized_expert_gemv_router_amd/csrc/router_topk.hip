@@ -16,7 +16,8 @@
 // With RMS norm, sum(x^2) of each staged token is taken once (fp64, one
 // wave per token) and the logit is inv_rms * sum(W x).  Logits are written
 // with agent-scope write-through stores, and the last workgroup to bump the
-// arrival counter selects top-K for every token, one token per wave.
+// arrival counter selects top-K: one token with the whole workgroup (E <=
+// 512), else one token per wave.
 //
 // More tokens: the logits of 16 tokens x 16 rows per workgroup on the fp64
 // MFMA (router_mfma_kernel, unscaled; H <= 4096 and E <= 512, else the
@@ -161,6 +162,61 @@ __device__ void select_token_lds(const RouterArgs& a, int t, double* lg, int* se
 }
 
 // One wave per router row (rows E.. hold the optional shared-gate vector).
+// LDS of the workgroup selection.
+struct BlockSelLds {
+  double lg[64 * kWaves];
+  double red[kWaves];
+  int wk[2 * kWaves];
+  int64_t ck[64 * kWaves];
+  int ci[64 * kWaves];
+  int cnt[kWaves];
+  int sel[MOEQ_MAX_TOPK];
+  double selv[MOEQ_MAX_TOPK];
+};
+
+// Selection for token t by the whole workgroup (kWaves waves), E <= 64 *
+// kWaves: thread i holds logit v of expert i as an order key; the
+// threshold top-K over the workgroup (samples, candidates, ranking by
+// counting; the two-level wave selection when more than 64 candidates
+// pass), then wave 0 takes the softmax weights.  g: the shared-gate logit
+// (thread 0).
+__device__ void block_select(const RouterArgs& a, int t, double v, double g, BlockSelLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, K = a.k;
+  const int64_t key = tid < E ? order_key(v) : kNoKey;
+  if (tid < E) {
+    L.lg[tid] = v;
+    if (a.logits_out) a.logits_out[(int64_t)t * E + tid] = v;
+  }
+  topk_samples<kWaves>(key, K, L.wk);
+  __syncthreads();
+  topk_candidates<kWaves>(key, tid, K, L.wk, L.ck, L.ci, L.cnt);
+  __syncthreads();
+  const bool fast = topk_select<kWaves>(K, L.ck, L.ci, L.cnt, [&](int r, int win) {
+    if (wave == 0) L.sel[r] = win;
+  });
+  if (!fast) block_topk_keys<kWaves, 1, 2>(L.lg, E, K, L.ck, L.ci, L.sel, L.selv);   // block-uniform
+  __syncthreads();
+  if (wave == 0) {
+    const int mine = lane < K ? L.sel[lane] : 0;
+    const double top = L.lg[L.sel[0]];   // rank 0 is the maximum
+    const double ex = lane < K ? exp(L.lg[mine] - top) : 0.0;
+    double z;
+    if (a.no_renorm) {
+      double part = 0.0;
+      for (int e = lane; e < E; e += 64) part += exp(L.lg[e] - top);
+      z = wave_sum_f64_dpp(part);
+    } else {
+      z = wave_sum_f64_dpp(ex);
+    }
+    if (lane < K) {
+      a.topk_idx[(int64_t)t * K + lane] = mine;
+      a.topk_w[(int64_t)t * K + lane] = (float)(ex / z);
+    }
+    if (lane == 0 && a.shared_w) a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-g))) : 1.0f;
+  }
+}
+
 // SELECT: the last workgroup to arrive selects for every token (small
 // batches); otherwise select_kernel does, one wave per token, in a second
 // launch.
@@ -275,7 +331,12 @@ __global__ __launch_bounds__(kThreads) void router_kernel(RouterArgs a) {
   __syncthreads();
   if (!is_last) return;
   if (tid == 0) st_agent(a.counter, 0u);
-  if (E <= 64) {
+  if (a.T == 1 && E <= 64 * kWaves) {   // one token: the whole workgroup selects it
+    __shared__ BlockSelLds L;
+    const double v = tid < E ? ld_agent(a.logits + tid) : 0.0;
+    const double g = (tid == 0 && a.shared_w && a.shared_gate) ? ld_agent(a.logits + E) : 0.0;
+    block_select(a, 0, v, g, L);
+  } else if (E <= 64) {
     select_tokens_keys<1>(a, wave, kWaves, sel[wave], selv[wave]);
   } else if (E <= 128) {
     select_tokens_keys<2>(a, wave, kWaves, sel[wave], selv[wave]);
@@ -387,23 +448,13 @@ __global__ __launch_bounds__(64) void select_kernel(RouterArgs a) {
   select_token_lds(a, blockIdx.x, reinterpret_cast<double*>(smem_raw), sel, selv);
 }
 
-// One workgroup of kWaves waves per token (token blockIdx.x), E <= 64 *
-// kWaves: each thread holds one logit as an order key, the threshold top-K
-// over the workgroup (samples, candidates, ranking by counting; the
-// two-level wave selection when more than 64 candidates pass), then wave 0
-// takes the softmax weights.  `raw`: the logits are unscaled sums, and with
-// RMS norm the workgroup takes the token's 1/rms first.
+// One workgroup per token (token blockIdx.x), E <= 64 * kWaves: the
+// workgroup selection.  `raw`: the logits are unscaled sums, and with RMS
+// norm the workgroup takes the token's 1/rms first.
 __global__ __launch_bounds__(kThreads) void select_block_kernel(RouterArgs a, int raw) {
-  __shared__ double lg[64 * kWaves];
-  __shared__ double red[kWaves];
-  __shared__ int wk[2 * kWaves];
-  __shared__ int64_t ck[64 * kWaves];
-  __shared__ int ci[64 * kWaves];
-  __shared__ int cnt[kWaves];
-  __shared__ int sel[MOEQ_MAX_TOPK];
-  __shared__ double selv[MOEQ_MAX_TOPK];
+  __shared__ BlockSelLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x, E = a.E, K = a.k, H = a.H;
+  const int t = blockIdx.x, E = a.E, H = a.H;
   const double* src = a.logits + (int64_t)t * (E + 1);
   // the logit first: its load is in flight during the sum of squares
   const double raw_v = tid < E ? ld_agent(src + tid) : 0.0;
@@ -427,47 +478,14 @@ __global__ __launch_bounds__(kThreads) void select_block_kernel(RouterArgs a, in
       for (int j = 0; j < 8; ++j) ss = fma(xv[j], xv[j], ss);
     }
     ss = wave_sum_f64_dpp(ss);
-    if (lane == 0) red[wave] = ss;
+    if (lane == 0) L.red[wave] = ss;
     __syncthreads();
     double tot = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += red[w];
+    for (int w = 0; w < kWaves; ++w) tot += L.red[w];
     scale = 1.0 / sqrt(tot / (double)H + 1e-6);
   }
-  const double v = raw_v * scale;
-  const int64_t key = tid < E ? order_key(v) : kNoKey;
-  if (tid < E) {
-    lg[tid] = v;
-    if (a.logits_out) a.logits_out[(int64_t)t * E + tid] = v;
-  }
-  topk_samples<kWaves>(key, K, wk);
-  __syncthreads();
-  topk_candidates<kWaves>(key, tid, K, wk, ck, ci, cnt);
-  __syncthreads();
-  const bool fast = topk_select<kWaves>(K, ck, ci, cnt, [&](int r, int win) {
-    if (wave == 0) sel[r] = win;
-  });
-  if (!fast) block_topk_keys<kWaves, 1, 2>(lg, E, K, ck, ci, sel, selv);   // block-uniform
-  __syncthreads();
-  if (wave == 0) {
-    const int mine = lane < K ? sel[lane] : 0;
-    const double top = lg[sel[0]];   // rank 0 is the maximum
-    const double ex = lane < K ? exp(lg[mine] - top) : 0.0;
-    double z;
-    if (a.no_renorm) {
-      double part = 0.0;
-      for (int e = lane; e < E; e += 64) part += exp(lg[e] - top);
-      z = wave_sum_f64_dpp(part);
-    } else {
-      z = wave_sum_f64_dpp(ex);
-    }
-    if (lane < K) {
-      a.topk_idx[(int64_t)t * K + lane] = mine;
-      a.topk_w[(int64_t)t * K + lane] = (float)(ex / z);
-    }
-    if (lane == 0 && a.shared_w)
-      a.shared_w[t] = a.shared_gate ? (float)(1.0 / (1.0 + exp(-raw_g * scale))) : 1.0f;
-  }
+  block_select(a, t, raw_v * scale, raw_g * scale, L);
 }
 
 template <int CPL>
