@@ -321,6 +321,66 @@ def test_zero_shared_gate_vector_halves_shared_contribution():
     np.testing.assert_allclose(gated["y"] - h, 0.5 * (ungated["y"] - h), rtol=1e-14, atol=1e-15)
 
 
+def _one_hot_gate(H, j, c):
+    """bf16 gate vector c * e_j (c exactly representable in bf16)."""
+    g = np.zeros(H)
+    g[j] = c
+    gb = bk.f64_to_bf16(g)
+    assert bk.bf16_to_f64(gb)[j] == c
+    return gb
+
+
+@pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("j,c", [(0, 0.75), (5, -1.5), (77, 2.0), (127, -0.375)])
+def test_one_hot_shared_gate_closed_form(rms, j, c):
+    """A one-hot gate c * e_j gives gamma = sigmoid(c * xhat_j): xhat = h without
+    the norm flag, h_j / sqrt(mean(h^2) + 1e-6) with it.  The shared term of the
+    output is then gamma times the dense SwiGLU expert applied to xhat
+    (K = 0, so nothing else is added to the residual).  A sign slip in the
+    exponent, a dot taken over h instead of xhat, or the gate applied to the
+    wrong term fails here."""
+    H, I, E = 128, 64, 6
+    rng, blobs, wr = _tiny_layer_inputs(E=E, H=H, I=I, seed=16)
+    h = rng.standard_normal((2, H)) * 3.0
+    flags = oracle.RMSNORM if rms else 0
+    out = oracle.moe_layer(shape(H, I, E, 1), blobs, wr, h, 0, flags=flags,
+                           shared_gate=_one_hot_gate(H, j, c))
+    for t in range(2):
+        xhat = h[t] / math.sqrt(np.mean(h[t] ** 2) + 1e-6) if rms else h[t]
+        gamma = 1.0 / (1.0 + math.exp(-c * xhat[j]))
+        assert math.isclose(out["gamma"][t], gamma, rel_tol=1e-14)
+        y = h[t] + gamma * _dense_expert(blobs[E], H, I, xhat)
+        np.testing.assert_allclose(out["y"][t], y, rtol=1e-10, atol=1e-10 * np.abs(y).max())
+
+
+def test_shared_gate_sign_and_scale_symmetries():
+    """sigmoid(-z) = 1 - sigmoid(z): negating the gate vector maps gamma to
+    1 - gamma; with the norm flag, scaling h (well above the epsilon) leaves
+    gamma unchanged, and without it the logit of gamma is the dot product
+    gate . h, scaled with h."""
+    H, I, E = 128, 64, 6
+    rng, blobs, wr = _tiny_layer_inputs(E=E, H=H, I=I, seed=17)
+    h = rng.standard_normal((3, H)) * 2.0
+    gv = bk.f64_to_bf16(rng.standard_normal(H) * 0.1)
+    neg = bk.f64_to_bf16(-bk.bf16_to_f64(gv))
+    sh = shape(H, I, E, 1)
+    for flags in (0, oracle.RMSNORM):
+        _, _, _, g_pos = oracle.route(sh, wr, h, 2, flags, shared_gate=gv)
+        _, _, _, g_neg = oracle.route(sh, wr, h, 2, flags, shared_gate=neg)
+        np.testing.assert_allclose(g_pos + g_neg, 1.0, rtol=0, atol=1e-15)
+        assert np.all(np.abs(g_pos - 0.5) > 1e-6)
+    big = h * 1e4          # mean(h^2) ~ 4e8: the 1e-6 under the root is below fp64 resolution
+    _, _, _, g1 = oracle.route(sh, wr, big, 2, oracle.RMSNORM, shared_gate=gv)
+    _, _, _, g8 = oracle.route(sh, wr, 8.0 * big, 2, oracle.RMSNORM, shared_gate=gv)
+    np.testing.assert_allclose(g8, g1, rtol=1e-13)
+    _, _, _, r1 = oracle.route(sh, wr, h, 2, 0, shared_gate=gv)
+    _, _, _, r8 = oracle.route(sh, wr, 8.0 * h, 2, 0, shared_gate=gv)
+    z1 = np.log(r1 / (1.0 - r1))
+    z8 = np.log(r8 / (1.0 - r8))
+    np.testing.assert_allclose(z8, 8.0 * z1, rtol=1e-9)
+    np.testing.assert_allclose(z1, h @ bk.bf16_to_f64(gv), rtol=1e-9)
+
+
 def test_layer_intermediates_are_consistent():
     """gu, a and d exported per slot are the expert's own g, u, silu(g)*u and Wd a."""
     cfg = synth.CONFIGS["tiny"]
