@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--tokens-pool", type=int, default=64, help="distinct token vectors")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--probe-handoff", action="store_true",
+                   help="only run the cross-workgroup hand-off latency probe sweep (diagnostic)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return p.parse_args()
@@ -429,6 +431,50 @@ def calibrate_copy(mib, dev):
     print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
+def probe_handoff():
+    """Hand-off latency sweep: one JSON line per (pattern, words, layout, back-off)."""
+    import quantized_expert_gemv_router_amd as q
+    names = {0: "tagged all-gather", 1: "flag + payload", 2: "ping-pong", 3: "counter barrier",
+             4: "gather to one + broadcast", 5: "gather to one + broadcast + one data read",
+             6: "tagged all-gather, pipelined polls"}
+    cases = [(6, w, w, s, d) for w in (1, 4, 8) for s in (0, 1, 2) for d in (2, 4)]
+    cases += [(0, w, w, s, 1) for w in (1, 4, 8) for s in (0, 1)]
+    cases += [(2, 1, 1, s, p) for s in (0, 1) for p in (1, 8)]
+    cases += [(3, 1, 1, s, 1) for s in (0, 1)]
+    cases += [(0, w, w, s, 1) for w in (1, 2, 4, 8, 16, 32) for s in (0, 1)]
+    cases += [(0, w, st, 1, 1) for w in (1, 4, 16) for st in (16, 64, 512)]
+    cases += [(1, w, w, 1, 1) for w in (1, 4, 16)]
+    cases += [(4, w, w, 1, c) for w in (1, 4, 16) for c in (1, 8, 32)]
+    cases += [(5, w, w, 1, c) for w in (4, 16) for c in (8, 32)]
+    xcc_logged = False
+    for mode, w, stride, s, peer in cases:
+        if stride < w:
+            continue
+        rounds = 2000
+        try:
+            q.moeq_probe_handoff(mode, w, 50, s, peer, stride=stride)            # warm-up
+            r = q.moeq_probe_handoff(mode, w, rounds, s, peer, stride=stride)
+        except q.MoeqError as e:
+            print(json.dumps({"probe": names[mode], "mode": mode, "words_per_block": w, "sleep": s,
+                              "error": str(e)}), flush=True)
+            if e.code != q.E_UNSUPPORTED:
+                break          # a wait gave up: stop the sweep
+            continue
+        rec = {"probe": names[mode], "mode": mode, "words_per_block": w, "stride_words": stride, "sleep": s,
+               "us_per_round": round(r["ticks"] * 0.01 / rounds, 3), "stale_words": r["stale"]}
+        if mode in (4, 5):
+            rec["go_copies"] = peer
+        if mode == 6:
+            rec["loads_in_flight"] = peer
+        if mode == 2:
+            rec["peer"] = peer
+            rec["us_one_way"] = round(r["ticks"] * 0.01 / rounds / 2, 3)
+        if not xcc_logged:
+            rec["xcc_of_workgroup"] = r["xcc"]
+            xcc_logged = True
+        print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -441,6 +487,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probe_handoff:
+        probe_handoff()
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, dev)
         return

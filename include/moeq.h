@@ -237,6 +237,37 @@ int moeq_stack_clock_trace(int64_t* clocks);
  * timed out).  Clears it. */
 int moe_read_device_status(void* workspace, void* stream, int32_t* status);
 
+/* Diagnostic: latency of cross-workgroup hand-offs on this device.  One
+ * workgroup of 512 threads per CU (cooperative launch) runs `rounds` rounds
+ * of one pattern after a start barrier:
+ *   mode 0  tagged all-gather: every workgroup publishes words_per_block
+ *           64-bit words carrying the round's tag (writer j's words from
+ *           word j * stride); every workgroup polls all of them (the words
+ *           are their own flags);
+ *   mode 1  flag + payload: payload words, then one tagged flag word per
+ *           workgroup; readers poll the flags, then read the payload once;
+ *   mode 2  ping-pong: workgroups 0 and `peer` bounce one tagged word (two
+ *           one-way hand-offs per round);
+ *   mode 3  counter barrier: one atomic counter, polled until every
+ *           workgroup has added its round;
+ *   mode 4  gather + broadcast: only workgroup 0 polls the published words,
+ *           then writes the round's tag to `peer` go words (4 KiB apart)
+ *           that the other workgroups poll (workgroup id mod peer);
+ *   mode 5  mode 4, then every workgroup reads all the words once;
+ *   mode 6  mode 0 with `peer` (2 or 4) staggered loads of every polled
+ *           word in flight (at most 2048 words).
+ * `sleep` (0..3) is the back-off between polls (s_sleep 0, 1, 2, 4).
+ * scratch: device, moeq_probe_scratch_bytes(words_per_block, stride) bytes,
+ * cleared by the call.  Synchronises `stream`; *ticks = 100 MHz wall-clock
+ * ticks of all rounds as seen by workgroup 0; *mismatches (may be NULL) =
+ * payload words read with a stale tag in mode 1; xcc_ids (host [CUs], may
+ * be NULL) receives the XCD id each workgroup ran on.  MOEQ_E_DEVICE if a
+ * wait gave up.  words_per_block * (CUs) <= 8192, stride >= words_per_block. */
+int64_t moeq_probe_scratch_bytes(int words_per_block, int stride);
+int moeq_probe_handoff(int mode, int words_per_block, int stride, int rounds, int sleep, int peer,
+                       void* scratch, int64_t scratch_bytes, int64_t* ticks, int64_t* mismatches,
+                       int32_t* xcc_ids, void* stream);
+
 /* ------------------------------------------------------------------ pool
  * Expert slot pool (openclawradar.com/fr, Flash-MoE write-up: experts kept
  * in a bounded number of resident slots and loaded when the router asks for

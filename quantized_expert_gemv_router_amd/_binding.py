@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.moeq_poolsim_stats.argtypes = [_P, ctypes.POINTER(I64)]
         L.moeq_poolsim_destroy.argtypes = [_P]
         L.moeq_poolsim_destroy.restype = None
+        L.moeq_probe_scratch_bytes.restype = I64
+        L.moeq_probe_scratch_bytes.argtypes = [_I, _I]
+        L.moeq_probe_handoff.argtypes = [_I, _I, _I, _I, _I, _I, _P, I64, ctypes.POINTER(I64),
+                                         ctypes.POINTER(I64), _P, _P]
         _lib = L
     return _lib
 
@@ -315,6 +319,24 @@ def moeq_last_stack_path() -> int:
 def moeq_stack_clock_trace(clocks: torch.Tensor) -> int:
     """Arm the diagnostic phase clock trace (int64 device tensor [L, 24])."""
     return lib().moeq_stack_clock_trace(_ptr(clocks))
+
+
+def moeq_probe_handoff(mode: int, words_per_block: int, rounds: int, sleep: int = 1, peer: int = 1,
+                       stride: int | None = None, stream=None) -> dict:
+    """Diagnostic hand-off probe: {ticks (100 MHz) of all rounds, stale payload
+    words, XCD id of each workgroup}."""
+    stride = words_per_block if stride is None else stride
+    nbytes = lib().moeq_probe_scratch_bytes(words_per_block, stride)
+    if nbytes < 0:
+        raise MoeqError(E_INVALID, "moeq_probe_scratch_bytes failed")
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ticks, bad = ctypes.c_int64(), ctypes.c_int64()
+    xcc = (ctypes.c_int32 * 1024)()
+    _check(lib().moeq_probe_handoff(mode, words_per_block, stride, rounds, sleep, peer, _ptr(scratch), nbytes,
+                                    ctypes.byref(ticks), ctypes.byref(bad), ctypes.cast(xcc, _P),
+                                    _stream(stream)))
+    n = torch.cuda.get_device_properties(0).multi_processor_count
+    return dict(ticks=ticks.value, stale=bad.value, xcc=list(xcc[:n]))
 
 
 def moe_read_device_status(workspace: torch.Tensor, stream=None) -> int:

@@ -338,4 +338,53 @@ int moe_read_device_status(void* workspace, void* stream, int32_t* status) {
   return ok();
 }
 
+int64_t moeq_probe_scratch_bytes(int words_per_block, int stride) {
+  const int nb = device_cus();
+  if (nb < 1 || words_per_block < 1 || stride < words_per_block) return -1;
+  return probe_scratch_bytes(nb, words_per_block, stride);
+}
+
+int moeq_probe_handoff(int mode, int words_per_block, int stride, int rounds, int sleep, int peer,
+                       void* scratch, int64_t scratch_bytes, int64_t* ticks, int64_t* mismatches,
+                       int32_t* xcc_ids, void* stream) {
+  const int nb = device_cus();
+  if (nb < 1) return fail(MOEQ_E_HIP, "no device");
+  if (nb > 1024) return fail(MOEQ_E_UNSUPPORTED, "the probe handles at most 1024 CUs");
+  if (mode < 0 || mode > 6) return fail(MOEQ_E_INVALID, "mode=%d outside [0, 6]", mode);
+  if (mode == 6 && words_per_block * nb > 4 * 512)
+    return fail(MOEQ_E_UNSUPPORTED, "pipelined polls handle at most 2048 words");
+  if (words_per_block < 1 || (int64_t)words_per_block * nb > probe_max_words())
+    return fail(MOEQ_E_UNSUPPORTED, "words_per_block=%d: the probe polls at most %d words", words_per_block,
+                probe_max_words());
+  if (stride < words_per_block) return fail(MOEQ_E_INVALID, "stride=%d < words_per_block", stride);
+  if (rounds < 1 || rounds > (1 << 24)) return fail(MOEQ_E_INVALID, "rounds=%d outside [1, 2^24]", rounds);
+  if (mode == 2 && (peer < 1 || peer >= nb)) return fail(MOEQ_E_INVALID, "peer=%d outside [1, %d)", peer, nb);
+  if ((mode == 4 || mode == 5) && (peer < 1 || peer > 64))
+    return fail(MOEQ_E_INVALID, "copies=%d outside [1, 64]", peer);
+  const int64_t need = probe_scratch_bytes(nb, words_per_block, stride);
+  if (!scratch || !ticks || scratch_bytes < need)
+    return fail(MOEQ_E_INVALID, "scratch (>= moeq_probe_scratch_bytes) and ticks must be given");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemsetAsync(scratch, 0, (size_t)need, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync probe scratch");
+  e = launch_probe(mode, words_per_block, stride, rounds, sleep, peer, scratch, nb, st);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "probe synchronise");
+  uint32_t ctl[4];
+  int32_t status = 0;
+  const char* s = static_cast<const char*>(scratch);
+  if ((e = hipMemcpy(ctl, s, sizeof ctl, hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(&status, s + 64, sizeof status, hipMemcpyDeviceToHost)) != hipSuccess ||
+      (e = hipMemcpy(ticks, s + 128, sizeof(int64_t), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "probe read-back");
+  if (xcc_ids && (e = hipMemcpy(xcc_ids, s + 4096, sizeof(int32_t) * nb, hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "probe read-back");
+  if (xcc_ids)
+    for (int i = 0; i < nb; ++i) xcc_ids[i] -= 1;
+  if (mismatches) *mismatches = ctl[3];
+  if (status != 0) return fail(MOEQ_E_DEVICE, "probe wait timed out (status %d)", status);
+  return ok();
+}
+
 }  // extern "C"

@@ -133,4 +133,11 @@ int stack_barrier_words();
 // hipErrorNotSupported: no persistent instantiation for this shape.
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream);
 
+// ------------------------------------------------ hand-off probe (diagnostic)
+int64_t probe_scratch_bytes(int nb, int W, int stride);
+int probe_max_words();
+hipError_t launch_probe(int mode, int W, int stride, int rounds, int sleep, int peer, void* scratch, int nb,
+                        hipStream_t stream);
+int device_cus();
+
 }  // namespace moeq

@@ -760,6 +760,8 @@ hipError_t launch_t(const StackArgs& a, int nb, size_t lds, hipStream_t stream) 
       dim3(nb), dim3(kThreads), params, (unsigned int)lds, stream);
 }
 
+}  // namespace
+
 int device_cus() {
   static int n = [] {
     int dev = 0, cus = 0;
@@ -769,6 +771,8 @@ int device_cus() {
   }();
   return n;
 }
+
+namespace {
 
 // Does instantiation <BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW> cover
 // this shape on nb blocks?
