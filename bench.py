@@ -71,6 +71,47 @@ def cores():
     return len(os.sched_getaffinity(0))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class OracleThreads:
+    """Sets the OpenMP thread count of the oracle library (libgomp is shared,
+    so omp_set_num_threads reaches the oracle's parallel loops)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.n = n
+        self.gomp = ctypes.CDLL("libgomp.so.1")
+
+    def __enter__(self):
+        self.prev = self.gomp.omp_get_max_threads()
+        self.gomp.omp_set_num_threads(self.n)
+        return self
+
+    def __exit__(self, *exc):
+        self.gomp.omp_set_num_threads(self.prev)
+
+
+TOL = 2e-3   # max |gpu - oracle| <= TOL * max |oracle|
+
+
+class ParityError(RuntimeError):
+    pass
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(gpu - ref).max() / np.abs(ref).max())
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline_layer(cfg, seconds: float):
@@ -89,9 +130,20 @@ def cpu_baseline_layer(cfg, seconds: float):
         oracle.run_layer(cfg, 0, x, want_intermediates=False, blob_cache=cache)
         busy += time.perf_counter() - t0
         done += T
+    # the same oracle on one thread, one token at a time
+    x1 = x[:1]
+    done1, busy1 = 0, 0.0
+    with OracleThreads(1):
+        while busy1 < min(4.0, seconds / 3):
+            t0 = time.perf_counter()
+            oracle.run_layer(cfg, 0, x1, want_intermediates=False, blob_cache=cache)
+            busy1 += time.perf_counter() - t0
+            done1 += 1
     return dict(value=round(done / busy, 3), unit="tokens/s", cores=min(T, n), kind="oracle",
+                cpu_model=cpu_model(), one_thread_value=round(done1 / busy1, 3),
                 sample=f"{done} tokens through one {cfg.name} layer in batches of {T} "
-                       f"({busy:.1f} s of oracle time; expert blobs generated beforehand)")
+                       f"({busy:.1f} s of oracle time; expert blobs generated beforehand); "
+                       f"one_thread_value: {done1} tokens one at a time on 1 thread ({busy1:.1f} s)")
 
 
 def cpu_baseline_stack(cfg, seconds: float):
@@ -120,11 +172,30 @@ def cpu_baseline_stack(cfg, seconds: float):
         if busy >= seconds:
             break
     per_token_layer = busy / (layers * T)
+    # one thread, one token, first layers of the stack
+    h1 = h[:1]
+    busy1, layers1 = 0.0, 0
+    with OracleThreads(1):
+        for l in range(cfg.layers):
+            wr = synth.router(cfg, l)
+            _, idx, _, _ = oracle.route(shape, wr, h1, cfg.top_k, oracle.layer_flags(cfg))
+            need = set(int(e) for e in np.unique(idx)) | set(range(cfg.n_experts, cfg.n_slots))
+            blobs = {e: synth.expert_blob(cfg, l, e) for e in need}
+            t0 = time.perf_counter()
+            out = oracle.moe_layer(shape, blobs, wr, h1, cfg.top_k, oracle.layer_flags(cfg),
+                                   want_intermediates=False)
+            busy1 += time.perf_counter() - t0
+            h1 = out["y"]
+            layers1 += 1
+            if busy1 >= min(4.0, seconds / 3):
+                break
     return dict(value=round(1.0 / (per_token_layer * cfg.layers), 4), unit="tokens/s",
-                cores=min(T, n), kind="oracle",
+                cores=min(T, n), kind="oracle", cpu_model=cpu_model(),
+                one_thread_value=round(1.0 / (busy1 / layers1 * cfg.layers), 4),
                 sample=f"{T} tokens through {layers} of {cfg.layers} layers ({busy:.1f} s of oracle "
                        f"time, blob generation excluded); tokens/s = 1 / (60 x measured "
-                       f"per-token-layer time)")
+                       f"per-token-layer time); one_thread_value: 1 token through {layers1} layers "
+                       f"on 1 thread ({busy1:.1f} s), scaled the same way")
 
 
 # -------------------------------------------------------------- workloads
@@ -172,6 +243,50 @@ def setup_layers(cfg, n_layers, dev, stream):
     return shape, table, routers, bf16
 
 
+def parity_stack(cfg, shape, table, rt, ws, h0, stream):
+    """One token through all layers with traces, checked against the fp64
+    oracle teacher-forced on the GPU's own layer inputs: top-K exact at every
+    layer, outputs within TOL on a spread of layers."""
+    import ctypes
+    import torch
+    import oracle
+    import quantized_expert_gemv_router_amd as q
+
+    L, K, H = cfg.layers, cfg.top_k, cfg.hidden
+    h = h0.clone()
+    tk = torch.empty((L, 1, K), dtype=torch.int32, device=h.device)
+    hk = torch.empty((L, 1, H), dtype=torch.float32, device=h.device)
+    rc = q.lib().moe_expert_stack_decode(ctypes.byref(shape), table.view(), rt.ptr(), 0, L, 1, K, 0,
+                                         h.data_ptr(), tk.data_ptr(), hk.data_ptr(), ws.data_ptr(),
+                                         stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(q.moeq_last_error())
+    status = q.moe_read_device_status(ws, stream)
+    if status != 0:
+        raise ParityError(f"device status {status} in the parity run")
+    idx = tk.cpu().numpy()[:, 0, :]
+    hs = hk.cpu().numpy()[:, 0, :].astype(np.float64)
+    outs = [hs[l + 1] for l in range(L - 1)] + [h.cpu().numpy()[0].astype(np.float64)]
+    sh = oracle.shape_of(cfg)
+    flags = oracle.layer_flags(cfg)
+    import synth
+    for l in range(L):
+        _, ref_idx, _, _ = oracle.route(sh, synth.router(cfg, l), hs[l][None, :], K, flags)
+        if not np.array_equal(ref_idx[0], idx[l]):
+            raise ParityError(f"layer {l}: GPU top-K {idx[l].tolist()} != oracle {ref_idx[0].tolist()}")
+    checked = sorted(set([0, 1, L // 4, L // 2, 3 * L // 4, L - 2, L - 1]))
+    worst = 0.0
+    for l in checked:
+        exp = oracle.run_layer(cfg, l, hs[l][None, :], want_intermediates=False)
+        e = rel_err(outs[l], exp["y"][0])
+        worst = max(worst, e)
+        if not e <= TOL:
+            raise ParityError(f"layer {l}: output rel err {e:.3e} > {TOL}")
+    return {"topk_exact_layers": L, "layers": L, "outputs_checked_layers": checked,
+            "max_rel_err": float(f"{worst:.3e}"), "tol": TOL,
+            "reference": "fp64 oracle, teacher-forced on the GPU's layer inputs"}
+
+
 def run_stack(args, cfg, dev, stream):
     import torch
     import quantized_expert_gemv_router_amd as q
@@ -187,6 +302,9 @@ def run_stack(args, cfg, dev, stream):
     tks = torch.empty((total, cfg.layers, 1, K), dtype=torch.int32, device=dev)
     ws = q.new_workspace(shape, 1, K, dev)
     flags = q.F_STACK_LAYERWISE if args.layerwise else 0
+    log("[bench] parity: one token through all layers against the fp64 oracle")
+    parity = parity_stack(cfg, shape, table, rt, ws, pool[0], stream)
+    log(f"[bench] parity ok: {parity}")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -246,7 +364,44 @@ def run_stack(args, cfg, dev, stream):
     })
     rec["config"].update(layers_per_step=cfg.layers, resident_gb=round(
         cfg.layers * cfg.n_slots * cfg.expert_bytes / 1e9, 1))
+    rec["parity"] = parity
     return rec
+
+
+def parity_prefill(cfg, shape, table, rt, stream, n_sample=16):
+    """Layer 0 of the prefill on its own: top-K of every token against the
+    fp64 oracle router, outputs of a seeded token sample against the oracle
+    layer."""
+    import torch
+    import oracle
+    import quantized_expert_gemv_router_amd as q
+    import synth
+
+    T, K = cfg.tokens, cfg.top_k
+    x64 = synth.bf16_to_f64(synth.tokens(cfg, 3000, T))
+    h = torch.from_numpy(x64.astype(np.float32)).to("cuda")
+    ws = q.new_prefill_workspace(shape, T, K, h.device)
+    tk = q.moe_expert_stack_prefill(shape, table, rt, h, K, layer0=0, L=1, workspace=ws, trace=True,
+                                    stream=stream)
+    status = q.moe_read_device_status(ws, stream)
+    if status != 0:
+        raise ParityError(f"device status {status} in the prefill parity run")
+    idx = tk.cpu().numpy()[0]
+    y = h.cpu().numpy().astype(np.float64)
+    sh = oracle.shape_of(cfg)
+    _, ref_idx, _, _ = oracle.route(sh, synth.router(cfg, 0), x64, K, oracle.layer_flags(cfg))
+    bad = np.flatnonzero(~np.all(ref_idx == idx, axis=1))
+    if bad.size:
+        raise ParityError(f"prefill layer 0: top-K differs on {bad.size} tokens (first {bad[:5].tolist()})")
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(T, size=min(n_sample, T), replace=False))
+    exp = oracle.run_layer(cfg, 0, x64[sample], want_intermediates=False)
+    e = rel_err(y[sample], exp["y"])
+    if not e <= TOL:
+        raise ParityError(f"prefill layer 0: output rel err {e:.3e} > {TOL}")
+    del ws
+    return {"topk_exact_tokens": int(T), "layer": 0, "outputs_checked_tokens": sample.tolist(),
+            "max_rel_err": float(f"{e:.3e}"), "tol": TOL, "reference": "fp64 oracle"}
 
 
 def run_prefill(args, cfg, dev, stream):
@@ -263,6 +418,9 @@ def run_prefill(args, cfg, dev, stream):
     sets = [torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, 3000 + i, T)).astype(np.float32)).to(dev)
             for i in range(min(total, 4))]
     hs = [sets[s % len(sets)].clone() for s in range(total)]
+    log("[bench] parity: prefill layer 0 against the fp64 oracle")
+    parity = parity_prefill(cfg, shape, table, rt, stream)
+    log(f"[bench] parity ok: {parity}")
     ws = q.new_prefill_workspace(shape, T, K, dev)
     tk = torch.empty((cfg.layers, T, K), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
@@ -324,6 +482,7 @@ def run_prefill(args, cfg, dev, stream):
     })
     rec["config"].update(layers_per_step=cfg.layers, experts_touched_per_layer=float(touched.mean()),
                          resident_gb=round(cfg.layers * cfg.n_slots * cfg.expert_bytes / 1e9, 1))
+    rec["parity"] = parity
     return rec
 
 
@@ -346,6 +505,27 @@ def run_layer_workload(args, cfg, dev, stream):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
+
+    # parity: instance 0, token set 0, through the same three calls
+    import oracle
+    log("[bench] parity: one step against the fp64 oracle")
+    x0 = pool[0]
+    q.moe_router_topk(shape, x0, routers[0], K, 0, None, ws, out=(idx_all[0], w, sw), stream=stream)
+    q.moe_q4_expert_gemv(shape, table, 0, x0, idx_all[0], K, 0, ws, gu, stream=stream)
+    q.moe_swiglu_down_combine(shape, table, 0, gu, idx_all[0], w, sw, x0, K, ws, y, stream=stream)
+    status = q.moe_read_device_status(ws, stream)
+    if status != 0:
+        raise ParityError(f"device status {status} in the parity run")
+    x64 = synth.bf16_to_f64(synth.tokens(cfg, 100, T))
+    exp = oracle.run_layer(cfg, 0, x64, want_intermediates=False)
+    if not np.array_equal(idx_all[0].cpu().numpy(), exp["idx"]):
+        raise ParityError("top-K differs from the oracle")
+    e = rel_err(y.cpu().numpy(), exp["y"])
+    if not e <= TOL:
+        raise ParityError(f"output rel err {e:.3e} > {TOL}")
+    parity = {"topk_exact_tokens": T, "max_rel_err": float(f"{e:.3e}"), "tol": TOL,
+              "reference": "fp64 oracle, same inputs"}
+    log(f"[bench] parity ok: {parity}")
 
     def step(s, slot=None):
         l = s % n_inst
@@ -394,6 +574,7 @@ def run_layer_workload(args, cfg, dev, stream):
                      "bytes_per_launch": int(gemv_bytes)},
     })
     rec["config"].update(layers_per_step=1, layer_instances=n_inst)
+    rec["parity"] = parity
     return rec
 
 

@@ -93,9 +93,9 @@ WorkspaceLayout workspace_layout(const moeq_shape& s, int T, int k) {
   w.dbuf = w.logits + align_up((int64_t)T * (s.n_experts + 1) * 8);
   w.st_bar = w.dbuf + align_up((int64_t)T * KS * s.hidden * 4);
   w.st_logits = w.st_bar + align_up((int64_t)stack_barrier_words() * 4);
-  w.st_abuf = w.st_logits + align_up((int64_t)s.n_experts * 16);
-  w.st_h = w.st_abuf + align_up(KS * s.inter * 8);
-  w.st_idx = w.st_h + align_up((int64_t)s.hidden * 8);
+  w.st_abuf = w.st_logits + align_up((int64_t)2 * s.n_experts * 16);
+  w.st_h = w.st_abuf + align_up(2 * KS * s.inter * 8);
+  w.st_idx = w.st_h + align_up((int64_t)2 * s.hidden * 8);
   w.st_w = w.st_idx + align_up((int64_t)T * k * 4);
   w.st_sw = w.st_w + align_up((int64_t)T * k * 4);
   w.st_gu = w.st_sw + align_up((int64_t)T * 4);

@@ -23,8 +23,9 @@ inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; 
 //   [0, 4096)        u32 words: [0] router arrival counter, [1] status word
 //   logits           f64 [T][E + 1]   (last column: shared-gate logit)
 //   dbuf             f32 [T][k + S][H] per-slot down outputs (multi-token)
-//   stack area       barrier words, tagged words (fp64 logit halves [E][2],
-//                    activations [k + S][I], hidden state [H]), and the
+//   stack area       barrier words, tagged words double-buffered by layer
+//                    parity (fp64 logit halves [2][E][2], activations
+//                    [2][k + S][I], hidden state [2][H]), and the
 //                    per-layer path's routing
 //                    (idx [T][k], w [T][k], shared w [T]) and gate_up
 //                    [T][k + S][2][I]
@@ -121,9 +122,9 @@ struct StackArgs {
   float* h;                        // [H] in/out
   int32_t* topk_trace;             // [L][K] or null
   float* h_trace;                  // [L][H] or null
-  uint64_t* lwords;                // [E][2] tagged halves of the fp64 logits
-  uint64_t* awords;                // [K + S][I] tagged activations
-  uint64_t* hwords;                // [H] tagged hidden state between layers
+  uint64_t* lwords;                // [2][E][2] tagged halves of the fp64 logits (by layer parity)
+  uint64_t* awords;                // [2][K + S][I] tagged activations
+  uint64_t* hwords;                // [2][H] tagged hidden state between layers
   uint32_t* bar;                   // barrier counters (stack_barrier_words())
   int32_t* status;
   int64_t* clocks;                 // diagnostic: [L][kStackClockEvents] wall-clock stamps of block 0, or null

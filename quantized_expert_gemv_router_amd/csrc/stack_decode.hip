@@ -23,8 +23,13 @@
 //            (threshold on the keys' high words, every wave keeps its own
 //            copy of the selection), then streams its gate/up rows
 //   a:       each block publishes silu(g)*u for its gate/up rows; every block
-//            polls all activations of the K + S slots, then its down rows
-//            and the combine with the residual.
+//            polls all activations, then applies its down rows and the
+//            combine with the residual.  The shared expert does not wait
+//            for routing: its gate/up rows are applied and its activations
+//            published while the logits travel, and every block applies its
+//            down rows (requested with the previous layer's prefetch) before
+//            it polls the routed slots' activations, so only the K routed
+//            slots' activations and down rows sit after the last hand-off.
 // Loads are issued as early as their addresses are known and their data
 // does not compete with loads on the critical path: the router and
 // shared-expert pointers of every layer are cached in LDS at start; the
@@ -119,9 +124,14 @@ struct GridBarrier {
 // high half.  Readers poll the word until the tag they expect shows up, so
 // the word is its own flag and no fence or grid barrier sits between the
 // writer and its readers.  Each word has one writing block for the whole
-// launch, and a block writes layer l+1's value only after every block has
-// read layer l's (each layer's three handoffs form a chain), so a reader
-// never sees a tag newer than the one it waits for.
+// launch.  The words are double-buffered by layer parity, so a word read
+// for layer l is next overwritten with layer l+2's value.  Every block owns
+// at least one row of h (the launcher requires H >= blocks), and a block
+// publishes its h rows of layer l+1 only after it has read everything of
+// layer l (h, logits, activations); every writer of a layer-(l+2) value has
+// first polled all of layer l+1's h.  So no word is overwritten before
+// every block has read it, and a reader never sees a tag newer than the
+// one it waits for.
 __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t payload, uint32_t tag) {
   st_agent(p, ((uint64_t)tag << 32) | payload);
 }
@@ -258,8 +268,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t wr[CPLR][HW];
   u32x4 qg[RPWG][CPLG];
   uint32_t sg[RPWG][CPLG];
-  u32x4 qd[STEPSD][CPLD];
+  u32x4 qd[STEPSD][CPLD];          // routed slots' down rows
   uint32_t sd[STEPSD][CPLD];
+  u32x4 qsh[CPLD];                 // the shared expert's down rows
+  uint32_t ssh[CPLD];
   const uint8_t* tnext[kTblPer];   // this layer's pointer-table row, in flight to LDS
 
   // gate/up rows: task t = m * kWaves + wave, the shared experts' rows first,
@@ -370,40 +382,45 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     }
   };
   // down rows: a wave owns RPSD of the block's output rows (LPRD lanes
-  // each), for every slot: step s is slot s, so the combine of a row stays
-  // in the wave
-  rsrc_t dsrc[STEPSD];       // slot s's expert blob, or an empty range
-  auto down_row = [&](int s, int& j, int& row) {
-    j = s;
+  // each), for every slot: step s is routed slot s, so the combine of a row
+  // stays in the wave; the shared expert's rows have their own registers
+  rsrc_t dsrc[STEPSD];       // routed slot s's expert blob, or an empty range
+  const uint32_t blob_bytes_all = 3u * (uint32_t)H * I * BITS / 8 + 3u * (uint32_t)(H / 64) * I * 4u;
+  auto down_row = [&](int& row) {
     const int i = wave * RPSD + lane / LPRD;
     row = i < RD ? b + NB * i : H;   // H: no row
   };
   auto plan_down = [&]() {
-    const uint32_t blob_bytes = 3u * (uint32_t)H * I * BITS / 8 + 3u * (uint32_t)(H / 64) * I * 4u;
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
-      const uint8_t* blob = s < KS ? uniform_ptr(eblob[s]) : nullptr;
-      dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes : 0u);
+      const uint8_t* blob = s < K ? uniform_ptr(eblob[s]) : nullptr;
+      dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u);
     }
   };
-  auto issue_down = [&]() {
+  auto down_load = [&](rsrc_t src, u32x4 (&q)[CPLD], uint32_t (&sbw)[CPLD]) {
     const uint32_t row_bytes = (uint32_t)I * BITS / 8;
     const uint32_t gpr = I / 64;
     const uint32_t q_off = 2u * (uint32_t)H * I * BITS / 8;
     const uint32_t sb_off = 3u * (uint32_t)H * I * BITS / 8 + 2u * (uint32_t)H * (I / 64) * 4u;
     const int sub = lane % LPRD;
+    int row;
+    down_row(row);
+    if (row >= H) row = 0;   // padding lane: re-reads a valid row, skipped by the dots
 #pragma unroll
-    for (int s = 0; s < STEPSD; ++s) {
-      int j, row;
-      down_row(s, j, row);
-      if (row >= H) row = 0;   // padding lane: re-reads a valid row, skipped by the dots
-#pragma unroll
-      for (int c = 0; c < CPLD; ++c) {
-        const int cc = min(sub + LPRD * c, nchD - 1);
-        qd[s][c] = load_rsrc_b128(dsrc[s], q_off + (uint32_t)row * row_bytes + (uint32_t)cc * 16u);
-        sd[s][c] = load_rsrc_b32(dsrc[s], sb_off + ((uint32_t)row * gpr + (uint32_t)(cc * PC / 64)) * 4u);
-      }
+    for (int c = 0; c < CPLD; ++c) {
+      const int cc = min(sub + LPRD * c, nchD - 1);
+      q[c] = load_rsrc_b128(src, q_off + (uint32_t)row * row_bytes + (uint32_t)cc * 16u);
+      sbw[c] = load_rsrc_b32(src, sb_off + ((uint32_t)row * gpr + (uint32_t)(cc * PC / 64)) * 4u);
     }
+  };
+  auto issue_down = [&]() {
+#pragma unroll
+    for (int s = 0; s < STEPSD; ++s) down_load(dsrc[s], qd[s], sd[s]);
+    issue_fence();
+  };
+  auto issue_down_shared = [&]() {   // eblob[K] holds the layer's shared expert
+    const uint8_t* blob = S > 0 ? uniform_ptr(eblob[min(K, KS - 1)]) : nullptr;
+    down_load(make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u), qsh, ssh);
     issue_fence();
   };
   auto load_tbl_row = [&](int layer) {   // into registers; stored to LDS after the next barrier
@@ -441,17 +458,22 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   if (tid == 0) fail_flag = 0;
   // this block's tagged words start at tag 0 (no layer's); one grid
   // barrier puts every clear before any layer's write
-  for (int j = tid; j < RW; j += kThreads) {
-    const int r = b + NB * j;
-    if (r < E) { st_agent(a.lwords + 2 * r, uint64_t{0}); st_agent(a.lwords + 2 * r + 1, uint64_t{0}); }
-  }
-  for (int t = tid; t < KS * RG; t += kThreads) {
-    const int j = t / RG, row = b + NB * (t - j * RG);
-    if (row < I) st_agent(a.awords + (int64_t)j * I + row, uint64_t{0});
-  }
-  for (int i = tid; i < RD; i += kThreads) {
-    const int row = b + NB * i;
-    if (row < H) st_agent(a.hwords + row, uint64_t{0});
+  for (int par = 0; par < 2; ++par) {
+    uint64_t* lw = a.lwords + (int64_t)par * 2 * E;
+    uint64_t* aw = a.awords + (int64_t)par * KS * I;
+    uint64_t* hw = a.hwords + (int64_t)par * H;
+    for (int j = tid; j < RW; j += kThreads) {
+      const int r = b + NB * j;
+      if (r < E) { st_agent(lw + 2 * r, uint64_t{0}); st_agent(lw + 2 * r + 1, uint64_t{0}); }
+    }
+    for (int t = tid; t < KS * RG; t += kThreads) {
+      const int j = t / RG, row = b + NB * (t - j * RG);
+      if (row < I) st_agent(aw + (int64_t)j * I + row, uint64_t{0});
+    }
+    for (int i = tid; i < RD; i += kThreads) {
+      const int row = b + NB * i;
+      if (row < H) st_agent(hw + row, uint64_t{0});
+    }
   }
   if (tid < S) eblob[K + tid] = shp[0];
   if (!bar.sync(a.status, &bar_flag)) return;
@@ -460,6 +482,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   plan_gu(K, KS);
   issue_router();
   issue_gu();
+  issue_down_shared();
   uint32_t* const abort_word = a.bar + 32 * (1 + kGroups);
   auto block_failed = [&](bool ok) -> bool {   // whole block
     if (!ok) fail_flag = 1;
@@ -480,6 +503,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       lane = tid & 63;
     }
     stamp(li, 0);
+    const int par = li & 1;
+    const uint64_t* hw_in = a.hwords + (int64_t)par * H;
+    uint64_t* hw_out = a.hwords + (int64_t)(par ^ 1) * H;
+    uint64_t* lw = a.lwords + (int64_t)par * 2 * E;
+    uint64_t* aw = a.awords + (int64_t)par * KS * I;
     // ------------------------------------------------------------ phase R
     // h -> LDS with sum of squares (fp64) and max |h|
     {
@@ -500,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           hw[2 * i] = hw[2 * i + 1] = 0u;
           if (2 * (tid + i * kThreads) < H) valid |= 3u << (2 * i);
         }
-        ok = take_tagged<2 * HW>(a.hwords, [&](int i) { return 2 * (tid + (i >> 1) * kThreads) + (i & 1); },
+        ok = take_tagged<2 * HW>(hw_in, [&](int i) { return 2 * (tid + (i >> 1) * kThreads) + (i & 1); },
                                  valid, (uint32_t)li, hw, abort_word, a.status);
 #pragma unroll
         for (int i = 0; i < HW; ++i) hv[i] = ((uint64_t)hw[2 * i + 1] << 32) | hw[2 * i];
@@ -554,8 +582,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       for (int w = 0; w < kWaves; ++w) d += rpart[tid * kWaves + w];
       const int r = b + NB * tid;
       const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
-      put_tagged(a.lwords + 2 * r, (uint32_t)bits, tag);
-      put_tagged(a.lwords + 2 * r + 1, (uint32_t)(bits >> 32), tag);
+      put_tagged(lw + 2 * r, (uint32_t)bits, tag);
+      put_tagged(lw + 2 * r + 1, (uint32_t)(bits >> 32), tag);
     }
     // xhat -> fp16 pairs, one packed word per thread; the norm and the
     // rescale come from the h pass above, so no further reductions
@@ -582,6 +610,16 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     stamp(li, 2);
     gu_dots(K, KS);                 // the shared expert's rows are already here
     stamp(li, 3);
+    if (S > 0) {                    // publish its activations before routing is known
+      block_sync_lds();
+      for (int t = tid; t < RG; t += kThreads) {
+        const int row = b + NB * t;
+        if (row < I) {
+          const float g = gres[(K * 2) * RG + t], u = gres[(K * 2 + 1) * RG + t];
+          put_tagged(aw + (int64_t)K * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
+        }
+      }
+    }
     stamp(li, 4);
 
     // ------------------------------------------------------------ phase G
@@ -591,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int e0 = 0; e0 < E; e0 += kThreads) {   // one logit (two words) per thread per pass
       const int e = e0 + tid;
       uint32_t w[2] = {0u, 0u};
-      const bool ok = take_tagged<2>(a.lwords + 2 * e, [](int i) { return i; }, e < E ? 3u : 0u, tag, w,
+      const bool ok = take_tagged<2>(lw + 2 * e, [](int i) { return i; }, e < E ? 3u : 0u, tag, w,
                                      abort_word, a.status);
       if (e < E) {
         const double v = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
@@ -642,12 +680,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     stamp0(li, 13);
     __syncthreads();
     stamp(li, 6);
-    plan_down();                     // every slot's down rows (eblob is complete now)
-    for (int t = tid; t < KS * RG; t += kThreads) {
+    plan_down();                     // routed slots' down rows (eblob is complete now)
+    for (int t = tid; t < K * RG; t += kThreads) {
       const int j = t / RG, i = t - j * RG, row = b + NB * i;
       if (row < I) {
         const float g = gres[(j * 2) * RG + i], u = gres[(j * 2 + 1) * RG + i];
-        put_tagged(a.awords + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
+        put_tagged(aw + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
       }
     }
     // down rows of every slot, in flight while the activations arrive (not
@@ -658,27 +696,27 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     stamp(li, 8);
 
     // ------------------------------------------------------------ phase D
-    // activations: one packed word of one slot per thread, staged with a
-    // power-of-two scale per 16-byte chunk (the four threads of a chunk
-    // agree on it with two lane shuffles), so staging needs no block-wide
-    // maximum; the one block barrier below also settles a failed poll
-    {
+    // activations of slots [s0, s0 + ns): one packed word of one slot per
+    // thread, staged with a power-of-two scale per 16-byte chunk (the four
+    // threads of a chunk agree on it with two lane shuffles), so staging
+    // needs no block-wide maximum; the block barrier after it also settles
+    // a failed poll
+    auto take_acts = [&](int s0, int ns) -> bool {
       const int nwa = I / PW;
-      const int total = KS * nwa;
+      const int total = ns * nwa;
       bool got_all = true;
       for (int t0 = 0; t0 < total; t0 += kThreads) {
         const int t = t0 + tid;
         const bool ok = t < total;
-        const int m = ok ? t / nwa : 0, w = ok ? t - m * nwa : 0;
+        const int m = ok ? s0 + t / nwa : s0, w = ok ? t - (m - s0) * nwa : 0;
         float v[PW];
         uint32_t raw[PW];
 #pragma unroll
         for (int j = 0; j < PW; ++j) raw[j] = 0u;
-        const uint64_t* src = a.awords + (int64_t)m * I + (int64_t)w * PW;
+        const uint64_t* src = aw + (int64_t)m * I + (int64_t)w * PW;
         const bool got = take_tagged<PW>(src, [](int j) { return j; }, ok ? (uint32_t)((1ull << PW) - 1) : 0u,
                                          tag, raw, abort_word, a.status);
         got_all = got_all && got;
-        stamp0(li, 16);
         float lm = 0.0f;
 #pragma unroll
         for (int j = 0; j < PW; ++j) {
@@ -688,45 +726,55 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         lm = fmaxf(lm, __shfl_xor(lm, 1, 64));
         lm = fmaxf(lm, __shfl_xor(lm, 2, 64));
         const float p = pow2_stage_factor(lm);
-        float2 s = make_float2(0.0f, 0.0f);
-        if (ok) s = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w, nchD);
-        s = quad_sum(s);
+        float2 sums = make_float2(0.0f, 0.0f);
+        if (ok) sums = stage_word<BITS>(v, p, ap + (int64_t)m * (I / 2), w, nchD);
+        sums = quad_sum(sums);
         if (ok && (tid & 3) == 0)
-          *reinterpret_cast<float4*>(as + kActSums * (m * nchD + (w >> 2))) = make_float4(s.x, s.y, 1.0f / p, 0.0f);
+          *reinterpret_cast<float4*>(as + kActSums * (m * nchD + (w >> 2))) =
+              make_float4(sums.x, sums.y, 1.0f / p, 0.0f);
       }
-      if (block_failed(got_all)) return;
-      stamp0(li, 17);
-    }
-    stamp(li, 9);
-    {
-      // down rows of every slot and the combine, in registers: lane LPRD-1
-      // of each row group ends with the row's h
+      return !block_failed(got_all);
+    };
+    // one slot's down rows against its staged activations: the row's sum is
+    // valid in lane LPRD-1 of each row group
+    auto down_dot = [&](int s, const u32x4 (&q)[CPLD], const uint32_t (&sbw)[CPLD], bool ok) -> float {
       const int sub = lane % LPRD;
-      const int i = wave * RPSD + lane / LPRD;
-      const int row = b + NB * i;
-      const bool ok = i < RD && row < H;
-      float acc = ok ? hs[row] : 0.0f;
+      float part = 0.0f;
 #pragma unroll
-      for (int s = 0; s < STEPSD; ++s) {
-        if (s >= KS) break;
-        float part = 0.0f;
+      for (int c = 0; c < CPLD; ++c) {
+        const int cc = min(sub + LPRD * c, nchD - 1);
+        const XChunk<BITS> x = load_xchunk<BITS>(ap + (int64_t)s * (I / 2), cc, nchD);
+        const float4 xsm = *reinterpret_cast<const float4*>(as + kActSums * (s * nchD + cc));
+        if (ok && sub + LPRD * c < nchD)
+          part += chunk_affine(chunk_dot<BITS>(q[c], x), sbw[c], make_float2(xsm.x, xsm.y)) * xsm.z;
+      }
+      return group_sum_dpp<LPRD>(part);
+    };
+    const int sub = lane % LPRD;
+    const int di = wave * RPSD + lane / LPRD;
+    const int drow = b + NB * di;
+    const bool dok = di < RD && drow < H;
+    float acc = dok ? hs[drow] : 0.0f;
+    // the shared expert first: its activations were published in phase R
+    if (S > 0) {
+      if (!take_acts(K, 1)) return;
+      acc += down_dot(K, qsh, ssh, dok);
+    }
+    stamp0(li, 16);
+    // the routed slots
+    if (!take_acts(0, K)) return;
+    stamp0(li, 17);
+    stamp(li, 9);
 #pragma unroll
-        for (int c = 0; c < CPLD; ++c) {
-          const int cc = min(sub + LPRD * c, nchD - 1);
-          const XChunk<BITS> x = load_xchunk<BITS>(ap + (int64_t)s * (I / 2), cc, nchD);
-          const float4 xsm = *reinterpret_cast<const float4*>(as + kActSums * (s * nchD + cc));
-          if (ok && sub + LPRD * c < nchD)
-            part += chunk_affine(chunk_dot<BITS>(qd[s][c], x), sd[s][c], make_float2(xsm.x, xsm.y)) * xsm.z;
-        }
-        const float d = group_sum_dpp<LPRD>(part);
-        acc = fmaf(s < K ? selw[s] : 1.0f, d, acc);   // slot order: routed, then shared
-      }
-      stamp0(li, 18);
-      if (ok && sub == LPRD - 1) {
-        if (a.h_trace) a.h_trace[(int64_t)li * H + row] = hs[row];
-        if (li + 1 == L) a.h[row] = acc;   // complete when the launch ends
-        else put_tagged(a.hwords + row, __float_as_uint(acc), tag);
-      }
+    for (int s = 0; s < STEPSD; ++s) {
+      if (s >= K) break;
+      acc = fmaf(selw[s], down_dot(s, qd[s], sd[s], dok), acc);
+    }
+    stamp0(li, 18);
+    if (dok && sub == LPRD - 1) {
+      if (a.h_trace) a.h_trace[(int64_t)li * H + drow] = hs[drow];
+      if (li + 1 == L) a.h[drow] = acc;   // complete when the launch ends
+      else put_tagged(hw_out + drow, __float_as_uint(acc), tag);
     }
     stamp(li, 10);
     if (li + 1 == L) break;
@@ -738,6 +786,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     plan_gu(K, KS);
     issue_router();
     issue_gu();
+    issue_down_shared();
     stamp0(li, 11);
   }
   if (a.clocks && b == 0) {   // stamps were kept in LDS so taking them adds no memory traffic
@@ -777,7 +826,7 @@ namespace {
 // Does instantiation <BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW> cover
 // this shape on nb blocks?
 struct Geometry {
-  int nb, rw, H, I, E, S, KS, bits;
+  int nb, rw, H, I, E, S, K, KS, bits;
   bool fits(int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW) const {
     if (bits != BITS) return false;
     // expert blobs are addressed with 32-bit byte offsets
@@ -790,7 +839,8 @@ struct Geometry {
     const int nchd = I / PC;
     if (nchd > LPRD * CPLD) return false;
     if (KS * (I * BITS / 32) > kThreads) return false;   // one activation word per thread
-    if (KS > STEPSD) return false;                 // one down step per slot
+    if (K > STEPSD) return false;                  // one down step per routed slot
+    if (H < nb) return false;                      // every block owns a row of h (hand-off safety)
     if (RD > kWaves * (64 / LPRD)) return false;   // every output row owned by a wave
     if (H > 2 * kThreads * HW) return false;
     if (E + S > kTblPer * kThreads) return false;
@@ -820,11 +870,11 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   const size_t lds =
       (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD, a.clocks ? a.L * kStackClockEvents : 0).total;
   if (lds > 96 * 1024) return hipErrorNotSupported;
-  const Geometry g{nb, rw, a.H, a.I, a.E, a.S, KS, a.bits};
+  const Geometry g{nb, rw, a.H, a.I, a.E, a.S, a.K, KS, a.bits};
   // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,
   // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
-  if (g.fits(4, 2, 2, 4, 32, 1, 4, 4)) return launch_t<4, 2, 2, 4, 32, 1, 4, 4>(a, nb, lds, stream);
-  if (g.fits(2, 2, 1, 5, 32, 1, 5, 4)) return launch_t<2, 2, 1, 5, 32, 1, 5, 4>(a, nb, lds, stream);
+  if (g.fits(4, 2, 2, 4, 32, 1, 3, 4)) return launch_t<4, 2, 2, 4, 32, 1, 3, 4>(a, nb, lds, stream);
+  if (g.fits(2, 2, 1, 5, 32, 1, 4, 4)) return launch_t<2, 2, 1, 5, 32, 1, 4, 4>(a, nb, lds, stream);
   if (g.fits(4, 1, 1, 1, 64, 1, 3, 1)) return launch_t<4, 1, 1, 1, 64, 1, 3, 1>(a, nb, lds, stream);
   return hipErrorNotSupported;
 }
