@@ -274,17 +274,27 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t ssh[CPLD];
   const uint8_t* tnext[kTblPer];   // this layer's pointer-table row, in flight to LDS
 
-  // gate/up rows: task t = m * kWaves + wave, the shared experts' rows first,
-  // then the routed ones, so every wave takes part in both phases
+  // gate/up rows: register slot m = 0 holds the shared expert's rows (task
+  // u = wave), slots m >= 1 the routed slots' (task u = (m - 1) * kWaves +
+  // wave, slot u / 2RG); within a slot, task u % 2RG is section (gate, up)
+  // and row b + NB * i.  The shared rows are requested a layer ahead and
+  // stay in their registers while the routed rows are requested.
   auto gu_task = [&](int m, int& j, int& sec, int& row) -> bool {
-    const int t = m * kWaves + wave, nsh = S * 2 * RG;
-    const bool shared = t < nsh;
-    const int u = shared ? t : t - nsh;
-    j = (shared ? K : 0) + u / (2 * RG);
+    int u;
+    bool valid;
+    if (m == 0) {
+      u = wave;
+      j = K;
+      valid = S > 0 && u < 2 * RG;
+    } else {
+      u = (m - 1) * kWaves + wave;
+      j = u / (2 * RG);
+      valid = j < K;
+    }
     const int tj = u % (2 * RG);
     sec = tj / RG;
     row = b + NB * (tj % RG);
-    return (shared ? j < KS : j < K) && row < I;
+    return valid && row < I;
   };
   // Loads are planned (every LDS read they need) before any is issued: an
   // LDS read between loads makes the compiler wait for the loads in flight.
@@ -307,21 +317,22 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 #pragma unroll
       for (int i = 0; i < HW; ++i) wr[k][i] = load_rsrc_b32(rplan[k], (uint32_t)(tid + i * kThreads) * 4u);
   };
-  // gate/up rows of the tasks whose slot is in [jlo, jhi); gu_task is
-  // uniform over a wave, so each row is one scalar buffer resource
+  // gate/up rows of the register slots m in [mlo, mhi) (constants at every
+  // call); gu_task is uniform over a wave, so each row is one scalar buffer
+  // resource
   rsrc_t gq[RPWG];               // the task's expert blob, or an empty range: no task
   uint32_t gqo[RPWG], gso[RPWG]; // byte offsets of its quantized row and scale/bias words
   bool ghave[RPWG];
-  auto plan_gu = [&](int jlo, int jhi) {
+  auto plan_gu = [&](int mlo, int mhi) {
     const uint32_t row_bytes = (uint32_t)H * BITS / 8;
     const uint32_t gpr = H / 64;
     const uint32_t sb_off = 3u * (uint32_t)H * I * BITS / 8;
     const uint32_t blob_bytes = sb_off + 3u * (uint32_t)(H / 64) * I * 4u;
 #pragma unroll
     for (int m = 0; m < RPWG; ++m) {
+      if (m < mlo || m >= mhi) continue;
       int j, sec, row;
-      const bool ok = gu_task(m, j, sec, row);
-      ghave[m] = ok && j >= jlo && j < jhi;
+      ghave[m] = gu_task(m, j, sec, row);
       // routed slots: this wave's own copy of the selection; the shared one
       // from eblob.  A missing expert (null) loads nothing.
       const int jj = ghave[m] ? j : K;
@@ -336,25 +347,26 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   };
   // chunk-major: the dots take one staged x chunk at a time against every
   // row of the wave, so each chunk is read from LDS once
-  auto issue_gu = [&]() {
+  auto issue_gu = [&](int mlo, int mhi) {
 #pragma unroll
     for (int c = 0; c < CPLG; ++c) {
       const int cc = min(lane + 64 * c, nchG - 1);   // past the row: the dots skip it
 #pragma unroll
       for (int m = 0; m < RPWG; ++m) {
+        if (m < mlo || m >= mhi) continue;
         qg[m][c] = load_rsrc_b128(gq[m], gqo[m] + (uint32_t)cc * 16u);
         sg[m][c] = load_rsrc_b32(gq[m], gso[m] + (uint32_t)(cc * PC / 64) * 4u);
       }
     }
     issue_fence();
   };
-  auto gu_dots = [&](int jlo, int jhi) {
+  auto gu_dots = [&](int mlo, int mhi) {
     bool live[RPWG];
     bool any = false;
 #pragma unroll
     for (int m = 0; m < RPWG; ++m) {
       int j, sec, row;
-      live[m] = gu_task(m, j, sec, row) && j >= jlo && j < jhi;
+      live[m] = m >= mlo && m < mhi && gu_task(m, j, sec, row);
       any = any || live[m];
     }
     if (!any) return;
@@ -479,9 +491,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   if (!bar.sync(a.status, &bar_flag)) return;
   block_sync_lds();
   plan_router(0);
-  plan_gu(K, KS);
+  plan_gu(0, 1);
   issue_router();
-  issue_gu();
+  issue_gu(0, 1);
   issue_down_shared();
   uint32_t* const abort_word = a.bar + 32 * (1 + kGroups);
   auto block_failed = [&](bool ok) -> bool {   // whole block
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         for (int k = 0; k < CPLR; ++k) rpart[k * kWaves + wave] = racc[k];
       }
     }
-    __syncthreads();
+    block_sync_lds();
     stamp(li, 1);
     double ss = 0.0;
     float mx = 0.0f;
@@ -606,21 +618,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         if ((tid & 3) == 0 && w < nw) *reinterpret_cast<float2*>(xs + kChunkSums * (w >> 2)) = s;
       }
     }
-    __syncthreads();
+    block_sync_lds();
     stamp(li, 2);
-    gu_dots(K, KS);                 // the shared expert's rows are already here
-    stamp(li, 3);
-    if (S > 0) {                    // publish its activations before routing is known
-      block_sync_lds();
-      for (int t = tid; t < RG; t += kThreads) {
-        const int row = b + NB * t;
-        if (row < I) {
-          const float g = gres[(K * 2) * RG + t], u = gres[(K * 2 + 1) * RG + t];
-          put_tagged(aw + (int64_t)K * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
-        }
-      }
-    }
-    stamp(li, 4);
 
     // ------------------------------------------------------------ phase G
     // this layer's pointer-table row lands while the logits are polled
@@ -646,10 +645,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     bool fast = false;
     if (E <= kThreads) {
       topk_candidates<kWaves>(key, tid, K, sample_k, candk, candi, cand_cnt);
-      __syncthreads();
+      stamp0(li, 19);
+      block_sync_lds();
+      stamp0(li, 20);
       fast = topk_select<kWaves>(K, candk, candi, cand_cnt, [&](int r, int win) { wsel[wave][r] = win; });
     } else {
-      __syncthreads();
+      block_sync_lds();
     }
     if (!fast) {   // block-uniform
       if (E <= kThreads) block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
@@ -657,28 +658,38 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (lane < K) wsel[wave][lane] = sel[lane];
     }
     stamp0(li, 14);
-    plan_gu(0, K);                   // routed gate/up rows
-    issue_gu();
+    plan_gu(1, RPWG);                // routed gate/up rows
+    issue_gu(1, RPWG);
     stamp0(li, 5);
-    // while they arrive: wave 0 takes the softmax weights and the blob
-    // pointers the down rows use (read after the next block barrier)
-    if (wave == 0) {
-      if (lane < K) selv[lane] = (unsigned)wsel[0][lane] < (unsigned)E ? lg[wsel[0][lane]] : -INFINITY;
-      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
-                                  : wave_softmax_selected(selv, K);
-      if (lane < K) {
-        selw[lane] = w;
-        const int e = wsel[0][lane];
-        const uint8_t* bp = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
-        eblob[lane] = bp;
-        if (bp == nullptr) set_status(a.status, kStatusBadExpert);
-        if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
-      }
+    // while they arrive: wave 0 records the blob pointers the down rows use
+    // (read after the next block barrier); the softmax weights wait until
+    // the activations are in flight
+    if (wave == 0 && lane < K) {
+      const int e = wsel[0][lane];
+      const uint8_t* bp = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
+      eblob[lane] = bp;
+      if (bp == nullptr) set_status(a.status, kStatusBadExpert);
+      if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
     }
     stamp0(li, 15);
-    gu_dots(0, K);
+    // the shared expert's gate/up rows (requested a layer ahead) while the
+    // routed rows arrive, and its activations published at once
+    if (S > 0) {
+      gu_dots(0, 1);
+      stamp0(li, 3);
+      block_sync_lds();
+      for (int t = tid; t < RG; t += kThreads) {
+        const int row = b + NB * t;
+        if (row < I) {
+          const float g = gres[(K * 2) * RG + t], u = gres[(K * 2 + 1) * RG + t];
+          put_tagged(aw + (int64_t)K * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
+        }
+      }
+      stamp0(li, 4);
+    }
+    gu_dots(1, RPWG);
     stamp0(li, 13);
-    __syncthreads();
+    block_sync_lds();
     stamp(li, 6);
     plan_down();                     // routed slots' down rows (eblob is complete now)
     for (int t = tid; t < K * RG; t += kThreads) {
@@ -693,6 +704,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // every block is waiting for)
     issue_down();
     stamp0(li, 7);
+    // the softmax weights of the selection (wave 0), read by the combine
+    // after the activation hand-off's block barriers
+    if (wave == 0) {
+      if (lane < K) selv[lane] = (unsigned)wsel[0][lane] < (unsigned)E ? lg[wsel[0][lane]] : -INFINITY;
+      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
+                                  : wave_softmax_selected(selv, K);
+      if (lane < K) selw[lane] = w;
+    }
     stamp(li, 8);
 
     // ------------------------------------------------------------ phase D
@@ -783,9 +802,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     if (S > 0 && tid == 0) eblob[K] = shp[li + 1];   // at most one shared expert
     block_sync_lds();
     plan_router(li + 1);
-    plan_gu(K, KS);
+    plan_gu(0, 1);
     issue_router();
-    issue_gu();
+    issue_gu(0, 1);
     issue_down_shared();
     stamp0(li, 11);
   }
@@ -835,7 +854,8 @@ struct Geometry {
     if (rw > CPLR) return false;
     if (H / PC > 64 * CPLG) return false;
     const int RG = (I + nb - 1) / nb, RD = (H + nb - 1) / nb;
-    if (KS * 2 * RG > kWaves * RPWG) return false;
+    if (S > 0 && 2 * RG > kWaves) return false;              // shared rows: register slot 0
+    if (K * 2 * RG > kWaves * (RPWG - 1)) return false;      // routed rows: slots 1 ..
     const int nchd = I / PC;
     if (nchd > LPRD * CPLD) return false;
     if (KS * (I * BITS / 32) > kThreads) return false;   // one activation word per thread
@@ -875,7 +895,7 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
   if (g.fits(4, 2, 2, 4, 32, 1, 3, 4)) return launch_t<4, 2, 2, 4, 32, 1, 3, 4>(a, nb, lds, stream);
   if (g.fits(2, 2, 1, 5, 32, 1, 4, 4)) return launch_t<2, 2, 1, 5, 32, 1, 4, 4>(a, nb, lds, stream);
-  if (g.fits(4, 1, 1, 1, 64, 1, 3, 1)) return launch_t<4, 1, 1, 1, 64, 1, 3, 1>(a, nb, lds, stream);
+  if (g.fits(4, 1, 1, 2, 64, 1, 3, 1)) return launch_t<4, 1, 1, 2, 64, 1, 3, 1>(a, nb, lds, stream);
   return hipErrorNotSupported;
 }
 
