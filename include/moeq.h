@@ -188,6 +188,28 @@ int moe_expert_stack_decode(const moeq_shape* shape, const moeq_experts* experts
                             uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
                             void* workspace, void* stream);
 
+/* moe_expert_stack_decode with no workspace argument and no allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The workspace is a
+ * static device array of MOEQ_NOALLOC_SCRATCH_BYTES per GPU, held by the
+ * library until the process ends; its address is taken once per device (the
+ * first call on a device, with that device current, also clears it on
+ * `stream`).  Arguments as moe_expert_stack_decode, plus
+ *   status_out  device int32 or NULL: receives the call's status word
+ *               (0 = clean, bits as in moe_read_device_status), which is
+ *               then cleared for the next call.
+ * MOEQ_E_UNSUPPORTED when the shape's workspace (moeq_workspace_bytes for T
+ * and k) exceeds MOEQ_NOALLOC_SCRATCH_BYTES (8 MiB: T = 1 fits every shape
+ * within the other limits, and so does a 16-token batch at hidden 4096,
+ * intermediate 1024, 512 experts, top-10).  All calls on one GPU share the array: calls that
+ * overlap in time on one GPU (several streams or host threads) race and
+ * must be serialised by the caller. */
+#define MOEQ_NOALLOC_SCRATCH_BYTES (8 << 20)
+int moe_expert_stack_decode_noalloc(const moeq_shape* shape, const moeq_experts* experts,
+                                    const uint16_t* const* w_router, int layer0, int L, int T, int k,
+                                    uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
+                                    int32_t* status_out, void* stream);
+
 /* Prefill: T tokens (any T >= 1; the configured workload is 2048) through
  * the stacked layers [layer0, layer0 + L) on the fp32 residual stream h
  * [T][H], in place; per layer and token the same computation as

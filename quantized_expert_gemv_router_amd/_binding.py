@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moeq_stack_clock_trace.argtypes = [_P]
         L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                               _P, _P]
+        L.moe_expert_stack_decode_noalloc.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
+                                                      _P, _P]
         L.moe_expert_stack_prefill.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P, _P]
         L.moeq_prefill_workspace_bytes.argtypes = [S, _I, _I, ctypes.POINTER(ctypes.c_int64)]
         L.moeq_prefill_timing.argtypes = [_I]
@@ -265,6 +267,26 @@ def moe_expert_stack_decode(shape: Shape, experts: ExpertTable, routers: RouterT
     _check(lib().moe_expert_stack_decode(ctypes.byref(shape), experts.view(), routers.ptr(), layer0, L, T,
                                          k, flags, _ptr(h), _ptr(tk), _ptr(hk), _ptr(workspace),
                                          _stream(stream)))
+    return (tk, hk) if trace else None
+
+
+def moe_expert_stack_decode_noalloc(shape: Shape, experts: ExpertTable, routers: RouterTable, h: torch.Tensor,
+                                    k: int, layer0: int = 0, L: int | None = None, flags: int = 0,
+                                    trace: bool = False, status: torch.Tensor | None = None, stream=None):
+    """moe_expert_stack_decode on the library's static scratch (no workspace,
+    no allocation by the library).  `status`: optional int32 device tensor [1]
+    that receives the call's status word."""
+    T = h.shape[0]
+    L = experts.n_layers - layer0 if L is None else L
+    if h.dtype != torch.float32:
+        raise ValueError("the stack runs on an fp32 residual stream")
+    tk = hk = None
+    if trace:
+        tk = torch.empty((L, T, k), dtype=torch.int32, device=h.device)
+        hk = torch.empty((L, T, shape.hidden), dtype=torch.float32, device=h.device)
+    _check(lib().moe_expert_stack_decode_noalloc(ctypes.byref(shape), experts.view(), routers.ptr(), layer0, L,
+                                                 T, k, flags, _ptr(h), _ptr(tk), _ptr(hk), _ptr(status),
+                                                 _stream(stream)))
     return (tk, hk) if trace else None
 
 

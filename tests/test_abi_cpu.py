@@ -127,3 +127,18 @@ def test_expert_call_validation_without_gpu():
 
 def test_abi_version():
     assert q.moeq_abi_version() >= 1
+
+
+def test_noalloc_rejects_workspace_above_static_scratch_without_gpu():
+    """The allocation-free stack decode refuses shapes whose workspace does not
+    fit its static scratch (before any device call), and bad counts."""
+    L = q.lib()
+    big = q.Shape(8192, 8192, 4096, 1, 4, 64)
+    assert L.moe_expert_stack_decode_noalloc(ctypes.byref(big), None, None, 0, 1, 64, 16, 0, None, None,
+                                             None, None, None) == E_UNSUPPORTED
+    assert b"static scratch" in L.moeq_last_error()
+    s = q.Shape(4096, 1024, 512, 1, 4, 64)
+    assert L.moe_expert_stack_decode_noalloc(ctypes.byref(s), None, None, 0, 1, -1, 3, 0, None, None,
+                                             None, None, None) == E_INVALID
+    assert L.moe_expert_stack_decode_noalloc(ctypes.byref(s), None, None, 0, 1, 1, 17, 0, None, None,
+                                             None, None, None) == E_UNSUPPORTED
