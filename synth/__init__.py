@@ -78,6 +78,11 @@ CONFIGS = {
     # prefill variant: 2048 tokens, top-10 + 1 shared per layer
     "stack60_prefill": MoEConfig("stack60_prefill", 4096, 512, 1024, 10, 1, 2048,
                                  layers=60, rmsnorm=True, **_FOUR),
+    # longer prompts through the same layers (past the MFMA ridge)
+    "stack60_prefill_4k": MoEConfig("stack60_prefill_4k", 4096, 512, 1024, 10, 1, 4096,
+                                    layers=60, rmsnorm=True, **_FOUR),
+    "stack60_prefill_8k": MoEConfig("stack60_prefill_8k", 4096, 512, 1024, 10, 1, 8192,
+                                    layers=60, rmsnorm=True, **_FOUR),
 }
 
 
