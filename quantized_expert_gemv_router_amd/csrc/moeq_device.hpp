@@ -247,6 +247,17 @@ __device__ __forceinline__ T load_stream(const T* p) {
   return __builtin_nontemporal_load((GlobalT*)p);
 }
 
+// A global load with the default (temporal) cache policy: the L2 keeps the
+// line.  For data whose line is consumed by more than one request (a row
+// read in 64-byte halves a chunk apart, activation rows re-read by the
+// weight tiles of one XCD), a non-temporal load would let the line go
+// before its second use and fetch it again.
+template <class T>
+__device__ __forceinline__ T load_keep(const T* p) {
+  using GlobalT = __attribute__((address_space(1))) const T;
+  return *(GlobalT*)p;
+}
+
 // Range-checked streaming loads through a buffer resource (base address in
 // scalar registers, byte size).  A load whose offset lies outside [0, size)
 // returns zeros without touching memory, so a wave can issue its loads

@@ -50,6 +50,8 @@ constexpr int kNT = 4 * 16 * kNBW;      // weight rows per tile
 constexpr int kKC = 128;                // K per chunk (two groups of 64)
 constexpr int kPitch = kKC + 8;         // LDS row pitch in halves (bank spread)
 constexpr int kSbWin = 8;               // chunks per scale/bias window (16 groups)
+constexpr int kSbPitch = 2 * kSbWin + 4; // LDS words per row of a window: 16 rows read at one
+                                         // group offset fall in distinct banks
 
 // position of value j of a packed word in the stored (MFMA) order
 __device__ __forceinline__ int perm_pos(int r) {
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
   __shared__ __align__(16) _Float16 As[2][kMT * kPitch];
   // scale/bias words of the tile's rows, windows of 2*kSbWin groups,
   // double-buffered: [buffer][matrix][row][group in window]
-  __shared__ __align__(16) uint32_t Sb[2][NMAT][NTR][2 * kSbWin];
+  __shared__ __align__(16) uint32_t Sb[2][NMAT][NTR][kSbPitch];
   __shared__ int32_t src_row[kMT], dst_row[kMT];
   __shared__ int s_e, s_row0, s_n;
 
@@ -404,11 +406,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
       const int w = min(win, (NC - 1) / kSbWin);
       const int g0 = w * 2 * kSbWin + 4 * sb_qt;          // first group of this thread's four
       const uint32_t* p = sb_src + (int64_t)piece * PR * gpr + w * 2 * kSbWin;
-      if (g0 + 4 <= gpr) return load_stream(reinterpret_cast<const u32x4*>(p));
+      if (g0 + 4 <= gpr) return load_keep(reinterpret_cast<const u32x4*>(p));
       u32x4 v = {0u, 0u, 0u, 0u};                          // rows shorter than a window
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (g0 + e < gpr) v[e] = load_stream(p + e);
+        if (g0 + e < gpr) v[e] = load_keep(p + e);
       return v;
     };
     auto store_sb = [&](int buf, int piece, u32x4 v) {
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
     auto load_a = [&](int c, u32x4 (&v)[AV]) {
       const u32x4* p = reinterpret_cast<const u32x4*>(asrc + c * kKC + apart * (8 * AV));
 #pragma unroll
-      for (int i = 0; i < AV; ++i) v[i] = load_stream(p + i);
+      for (int i = 0; i < AV; ++i) v[i] = load_keep(p + i);
     };
     auto store_a = [&](int buf, const u32x4 (&v)[AV]) {
       u32x4* d = reinterpret_cast<u32x4*>(&As[buf][arow * kPitch + apart * (8 * AV)]);
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void gemm_kernel(GemmArgs
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int nb = 0; nb < kNBW; ++nb) r.q[m][nb] = load_stream(reinterpret_cast<const u32x4*>(qrow[m][nb] + 16 * c));
+        for (int nb = 0; nb < kNBW; ++nb) r.q[m][nb] = load_keep(reinterpret_cast<const u32x4*>(qrow[m][nb] + 16 * c));
     };
 
     float4v acc[NMAT][kNBW][kMB];
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(kResThreads, 1) void down_resident_kernel(GemmArgs 
     for (int i = 0; i < kResUnits; ++i) {
       const int x = min(tid + i * kResThreads, kMT * upr - 1);
       const int r = x / upr, u = x - r * upr;
-      av[i] = load_stream(reinterpret_cast<const u32x4*>(a.abuf + (int64_t)src_row[r] * I) + u);
+      av[i] = load_keep(reinterpret_cast<const u32x4*>(a.abuf + (int64_t)src_row[r] * I) + u);
     }
 
     // weights: flat chunk f = t * NC + c over the run's tiles; lane quarter
@@ -625,8 +627,8 @@ __global__ __launch_bounds__(kResThreads, 1) void down_resident_kernel(GemmArgs 
 #pragma unroll
       for (int nb = 0; nb < kNBW; ++nb) {
         const int n = (nt0 + t) * NTR + wave * (16 * kNBW) + nb * 16 + (lane & 15);
-        r.q[nb] = load_stream(reinterpret_cast<const u32x4*>(dq + (int64_t)n * (I / 2)) + 4 * c + q4);
-        r.sb[nb] = load_stream(dsb + (int64_t)n * (I / 64) + 2 * c + (q4 >> 1));
+        r.q[nb] = load_keep(reinterpret_cast<const u32x4*>(dq + (int64_t)n * (I / 2)) + 4 * c + q4);
+        r.sb[nb] = load_keep(dsb + (int64_t)n * (I / 64) + 2 * c + (q4 >> 1));
       }
     };
 #pragma unroll
