@@ -293,29 +293,40 @@ int moeq_probe_handoff(int mode, int words_per_block, int stride, int rounds, in
 /* ------------------------------------------------------------------ pool
  * Expert slot pool (openclawradar.com/fr, Flash-MoE write-up: experts kept
  * in a bounded number of resident slots and loaded when the router asks for
- * them; fr.news.hada.io, Flash-MoE, "SSD Expert Streaming": one contiguous
- * 6.75 MiB read per expert).  The pool owns the placement of experts in a
- * caller-provided device arena of n_slots slots and writes the device
- * pointer table that the expert calls read (entries of non-resident experts
- * are NULL).  Misses are copied from a pinned host image of every blob by
- * hipMemcpyAsync on `copy_stream`; the compute stream is made to wait on an
- * event, so no kernel reads a slot before its copy lands.  The least
+ * them, the engine's copies split over several I/O streams in the
+ * openclawradar.com/ru article, "Эффективные оптимизации"; fr.news.hada.io,
+ * Flash-MoE, "SSD Expert Streaming": one contiguous 6.75 MiB read per
+ * expert).  The pool owns the placement of experts in a caller-provided
+ * device arena of n_slots slots and writes the device pointer table that the
+ * expert calls read (entries of non-resident experts are NULL).  Misses are
+ * copied from pinned host memory by hipMemcpyAsync, spread round robin over
+ * the caller's copy streams; the compute stream is made to wait on an event
+ * of each, so no kernel reads a slot before its copy lands.  The least
  * recently acquired unpinned slot is evicted first, and only after the
  * last layer that used it was released (its release event is awaited on
- * the copy stream).  A pool is used from one host thread. */
+ * the copy stream of the miss and on the stream that edits the table).  A
+ * pool is used from one host thread. */
 typedef struct moeq_pool moeq_pool;
 
-/*   n_layers     layers in the host image and the table
- *   arena        device, n_slots * slot_bytes bytes, 256-byte aligned
- *   slot_bytes   multiple of 256, >= moeq_expert_bytes(shape)
- *   host_src     pinned host memory (hipHostMalloc), n_layers * (E + S)
- *                blobs, blob (l, e) at byte (l * (E + S) + e) * slot_bytes
- *   table        device array [n_layers][E + S] of pointers, set to NULL here
- *   copy_stream  stream for the copies and table edits (caller-owned)
- * The arena, host image, table and stream stay caller-owned and must
- * outlive the pool.  The pool allocates its host metadata and events. */
+#define MOEQ_POOL_MAX_COPY_STREAMS 8
+
+/*   n_layers        layers in the host table and the device table
+ *   arena           device, n_slots * slot_bytes bytes, 256-byte aligned
+ *   slot_bytes      multiple of 256, >= moeq_expert_bytes(shape)
+ *   host_blobs      host array [n_layers * (E + S)] of pointers to pinned host
+ *                   memory (hipHostMalloc, pinned tensors), one expert blob
+ *                   each, entry (l, e) at index l * (E + S) + e; the blobs
+ *                   need not be contiguous.  The array is copied; the blobs
+ *                   stay caller-owned.
+ *   table           device array [n_layers][E + S] of pointers, set to NULL here
+ *   copy_streams    host array of n_copy_streams (1 .. 8) streams for the
+ *                   copies; the first also carries the table edits
+ * The arena, host blobs, table and streams stay caller-owned and must
+ * outlive the pool.  The pool allocates its host metadata and events.
+ * MOEQ_E_INVALID if a host blob is not pinned. */
 int moe_pool_create(const moeq_shape* shape, int n_layers, void* arena, int64_t n_slots, int64_t slot_bytes,
-                    const void* host_src, const void** table, void* copy_stream, moeq_pool** out);
+                    const void* const* host_blobs, const void** table, void* const* copy_streams,
+                    int n_copy_streams, moeq_pool** out);
 
 /* Every expert resident, blob i in slot i (needs n_slots >= n_layers*(E+S));
  * `stream` waits for the copy. */

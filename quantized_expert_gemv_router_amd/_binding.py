@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.moeq_prefill_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
         H = ctypes.POINTER(ctypes.c_void_p)
         I64 = ctypes.c_int64
-        L.moe_pool_create.argtypes = [S, _I, _P, I64, I64, _P, _P, _P, H]
+        L.moe_pool_create.argtypes = [S, _I, _P, I64, I64, _P, _P, _P, _I, H]
         L.moe_pool_make_resident.argtypes = [_P, _P]
         L.moe_pool_acquire.argtypes = [_P, _I, _P, _I, _P, X]
         L.moe_pool_release.argtypes = [_P, _I, _P]
@@ -403,20 +403,36 @@ class PoolView:
 
 
 class Pool:
-    """moe_pool_*: expert slots in a device arena, filled from a pinned host
-    image of every (layer, expert) blob on demand, least recently used slot
-    evicted.  `host_src` is a pinned uint8 CPU tensor laid out blob (l, e) at
-    (l * (E + S) + e) * slot_bytes; `table` an int64 device tensor of
-    n_layers * (E + S) entries (the pointer table the pool writes)."""
+    """moe_pool_*: expert slots in a device arena, filled on demand from pinned
+    host blobs, least recently used slot evicted.  `host` is either one
+    pinned uint8 CPU tensor laid out blob (l, e) at (l * (E + S) + e) *
+    slot_bytes, or a list of per-layer pinned tensors [E + S slots of
+    slot_bytes], or a list of n_layers * (E + S) host addresses of pinned
+    blobs; `table` an int64 device tensor of n_layers * (E + S) entries (the
+    pointer table the pool writes); `copy_stream` one stream or a list of
+    them (misses are spread over them)."""
 
     def __init__(self, shape: Shape, n_layers: int, arena: torch.Tensor, n_slots: int, slot_bytes: int,
-                 host_src: torch.Tensor, table: torch.Tensor, copy_stream=None):
+                 host, table: torch.Tensor, copy_stream=None):
         self._h = ctypes.c_void_p()
-        self.shape, self.arena, self.host_src, self.table = shape, arena, host_src, table
-        self.copy_stream = copy_stream
+        self.shape, self.arena, self.host, self.table = shape, arena, host, table
+        per = shape.n_slots
+        if isinstance(host, torch.Tensor):
+            base = host.data_ptr()
+            ptrs = [base + i * slot_bytes for i in range(n_layers * per)]
+        elif len(host) and isinstance(host[0], torch.Tensor):
+            ptrs = [t.data_ptr() + e * slot_bytes for t in host for e in range(per)]
+        else:
+            ptrs = [int(v) for v in host]
+        if len(ptrs) != n_layers * per:
+            raise ValueError(f"host blobs: {len(ptrs)} given, {n_layers * per} needed")
+        self._ptrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        streams = copy_stream if isinstance(copy_stream, (list, tuple)) else [copy_stream]
+        self.copy_streams = streams
+        self._streams = (ctypes.c_void_p * len(streams))(*[_stream(st) for st in streams])
         _check(lib().moe_pool_create(ctypes.byref(shape), n_layers, _ptr(arena), n_slots, slot_bytes,
-                                     host_src.data_ptr(), _ptr(table), _stream(copy_stream),
-                                     ctypes.byref(self._h)))
+                                     ctypes.cast(self._ptrs, _P), _ptr(table), ctypes.cast(self._streams, _P),
+                                     len(streams), ctypes.byref(self._h)))
 
     def make_resident(self, stream=None):
         _check(lib().moe_pool_make_resident(self._h, _stream(stream)))

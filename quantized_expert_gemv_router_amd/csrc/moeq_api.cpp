@@ -109,7 +109,7 @@ using namespace moeq;
 
 extern "C" {
 
-int moeq_abi_version(void) { return 1; }
+int moeq_abi_version(void) { return 2; }
 
 const char* moeq_last_error(void) { return g_last_error.c_str(); }
 

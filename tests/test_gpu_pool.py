@@ -37,12 +37,22 @@ class Setup:
                                       self.stride)
         self.routers = [bf16_dev(synth.router(cfg, l)) for l in range(L)]
         self.copy = torch.cuda.Stream()
+        self.copies = [self.copy] + [torch.cuda.Stream() for _ in range(3)]
+        # the same blobs as separate pinned allocations, one per layer
+        self.host_layers = []
+        for l in range(L):
+            t = torch.empty(P * self.stride, dtype=torch.uint8, pin_memory=True)
+            t.copy_(self.host[l * P * self.stride:(l + 1) * P * self.stride])
+            self.host_layers.append(t)
 
-    def pool(self, n_slots):
+    def pool(self, n_slots, streams=1):
         P, L = self.cfg.n_slots, self.cfg.layers
         arena = torch.empty(n_slots * self.stride, dtype=torch.uint8, device="cuda")
         table = torch.zeros(L * P, dtype=torch.int64, device="cuda")
-        return q.Pool(self.shape, L, arena, n_slots, self.stride, self.host, table, self.copy)
+        if streams == 1:   # one contiguous host image, one copy stream
+            return q.Pool(self.shape, L, arena, n_slots, self.stride, self.host, table, self.copy)
+        # per-layer host allocations, misses spread over several copy streams
+        return q.Pool(self.shape, L, arena, n_slots, self.stride, self.host_layers, table, self.copies[:streams])
 
     def token(self, i):
         return bf16_dev(synth.tokens(self.cfg, 500 + i, 1))
@@ -62,14 +72,15 @@ def run_layer(S, experts, layer, x, ws):
     return idx, gu, y
 
 
+@pytest.mark.parametrize("streams", [1, 4])
 @pytest.mark.parametrize("extra_layers", [-1, 1])
-def test_pool_matches_resident_and_policy(setup, extra_layers):
+def test_pool_matches_resident_and_policy(setup, extra_layers, streams):
     S, cfg = setup, setup.cfg
     # two layers' worth of slots forces evictions on every layer; one layer
     # more than the stack keeps recently used experts around (hits)
     n_slots = (2 if extra_layers < 0 else cfg.layers + extra_layers) * (cfg.top_k + cfg.n_shared)
-    say(f"[pool] {cfg.name}: {n_slots} slots for {cfg.layers} x {cfg.n_slots} experts")
-    pool = S.pool(n_slots)
+    say(f"[pool] {cfg.name}: {n_slots} slots for {cfg.layers} x {cfg.n_slots} experts, {streams} copy streams")
+    pool = S.pool(n_slots, streams)
     sim = q.PoolSim(cfg.layers, cfg.n_slots, n_slots)
     ws = q.new_workspace(S.shape, 1, cfg.top_k)
     ws_r = q.new_workspace(S.shape, 1, cfg.top_k)
@@ -98,7 +109,7 @@ def test_pool_matches_resident_and_policy(setup, extra_layers):
     # the same requests again, acquired and released back to back with no
     # host synchronisation: copies into reused slots must wait for the
     # kernels of the layers that used them
-    pool2 = S.pool(n_slots)
+    pool2 = S.pool(n_slots, streams)
     outs = []
     for l, ids, x, _ in requests:
         view = pool2.acquire(l, ids)

@@ -161,12 +161,16 @@ def test_pool_create_validates_before_touching_a_device():
     L = B.lib()
     shape = q.Shape(256, 128, 8, 1, 4, 64)
     h = ctypes.c_void_p()
-    args = dict(n_layers=2, arena=0x1000, n_slots=4, slot_bytes=55296, host=0x2000, table=0x3000)
+    blobs = (ctypes.c_void_p * 18)(*[0x2000 + i * 55296 for i in range(18)])
+    streams = (ctypes.c_void_p * 1)(None)
+    args = dict(n_layers=2, arena=0x1000, n_slots=4, slot_bytes=55296, host=ctypes.cast(blobs, ctypes.c_void_p),
+                table=0x3000, streams=ctypes.cast(streams, ctypes.c_void_p), n_streams=1)
 
     def create(**kw):
         a = dict(args, **kw)
         return L.moe_pool_create(ctypes.byref(shape), a["n_layers"], a["arena"], a["n_slots"],
-                                 a["slot_bytes"], a["host"], a["table"], None, ctypes.byref(h))
+                                 a["slot_bytes"], a["host"], a["table"], a["streams"], a["n_streams"],
+                                 ctypes.byref(h))
 
     assert create(arena=None) == B.E_INVALID
     assert create(table=None) == B.E_INVALID
@@ -175,8 +179,11 @@ def test_pool_create_validates_before_touching_a_device():
     assert create(n_layers=0) == B.E_INVALID
     assert create(slot_bytes=55296 - 256) == B.E_INVALID     # below the expert size
     assert create(slot_bytes=55296 + 8) == B.E_INVALID       # not a multiple of 256
+    assert create(n_streams=0) == B.E_INVALID                # at least one copy stream
+    assert create(n_streams=9) == B.E_INVALID                # at most eight
+    assert create(streams=None) == B.E_INVALID
     bad = q.Shape(256, 128, 8, 1, 3, 64)
-    assert L.moe_pool_create(ctypes.byref(bad), 2, 0x1000, 4, 55296, 0x2000, 0x3000, None,
+    assert L.moe_pool_create(ctypes.byref(bad), 2, 0x1000, 4, 55296, args["host"], 0x3000, args["streams"], 1,
                              ctypes.byref(h)) == B.E_UNSUPPORTED
     assert h.value is None
     # the stats, release and acquire calls refuse a NULL pool
