@@ -52,6 +52,8 @@ def parse():
                             "stack60_prefill_4k", "stack60_prefill_8k", "pool_decode"])
     p.add_argument("--layerwise", action="store_true",
                    help="stack60_decode: per-layer launches instead of the persistent kernel")
+    p.add_argument("--fused-layer", action="store_true",
+                   help="one-token layer workloads: one persistent launch per layer instead of the three calls")
     p.add_argument("--instances", type=int, default=8, help="layer instances for cold rotation")
     p.add_argument("--tokens-pool", type=int, default=64, help="distinct token vectors")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -503,6 +505,106 @@ def run_prefill(args, cfg, dev, stream):
     return rec
 
 
+def run_layer_fused(args, cfg, dev, stream):
+    """One decode token through one layer per step as a single persistent
+    launch (router, top-K, gate/up, SwiGLU, down and combine in one kernel,
+    the layer input taken as is: MOEQ_F_STACK_NO_NORM), rotating over
+    --instances resident layer instances so the expert bytes come from HBM."""
+    import ctypes
+    import torch
+    import quantized_expert_gemv_router_amd as q
+    import synth
+    import oracle
+
+    n_inst = args.instances
+    shape, table, routers, bf16 = setup_layers(cfg, n_inst, dev, stream)
+    rt = q.RouterTable(routers, device=dev)
+    K = cfg.top_k
+    ws = q.new_workspace(shape, 1, K, dev)
+    total = args.warmup + args.steps
+    tok = [torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, 100 + i, 1)).astype(np.float32)).to(dev)
+           for i in range(args.tokens_pool)]
+    hs = [tok[s % args.tokens_pool].clone() for s in range(total)]
+    tks = torch.empty((total, 1, 1, K), dtype=torch.int32, device=dev)
+    flags = q.F_STACK_NO_NORM
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(s, slot=None):
+        l = s % n_inst
+        if slot is not None:
+            ev[slot][0].record(stream)
+        rc = q.lib().moe_expert_stack_decode(ctypes.byref(shape), table.view(), rt.ptr(), l, 1, 1, K, flags,
+                                             hs[s].data_ptr(), tks[s].data_ptr(), None, ws.data_ptr(),
+                                             stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(q.moeq_last_error())
+        if slot is not None:
+            ev[slot][1].record(stream)
+
+    # parity: instance 0, token 0 against the fp64 oracle
+    log("[bench] parity: one fused layer against the fp64 oracle")
+    h0 = tok[0].clone()
+    tk0 = torch.empty((1, 1, K), dtype=torch.int32, device=dev)
+    rc = q.lib().moe_expert_stack_decode(ctypes.byref(shape), table.view(), rt.ptr(), 0, 1, 1, K, flags,
+                                         h0.data_ptr(), tk0.data_ptr(), None, ws.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(q.moeq_last_error())
+    status = q.moe_read_device_status(ws, stream)
+    if status != 0:
+        raise ParityError(f"device status {status} in the parity run")
+    path = q.moeq_last_stack_path()
+    exp = oracle.run_layer(cfg, 0, synth.bf16_to_f64(synth.tokens(cfg, 100, 1)), want_intermediates=False)
+    if not np.array_equal(tk0.cpu().numpy()[0], exp["idx"]):
+        raise ParityError("top-K differs from the oracle")
+    e = rel_err(h0.cpu().numpy(), exp["y"])
+    if not e <= TOL:
+        raise ParityError(f"output rel err {e:.3e} > {TOL}")
+    parity = {"topk_exact_tokens": 1, "max_rel_err": float(f"{e:.3e}"), "tol": TOL, "reference": "fp64 oracle"}
+    log(f"[bench] parity ok: {parity}")
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            step(s)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + i, slot=i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    status = q.moe_read_device_status(ws, stream)
+    if status != 0:
+        raise RuntimeError(f"device status {status} after the timed region")
+    elapsed_ms = start.elapsed_time(end)
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    idx = tks[args.warmup:].cpu().numpy()
+    distinct = np.array([len(np.unique(idx[s])) for s in range(args.steps)]) + cfg.n_shared
+    expert_bytes = distinct * cfg.expert_bytes
+    router_bytes = cfg.n_experts * cfg.hidden * 2
+    per_launch = float(expert_bytes.mean())
+    sec = elapsed_ms / 1e3
+    rec = base_record(args, cfg, steps_tokens=args.steps, elapsed_ms=elapsed_ms, wall=wall)
+    path_name = "persistent" if path == 1 else "per-layer"
+    rec.update({
+        "gbps_expert": round(expert_bytes.sum() / sec / 1e9, 1),
+        "gbps_all_bytes": round((expert_bytes.sum() + args.steps * router_bytes) / sec / 1e9, 1),
+        "frac_hbm_peak": round(expert_bytes.sum() / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "expert_layers_per_s": round(args.steps / sec, 1),
+        "path": path_name,
+        "roofline": {"kernel": "stack_kernel (one layer, one persistent launch)" if path == 1
+                     else "per-layer launches (3)", "bound": "hbm",
+                     "achieved": round(per_launch / (launch_ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(per_launch / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 3),
+                     "bytes_per_launch": int(per_launch), "router_bytes_per_launch": router_bytes},
+        "parity": parity,
+    })
+    rec["config"].update(layers_per_step=1, layer_instances=n_inst)
+    return rec
+
+
 def run_layer_workload(args, cfg, dev, stream):
     import torch
     import quantized_expert_gemv_router_amd as q
@@ -875,6 +977,8 @@ def main():
         rec = run_prefill(args, cfg, dev, stream)
     elif cfg.layers > 1:
         rec = run_stack(args, cfg, dev, stream)
+    elif cfg.tokens == 1 and args.fused_layer:
+        rec = run_layer_fused(args, cfg, dev, stream)
     else:
         rec = run_layer_workload(args, cfg, dev, stream)
     if not args.no_cpu_baseline:

@@ -71,7 +71,12 @@ enum {
   MOEQ_F_RMSNORM = 2u,
   /* moe_expert_stack_decode only: run the layers one launch sequence at a
    * time (router, gate/up, down per layer) instead of the persistent kernel. */
-  MOEQ_F_STACK_LAYERWISE = 4u
+  MOEQ_F_STACK_LAYERWISE = 4u,
+  /* moe_expert_stack_decode only: each layer takes its input h as is (no
+   * RMS norm): one layer of this call computes what moe_router_topk,
+   * moe_q4_expert_gemv and moe_swiglu_down_combine compute without
+   * MOEQ_F_RMSNORM (for a single decode layer in one launch). */
+  MOEQ_F_STACK_NO_NORM = 8u
 };
 
 /* Limits of the current kernels (larger values return MOEQ_E_UNSUPPORTED). */
@@ -175,7 +180,7 @@ int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts
  *   h           device [T][H] f32, in/out
  *   topk_trace  device [L][T][k] int32 out, or NULL
  *   h_trace     device [L][T][H] f32 out (the input of each layer), or NULL
- *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE
+ *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE, MOEQ_F_STACK_NO_NORM
  * T == 1 runs one persistent cooperative launch for all L layers (no host
  * involvement: the workgroups hand the logits, the activations and the
  * hidden state to each other through tagged words in the workspace) when

@@ -231,7 +231,7 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
                             void* workspace, void* stream) {
   if (int rc = check_shape(s)) return rc;
   if (int rc = check_tk(s, T, k)) return rc;
-  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_STACK_LAYERWISE))
+  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_STACK_LAYERWISE | MOEQ_F_STACK_NO_NORM))
     return fail(MOEQ_E_UNSUPPORTED, "unknown or inapplicable flag bits 0x%x", flags);
   if (!ex || !ex->blobs) return fail(MOEQ_E_INVALID, "experts view or its blob table is NULL");
   if (L < 0 || layer0 < 0 || layer0 + L > ex->n_layers)
@@ -253,6 +253,7 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     a.H = s->hidden; a.I = s->inter; a.E = s->n_experts; a.S = s->n_shared; a.K = k;
     a.bits = s->bits;
     a.no_renorm = (flags & MOEQ_F_NO_RENORM) != 0;
+    a.no_norm = (flags & MOEQ_F_STACK_NO_NORM) != 0;
     a.h = h;
     a.topk_trace = topk_trace;
     a.h_trace = h_trace;
@@ -281,7 +282,8 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
   float* w = reinterpret_cast<float*>(ws + W.st_w);
   float* sw = reinterpret_cast<float*>(ws + W.st_sw);
   float* gu = reinterpret_cast<float*>(ws + W.st_gu);
-  const uint32_t lf = MOEQ_F_RMSNORM | (flags & MOEQ_F_NO_RENORM);
+  const uint32_t norm = (flags & MOEQ_F_STACK_NO_NORM) ? 0u : (uint32_t)MOEQ_F_RMSNORM;
+  const uint32_t lf = norm | (flags & MOEQ_F_NO_RENORM);
   for (int l = 0; l < L; ++l) {
     const int layer = layer0 + l;
     if (h_trace) {
@@ -295,7 +297,7 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
       RouterArgs a{};
       a.x = h;
       a.x_f32 = 1;
-      a.rmsnorm = 1;
+      a.rmsnorm = norm != 0;
       a.no_renorm = (lf & MOEQ_F_NO_RENORM) != 0;
       a.w_table = w_router;
       a.w_layer = layer;
@@ -306,7 +308,7 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
       hipError_t e = launch_router_topk(a, st);
       if (e != hipSuccess) return hip_fail(e, "router kernel launch");
     }
-    int rc = moe_q4_expert_gemv(s, ex, layer, h, MOEQ_F32, MOEQ_F_RMSNORM, idx_l, T, k, workspace, gu, stream);
+    int rc = moe_q4_expert_gemv(s, ex, layer, h, MOEQ_F32, norm, idx_l, T, k, workspace, gu, stream);
     if (rc) return rc;
     rc = moe_swiglu_down_combine(s, ex, layer, gu, idx_l, w, s->n_shared ? sw : nullptr, h, MOEQ_F32, T,
                                  k, workspace, h, stream);

@@ -118,6 +118,7 @@ struct StackArgs {
   int layer0, L;
   int H, I, E, S, K, bits;
   int no_renorm;
+  int no_norm;                     // layer input taken as is (no RMS norm)
   int router_rows;                 // set by the launcher
   float* h;                        // [H] in/out
   int32_t* topk_trace;             // [L][K] or null

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) { ss += ssum[i]; mx = fmaxf(mx, hmax[i]); }
-    const double inv = 1.0 / sqrt(ss / (double)H + 1e-6);
+    const double inv = a.no_norm ? 1.0 : 1.0 / sqrt(ss / (double)H + 1e-6);
     const uint32_t tag = (uint32_t)li + 1u;
     if (tid < RW && b + NB * tid < E) {   // logits of this block's router rows
       double d = 0.0;

@@ -106,6 +106,30 @@ def test_stack_all_logits_tied(flags):
         assert_close(outs[l], exp["y"][0], f"tied layer {l} output")
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit"])
+def test_single_layer_no_norm_matches_oracle(name):
+    """One layer through the stack entry with MOEQ_F_STACK_NO_NORM (the layer
+    input taken as is, as the one-layer calls without the norm flag): the
+    persistent launch and the per-layer launches both give the oracle's
+    exact top-K and an output within the bar, for the configured one-token
+    layers (bf16 token, no norm, gamma = 1)."""
+    cfg = synth.CONFIGS[name]
+    shape, ex, rt = build_stack(cfg, 2)
+    for ts in (0, 1):
+        x64 = synth.bf16_to_f64(synth.tokens(cfg, ts, 1))
+        for layer in (0, 1):
+            exp = oracle.run_layer(cfg, layer, x64, want_intermediates=False)
+            for flags in (q.F_STACK_NO_NORM, q.F_STACK_NO_NORM | q.F_STACK_LAYERWISE):
+                h = torch.from_numpy(x64.astype(np.float32)).cuda()
+                ws = q.new_workspace(shape, 1, cfg.top_k)
+                tk, _ = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, layer0=layer, L=1, flags=flags,
+                                                  workspace=ws, trace=True)
+                assert q.moeq_last_stack_path() == (2 if flags & q.F_STACK_LAYERWISE else 1)
+                assert q.moe_read_device_status(ws) == 0
+                assert np.array_equal(tk.cpu().numpy()[0], exp["idx"]), (name, ts, layer, flags)
+                assert_close(h.cpu().numpy(), exp["y"], f"{name} layer {layer} flags {flags}")
+
+
 def test_stack_2bit_full_width():
     """The 2-bit persistent instantiation (hidden 4096, 512 experts, top-4 +
     1 shared) on three layers, gated per layer along its own trajectory."""
