@@ -31,6 +31,10 @@
  *   q sections hold rows of packed unsigned values, 32/bits per
  *   little-endian u32, value j of a row at bit bits*(j mod (32/bits)) of
  *   word j/(32/bits); gate/up rows run over hidden, down rows over inter.
+ *   3-bit rows (values 0..7, 3*cols/8 bytes) hold two planes: first the
+ *   low two bits of every value, packed as a 2-bit row (value j at bit
+ *   2*(j mod 16) of word j/16), then the high bit: value j at bit
+ *   2*(j mod 16) + ((j/16) mod 2) of word j/32 of the plane.
  *   sb sections hold one u32 per (row, group of 64 inputs): bf16 scale in
  *   the low half, bf16 bias in the high half.
  *
@@ -77,10 +81,19 @@ void oracle_dequant_row(const oracle_shape* s, const uint8_t* blob, int sec,
   const uint8_t* sb = blob + 3 * qbytes(s) + sec * sbbytes(s);
   int64_t words_per_row = cols / per_word;
   int64_t groups_per_row = cols / s->group;
+  const int64_t row_bytes = (int64_t)cols * s->bits / 8;
   for (int j = 0; j < cols; ++j) {
-    uint32_t word;
-    memcpy(&word, q + 4 * ((int64_t)row * words_per_row + j / per_word), 4);
-    uint32_t v = (word >> (s->bits * (j % per_word))) & mask;
+    uint32_t word, v;
+    if (s->bits == 3) {   /* low-bits plane, then high-bit plane */
+      const uint8_t* r = q + (int64_t)row * row_bytes;
+      uint32_t hw;
+      memcpy(&word, r + 4 * (j / 16), 4);
+      memcpy(&hw, r + cols / 4 + 4 * (j / 32), 4);
+      v = ((word >> (2 * (j % 16))) & 3u) + 4u * ((hw >> (2 * (j % 16) + (j / 16) % 2)) & 1u);
+    } else {
+      memcpy(&word, q + 4 * ((int64_t)row * words_per_row + j / per_word), 4);
+      v = (word >> (s->bits * (j % per_word))) & mask;
+    }
     uint32_t pair;
     memcpy(&pair, sb + 4 * ((int64_t)row * groups_per_row + j / s->group), 4);
     double scale = bf16_value((uint16_t)(pair & 0xFFFFu));

@@ -62,6 +62,7 @@ class MoEConfig:
 
 _FOUR = dict(bits=4, s_lo=0.001, s_hi=0.02, bias_mult=-8.0)
 _TWO = dict(bits=2, s_lo=0.004, s_hi=0.08, bias_mult=-1.5)
+_THREE = dict(bits=3, s_lo=0.002, s_hi=0.04, bias_mult=-3.5)
 
 CONFIGS = {
     # hidden 256, 8 experts, I=128, top-2 + 1 shared, 1 token
@@ -70,6 +71,8 @@ CONFIGS = {
     "decode_4bit": MoEConfig("decode_4bit", 4096, 512, 1024, 3, 1, 1, **_FOUR),
     # same layer, 2-bit experts, top-4 + 1 shared
     "decode_2bit": MoEConfig("decode_2bit", 4096, 512, 1024, 4, 1, 1, **_TWO),
+    # the same layer with 3-bit affine experts (values 0..7, bias -3.5 * scale)
+    "decode_3bit": MoEConfig("decode_3bit", 4096, 512, 1024, 4, 1, 1, **_THREE),
     # batched decode, top-10 + 1 shared, 16 tokens
     "batch16_top10": MoEConfig("batch16_top10", 4096, 512, 1024, 10, 1, 16, **_FOUR),
     # 60 resident layers, 1-token decode, top-3 + 1 shared, RMS norm between layers

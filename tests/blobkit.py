@@ -5,6 +5,10 @@ row-by-row decoder and of the HIP kernels, so that the pins can build blobs
 with chosen values and decode whole matrices with a different algorithm:
   [gate.q | up.q | down.q | gate.sb | up.sb | down.sb]
   value j of a row in word j // (32/bits) at bit bits * (j % (32/bits))
+  3-bit rows: a low-bits plane (the row's values & 3 packed as a 2-bit
+  row), then a high-bit plane of cols/32 words in which word w holds the
+  high bits of values 32w..32w+15 at the even bits and of 32w+16..32w+31
+  at the odd bits
   sb: u32 per (row, group of 64 inputs) = bf16 scale | bf16 bias << 16
 """
 from __future__ import annotations
@@ -24,8 +28,28 @@ def bf16_to_f64(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _pack_hi_plane(hi: np.ndarray) -> np.ndarray:
+    """High bits [rows, cols] -> words [rows, cols/32]: in each block of 32
+    values, the first 16 at even bits, the next 16 at odd bits."""
+    rows, cols = hi.shape
+    blk = hi.reshape(rows, cols // 32, 2, 16).astype(np.uint32)
+    shifts = (2 * np.arange(16, dtype=np.uint32))[None, None, None, :] + np.arange(2, dtype=np.uint32)[None, None, :, None]
+    return (blk << shifts).sum(axis=(2, 3), dtype=np.uint64).astype(np.uint32)
+
+
+def _unpack_hi_plane(words: np.ndarray, cols: int) -> np.ndarray:
+    rows = words.shape[0]
+    shifts = (2 * np.arange(16, dtype=np.uint32))[None, None, None, :] + np.arange(2, dtype=np.uint32)[None, None, :, None]
+    bits = (words[:, :, None, None] >> shifts) & np.uint32(1)
+    return bits.reshape(rows, cols).astype(np.int64)
+
+
 def pack_q(q: np.ndarray, bits: int) -> np.ndarray:
     rows, cols = q.shape
+    if bits == 3:
+        lo = pack_q(q & 3, 2)
+        hi = _pack_hi_plane(q >> 2)
+        return np.concatenate([lo, hi], axis=1)
     pw = 32 // bits
     words = np.zeros((rows, cols // pw), dtype=np.uint32)
     for m in range(pw):
@@ -35,6 +59,8 @@ def pack_q(q: np.ndarray, bits: int) -> np.ndarray:
 
 def unpack_q(words: np.ndarray, cols: int, bits: int) -> np.ndarray:
     rows = words.shape[0]
+    if bits == 3:
+        return unpack_q(words[:, :cols // 16], cols, 2) + 4 * _unpack_hi_plane(words[:, cols // 16:], cols)
     pw = 32 // bits
     q = np.empty((rows, cols), dtype=np.int64)
     mask = (1 << bits) - 1

@@ -37,6 +37,8 @@ def test_expert_bytes_match_page_figure():
     b4 = oracle.expert_bytes(shape(H, 1024, bits=4))
     assert b4 == 7_077_888 == int(fig["expert_size_mb"]["value"] * 2 ** 20)
     assert oracle.expert_bytes(shape(H, 1024, bits=2)) == 3_932_160
+    # 3-bit: 3 bits per value (two planes) + the same scale/bias words
+    assert oracle.expert_bytes(shape(H, 1024, bits=3)) == 3 * (H * 1024 * 3 // 8 + H * 1024 // 64 * 4) == 5_505_024
     assert oracle.expert_bytes(shape(256, 128, bits=4)) == 55_296
     for name, cfg in synth.CONFIGS.items():
         assert oracle.expert_bytes(oracle.shape_of(cfg)) == cfg.expert_bytes, name
@@ -44,7 +46,7 @@ def test_expert_bytes_match_page_figure():
 
 # --------------------------------------------------------- dequant + GEMV
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 @pytest.mark.parametrize("sec", [0, 1, 2])
 def test_zero_values_give_bias_times_group_sum(bits, sec):
     """All-zero packed values: y_r = sum_g b_{r,g} * X_g, X_g = sum of x over group g."""
@@ -63,7 +65,7 @@ def test_zero_values_give_bias_times_group_sum(bits, sec):
     np.testing.assert_allclose(y, expect, rtol=1e-12, atol=1e-14)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_one_hot_input_recovers_dequantised_column(bits):
     """x = e_j: y_r = scale_{r, j//64} * q_{r,j} + bias_{r, j//64}."""
     rng = np.random.default_rng(2)
@@ -96,7 +98,7 @@ def test_hand_worked_row():
     assert np.all(y == -16.0)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_constant_values(bits):
     """Every packed value = c: y_r = sum_g (c * s_{r,g} + b_{r,g}) * X_g."""
     rng = np.random.default_rng(3)
@@ -113,13 +115,13 @@ def test_constant_values(bits):
     np.testing.assert_allclose(y, expect, rtol=1e-12)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_three_algebraic_forms_agree(bits):
     """Explicit dequantise-then-dot (oracle) == the FMA form on the Flash-MoE
     page, sum_j fma(q_j, s*x_j, b*x_j) ('Noyau de déquantification optimisé
     FMA') == the per-group form s*sum(q x) + b*sum(x), to fp64 rounding."""
     cfg = synth.CONFIGS["tiny"] if bits == 4 else synth.with_changes(
-        synth.CONFIGS["decode_2bit"], hidden=256, inter=128, n_experts=8)
+        synth.CONFIGS[f"decode_{bits}bit"], hidden=256, inter=128, n_experts=8)
     blob = synth.expert_blob(cfg, 0, 1)
     x = bk.bf16_to_f64(synth.tokens(cfg, 0, 1)[0])
     y = oracle.section_matvec(oracle.shape_of(cfg), blob, 0, x)
@@ -135,7 +137,7 @@ def test_three_algebraic_forms_agree(bits):
     np.testing.assert_allclose(y, group_form, rtol=0, atol=1e-12 * scale)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_2bit"])
+@pytest.mark.parametrize("name", ["tiny", "decode_2bit", "decode_3bit"])
 def test_section_matvec_equals_dense_decode_and_matmul(name):
     """The oracle's row loop equals a dense decode (vectorised, test-side)
     followed by numpy's matmul, on the generator's own blobs."""
@@ -167,6 +169,45 @@ def test_two_bit_expert_in_four_bit_container_is_identical():
     o4 = oracle.expert_ffn(shape(H, I, bits=4), b4, x)
     for a, b in zip(o2, o4):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("lo_bits,hi_bits,qmax", [(3, 4, 7), (2, 3, 3)])
+def test_narrower_values_in_wider_container_are_identical(lo_bits, hi_bits, qmax):
+    """The same values (0..qmax), scales and biases packed as 3-bit and as
+    4-bit, or as 2-bit and as 3-bit, give a bit-identical expert output: the
+    3-bit planes decode to the values a plain packing holds."""
+    rng = np.random.default_rng(6)
+    H, I = 256, 128
+    mats = bk.random_mats(rng, H, I, lo_bits, qmax=qmax, s_range=(0.002, 0.04), bias_mult=-3.5)
+    a = bk.build_blob(H, I, lo_bits, mats)
+    b = bk.build_blob(H, I, hi_bits, mats)
+    x = rng.standard_normal(H)
+    oa = oracle.expert_ffn(shape(H, I, bits=lo_bits), a, x)
+    ob = oracle.expert_ffn(shape(H, I, bits=hi_bits), b, x)
+    for u, v in zip(oa, ob):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_three_bit_plane_positions_hand_worked():
+    """One 3-bit row of 64 values written bit by bit from the layout rule
+    (low plane: value j's two low bits at bit 2(j mod 16) of word j/16; high
+    plane: value j's high bit at bit 2(j mod 16) + (j/16 mod 2) of word j/32)
+    decodes to the values: a transposed plane or a wrong bit offset fails."""
+    H, I = 64, 64
+    vals = (np.arange(64) * 5 + 3) % 8
+    lo = np.zeros(4, dtype=np.uint32)
+    hi = np.zeros(2, dtype=np.uint32)
+    for j, v in enumerate(vals):
+        lo[j // 16] |= np.uint32((int(v) & 3) << (2 * (j % 16)))
+        hi[j // 32] |= np.uint32((int(v) >> 2) << (2 * (j % 16) + (j // 16) % 2))
+    row = np.concatenate([lo, hi])
+    q = np.tile(vals, (I, 1))
+    mats = {n: (q if n != "down" else np.tile(vals, (H, 1)), bk.f64_to_bf16(np.full((r, 1), 0.5)),
+                bk.f64_to_bf16(np.full((r, 1), -1.0))) for n, r in (("gate", I), ("up", I), ("down", H))}
+    blob = bk.build_blob(H, I, 3, mats)
+    assert np.array_equal(blob[:24].view(np.uint32), row)
+    w = oracle.dequant_row(shape(H, I, bits=3), blob, 0, 0)
+    np.testing.assert_array_equal(w, 0.5 * vals - 1.0)
 
 
 # ------------------------------------------------------------------ routing
