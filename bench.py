@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--workload", default="stack60_decode",
                    choices=["stack60_decode", "decode_4bit", "decode_2bit", "batch16_top10", "stack60_prefill",
-                            "stack60_prefill_4k", "stack60_prefill_8k", "pool_decode"])
+                            "stack60_prefill_4k", "stack60_prefill_8k", "pool_decode", "decode_3bit"])
     p.add_argument("--layerwise", action="store_true",
                    help="stack60_decode: per-layer launches instead of the persistent kernel")
     p.add_argument("--fused-layer", action="store_true",

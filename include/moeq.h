@@ -91,7 +91,7 @@ typedef struct moeq_shape {
   int32_t inter;      /* I, multiple of 64 */
   int32_t n_experts;  /* E routed experts per layer */
   int32_t n_shared;   /* S always-active experts per layer, 0 or 1 */
-  int32_t bits;       /* 4 or 2 */
+  int32_t bits;       /* 4, 3 or 2 (3: hidden and inter multiples of 128) */
   int32_t group;      /* 64 */
 } moeq_shape;
 
@@ -214,6 +214,21 @@ int moe_expert_stack_decode_noalloc(const moeq_shape* shape, const moeq_experts*
                                     const uint16_t* const* w_router, int layer0, int L, int T, int k,
                                     uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
                                     int32_t* status_out, void* stream);
+
+/* moe_expert_stack_decode over layers of different widths (per-layer mixes
+ * of 4-, 3- and 2-bit experts; Flash-MoE, fr.news.hada.io, "Résultats de
+ * performance": 4-bit and 2-bit expert sets; openclawradar.com/ru,
+ * "Эффективные оптимизации": lower-bit experts).  layer_bits: host [L],
+ * layer layer0 + l holds blobs of layer_bits[l] bits; every other argument
+ * as moe_expert_stack_decode with shape.bits ignored.  Each maximal run of
+ * layers of one width is one moe_expert_stack_decode call (persistent
+ * where the width has a persistent instantiation, else per-layer
+ * launches); moeq_last_stack_path then reports 1 or 2 if every run took
+ * that path, 3 if they differed. */
+int moe_expert_stack_decode_mixed(const moeq_shape* shape, const int32_t* layer_bits, const moeq_experts* experts,
+                                  const uint16_t* const* w_router, int layer0, int L, int T, int k,
+                                  uint32_t flags, float* h, int32_t* topk_trace, float* h_trace,
+                                  void* workspace, void* stream);
 
 /* Prefill: T tokens (any T >= 1; the configured workload is 2048) through
  * the stacked layers [layer0, layer0 + L) on the fp32 residual stream h

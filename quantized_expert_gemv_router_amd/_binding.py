@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moeq_stack_clock_trace.argtypes = [_P]
         L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                               _P, _P]
+        L.moe_expert_stack_decode_mixed.argtypes = [S, _P, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
+                                                    _P, _P]
         L.moe_expert_stack_decode_noalloc.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                                       _P, _P]
         L.moe_expert_stack_prefill.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P, _P]
@@ -267,6 +269,26 @@ def moe_expert_stack_decode(shape: Shape, experts: ExpertTable, routers: RouterT
     _check(lib().moe_expert_stack_decode(ctypes.byref(shape), experts.view(), routers.ptr(), layer0, L, T,
                                          k, flags, _ptr(h), _ptr(tk), _ptr(hk), _ptr(workspace),
                                          _stream(stream)))
+    return (tk, hk) if trace else None
+
+
+def moe_expert_stack_decode_mixed(shape: Shape, layer_bits, experts: ExpertTable, routers: RouterTable,
+                                  h: torch.Tensor, k: int, layer0: int = 0, flags: int = 0,
+                                  workspace: torch.Tensor | None = None, trace: bool = False, stream=None):
+    """moe_expert_stack_decode over layers of different widths: layer_bits[l]
+    bits for layer layer0 + l.  Returns (topk_trace, h_trace) when trace."""
+    T = h.shape[0]
+    L = len(layer_bits)
+    if workspace is None:
+        workspace = new_workspace(shape, T, k, h.device)
+    bits = (ctypes.c_int32 * max(L, 1))(*[int(b) for b in layer_bits])
+    tk = hk = None
+    if trace:
+        tk = torch.empty((L, T, k), dtype=torch.int32, device=h.device)
+        hk = torch.empty((L, T, shape.hidden), dtype=torch.float32, device=h.device)
+    _check(lib().moe_expert_stack_decode_mixed(ctypes.byref(shape), ctypes.cast(bits, _P), experts.view(),
+                                               routers.ptr(), layer0, L, T, k, flags, _ptr(h), _ptr(tk), _ptr(hk),
+                                               _ptr(workspace), _stream(stream)))
     return (tk, hk) if trace else None
 
 

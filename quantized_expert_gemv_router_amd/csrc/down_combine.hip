@@ -1,4 +1,4 @@
-// SwiGLU, down projection and weighted combine (Flash-MoE,
+// SwiGLU, down projection and weighted combine of 4-, 3- or 2-bit experts (Flash-MoE,
 // fr.news.hada.io, "Shaders de calcul Metal": SwiGLU and MoE combine +
 // residual + gate; "Deferred GPU Expert Compute": the combined output stays
 // on the GPU for the next layer):
@@ -47,6 +47,7 @@ struct DownTile {
   static constexpr int RPS = 64 / LPR;
   static constexpr int STEPS = (ROWS + RPS - 1) / RPS;
   u32x4 q[STEPS][CPL];
+  uint2 qh[STEPS][CPL];   // 3-bit: the chunk's high-bit plane
   uint32_t sbw[STEPS][CPL];
 
   __device__ __forceinline__ void load(const uint8_t* blob, int H, int I, int wrow0, int lane) {
@@ -63,8 +64,10 @@ struct DownTile {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int cc = sub + LPR * c;
+        qh[s][c] = make_uint2(0u, 0u);
         if (row_ok && cc < nch) {
           q[s][c] = load_stream(reinterpret_cast<const u32x4*>(blob + qoff + r * row_bytes) + cc);
+          if constexpr (BITS == 3) qh[s][c] = load_stream_u2(blob + qoff + r * row_bytes + I / 4 + 8 * cc);
           sbw[s][c] = load_stream(sb + (int64_t)r * gpr + (cc * PC) / 64);
         } else {
           q[s][c] = u32x4{0u, 0u, 0u, 0u};
@@ -82,7 +85,9 @@ struct DownTile {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int cc = sub + LPR * c;
-      if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[s][c], xp, cc, nch), sbw[s][c], xs + kChunkSums * cc);
+      if (cc < nch)
+        part += chunk_term<BITS>(chunk_dot_q<BITS>(q[s][c], qh[s][c], load_xchunk<BITS>(xp, cc, nch)), sbw[s][c],
+                                 *reinterpret_cast<const float2*>(xs + kChunkSums * cc));
     }
     return group_sum_dpp<LPR>(part) * undo;
   }
@@ -130,6 +135,7 @@ struct DownRows {
   static constexpr int RW = STEPS * RPS;          // rows per wave per tile
   static constexpr int TR = kWaves * RW;          // rows per tile
   u32x4 q[STEPS][CPL];
+  uint2 qh[STEPS][CPL];   // 3-bit: the chunk's high-bit plane
   uint32_t sb[STEPS][CPL];
 };
 
@@ -155,6 +161,14 @@ __device__ __forceinline__ void issue_down_tile(DownRows<BITS, LPR, CPL>& t, rsr
       const uint32_t qo = ok ? (uint32_t)r * (uint32_t)row_bytes + 16u * (uint32_t)cc : q_bytes;
       const uint32_t so = ok ? 4u * ((uint32_t)r * (uint32_t)gpr + (uint32_t)(cc * PC / 64)) : s_bytes;
       t.q[s][c] = load_rsrc_b128(rq, qo);
+      if constexpr (BITS == 3) {
+        // the high-bit plane follows the low plane (2/3 of the row's bytes)
+        const uint32_t ho = ok ? (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(2 * row_bytes / 3) + 8u * (uint32_t)cc
+                               : q_bytes;
+        t.qh[s][c] = load_rsrc_b64(rq, ho);
+      } else {
+        t.qh[s][c] = make_uint2(0u, 0u);
+      }
       t.sb[s][c] = load_rsrc_b32(rs, so);
     }
   }
@@ -201,7 +215,7 @@ __device__ __forceinline__ void apply_down_tile(const DownRows<BITS, LPR, CPL>& 
         } else {
 #pragma unroll
           for (int m = 0; m < MMAX; ++m)
-            if (m < nv) part[s][m] += chunk_affine(chunk_dot<BITS>(t.q[s][c], xc[m]), t.sb[s][c], x2[m]);
+            if (m < nv) part[s][m] += chunk_term<BITS>(chunk_dot_q<BITS>(t.q[s][c], t.qh[s][c], xc[m]), t.sb[s][c], x2[m]);
         }
       }
     }
@@ -448,7 +462,7 @@ hipError_t launch_t(const DownArgs& a, hipStream_t stream) {
 
 template <int BITS, int LPR, int CPL>
 hipError_t launch_w(const DownArgs& a, hipStream_t stream) {
-  const int nwords = a.I * BITS / 32;
+  const int nwords = a.I / Pack<BITS>::kPerWord;   // staged words per activation vector
   const int wmax = (nwords + kThreads - 1) / kThreads;
   if (wmax <= 1) return launch_t<BITS, LPR, CPL, 1>(a, stream);
   if (wmax <= 2) return launch_t<BITS, LPR, CPL, 2>(a, stream);
@@ -472,7 +486,9 @@ hipError_t launch_bits(const DownArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_down_combine(const DownArgs& a, hipStream_t stream) {
-  return a.bits == 4 ? launch_bits<4>(a, stream) : launch_bits<2>(a, stream);
+  if (a.bits == 4) return launch_bits<4>(a, stream);
+  if (a.bits == 3) return launch_bits<3>(a, stream);
+  return launch_bits<2>(a, stream);
 }
 
 }  // namespace moeq

@@ -1,5 +1,5 @@
 // Gate and up projections of the selected experts and the shared expert:
-// group-wise affine 4-bit / 2-bit dequantised mat-vec (Flash-MoE,
+// group-wise affine 4-bit / 3-bit / 2-bit dequantised mat-vec (Flash-MoE,
 // fr.news.hada.io, "Noyau de déquantification optimisé FMA" and "Shaders de
 // calcul Metal").  For row r of [gate; up] and token t:
 //   y[r] = sum_g ( s[r,g] * sum_{j in g} q[r,j] x[t,j] + b[r,g] * sum_{j in g} x[t,j] )
@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
   const int row0 = rb * RPB + wave * RPW;
 
   u32x4 q[RPW][CPL];
+  uint2 qh[RPW][CPL];   // 3-bit: the chunk's high-bit plane
   uint32_t sbw[RPW][CPL];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -75,8 +76,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int cc = lane + 64 * c;
+      qh[i][c] = make_uint2(0u, 0u);
       if (r < 2 * I && cc < nch) {
         q[i][c] = load_stream(reinterpret_cast<const u32x4*>(blob + r * row_bytes) + cc);
+        if constexpr (BITS == 3) qh[i][c] = load_stream_u2(blob + r * row_bytes + H / 4 + 8 * cc);
         sbw[i][c] = load_stream(sb + (int64_t)r * gpr + (cc * PC) / 64);
       } else {
         q[i][c] = u32x4{0u, 0u, 0u, 0u};
@@ -103,7 +106,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int n_rb, in
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int cc = lane + 64 * c;
-          if (cc < nch) part += chunk_affine(chunk_dot<BITS>(q[i][c], xp, cc, nch), sbw[i][c], xs + kChunkSums * cc);
+          if (cc < nch)
+            part += chunk_term<BITS>(chunk_dot_q<BITS>(q[i][c], qh[i][c], load_xchunk<BITS>(xp, cc, nch)), sbw[i][c],
+                                     *reinterpret_cast<const float2*>(xs + kChunkSums * cc));
         }
         const float v = wave_sum_dpp(part) * undo[m];
         if (lane == 0) {
@@ -125,6 +130,7 @@ constexpr int kTileRows = kWaves * kBatchRPW;     // rows per tile
 template <int BITS, int CPL>
 struct GuTile {
   u32x4 q[kBatchRPW][CPL];
+  uint2 qh[kBatchRPW][CPL];   // 3-bit: the chunk's high-bit plane
   uint32_t sb[kBatchRPW][CPL];
 };
 
@@ -149,6 +155,14 @@ __device__ __forceinline__ void issue_gu_tile(GuTile<BITS, CPL>& t, rsrc_t rq, r
       const uint32_t qo = ok ? (uint32_t)r * (uint32_t)row_bytes + 16u * (uint32_t)cc : q_bytes;
       const uint32_t so = ok ? 4u * ((uint32_t)r * (uint32_t)gpr + (uint32_t)(cc * PC / 64)) : s_bytes;
       t.q[i][c] = load_rsrc_b128(rq, qo);
+      if constexpr (BITS == 3) {
+        // the high-bit plane follows the low plane (2/3 of the row's bytes)
+        const uint32_t ho = ok ? (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(2 * row_bytes / 3) + 8u * (uint32_t)cc
+                               : q_bytes;
+        t.qh[i][c] = load_rsrc_b64(rq, ho);
+      } else {
+        t.qh[i][c] = make_uint2(0u, 0u);
+      }
       t.sb[i][c] = load_rsrc_b32(rs, so);
     }
   }
@@ -242,7 +256,7 @@ __device__ __forceinline__ void apply_gu_tile(const GuTile<BITS, CPL>& t, const 
             const float2 x2 = *reinterpret_cast<const float2*>(xs + kChunkSums * cc);
 #pragma unroll
             for (int i = 0; i < kBatchRPW; ++i)
-              part[i][m] += chunk_affine(chunk_dot<BITS>(t.q[i][c], xc), t.sb[i][c], x2);
+              part[i][m] += chunk_term<BITS>(chunk_dot_q<BITS>(t.q[i][c], t.qh[i][c], xc), t.sb[i][c], x2);
           }
         }
       }
@@ -411,9 +425,10 @@ hipError_t launch_rpw(const GemvArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_expert_gemv(const GemvArgs& a, hipStream_t stream) {
-  const int nch = a.H * a.bits / 128;                 // 16-byte chunks per row
+  const int pbits = a.bits == 3 ? 2 : a.bits;         // the staged layout's (low plane's) bits
+  const int nch = a.H * pbits / 128;                  // 16-byte (low-plane) chunks per row
   const int cpl = (nch + 63) / 64;
-  const int nwords = a.H * a.bits / 32;               // packed words per input vector
+  const int nwords = a.H * pbits / 32;                // staged words per input vector
   const int wmax = (nwords + kThreads - 1) / kThreads;
   if (a.T > 1) {
     const int cus = cu_count();
@@ -422,6 +437,10 @@ hipError_t launch_expert_gemv(const GemvArgs& a, hipStream_t stream) {
       if (cpl <= 2) return wmax <= 2 ? launch_batch<4, 2, 2>(a, stream, cus) : launch_batch<4, 2, 4>(a, stream, cus);
       return launch_batch<4, 4, 4>(a, stream, cus);
     }
+    if (a.bits == 3) {
+      if (cpl <= 1) return launch_batch<3, 1, 1>(a, stream, cus);
+      return launch_batch<3, 2, 2>(a, stream, cus);
+    }
     if (cpl <= 1) return launch_batch<2, 1, 1>(a, stream, cus);
     return launch_batch<2, 2, 2>(a, stream, cus);
   }
@@ -429,6 +448,10 @@ hipError_t launch_expert_gemv(const GemvArgs& a, hipStream_t stream) {
     if (cpl <= 1) return wmax <= 1 ? launch_rpw<4, 1, 1>(a, stream) : launch_rpw<4, 1, 2>(a, stream);
     if (cpl <= 2) return wmax <= 2 ? launch_rpw<4, 2, 2>(a, stream) : launch_rpw<4, 2, 4>(a, stream);
     return launch_rpw<4, 4, 4>(a, stream);
+  }
+  if (a.bits == 3) {
+    if (cpl <= 1) return launch_rpw<3, 1, 1>(a, stream);
+    return launch_rpw<3, 2, 2>(a, stream);
   }
   if (cpl <= 1) return launch_rpw<2, 1, 1>(a, stream);
   return launch_rpw<2, 2, 2>(a, stream);

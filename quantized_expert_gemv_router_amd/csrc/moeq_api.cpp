@@ -41,12 +41,15 @@ int check_shape(const moeq_shape* s) {
   if (s->hidden <= 0 || s->inter <= 0 || s->n_experts <= 0 || s->n_shared < 0)
     return fail(MOEQ_E_INVALID, "shape sizes must be positive (hidden=%d inter=%d n_experts=%d n_shared=%d)",
                 s->hidden, s->inter, s->n_experts, s->n_shared);
-  if (s->bits != 4 && s->bits != 2)
-    return fail(MOEQ_E_UNSUPPORTED, "bits=%d: only 4-bit and 2-bit experts are implemented", s->bits);
+  if (s->bits != 4 && s->bits != 3 && s->bits != 2)
+    return fail(MOEQ_E_UNSUPPORTED, "bits=%d: only 4-, 3- and 2-bit experts are implemented", s->bits);
   if (s->group != 64)
     return fail(MOEQ_E_UNSUPPORTED, "group=%d: only groups of 64 are implemented", s->group);
   if (s->hidden % 64 || s->inter % 64)
     return fail(MOEQ_E_UNSUPPORTED, "hidden=%d inter=%d must be multiples of 64", s->hidden, s->inter);
+  if (s->bits == 3 && (s->hidden % 128 || s->inter % 128))
+    return fail(MOEQ_E_UNSUPPORTED, "3-bit experts need hidden=%d and inter=%d to be multiples of 128 "
+                "(16-byte aligned rows)", s->hidden, s->inter);
   if (s->hidden > MOEQ_MAX_HIDDEN || s->inter > MOEQ_MAX_INTER)
     return fail(MOEQ_E_UNSUPPORTED, "hidden=%d inter=%d exceed %d/%d", s->hidden, s->inter,
                 MOEQ_MAX_HIDDEN, MOEQ_MAX_INTER);
@@ -316,6 +319,35 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
   }
   (void)KS;
   g_last_stack_path = 2;
+  return ok();
+}
+
+int moe_expert_stack_decode_mixed(const moeq_shape* s, const int32_t* layer_bits, const moeq_experts* ex,
+                                  const uint16_t* const* w_router, int layer0, int L, int T, int k, uint32_t flags,
+                                  float* h, int32_t* topk_trace, float* h_trace, void* workspace, void* stream) {
+  if (int rc = check_shape(s)) return rc;
+  if (L < 0) return fail(MOEQ_E_INVALID, "L=%d is negative", L);
+  if (L > 0 && !layer_bits) return fail(MOEQ_E_INVALID, "layer_bits is NULL");
+  for (int l = 0; l < L; ++l) {
+    moeq_shape sl = *s;
+    sl.bits = layer_bits[l];
+    if (int rc = check_shape(&sl)) return rc;
+  }
+  // maximal runs of layers of equal width, each one stack call
+  int paths = 0;
+  for (int l = 0; l < L;) {
+    int e = l + 1;
+    while (e < L && layer_bits[e] == layer_bits[l]) ++e;
+    moeq_shape sl = *s;
+    sl.bits = layer_bits[l];
+    int rc = moe_expert_stack_decode(&sl, ex, w_router, layer0 + l, e - l, T, k, flags, h,
+                                     topk_trace ? topk_trace + (int64_t)l * T * k : nullptr,
+                                     h_trace ? h_trace + (int64_t)l * T * s->hidden : nullptr, workspace, stream);
+    if (rc != MOEQ_OK) return rc;
+    paths |= 1 << g_last_stack_path;
+    l = e;
+  }
+  g_last_stack_path = paths == (1 << 1) ? 1 : (paths == (1 << 2) ? 2 : (paths ? 3 : 0));
   return ok();
 }
 

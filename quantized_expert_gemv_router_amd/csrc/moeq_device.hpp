@@ -106,6 +106,15 @@ template <> struct Pack<2> {
   static constexpr int kPerWord = 16, kPairsPerWord = 8, kPerChunk = 64, kUnitsPerChunk = 8;
   static constexpr float kSlotDiv[8] = {1.0f, 4.0f, 16.0f, 64.0f, 256.0f, 1.0f, 4.0f, 16.0f};
 };
+// 3-bit experts: a row holds a low-bits plane (the values' two low bits,
+// packed as a 2-bit row) followed by a high-bit plane of cols/32 words in
+// which word w holds the high bit of value 32w + m at bit 2m and of value
+// 32w + 16 + m at bit 2m + 1 (m < 16).  A chunk of 64 values is one 16-byte
+// unit of the low plane plus 8 bytes of the high plane, and the activations
+// are staged exactly as for 2-bit values.
+template <> struct Pack<3> : Pack<2> {};
+// Bits of packed values per staged chunk's low plane (the 16-byte unit).
+template <int BITS> constexpr int kPlaneBits = BITS == 3 ? 2 : BITS;
 // Floats of precomputed sums per staged chunk: X and 1024 * X'.
 constexpr int kChunkSums = 2;
 
@@ -170,6 +179,49 @@ __device__ __forceinline__ float chunk_dot(u32x4 q, const XChunk<BITS>& x) {
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* __restrict__ vec, int cc, int nch) {
   return chunk_dot<BITS>(q, load_xchunk<BITS>(vec, cc, nch));
+}
+
+// The high-bit plane of a 3-bit chunk against the chunk's staged pairs: for
+// low-plane word i the high bits sit at the even (i even) or odd (i odd) bits
+// of plane word i/2; shifted down by that parity each sits at the low bit of
+// its value's 2-bit field, so the 2-bit staging (pair slot m divided by 4^m)
+// serves them and the sum is 1024 X' + sum(high * x).
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_hi(uint2 h, const XChunk<BITS>& x) {
+  float acc = 0.0f;
+  const uint32_t mg = magic_pair();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 xa = x.u[2 * i], xb = x.u[2 * i + 1];
+    const uint32_t hw = (i >> 1) ? h.y : h.x;
+    const uint32_t w = (i & 1) ? hw >> 1 : hw, t = w >> 10;
+    acc = dot2((w & 0x00010001u) | mg, xa.x, acc);
+    acc = dot2((w & 0x00040004u) | mg, xa.y, acc);
+    acc = dot2((w & 0x00100010u) | mg, xa.z, acc);
+    acc = dot2((w & 0x00400040u) | mg, xa.w, acc);
+    acc = dot2((w & 0x01000100u) | mg, xb.x, acc);
+    acc = dot2((t & 0x00010001u) | mg, xb.y, acc);
+    acc = dot2((t & 0x00040004u) | mg, xb.z, acc);
+    acc = dot2((t & 0x00100010u) | mg, xb.w, acc);
+  }
+  return acc;
+}
+
+// Magic-exponent sum of one chunk of BITS-bit values: the low plane (or the
+// whole value) from q, at 3 bits plus 4 times the high plane from qh.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot_q(u32x4 q, uint2 qh, const XChunk<BITS>& x) {
+  if constexpr (BITS == 3) return chunk_dot<BITS>(q, x) + 4.0f * chunk_dot_hi<BITS>(qh, x);
+  else return chunk_dot<BITS>(q, x);
+}
+
+// One chunk's contribution s * (dot - n 1024 X') + b * X, n being the number
+// of 1024 X' offsets the sum carries (5 at 3 bits: one from the low plane,
+// four from the high plane's weight of 4).
+template <int BITS>
+__device__ __forceinline__ float chunk_term(float dot, uint32_t sb, float2 x) {
+  constexpr float kOffsets = BITS == 3 ? 5.0f : 1.0f;
+  return fmaf(bf16_lo(sb), dot - kOffsets * x.y, bf16_hi(sb) * x.x);
 }
 
 // One chunk's contribution: s * (dot - 1024 X') + b * X, with x the
@@ -247,6 +299,13 @@ __device__ __forceinline__ T load_stream(const T* p) {
   return __builtin_nontemporal_load((GlobalT*)p);
 }
 
+// Eight bytes at p (8-byte aligned), streamed.
+__device__ __forceinline__ uint2 load_stream_u2(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = load_stream(static_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // A global load with the default (temporal) cache policy: the L2 keeps the
 // line.  For data whose line is consumed by more than one request (a row
 // read in 64-byte halves a chunk apart, activation rows re-read by the
@@ -276,6 +335,11 @@ __device__ __forceinline__ u32x4 load_rsrc_b128(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t load_rsrc_b32(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCpolNonTemporal);
+}
+__device__ __forceinline__ uint2 load_rsrc_b64(rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCpolNonTemporal));
+  return make_uint2(v.x, v.y);
 }
 // Keeps the compiler from sinking loads issued above it into the branches
 // that use them (no wait is implied).

@@ -50,9 +50,82 @@ def run_and_check(cfg, flags=0, shared_gate=None, x_np=None, x_dev=None, check_g
     return out, ref
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit", "batch16_top10"])
+@pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit", "decode_3bit", "batch16_top10"])
 def test_config_parity(name):
     run_and_check(synth.CONFIGS[name])
+
+
+@pytest.mark.parametrize("H,I,E,k,T", [(256, 128, 8, 2, 1), (384, 256, 37, 5, 3), (4096, 1024, 512, 10, 16),
+                                       (8192, 8192, 6, 2, 2)])
+def test_three_bit_shapes(H, I, E, k, T):
+    """3-bit experts (two bit planes) through the one-token and the batched
+    kernels: small, ragged (not multiples of the tiles), the 16-token top-10
+    batch, and the widest rows."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_3bit"], name=f"q3_{H}_{T}", hidden=H, inter=I, n_experts=E,
+                             top_k=k, tokens=T)
+    run_and_check(cfg)
+
+
+def _arena_from_blobs(blobs, stride):
+    host = np.zeros((len(blobs), stride), dtype=np.uint8)
+    for e, b in enumerate(blobs):
+        host[e, :b.size] = b
+    return torch.from_numpy(host.reshape(-1)).cuda()
+
+
+def test_two_bit_values_in_four_bit_container():
+    """The same 2-bit values, scales and biases as a 2-bit layer and as a
+    4-bit layer: the fp64 oracle gives bit-identical results for both (a
+    pinned invariant); the GPU, whose two paths stage and dequantise
+    differently, gives the same top-K and both outputs within the bar of it."""
+    from tests import blobkit as bk
+    H, I, E, K = 256, 128, 8, 2
+    rng = np.random.default_rng(77)
+    mats = [bk.random_mats(rng, H, I, 2, s_range=(0.004, 0.08), bias_mult=-1.5) for _ in range(E + 1)]
+    wr = bk.f64_to_bf16(rng.standard_normal((E, H)) * 0.02)
+    x_np = bk.f64_to_bf16(rng.standard_normal((3, H)))
+    x64 = bk.bf16_to_f64(x_np)
+    outs = {}
+    for bits in (2, 4):
+        blobs = [bk.build_blob(H, I, bits, m) for m in mats]
+        stride = (blobs[0].size + 255) // 256 * 256
+        shape = q.Shape(H, I, E, 1, bits, 64)
+        ex = q.ExpertTable(shape, [_arena_from_blobs(blobs, stride)], stride)
+        out = q.moe_layer(shape, ex, 0, bf16_dev(x_np), bf16_dev(wr), K)
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(oracle.Shape(H, I, E, 1, bits, 64), dict(enumerate(blobs)), wr, x64, K)
+        outs[bits] = (out, ref)
+    assert np.array_equal(outs[2][1]["y"], outs[4][1]["y"])
+    for bits in (2, 4):
+        out, ref = outs[bits]
+        assert np.array_equal(out["idx"].cpu().numpy(), ref["idx"])
+        assert_close(out["y"].cpu().numpy(), ref["y"], f"{bits}-bit container output")
+    assert torch.equal(outs[2][0]["idx"], outs[4][0]["idx"])
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_expert_permutation_invariance(T):
+    """Permuting the routed experts (blobs and router rows together): the
+    selection maps through the permutation and the layer output is
+    bit-identical (each selected expert meets the same arithmetic in the same
+    slot)."""
+    cfg = synth.with_changes(synth.CONFIGS["tiny"], name="perm", n_experts=32, top_k=4, tokens=T)
+    shape = q.Shape.of(cfg)
+    stride = (cfg.expert_bytes + 255) // 256 * 256
+    host = synth.layer_blobs(cfg, 0, stride)
+    perm = np.random.default_rng(5).permutation(cfg.n_experts)   # new index n holds old expert perm[n]
+    host_p = host.copy()
+    host_p[:cfg.n_experts] = host[perm]
+    wr = synth.router(cfg, 0)
+    x = bf16_dev(synth.tokens(cfg, 9, T))
+    res = []
+    for h_, w_ in ((host, wr), (host_p, wr[perm])):
+        ex = q.ExpertTable(shape, [torch.from_numpy(h_.reshape(-1)).cuda()], stride)
+        res.append(q.moe_layer(shape, ex, 0, x, bf16_dev(np.ascontiguousarray(w_)), cfg.top_k))
+    torch.cuda.synchronize()
+    a, b = res
+    assert np.array_equal(perm[b["idx"].cpu().numpy()], a["idx"].cpu().numpy())
+    assert torch.equal(a["y"], b["y"])
 
 
 @pytest.mark.parametrize("bits", [4, 2])

@@ -130,6 +130,46 @@ def test_single_layer_no_norm_matches_oracle(name):
                 assert_close(h.cpu().numpy(), exp["y"], f"{name} layer {layer} flags {flags}")
 
 
+def _width_cfg(base, bits):
+    src = synth.CONFIGS[{4: "decode_4bit", 3: "decode_3bit", 2: "decode_2bit"}[bits]]
+    return synth.with_changes(base, bits=bits, s_lo=src.s_lo, s_hi=src.s_hi, bias_mult=src.bias_mult)
+
+
+def test_stack_mixed_widths_full_width():
+    """A stack whose layers hold 4-, 2- and 3-bit experts (hidden 4096, 512
+    experts, top-3 + 1 shared): moe_expert_stack_decode_mixed runs each run
+    of equal width as one stack call (persistent for 4 and 2 bits, per-layer
+    launches for 3 bits); every layer is checked against the oracle of its
+    own width on the GPU's input (teacher forcing)."""
+    base = synth.with_changes(synth.CONFIGS["stack60_decode"], name="mixed", layers=5)
+    bits = [4, 2, 2, 3, 4]
+    shape = q.Shape.of(base)
+    arenas = []
+    for l, b in enumerate(bits):
+        cl = _width_cfg(base, b)
+        stride = slot_stride(cl)
+        a = torch.empty(cl.n_slots * stride, dtype=torch.uint8, device="cuda")
+        synth.device_fill_experts(cl, l, a.data_ptr(), stride)
+        arenas.append((a, stride))
+    ptrs = torch.tensor([a.data_ptr() + e * st for a, st in arenas for e in range(base.n_slots)],
+                        dtype=torch.int64, device="cuda")
+    ex = q.ExpertTable.from_pointers(ptrs, len(bits))
+    rt = q.RouterTable([bf16_dev(synth.router(base, l)) for l in range(len(bits))])
+    torch.cuda.synchronize()
+    for ts in (0, 1):
+        h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(base, ts, 1)).astype(np.float32)).cuda()
+        ws = q.new_workspace(shape, 1, base.top_k)
+        tk, hk = q.moe_expert_stack_decode_mixed(shape, bits, ex, rt, h, base.top_k, workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == 3
+        assert q.moe_read_device_status(ws) == 0
+        hs = hk.cpu().numpy()[:, 0, :].astype(np.float64)
+        outs = [hs[l + 1] for l in range(len(bits) - 1)] + [h.cpu().numpy()[0].astype(np.float64)]
+        for l, b in enumerate(bits):
+            exp = oracle.run_layer(_width_cfg(base, b), l, hs[l][None, :], want_intermediates=False)
+            assert np.array_equal(tk.cpu().numpy()[l, 0], exp["idx"][0]), (ts, l, b)
+            assert_close(outs[l], exp["y"][0], f"mixed stack layer {l} ({b}-bit)")
+
+
 def test_stack_2bit_full_width():
     """The 2-bit persistent instantiation (hidden 4096, 512 experts, top-4 +
     1 shared) on three layers, gated per layer along its own trajectory."""
