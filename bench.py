@@ -62,6 +62,9 @@ def parse():
                    help="pool_decode: layers held in pinned host memory (7.08 MB x 513 per layer)")
     p.add_argument("--pool-slots", default="8,20,64,513", help="pool_decode: slots per layer to sweep")
     p.add_argument("--pool-streams", default="1,4", help="pool_decode: copy streams to sweep")
+    p.add_argument("--pool-reuse", default="0,0.6,0.9",
+                   help="pool_decode: token correlation a (token t+1 = a token t + sqrt(1-a^2) fresh) to sweep, "
+                        "with and without prefetch of the previous token's experts")
     p.add_argument("--probe-handoff", action="store_true",
                    help="only run the cross-workgroup hand-off latency probe sweep (diagnostic)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -741,14 +744,24 @@ def run_pool(args, cfg, dev, stream):
     ids_host = torch.empty((1, K), dtype=torch.int32, pin_memory=True)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(int(c) for c in args.pool_streams.split(",")))]
 
-    def token(pool, h, trace=None):
+    def token(pool, h, trace=None, prev=None, prefetch=False):
         for l in range(L):
             if trace is not None:
                 trace.append(h.clone())
+            if prefetch and prev is not None and prev[l] is not None:
+                # before this layer's routing resolves: the previous token's
+                # experts of the layer start their copies
+                pool.prefetch(l, prev[l])
             q.moe_router_topk(shape, h, routers[l], K, q.F_RMSNORM, None, ws, out=(idx, w, sw), stream=stream)
             ids_host.copy_(idx, non_blocking=True)
             stream.synchronize()
-            view = pool.acquire(l, ids_host[0].tolist() + list(range(E, P)), stream=stream)
+            sel = ids_host[0].tolist()
+            if prev is not None:
+                if prev[l] is not None:
+                    token.reused += len(set(sel) & set(prev[l]))
+                    token.routed += len(sel)
+                prev[l] = sel
+            view = pool.acquire(l, sel + list(range(E, P)), stream=stream)
             q.moe_q4_expert_gemv(shape, view, l, h, idx, K, q.F_RMSNORM, ws, gu, stream=stream)
             q.moe_swiglu_down_combine(shape, view, l, gu, idx, w, sw, h, K, ws, h, stream=stream)
             pool.release(l, stream=stream)
@@ -853,6 +866,47 @@ def run_pool(args, cfg, dev, stream):
             torch.cuda.empty_cache()
     at20 = [c for c in curve if c["slots_per_layer"] == 20] or curve
     head = max(at20, key=lambda c: c["tokens_per_s"])
+
+    # temporal reuse (a stand-in for correlated text, labelled as such): a
+    # chain of tokens x_{t+1} = a x_t + sqrt(1 - a^2) z_{t+1}, with and
+    # without prefetching the previous token's experts of each layer before
+    # its router runs; fewest slots, one copy stream
+    reuse_curve = []
+    slots_r = min(slots_list)
+    for alpha in [float(v) for v in args.pool_reuse.split(",")]:
+        beta = float(np.sqrt(max(0.0, 1.0 - alpha * alpha)))
+        for pf in (False, True):
+            pool, arena, table = make_pool(slots_r, 1)
+            prev = [None] * L
+            x = fresh(30000)
+            token.reused = token.routed = 0
+            with torch.cuda.stream(stream):
+                for i in range(max(args.warmup, 32)):
+                    x = alpha * x + beta * fresh(30001 + i)
+                    token(pool, x.clone(), prev=prev, prefetch=pf)
+            torch.cuda.synchronize()
+            st0 = pool.stats()
+            token.reused = token.routed = 0
+            chain = []
+            for i in range(args.steps):
+                x = alpha * x + beta * fresh(40000 + i)
+                chain.append(x.clone())
+            t0 = time.perf_counter()
+            with torch.cuda.stream(stream):
+                for i in range(args.steps):
+                    token(pool, chain[i], prev=prev, prefetch=pf)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            st = pool.stats()
+            hits, misses = st["hits"] - st0["hits"], st["misses"] - st0["misses"]
+            reuse_curve.append({"correlation_a": alpha, "prefetch": pf, "slots_per_layer": slots_r,
+                                "measured_reuse": round(token.reused / max(token.routed, 1), 4),
+                                "tokens_per_s": round(args.steps / dt, 2), "hit_rate": round(hits / max(hits + misses, 1), 4),
+                                "h2d_gbs": round((st["bytes_copied"] - st0["bytes_copied"]) / dt / 1e9, 2)})
+            log(f"[bench] {reuse_curve[-1]}")
+            pool.destroy()
+            del pool, arena, table
+            torch.cuda.empty_cache()
     sec = head["ms_per_token"] / 1e3
     rec = base_record(args, cfg, steps_tokens=args.steps, elapsed_ms=sec * args.steps * 1e3, wall=sec * args.steps)
     rec.update({
@@ -862,6 +916,7 @@ def run_pool(args, cfg, dev, stream):
                      "frac": round(head["h2d_gbs"] / 64.0, 4), "traffic": None,
                      "raw_copy_gbs_by_streams": raw},
         "curve": curve,
+        "reuse_curve": reuse_curve,
         "parity": parity,
     })
     rec["config"].update(layers_per_step=L, slots_per_layer=head["slots_per_layer"],

@@ -362,6 +362,17 @@ int moe_pool_make_resident(moeq_pool* pool, void* stream);
 int moe_pool_acquire(moeq_pool* pool, int layer, const int32_t* ids, int n, void* compute_stream,
                      moeq_experts* view);
 
+/* Temporal prefetch (openclawradar.com/ru, "Эффективные оптимизации": the
+ * next token reuses many of the previous token's experts, so their loads
+ * can start before routing resolves): copies the experts `ids` (host int32
+ * [n]) of `layer` that are not resident into unpinned slots (empty first,
+ * else least recently used) on the first copy stream, without pinning them;
+ * resident ones become most recently used.  Stops quietly when no unpinned
+ * slot is left.  A later acquire that finds them is a hit whose compute
+ * stream waits for these copies.  The copies count in the bytes-copied
+ * statistic; hits and misses count at acquire. */
+int moe_pool_prefetch(moeq_pool* pool, int layer, const int32_t* ids, int n);
+
 /* Unpins the layer's slots once the work queued so far on compute_stream is
  * done (an event is recorded there). */
 int moe_pool_release(moeq_pool* pool, int layer, void* compute_stream);
@@ -382,6 +393,8 @@ int moeq_poolsim_create(int n_layers, int per_layer, int64_t n_slots, moeq_pools
 int moeq_poolsim_make_resident(moeq_poolsim* pool);
 int moeq_poolsim_acquire(moeq_poolsim* pool, int layer, const int32_t* ids, int n, int32_t* slots,
                          int32_t* evicted, int32_t* missed, int32_t* n_out);
+int moeq_poolsim_prefetch(moeq_poolsim* pool, int layer, const int32_t* ids, int n, int32_t* slots,
+                          int32_t* evicted, int32_t* n_out);
 int moeq_poolsim_release(moeq_poolsim* pool, int layer);
 int moeq_poolsim_stats(const moeq_poolsim* pool, int64_t* out);
 void moeq_poolsim_destroy(moeq_poolsim* pool);

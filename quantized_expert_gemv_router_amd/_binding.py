@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.moe_pool_make_resident.argtypes = [_P, _P]
         L.moe_pool_acquire.argtypes = [_P, _I, _P, _I, _P, X]
         L.moe_pool_release.argtypes = [_P, _I, _P]
+        L.moe_pool_prefetch.argtypes = [_P, _I, _P, _I]
+        L.moeq_poolsim_prefetch.argtypes = [_P, _I, _P, _I, _P, _P, ctypes.POINTER(ctypes.c_int32)]
         L.moe_pool_stats.argtypes = [_P, ctypes.POINTER(I64)]
         L.moe_pool_destroy.argtypes = [_P]
         L.moe_pool_destroy.restype = None
@@ -469,6 +471,10 @@ class Pool:
     def release(self, layer: int, stream=None):
         _check(lib().moe_pool_release(self._h, layer, _stream(stream)))
 
+    def prefetch(self, layer: int, ids):
+        arr = _int32_host(ids)
+        _check(lib().moe_pool_prefetch(self._h, layer, ctypes.cast(arr, _P), len(ids)))
+
     def stats(self) -> dict:
         out = (ctypes.c_int64 * 4)()
         _check(lib().moe_pool_stats(self._h, out))
@@ -505,6 +511,15 @@ class PoolSim:
         _check(lib().moeq_poolsim_acquire(self._h, layer, ctypes.cast(arr, _P), n, slots, ev, miss,
                                           ctypes.byref(n_out)))
         return [(slots[i], ev[i], bool(miss[i])) for i in range(n_out.value)]
+
+    def prefetch(self, layer: int, ids) -> list:
+        """[(slot, evicted entry or -1)] per copy the prefetch plans."""
+        n = len(ids)
+        arr = _int32_host(ids)
+        slots, ev = ((ctypes.c_int32 * max(n, 1))() for _ in range(2))
+        n_out = ctypes.c_int32()
+        _check(lib().moeq_poolsim_prefetch(self._h, layer, ctypes.cast(arr, _P), n, slots, ev, ctypes.byref(n_out)))
+        return [(slots[i], ev[i]) for i in range(n_out.value)]
 
     def release(self, layer: int):
         _check(lib().moeq_poolsim_release(self._h, layer))

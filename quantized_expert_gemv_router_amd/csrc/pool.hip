@@ -37,6 +37,7 @@ struct moeq_pool {
   std::vector<char> released_valid;
   std::vector<hipEvent_t> ready;        // per copy stream: last work a compute stream must see
   std::vector<char> ready_valid;
+  std::vector<char> prefetched;         // [n_slots] last filled by a prefetch (on copy stream 0)
   int64_t bytes_copied = 0;
 };
 
@@ -189,6 +190,7 @@ int moe_pool_create(const moeq_shape* shape, int n_layers, void* arena, int64_t 
   p->released_valid.assign((size_t)n_layers, 0);
   p->ready.assign((size_t)n_copy_streams, nullptr);
   p->ready_valid.assign((size_t)n_copy_streams, 0);
+  p->prefetched.assign((size_t)n_slots, 0);
   auto cleanup = [&]() {
     for (hipEvent_t ev : p->released)
       if (ev) (void)hipEventDestroy(ev);
@@ -275,6 +277,13 @@ int moe_pool_acquire(moeq_pool* p, int layer, const int32_t* ids, int n, void* c
     p->next_stream = (p->next_stream + 1) % (int)ns;
     if (int r = wait_release(c, st.prev_layer)) return r;
     if (int r = wait_release(0, st.prev_layer)) return r;
+    // a slot last filled by a prefetch (copy stream 0) is overwritten only
+    // after that copy
+    if (p->prefetched[(size_t)st.slot] && c != 0 && p->ready_valid[0]) {
+      const hipError_t e = hipStreamWaitEvent(p->copy[c], p->ready[0], 0);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (prefetched slot)");
+    }
+    p->prefetched[(size_t)st.slot] = 0;
     uint8_t* dst = p->arena + (int64_t)st.slot * p->slot_bytes;
     const hipError_t e = hipMemcpyAsync(dst, p->host[(size_t)st.entry], (size_t)p->expert_bytes,
                                         hipMemcpyHostToDevice, p->copy[c]);
@@ -290,6 +299,41 @@ int moe_pool_acquire(moeq_pool* p, int layer, const int32_t* ids, int n, void* c
   if (int r = publish(p, compute, used)) return r;
   view->blobs = p->table;
   view->n_layers = p->core.n_layers;
+  return ok();
+}
+
+int moe_pool_prefetch(moeq_pool* p, int layer, const int32_t* ids, int n) {
+  if (int rc = check_pool(p)) return rc;
+  if (n < 0 || (n > 0 && !ids)) return fail(MOEQ_E_INVALID, "ids must hold n >= 0 host int32 values");
+  std::vector<PoolCore::Step> steps;
+  if (p->core.prefetch(layer, ids, n, steps) < 0)
+    return fail(MOEQ_E_INVALID, "layer %d outside [0, %d) or an id outside [0, %d)", layer, p->core.n_layers,
+                p->core.per_layer);
+  if (steps.empty()) return ok();
+  TableEdits ed{};
+  std::vector<char> waited((size_t)p->core.n_layers, 0);
+  for (const PoolCore::Step& st : steps) {
+    // the slot's previous user must be done with it
+    if (st.prev_layer >= 0 && p->released_valid[(size_t)st.prev_layer] && !waited[(size_t)st.prev_layer]) {
+      const hipError_t e = hipStreamWaitEvent(p->copy[0], p->released[(size_t)st.prev_layer], 0);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (slot reuse)");
+      waited[(size_t)st.prev_layer] = 1;
+    }
+    uint8_t* dst = p->arena + (int64_t)st.slot * p->slot_bytes;
+    const hipError_t e = hipMemcpyAsync(dst, p->host[(size_t)st.entry], (size_t)p->expert_bytes,
+                                        hipMemcpyHostToDevice, p->copy[0]);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (pool prefetch)");
+    p->bytes_copied += p->expert_bytes;
+    p->prefetched[(size_t)st.slot] = 1;
+    if (st.evicted >= 0)
+      if (int r = add_edit(p, ed, st.evicted, nullptr)) return r;
+    if (int r = add_edit(p, ed, st.entry, dst)) return r;
+  }
+  if (int r = flush_edits(p, ed)) return r;
+  // the next acquire's compute stream waits for these copies
+  const hipError_t e = hipEventRecord(p->ready[0], p->copy[0]);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (pool prefetch)");
+  p->ready_valid[0] = 1;
   return ok();
 }
 
@@ -356,6 +400,21 @@ int moeq_poolsim_acquire(moeq_poolsim* s, int layer, const int32_t* ids, int n, 
     slots[i] = steps[i].slot;
     evicted[i] = steps[i].evicted;
     missed[i] = steps[i].miss ? 1 : 0;
+  }
+  *n_out = (int32_t)steps.size();
+  return ok();
+}
+
+int moeq_poolsim_prefetch(moeq_poolsim* s, int layer, const int32_t* ids, int n, int32_t* slots,
+                          int32_t* evicted, int32_t* n_out) {
+  if (!s) return fail(MOEQ_E_INVALID, "pool is NULL");
+  if (n < 0 || (n > 0 && (!ids || !slots || !evicted)) || !n_out)
+    return fail(MOEQ_E_INVALID, "ids/slots/evicted must hold n entries, n_out non-NULL");
+  std::vector<PoolCore::Step> steps;
+  if (s->core.prefetch(layer, ids, n, steps) < 0) return fail(MOEQ_E_INVALID, "bad layer or id");
+  for (size_t i = 0; i < steps.size(); ++i) {
+    slots[i] = steps[i].slot;
+    evicted[i] = steps[i].evicted;
   }
   *n_out = (int32_t)steps.size();
   return ok();

@@ -34,7 +34,7 @@ struct PoolCore {
   std::vector<int32_t> last_layer;          // [n_slots] layer of the last acquire, or -1
   std::vector<std::vector<int64_t>> held;   // [n_layers] slots pinned by the layer
   uint64_t tick = 0;
-  int64_t hits = 0, misses = 0, evictions = 0;
+  int64_t hits = 0, misses = 0, evictions = 0, prefetches = 0;
 
   bool init(int32_t layers, int32_t per, int64_t slots) {
     if (layers <= 0 || per <= 0 || slots <= 0) return false;
@@ -130,6 +130,44 @@ struct PoolCore {
     return 0;
   }
 
+  // Plans a prefetch of `ids` for `layer`: each id not resident takes a
+  // victim slot (empty first, else least recently used; never a pinned slot
+  // or one this call already took) and is marked resident but not pinned;
+  // resident ids are only touched (they become most recently used).  Stops
+  // quietly when no slot is left.  Fills `steps` with the copies to make
+  // (miss = true).  Returns 0, or -1 for a bad layer or id.
+  int prefetch(int32_t layer, const int32_t* ids, int n, std::vector<Step>& steps) {
+    steps.clear();
+    if (layer < 0 || layer >= n_layers || n < 0) return -1;
+    for (int i = 0; i < n; ++i)
+      if (ids[i] < 0 || ids[i] >= per_layer) return -1;
+    ++tick;
+    std::vector<int64_t> taken;
+    for (int i = 0; i < n; ++i) {
+      const int32_t entry = layer * per_layer + ids[i];
+      const int64_t s0 = where[(size_t)entry];
+      if (s0 >= 0) {
+        last_tick[(size_t)s0] = tick;
+        continue;
+      }
+      const int64_t s = victim_excluding(taken);
+      if (s < 0) break;
+      Step st{entry, (int32_t)s, -1, last_layer[(size_t)s], true};
+      if (owner[(size_t)s] >= 0) {
+        st.evicted = owner[(size_t)s];
+        where[(size_t)owner[(size_t)s]] = -1;
+        ++evictions;
+      }
+      owner[(size_t)s] = entry;
+      where[(size_t)entry] = s;
+      last_tick[(size_t)s] = tick;
+      ++prefetches;
+      taken.push_back(s);
+      steps.push_back(st);
+    }
+    return 0;
+  }
+
   // Unpins the slots `layer` holds.  Returns how many.
   int64_t release(int32_t layer) {
     if (layer < 0 || layer >= n_layers) return -1;
@@ -140,6 +178,20 @@ struct PoolCore {
   }
 
  private:
+  // As victim(), skipping the slots in `skip`; -1 if none is left.
+  int64_t victim_excluding(const std::vector<int64_t>& skip) const {
+    int64_t best = -1;
+    for (int64_t s = 0; s < n_slots; ++s) {
+      if (pins[(size_t)s] != 0) continue;
+      bool skipped = false;
+      for (int64_t k : skip) skipped = skipped || k == s;
+      if (skipped) continue;
+      if (owner[(size_t)s] < 0) return s;
+      if (best < 0 || last_tick[(size_t)s] < last_tick[(size_t)best]) best = s;
+    }
+    return best;
+  }
+
   // An empty slot if any (lowest index), else the unpinned slot acquired
   // longest ago (lowest index on equal ticks).  The caller checked that one
   // exists.

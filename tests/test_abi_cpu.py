@@ -39,7 +39,9 @@ def test_expert_bytes():
     assert q.moeq_expert_bytes(q.Shape(4096, 1024, 512, 1, 4, 64)) == 7_077_888
     assert q.moeq_expert_bytes(q.Shape(4096, 1024, 512, 1, 2, 64)) == 3_932_160
     assert q.moeq_expert_bytes(q.Shape(256, 128, 8, 1, 4, 64)) == 55_296
-    assert q.moeq_expert_bytes(q.Shape(4096, 1024, 512, 1, 3, 64)) == -1
+    assert q.moeq_expert_bytes(q.Shape(4096, 1024, 512, 1, 3, 64)) == 5_505_024
+    assert q.moeq_expert_bytes(q.Shape(4096, 1024, 512, 1, 5, 64)) == -1
+    assert q.moeq_expert_bytes(q.Shape(4096, 1088, 512, 1, 3, 64)) == -1   # 3-bit rows need multiples of 128
     for cfg in synth.CONFIGS.values():
         assert q.moeq_expert_bytes(q.Shape.of(cfg)) == cfg.expert_bytes
 
@@ -58,7 +60,9 @@ def _ws(shape, T, k):
     ((4096, 1024, 8, 1, 4, 64), 1, 9, E_INVALID),
     ((4096, 1024, 512, 1, 4, 64), 1, 17, E_UNSUPPORTED),
     ((4096, 1024, 512, 1, 4, 64), 65, 3, E_UNSUPPORTED),
-    ((4096, 1024, 512, 1, 3, 64), 1, 3, E_UNSUPPORTED),
+    ((4096, 1024, 512, 1, 3, 64), 1, 3, OK),
+    ((4096, 1088, 512, 1, 3, 64), 1, 3, E_UNSUPPORTED),
+    ((4096, 1024, 512, 1, 5, 64), 1, 3, E_UNSUPPORTED),
     ((4096, 1024, 512, 1, 8, 64), 1, 3, E_UNSUPPORTED),
     ((4096, 1024, 512, 1, 4, 32), 1, 3, E_UNSUPPORTED),
     ((4100, 1024, 512, 1, 4, 64), 1, 3, E_UNSUPPORTED),

@@ -123,6 +123,37 @@ def test_pool_matches_resident_and_policy(setup, extra_layers, streams):
     pool2.destroy()
 
 
+def test_prefetch_keeps_outputs_bit_identical(setup):
+    """Prefetching the previous step's experts of each layer before its
+    routing (temporal prefetch) changes which copies happen when, never the
+    results: every layer output equals the resident experts' bit for bit,
+    and prefetched experts turn into hits."""
+    S, cfg = setup, setup.cfg
+    n_slots = 2 * (cfg.top_k + cfg.n_shared) + 2
+    pool = S.pool(n_slots)
+    ws = q.new_workspace(S.shape, 1, cfg.top_k)
+    ws_r = q.new_workspace(S.shape, 1, cfg.top_k)
+    prev = [None] * cfg.layers
+    hits_from_prefetch = 0
+    for step in range(5):
+        for l in range(cfg.layers):
+            x = S.token(700 + step * cfg.layers + l)
+            if prev[l] is not None:
+                pool.prefetch(l, prev[l])
+            idx_r, _, y_r = run_layer(S, S.resident, l, x, ws_r)
+            ids = idx_r.cpu().numpy()[0].tolist() + [cfg.n_experts] * cfg.n_shared
+            before = pool.stats()["hits"]
+            view = pool.acquire(l, ids)
+            hits_from_prefetch += pool.stats()["hits"] - before
+            _, _, y = run_layer(S, view, l, x, ws)
+            pool.release(l)
+            assert torch.equal(y, y_r), f"step {step} layer {l}: prefetched pool output differs"
+            prev[l] = ids
+    torch.cuda.synchronize()
+    assert hits_from_prefetch > 0
+    pool.destroy()
+
+
 def test_pool_resident_and_exhausted(setup):
     S, cfg = setup, setup.cfg
     ws = q.new_workspace(S.shape, 1, cfg.top_k)

@@ -182,7 +182,7 @@ def test_pool_create_validates_before_touching_a_device():
     assert create(n_streams=0) == B.E_INVALID                # at least one copy stream
     assert create(n_streams=9) == B.E_INVALID                # at most eight
     assert create(streams=None) == B.E_INVALID
-    bad = q.Shape(256, 128, 8, 1, 3, 64)
+    bad = q.Shape(256, 128, 8, 1, 5, 64)
     assert L.moe_pool_create(ctypes.byref(bad), 2, 0x1000, 4, 55296, args["host"], 0x3000, args["streams"], 1,
                              ctypes.byref(h)) == B.E_UNSUPPORTED
     assert h.value is None
@@ -191,3 +191,41 @@ def test_pool_create_validates_before_touching_a_device():
     assert L.moe_pool_stats(None, out) == B.E_INVALID
     assert L.moe_pool_release(None, 0, None) == B.E_INVALID
     L.moe_pool_destroy(None)
+
+
+def test_prefetch_makes_a_later_acquire_hit_and_never_takes_pinned_slots():
+    """Prefetched experts become resident unpinned (a later acquire of them is
+    a hit); resident ones are only touched; a prefetch never evicts a slot a
+    layer holds and stops quietly when no unpinned slot is left."""
+    sim = q.PoolSim(2, 8, 6)
+    assert [s for s, _ in sim.prefetch(0, [1, 2, 3])] == [0, 1, 2]
+    got = sim.acquire(0, [1, 2, 4])
+    assert [m for _, _, m in got] == [False, False, True]
+    st = sim.stats()
+    assert (st["hits"], st["misses"]) == (2, 1)
+    # layer 0 pins slots 0, 1 (hits) and 3 (miss); three slots are unpinned
+    plan = sim.prefetch(1, [0, 1, 2, 3, 4])
+    assert len(plan) == 3 and {s for s, _ in plan} == {2, 4, 5}
+    assert all(s not in (0, 1, 3) for s, _ in plan)
+    # slot 2 held layer 0's prefetched expert 3, which is evicted
+    assert (2, 0 * 8 + 3) in plan
+    sim.release(0)
+    # an id already resident is touched, not copied
+    assert sim.prefetch(1, [0]) == []
+    with pytest.raises(q.MoeqError):
+        sim.prefetch(2, [0])
+    with pytest.raises(q.MoeqError):
+        sim.prefetch(0, [8])
+
+
+def test_prefetch_touch_protects_from_eviction():
+    """A resident expert named in a prefetch becomes most recently used, so
+    the next miss evicts another slot."""
+    sim = q.PoolSim(1, 8, 2)
+    sim.acquire(0, [0])
+    sim.release(0)
+    sim.acquire(0, [1])
+    sim.release(0)
+    sim.prefetch(0, [0])            # touch expert 0: expert 1 is now the oldest
+    got = sim.acquire(0, [2])
+    assert got[0][1] == 1           # expert 1's slot was evicted
