@@ -76,7 +76,15 @@ enum {
    * RMS norm): one layer of this call computes what moe_router_topk,
    * moe_q4_expert_gemv and moe_swiglu_down_combine compute without
    * MOEQ_F_RMSNORM (for a single decode layer in one launch). */
-  MOEQ_F_STACK_NO_NORM = 8u
+  MOEQ_F_STACK_NO_NORM = 8u,
+  /* moe_expert_stack_decode only, diagnostic: the persistent launch runs a
+   * delay-injection build of its kernel, in which every wave sleeps a
+   * pseudo-random 0..~13 us before each hand-off publish.  The results must
+   * be bit-identical to the plain launch.  MOEQ_E_UNSUPPORTED where the
+   * shape has no such build (hidden 4096 / 512 experts / top-3 + 1 at
+   * 4 bits, and the small test shape), for T > 1 and with
+   * MOEQ_F_STACK_LAYERWISE. */
+  MOEQ_F_STACK_JITTER = 16u
 };
 
 /* Limits of the current kernels (larger values return MOEQ_E_UNSUPPORTED). */
@@ -180,7 +188,8 @@ int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts
  *   h           device [T][H] f32, in/out
  *   topk_trace  device [L][T][k] int32 out, or NULL
  *   h_trace     device [L][T][H] f32 out (the input of each layer), or NULL
- *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE, MOEQ_F_STACK_NO_NORM
+ *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE, MOEQ_F_STACK_NO_NORM,
+ *               MOEQ_F_STACK_JITTER
  * T == 1 runs one persistent cooperative launch for all L layers (no host
  * involvement: the workgroups hand the logits, the activations and the
  * hidden state to each other through tagged words in the workspace) when
@@ -267,7 +276,8 @@ int moeq_prefill_timing_read(double* ms, int32_t* launches);
  * took: 1 = persistent launch, 2 = per-layer launches, 0 = none yet. */
 int moeq_last_stack_path(void);
 
-/* Diagnostic: the next persistent moe_expert_stack_decode launch writes
+/* Diagnostic: the calling thread's next persistent moe_expert_stack_decode
+ * launch writes
  * wall-clock stamps (100 MHz device counter) of its phase boundaries, as
  * seen by workgroup 0, to the device array `clocks` [L][n] where n is the
  * return value (24).  The pointer is consumed by that launch. */

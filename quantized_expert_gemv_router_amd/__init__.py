@@ -9,7 +9,7 @@ library has not been built the import of the binding functions fails
 loudly; there is no CPU fallback.
 """
 from ._binding import (  # noqa: F401
-    BF16, F32, F_NO_RENORM, F_RMSNORM, F_STACK_LAYERWISE, F_STACK_NO_NORM,
+    BF16, F32, F_NO_RENORM, F_RMSNORM, F_STACK_LAYERWISE, F_STACK_NO_NORM, F_STACK_JITTER,
     MoeqError, E_UNSUPPORTED, Shape, ExpertTable, RouterTable, lib, library_path,
     moeq_abi_version, moeq_expert_bytes, moeq_workspace_bytes, moeq_last_error,
     moe_router_topk, moe_q4_expert_gemv, moe_swiglu_down_combine, moe_read_device_status,

@@ -10,7 +10,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_PKG, "libmoeq.so")
 
 BF16, F32 = 0, 1
-F_NO_RENORM, F_RMSNORM, F_STACK_LAYERWISE, F_STACK_NO_NORM = 1, 2, 4, 8
+F_NO_RENORM, F_RMSNORM, F_STACK_LAYERWISE, F_STACK_NO_NORM, F_STACK_JITTER = 1, 2, 4, 8, 16
 
 OK, E_INVALID, E_UNSUPPORTED, E_HIP, E_POOL_EXHAUSTED, E_DEVICE = 0, -1, -2, -3, -4, -5
 _CODE_NAMES = {E_INVALID: "MOEQ_E_INVALID", E_UNSUPPORTED: "MOEQ_E_UNSUPPORTED", E_HIP: "MOEQ_E_HIP",

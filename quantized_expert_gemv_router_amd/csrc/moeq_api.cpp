@@ -14,7 +14,7 @@ namespace moeq {
 namespace {
 thread_local std::string g_last_error;
 thread_local int g_last_stack_path = 0;
-int64_t* g_stack_clocks = nullptr;   // diagnostic phase stamps for the next persistent launch
+thread_local int64_t* g_stack_clocks = nullptr;   // diagnostic phase stamps for this thread's next persistent launch
 }  // namespace
 
 int fail(int code, const char* fmt, ...) {
@@ -234,7 +234,7 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
                             void* workspace, void* stream) {
   if (int rc = check_shape(s)) return rc;
   if (int rc = check_tk(s, T, k)) return rc;
-  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_STACK_LAYERWISE | MOEQ_F_STACK_NO_NORM))
+  if (flags & ~(uint32_t)(MOEQ_F_NO_RENORM | MOEQ_F_STACK_LAYERWISE | MOEQ_F_STACK_NO_NORM | MOEQ_F_STACK_JITTER))
     return fail(MOEQ_E_UNSUPPORTED, "unknown or inapplicable flag bits 0x%x", flags);
   if (!ex || !ex->blobs) return fail(MOEQ_E_INVALID, "experts view or its blob table is NULL");
   if (L < 0 || layer0 < 0 || layer0 + L > ex->n_layers)
@@ -257,6 +257,7 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     a.bits = s->bits;
     a.no_renorm = (flags & MOEQ_F_NO_RENORM) != 0;
     a.no_norm = (flags & MOEQ_F_STACK_NO_NORM) != 0;
+    a.jitter = (flags & MOEQ_F_STACK_JITTER) != 0;
     a.h = h;
     a.topk_trace = topk_trace;
     a.h_trace = h_trace;
@@ -277,7 +278,11 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     if (e != hipErrorNotSupported && e != hipErrorCooperativeLaunchTooLarge)
       return hip_fail(e, "persistent stack kernel launch");
     (void)hipGetLastError();
+    if (flags & MOEQ_F_STACK_JITTER)
+      return fail(MOEQ_E_UNSUPPORTED, "delay injection has no persistent instantiation for this shape");
   }
+  if (flags & MOEQ_F_STACK_JITTER)
+    return fail(MOEQ_E_UNSUPPORTED, "delay injection applies to the persistent one-token launch only");
 
   // per-layer path: router -> gate/up -> down/combine per layer, in place on h
   const int KS = k + s->n_shared;

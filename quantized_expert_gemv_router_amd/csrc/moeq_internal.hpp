@@ -119,6 +119,7 @@ struct StackArgs {
   int H, I, E, S, K, bits;
   int no_renorm;
   int no_norm;                     // layer input taken as is (no RMS norm)
+  int jitter;                      // diagnostic delay injection before every hand-off publish
   int router_rows;                 // set by the launcher
   float* h;                        // [H] in/out
   int32_t* topk_trace;             // [L][K] or null

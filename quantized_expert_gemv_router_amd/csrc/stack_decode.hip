@@ -166,6 +166,22 @@ __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint3
   }
 }
 
+// Delay injection (diagnostic instantiations, JIT = 1): before each of its
+// hand-off publishes a wave sleeps a pseudo-random 0 .. 63 times s_sleep 8
+// (up to ~13 us), a different amount per (workgroup, wave, layer, site).
+// The hand-offs carry their own ordering, so the results must not change.
+template <int JIT>
+__device__ __forceinline__ void jitter(int b, int wave, int li, int site) {
+  if constexpr (JIT != 0) {
+    uint32_t h = (uint32_t)b * 0x9E3779B1u ^ (uint32_t)(li * 4 + site) * 0x85EBCA77u ^ (uint32_t)wave * 0xC2B2AE3Du;
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    const int n = (int)(h & 63u);
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 // ------------------------------------------------------------------ layout
 struct StackLds {
   int hs, xp, xs, ap, as, gres, lg, tbl, clk, total;
@@ -211,7 +227,7 @@ __device__ __forceinline__ float2 stage_word(const float* v, float f, uint32_t* 
   return make_float2(X, Xs);
 }
 
-template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW>
+template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW, int JIT>
 __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   constexpr int PC = Pack<BITS>::kPerChunk, PW = Pack<BITS>::kPerWord;
   constexpr int RPSD = 64 / LPRD;          // down rows per wave step
@@ -589,6 +605,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int i = 0; i < kWaves; ++i) { ss += ssum[i]; mx = fmaxf(mx, hmax[i]); }
     const double inv = a.no_norm ? 1.0 : 1.0 / sqrt(ss / (double)H + 1e-6);
     const uint32_t tag = (uint32_t)li + 1u;
+    jitter<JIT>(b, wave, li, 0);
     if (tid < RW && b + NB * tid < E) {   // logits of this block's router rows
       double d = 0.0;
       for (int w = 0; w < kWaves; ++w) d += rpart[tid * kWaves + w];
@@ -678,6 +695,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       gu_dots(0, 1);
       stamp0(li, 3);
       block_sync_lds();
+      jitter<JIT>(b, wave, li, 1);
       for (int t = tid; t < RG; t += kThreads) {
         const int row = b + NB * t;
         if (row < I) {
@@ -692,6 +710,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     block_sync_lds();
     stamp(li, 6);
     plan_down();                     // routed slots' down rows (eblob is complete now)
+    jitter<JIT>(b, wave, li, 2);
     for (int t = tid; t < K * RG; t += kThreads) {
       const int j = t / RG, i = t - j * RG, row = b + NB * i;
       if (row < I) {
@@ -790,6 +809,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       acc = fmaf(selw[s], down_dot(s, qd[s], sd[s], dok), acc);
     }
     stamp0(li, 18);
+    jitter<JIT>(b, wave, li, 3);
     if (dok && sub == LPRD - 1) {
       if (a.h_trace) a.h_trace[(int64_t)li * H + drow] = hs[drow];
       if (li + 1 == L) a.h[drow] = acc;   // complete when the launch ends
@@ -818,13 +838,13 @@ __global__ void reset_barrier_kernel(uint32_t* bar) {
   for (int i = threadIdx.x; i < kBarWords; i += blockDim.x) bar[i] = 0u;
 }
 
-template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW>
+template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW, int JIT = 0>
 hipError_t launch_t(const StackArgs& a, int nb, size_t lds, hipStream_t stream) {
   hipLaunchKernelGGL(reset_barrier_kernel, dim3(1), dim3(256), 0, stream, a.bar);
   StackArgs args = a;
   void* params[] = {&args};
   return hipLaunchCooperativeKernel(
-      reinterpret_cast<const void*>(&stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW>),
+      reinterpret_cast<const void*>(&stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW, JIT>),
       dim3(nb), dim3(kThreads), params, (unsigned int)lds, stream);
 }
 
@@ -893,6 +913,11 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   const Geometry g{nb, rw, a.H, a.I, a.E, a.S, a.K, KS, a.bits};
   // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,
   // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
+  if (a.jitter) {   // delay-injection instantiations: the 60-layer shape and the small test shape
+    if (g.fits(4, 2, 2, 4, 32, 1, 3, 4)) return launch_t<4, 2, 2, 4, 32, 1, 3, 4, 1>(a, nb, lds, stream);
+    if (g.fits(4, 1, 1, 2, 64, 1, 3, 1)) return launch_t<4, 1, 1, 2, 64, 1, 3, 1, 1>(a, nb, lds, stream);
+    return hipErrorNotSupported;
+  }
   if (g.fits(4, 2, 2, 4, 32, 1, 3, 4)) return launch_t<4, 2, 2, 4, 32, 1, 3, 4>(a, nb, lds, stream);
   if (g.fits(2, 2, 1, 5, 32, 1, 4, 4)) return launch_t<2, 2, 1, 5, 32, 1, 4, 4>(a, nb, lds, stream);
   if (g.fits(4, 1, 1, 2, 64, 1, 3, 1)) return launch_t<4, 1, 1, 2, 64, 1, 3, 1>(a, nb, lds, stream);

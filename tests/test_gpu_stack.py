@@ -64,6 +64,27 @@ def compare_free_running(cfg, L, token_set, traces, gpu_h):
         f"{same} layers, h drift at layer {last} {drift:.2e}")
 
 
+def test_stack_small_shape_delay_injection():
+    """Small shape (8 experts: most workgroups own no router row): the
+    delay-injection build equals the plain launch bit for bit."""
+    cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_tiny_jit", hidden=256, inter=128,
+                             n_experts=8, top_k=2, layers=6)
+    shape, ex, rt = build_stack(cfg, cfg.layers)
+    for ts in (0, 1, 2):
+        x = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+        res = []
+        for flags in (0, q.F_STACK_JITTER):
+            h = x.clone()
+            ws = q.new_workspace(shape, 1, cfg.top_k)
+            tk, hk = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws, trace=True)
+            assert q.moeq_last_stack_path() == 1
+            assert q.moe_read_device_status(ws) == 0
+            res.append((tk, hk, h))
+        torch.cuda.synchronize()
+        for a, b in zip(*res):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
 def test_stack_small_shape(flags):
     cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_tiny", hidden=256, inter=128,
@@ -227,6 +248,27 @@ def test_stack60_oracle_fed_layers(stack60, flags, layers):
         assert np.array_equal(tk.cpu().numpy()[0], exp["idx"]), l
         worst = max(worst, assert_close(h.cpu().numpy(), exp["y"], f"layer {l} output"))
     say(f"  {len(layers)} layers flags={flags}: exact top-K on each, worst output rel err {worst:.2e}")
+
+
+def test_stack60_delay_injection_is_bit_identical(stack60):
+    """The delay-injection build of the persistent kernel (every wave sleeps a
+    pseudo-random 0..~13 us before each hand-off publish) gives top-K, layer
+    inputs and output bit-identical to the plain launch over all 60 layers:
+    the tagged hand-offs order the layers by themselves."""
+    cfg, (shape, ex, rt) = stack60
+    for ts in (5, 6):
+        x = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+        res = []
+        for flags in (0, q.F_STACK_JITTER):
+            h = x.clone()
+            ws = q.new_workspace(shape, 1, cfg.top_k)
+            tk, hk = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws, trace=True)
+            assert q.moeq_last_stack_path() == 1
+            assert q.moe_read_device_status(ws) == 0
+            res.append((tk, hk, h))
+        torch.cuda.synchronize()
+        for a, b in zip(*res):
+            assert torch.equal(a, b)
 
 
 def test_stack60_persistent_is_reproducible(stack60):
