@@ -283,6 +283,18 @@ int moeq_last_stack_path(void);
  * return value (24).  The pointer is consumed by that launch. */
 int moeq_stack_clock_trace(int64_t* clocks);
 
+/* Diagnostic: the calling thread's next persistent moe_expert_stack_decode
+ * launch writes, for every workgroup, n = 16 (the return value) entries per
+ * layer to the device array `clocks` [blocks][L][n], blocks = the device's
+ * compute units: stamps of the same clock at 0 layer start, 1 h polled,
+ * 2 own logits published, 3 logits polled, 4 top-K, 5 routed gate/up dot
+ * products, 6 routed activations published, 7 shared activations polled and
+ * applied, 8 routed activations polled (thread 0's view, no extra
+ * barriers), 9 h published (the workgroup's last wave); then thread 0's
+ * poll rounds for 10 h, 11 logits, 12 shared and 13 routed activations.
+ * The pointer is consumed by that launch. */
+int moeq_stack_block_clock_trace(int64_t* clocks);
+
 /* Synchronise `stream` and read the workspace status word: 0 = clean,
  * else a bitmask (1 = an expert id outside [0, E) or a NULL blob pointer
  * was seen, 2 = a wait between workgroups of the persistent stack kernel

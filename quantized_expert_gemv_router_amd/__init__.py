@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     MoeqError, E_UNSUPPORTED, Shape, ExpertTable, RouterTable, lib, library_path,
     moeq_abi_version, moeq_expert_bytes, moeq_workspace_bytes, moeq_last_error,
     moe_router_topk, moe_q4_expert_gemv, moe_swiglu_down_combine, moe_read_device_status,
-    moe_expert_stack_decode, moe_expert_stack_decode_mixed, moe_expert_stack_decode_noalloc, moeq_last_stack_path, moeq_stack_clock_trace,
+    moe_expert_stack_decode, moe_expert_stack_decode_mixed, moe_expert_stack_decode_noalloc, moeq_last_stack_path, moeq_stack_clock_trace, moeq_stack_block_clock_trace,
     new_workspace, moe_layer, Pool, PoolSim, PoolView,
     moe_expert_stack_prefill, moeq_prefill_workspace_bytes, new_prefill_workspace,
     moeq_prefill_timing, moeq_prefill_timing_read, PREFILL_KERNELS, moeq_probe_handoff,

@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.moe_read_device_status.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)]
         L.moeq_last_stack_path.restype = _I
         L.moeq_stack_clock_trace.argtypes = [_P]
+        L.moeq_stack_block_clock_trace.argtypes = [_P]
         L.moe_expert_stack_decode.argtypes = [S, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
                                               _P, _P]
         L.moe_expert_stack_decode_mixed.argtypes = [S, _P, X, _P, _I, _I, _I, _I, ctypes.c_uint32, _P, _P, _P,
@@ -365,6 +366,11 @@ def moeq_last_stack_path() -> int:
 def moeq_stack_clock_trace(clocks: torch.Tensor) -> int:
     """Arm the diagnostic phase clock trace (int64 device tensor [L, 24])."""
     return lib().moeq_stack_clock_trace(_ptr(clocks))
+
+
+def moeq_stack_block_clock_trace(clocks: torch.Tensor) -> int:
+    """Arm the diagnostic per-block clock trace (int64 device tensor [blocks, L, 16])."""
+    return lib().moeq_stack_block_clock_trace(_ptr(clocks))
 
 
 def moeq_probe_handoff(mode: int, words_per_block: int, rounds: int, sleep: int = 1, peer: int = 1,

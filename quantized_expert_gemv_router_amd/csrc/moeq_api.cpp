@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "moeq.h"
@@ -15,6 +16,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local int g_last_stack_path = 0;
 thread_local int64_t* g_stack_clocks = nullptr;   // diagnostic phase stamps for this thread's next persistent launch
+thread_local int64_t* g_stack_bclocks = nullptr;  // the same, every block
 }  // namespace
 
 int fail(int code, const char* fmt, ...) {
@@ -267,7 +269,9 @@ int moe_expert_stack_decode(const moeq_shape* s, const moeq_experts* ex,
     a.bar = reinterpret_cast<uint32_t*>(ws + W.st_bar);
     a.status = status;
     a.clocks = g_stack_clocks;
+    a.bclocks = g_stack_bclocks;
     g_stack_clocks = nullptr;
+    g_stack_bclocks = nullptr;
     hipError_t e = launch_stack_decode(a, st);
     if (e == hipSuccess) {
       g_last_stack_path = 1;
@@ -361,6 +365,11 @@ int moeq_last_stack_path(void) { return g_last_stack_path; }
 int moeq_stack_clock_trace(int64_t* clocks) {
   g_stack_clocks = clocks;
   return kStackClockEvents;
+}
+
+int moeq_stack_block_clock_trace(int64_t* clocks) {
+  g_stack_bclocks = clocks;
+  return kBlockClockEvents;
 }
 
 int moe_read_device_status(void* workspace, void* stream, int32_t* status) {

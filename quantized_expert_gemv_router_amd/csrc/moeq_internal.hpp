@@ -130,8 +130,10 @@ struct StackArgs {
   uint32_t* bar;                   // barrier counters (stack_barrier_words())
   int32_t* status;
   int64_t* clocks;                 // diagnostic: [L][kStackClockEvents] wall-clock stamps of block 0, or null
+  int64_t* bclocks;                // diagnostic: [blocks][L][kBlockClockEvents] stamps of every block, or null
 };
 constexpr int kStackClockEvents = 24;
+constexpr int kBlockClockEvents = 16;
 int stack_barrier_words();
 // hipErrorNotSupported: no persistent instantiation for this shape.
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream);

@@ -19,27 +19,28 @@
 //            of h, takes sum(h^2), max|h| and its router rows' partial dot
 //            products from the polled registers, and after one block
 //            barrier publishes its logits
-//   logits:  every block polls all E logits and selects top-K itself
-//            (threshold on the keys' high words, every wave keeps its own
-//            copy of the selection), then streams its gate/up rows
+//   logits:  every block polls all E logits and selects top-K itself (one
+//            wave, rounds on the keys' high words), then streams its
+//            gate/up rows
 //   a:       each block publishes silu(g)*u for its gate/up rows; every block
-//            polls all activations, then applies its down rows and the
-//            combine with the residual.  The shared expert does not wait
-//            for routing: its gate/up rows are applied and its activations
-//            published while the logits travel, and every block applies its
-//            down rows (requested with the previous layer's prefetch) before
-//            it polls the routed slots' activations, so only the K routed
-//            slots' activations and down rows sit after the last hand-off.
+//            polls all activations (shared and routed slots in one take),
+//            then applies its down rows and the combine with the residual.
+//            The shared expert does not wait for routing: its gate/up rows
+//            are applied and its activations published while the routed
+//            rows stream in, and its down rows are requested with the
+//            previous layer's prefetch.
 // Loads are issued as early as their addresses are known and their data
 // does not compete with loads on the critical path: the router and
 // shared-expert pointers of every layer are cached in LDS at start; the
-// next layer's router rows and shared-expert gate/up rows are requested
-// right after h is published, and the shared expert's gate/up is computed
-// while the logits travel; the down rows are requested once the gate/up
-// rows are consumed.  A poll's loads complete after every load the wave
-// issued before them (the vector memory counter is in order), which is why
-// nothing large is requested just before a poll that is on the critical
-// path.  Each block owns fixed rows of every matrix:
+// next layer's router rows and shared-expert gate/up and down rows are
+// requested right after h is published, and the shared expert's gate/up is
+// computed while the routed rows stream in; the routed down rows are
+// requested once the gate/up rows are consumed.  A poll's loads complete
+// after every load the wave issued before them (the vector memory counter
+// is in order), so whatever is requested just before a poll delays it:
+// the layer's loads were placed by measurement (requesting the down rows
+// with the routed gate/up rows, or the next layer's rows before the
+// activation poll, both cost more than they save).  Each block owns fixed rows of every matrix:
 //   router rows  e = b + NB*k (every thread takes the columns of the h
 //   values it polls);
 //   gate/up rows r = b + NB*i of every selected expert (a = silu(g)*u is
@@ -64,6 +65,7 @@ constexpr int kMaxKS = 8;                  // selected + shared experts per laye
 constexpr int kActSums = 4;                // per staged activation chunk: X, 1024 X', undo, pad
 constexpr int kMaxLayers = 128;            // per persistent launch
 constexpr int kTblPer = 8;                 // pointer-table entries per thread (E + S <= 4096)
+constexpr int kTopkSlots = 8;              // logits per lane in a one-wave top-K (E <= 512)
 static_assert(kWaves * MOEQ_MAX_TOPK <= 64 * 2, "top-K merge holds two candidates per lane");
 static_assert(2 * kWaves >= MOEQ_MAX_TOPK, "threshold top-K: at most two samples per wave");
 
@@ -142,7 +144,8 @@ __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t payload, uint32
 // raised it.
 template <int N, typename Idx>
 __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
-                                            uint32_t (&out)[N], uint32_t* abort, int32_t* status) {
+                                            uint32_t (&out)[N], uint32_t* abort, int32_t* status,
+                                            int& rounds) {
   uint32_t pending = valid;
   for (int spins = 0;; ++spins) {
     uint64_t v[N];
@@ -155,7 +158,10 @@ __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint3
         pending &= ~(1u << i);
       }
     }
-    if (pending == 0) return true;
+    if (pending == 0) {
+      rounds = spins + 1;
+      return true;
+    }
     if ((spins & 15) == 15 && ld_agent(abort) != 0u) return false;
     if (spins > kSpinLimit) {
       set_status(status, kStatusTimeout);
@@ -239,11 +245,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ double selv[MOEQ_MAX_TOPK];
   __shared__ int64_t candk[kWaves * 64];
   __shared__ int candi[kWaves * 64];
-  __shared__ int sample_k[2 * kWaves];
-  __shared__ int cand_cnt[kWaves];
-  __shared__ int wsel[kWaves][MOEQ_MAX_TOPK];   // each wave's copy of the selection
   __shared__ float selw[MOEQ_MAX_TOPK];
-  __shared__ const uint8_t* eblob[kMaxKS];
   __shared__ const uint16_t* rtr[kMaxLayers];
   __shared__ const uint8_t* shp[kMaxLayers];
   __shared__ float undo_x;
@@ -258,7 +260,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   const int nchG = H / PC, nchD = I / PC;
   const int RG = (I + NB - 1) / NB, RD = (H + NB - 1) / NB;
 
-  const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD, a.clocks ? L * kStackClockEvents : 0);
+  const int clk0 = a.clocks ? L * kStackClockEvents : 0;
+  const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD, clk0 + (a.bclocks ? L * kBlockClockEvents : 0));
   float* hs = reinterpret_cast<float*>(smem + LL.hs);               // [H]
   uint32_t* xp = reinterpret_cast<uint32_t*>(smem + LL.xp);         // [H/2]
   float* xs = reinterpret_cast<float*>(smem + LL.xs);               // [H/PC][kChunkSums]
@@ -268,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   double* lg = reinterpret_cast<double*>(smem + LL.lg);             // [E]
   const uint8_t** tbl = reinterpret_cast<const uint8_t**>(smem + LL.tbl);  // [E + S], this layer
   int64_t* clk = reinterpret_cast<int64_t*>(smem + LL.clk);         // [L][kStackClockEvents] if timed
+  int64_t* bclk = clk + clk0;                                        // [L][kBlockClockEvents] if timed
 
   GridBarrier bar;
   bar.base = a.bar;
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   rsrc_t gq[RPWG];               // the task's expert blob, or an empty range: no task
   uint32_t gqo[RPWG], gso[RPWG]; // byte offsets of its quantized row and scale/bias words
   bool ghave[RPWG];
-  auto plan_gu = [&](int mlo, int mhi) {
+  auto plan_gu = [&](int mlo, int mhi, const uint8_t* shared_blob) {
     const uint32_t row_bytes = (uint32_t)H * BITS / 8;
     const uint32_t gpr = H / 64;
     const uint32_t sb_off = 3u * (uint32_t)H * I * BITS / 8;
@@ -349,12 +353,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (m < mlo || m >= mhi) continue;
       int j, sec, row;
       ghave[m] = gu_task(m, j, sec, row);
-      // routed slots: this wave's own copy of the selection; the shared one
-      // from eblob.  A missing expert (null) loads nothing.
+      // routed slots: the selection; the shared slot: shared_blob.  A missing expert (null) loads nothing.
       const int jj = ghave[m] ? j : K;
-      const int e = jj < K ? wsel[wave][jj] : 0;
-      const uint8_t* blob = uniform_ptr(jj < K ? ((unsigned)e < (unsigned)E ? tbl[e] : nullptr)
-                                               : eblob[min(jj, KS - 1)]);
+      const int e = jj < K ? sel[jj] : 0;
+      const uint8_t* blob = uniform_ptr(jj < K ? ((unsigned)e < (unsigned)E ? tbl[e] : nullptr) : shared_blob);
       const uint32_t r = ghave[m] ? (uint32_t)(sec * I + row) : 0u;   // row of [gate; up]
       gq[m] = make_rsrc(blob, ghave[m] && blob != nullptr ? blob_bytes : 0u);
       gqo[m] = r * row_bytes;
@@ -418,10 +420,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     const int i = wave * RPSD + lane / LPRD;
     row = i < RD ? b + NB * i : H;   // H: no row
   };
-  auto plan_down = [&]() {
+  auto plan_down = [&]() {   // from the selection
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
-      const uint8_t* blob = s < K ? uniform_ptr(eblob[s]) : nullptr;
+      const int e = s < K ? sel[s] : -1;
+      const uint8_t* blob = uniform_ptr((unsigned)e < (unsigned)E ? tbl[e] : nullptr);
       dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u);
     }
   };
@@ -446,8 +449,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int s = 0; s < STEPSD; ++s) down_load(dsrc[s], qd[s], sd[s]);
     issue_fence();
   };
-  auto issue_down_shared = [&]() {   // eblob[K] holds the layer's shared expert
-    const uint8_t* blob = S > 0 ? uniform_ptr(eblob[min(K, KS - 1)]) : nullptr;
+  auto issue_down_shared = [&](const uint8_t* sblob) {   // the layer's shared expert (at most one)
+    const uint8_t* blob = uniform_ptr(sblob);
     down_load(make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u), qsh, ssh);
     issue_fence();
   };
@@ -477,6 +480,19 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   auto stamp0 = [&](int li, int ev) {
     if (a.clocks && b == 0 && tid == 0) clk[li * kStackClockEvents + ev] = (int64_t)wall_clock64();
   };
+  // diagnostic stamps of every block, by thread 0 (no block barrier):
+  // 0 layer start, 1 h polled, 2 own logits published, 3 logits polled,
+  // 4 top-K, 5 routed gate/up dots, 6 routed activations published, 7 shared
+  // activations polled and applied, 8 routed activations polled, 9 h
+  // published (the last wave's); poll rounds (most over the threads): 10 h, 11 logits,
+  // 12 shared activations, 13 routed activations
+  auto bstamp = [&](int li, int ev) {
+    if (a.bclocks && tid == 0) bclk[li * kBlockClockEvents + ev] = (int64_t)wall_clock64();
+  };
+  auto bcount = [&](int li, int ev, int n) {   // maximum over the block's threads
+    if (a.bclocks) atomicMax(reinterpret_cast<unsigned long long*>(bclk + li * kBlockClockEvents + ev),
+                             (unsigned long long)n);
+  };
 
   // prologue: router and shared-expert pointers of every layer, first rows
   for (int li = tid; li < L; li += kThreads) {
@@ -484,6 +500,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     shp[li] = S > 0 ? static_cast<const uint8_t*>(a.blobs[(int64_t)(a.layer0 + li) * tbl_n + E]) : nullptr;
   }
   if (tid == 0) fail_flag = 0;
+  if (a.bclocks)
+    for (int i = tid; i < L * kBlockClockEvents; i += kThreads) bclk[i] = 0;
   // this block's tagged words start at tag 0 (no layer's); one grid
   // barrier puts every clear before any layer's write
   for (int par = 0; par < 2; ++par) {
@@ -503,14 +521,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       if (row < H) st_agent(hw + row, uint64_t{0});
     }
   }
-  if (tid < S) eblob[K + tid] = shp[0];
   if (!bar.sync(a.status, &bar_flag)) return;
   block_sync_lds();
   plan_router(0);
-  plan_gu(0, 1);
+  plan_gu(0, 1, S > 0 ? shp[0] : nullptr);
   issue_router();
   issue_gu(0, 1);
-  issue_down_shared();
+  issue_down_shared(S > 0 ? shp[0] : nullptr);
   uint32_t* const abort_word = a.bar + 32 * (1 + kGroups);
   auto block_failed = [&](bool ok) -> bool {   // whole block
     if (!ok) fail_flag = 1;
@@ -531,6 +548,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       lane = tid & 63;
     }
     stamp(li, 0);
+    bstamp(li, 0);
     const int par = li & 1;
     const uint64_t* hw_in = a.hwords + (int64_t)par * H;
     uint64_t* hw_out = a.hwords + (int64_t)(par ^ 1) * H;
@@ -556,8 +574,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           hw[2 * i] = hw[2 * i + 1] = 0u;
           if (2 * (tid + i * kThreads) < H) valid |= 3u << (2 * i);
         }
+        int nr = 0;
         ok = take_tagged<2 * HW>(hw_in, [&](int i) { return 2 * (tid + (i >> 1) * kThreads) + (i & 1); },
-                                 valid, (uint32_t)li, hw, abort_word, a.status);
+                                 valid, (uint32_t)li, hw, abort_word, a.status, nr);
+        bcount(li, 10, nr);
 #pragma unroll
         for (int i = 0; i < HW; ++i) hv[i] = ((uint64_t)hw[2 * i + 1] << 32) | hw[2 * i];
       }
@@ -599,6 +619,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     }
     block_sync_lds();
     stamp(li, 1);
+    bstamp(li, 1);
     double ss = 0.0;
     float mx = 0.0f;
 #pragma unroll
@@ -614,6 +635,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       put_tagged(lw + 2 * r, (uint32_t)bits, tag);
       put_tagged(lw + 2 * r + 1, (uint32_t)(bits >> 32), tag);
     }
+    bstamp(li, 2);
     // xhat -> fp16 pairs, one packed word per thread; the norm and the
     // rescale come from the h pass above, so no further reductions
     {
@@ -641,52 +663,58 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // ------------------------------------------------------------ phase G
     // this layer's pointer-table row lands while the logits are polled
     load_tbl_row(a.layer0 + li);
-    int64_t key = kNoKey;   // this thread's logit (E <= kThreads)
     for (int e0 = 0; e0 < E; e0 += kThreads) {   // one logit (two words) per thread per pass
       const int e = e0 + tid;
       uint32_t w[2] = {0u, 0u};
+      int nr = 0;
       const bool ok = take_tagged<2>(lw + 2 * e, [](int i) { return i; }, e < E ? 3u : 0u, tag, w,
-                                     abort_word, a.status);
-      if (e < E) {
-        const double v = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
-        lg[e] = v;
-        key = order_key(v);
-      }
-      if (E <= kThreads) topk_samples<kWaves>(key, K, sample_k);
+                                     abort_word, a.status, nr);
+      bcount(li, 11, nr);
+      if (e < E) lg[e] = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
+      // the table row's loads were issued before the poll's, so they are in;
+      // the barrier below publishes both to every wave
+      if (e0 + kThreads >= E) store_tbl_row();
       if (block_failed(ok)) return;
     }
-    store_tbl_row();
     stamp0(li, 12);
-    // top-K: every wave ends with its own copy of the selection, so the
-    // gate/up rows are requested without another block barrier
-    bool fast = false;
-    if (E <= kThreads) {
-      topk_candidates<kWaves>(key, tid, K, sample_k, candk, candi, cand_cnt);
-      stamp0(li, 19);
+    bstamp(li, 3);
+    // top-K: wave 0 selects from all E logits (up to eight per lane; one
+    // wave alone on its SIMD finishes sooner than eight sharing four), one
+    // barrier hands the selection to the block; beyond 512 experts the
+    // waves select together
+    if (E <= 64 * kTopkSlots) {
+      if (wave == 0) {
+        int64_t kk[kTopkSlots];
+#pragma unroll
+        for (int i = 0; i < kTopkSlots; ++i) {
+          const int e = lane + 64 * i;
+          kk[i] = e < E ? order_key(lg[e]) : kNoKey;
+        }
+        wave_select_hi<kTopkSlots>(kk, K, [&](int r, int win) { sel[r] = win; });
+      }
       block_sync_lds();
-      stamp0(li, 20);
-      fast = topk_select<kWaves>(K, candk, candi, cand_cnt, [&](int r, int win) { wsel[wave][r] = win; });
     } else {
-      block_sync_lds();
-    }
-    if (!fast) {   // block-uniform
-      if (E <= kThreads) block_topk_keys<kWaves, 1, 2>(lg, E, K, candk, candi, sel, selv);
-      else block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
-      if (lane < K) wsel[wave][lane] = sel[lane];
+      block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
     }
     stamp0(li, 14);
-    plan_gu(1, RPWG);                // routed gate/up rows
+    bstamp(li, 4);
+    plan_gu(1, RPWG, nullptr);       // routed gate/up rows
     issue_gu(1, RPWG);
     stamp0(li, 5);
-    // while they arrive: wave 0 records the blob pointers the down rows use
-    // (read after the next block barrier); the softmax weights wait until
-    // the activations are in flight
-    if (wave == 0 && lane < K) {
-      const int e = wsel[0][lane];
-      const uint8_t* bp = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
-      eblob[lane] = bp;
-      if (bp == nullptr) set_status(a.status, kStatusBadExpert);
-      if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
+    // while they arrive: wave 0 checks the selected experts' blobs, records
+    // the trace and takes the softmax weights (read by the combine after
+    // the activation hand-off's block barrier)
+    if (wave == 0) {
+      if (lane < K) {
+        const int e = sel[lane];
+        const uint8_t* bp = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
+        if (bp == nullptr) set_status(a.status, kStatusBadExpert);
+        if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
+        selv[lane] = (unsigned)e < (unsigned)E ? lg[e] : -INFINITY;
+      }
+      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
+                                  : wave_softmax_selected(selv, K);
+      if (lane < K) selw[lane] = w;
     }
     stamp0(li, 15);
     // the shared expert's gate/up rows (requested a layer ahead) while the
@@ -707,9 +735,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     }
     gu_dots(1, RPWG);
     stamp0(li, 13);
+    bstamp(li, 5);
     block_sync_lds();
     stamp(li, 6);
-    plan_down();                     // routed slots' down rows (eblob is complete now)
     jitter<JIT>(b, wave, li, 2);
     for (int t = tid; t < K * RG; t += kThreads) {
       const int j = t / RG, i = t - j * RG, row = b + NB * i;
@@ -718,19 +746,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         put_tagged(aw + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
       }
     }
+    bstamp(li, 6);
     // down rows of every slot, in flight while the activations arrive (not
     // earlier: they would share the memory system with the gate/up rows
     // every block is waiting for)
+    plan_down();
     issue_down();
     stamp0(li, 7);
-    // the softmax weights of the selection (wave 0), read by the combine
-    // after the activation hand-off's block barriers
-    if (wave == 0) {
-      if (lane < K) selv[lane] = (unsigned)wsel[0][lane] < (unsigned)E ? lg[wsel[0][lane]] : -INFINITY;
-      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
-                                  : wave_softmax_selected(selv, K);
-      if (lane < K) selw[lane] = w;
-    }
     stamp(li, 8);
 
     // ------------------------------------------------------------ phase D
@@ -739,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // threads of a chunk agree on it with two lane shuffles), so staging
     // needs no block-wide maximum; the block barrier after it also settles
     // a failed poll
-    auto take_acts = [&](int s0, int ns) -> bool {
+    auto take_acts = [&](int s0, int ns, int count_ev) -> bool {
       const int nwa = I / PW;
       const int total = ns * nwa;
       bool got_all = true;
@@ -752,8 +774,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 #pragma unroll
         for (int j = 0; j < PW; ++j) raw[j] = 0u;
         const uint64_t* src = aw + (int64_t)m * I + (int64_t)w * PW;
+        int nr = 0;
         const bool got = take_tagged<PW>(src, [](int j) { return j; }, ok ? (uint32_t)((1ull << PW) - 1) : 0u,
-                                         tag, raw, abort_word, a.status);
+                                         tag, raw, abort_word, a.status, nr);
+        bcount(li, count_ev, nr);
         got_all = got_all && got;
         float lm = 0.0f;
 #pragma unroll
@@ -789,48 +813,54 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       return group_sum_dpp<LPRD>(part);
     };
     const int sub = lane % LPRD;
-    const int di = wave * RPSD + lane / LPRD;
-    const int drow = b + NB * di;
-    const bool dok = di < RD && drow < H;
-    float acc = dok ? hs[drow] : 0.0f;
-    // the shared expert first: its activations were published in phase R
-    if (S > 0) {
-      if (!take_acts(K, 1)) return;
-      acc += down_dot(K, qsh, ssh, dok);
-    }
-    stamp0(li, 16);
-    // the routed slots
-    if (!take_acts(0, K)) return;
+    // shared and routed activations in one take
+    if (!take_acts(0, KS, 13)) return;
     stamp0(li, 17);
+    bstamp(li, 8);
     stamp(li, 9);
+    jitter<JIT>(b, wave, li, 3);
+    {
+      int drow;
+      down_row(drow);
+      const bool dok = drow < H;
+      float acc = dok ? hs[drow] : 0.0f;
+      if (S > 0) acc += down_dot(K, qsh, ssh, dok);   // the shared expert first, then the slots in rank order
 #pragma unroll
-    for (int s = 0; s < STEPSD; ++s) {
-      if (s >= K) break;
-      acc = fmaf(selw[s], down_dot(s, qd[s], sd[s], dok), acc);
+      for (int s = 0; s < STEPSD; ++s) {
+        if (s >= K) break;
+        acc = fmaf(selw[s], down_dot(s, qd[s], sd[s], dok), acc);
+      }
+      if (dok && sub == LPRD - 1) {
+        if (a.h_trace) a.h_trace[(int64_t)li * H + drow] = hs[drow];
+        if (li + 1 == L) a.h[drow] = acc;   // complete when the launch ends
+        else put_tagged(hw_out + drow, __float_as_uint(acc), tag);
+      }
     }
     stamp0(li, 18);
-    jitter<JIT>(b, wave, li, 3);
-    if (dok && sub == LPRD - 1) {
-      if (a.h_trace) a.h_trace[(int64_t)li * H + drow] = hs[drow];
-      if (li + 1 == L) a.h[drow] = acc;   // complete when the launch ends
-      else put_tagged(hw_out + drow, __float_as_uint(acc), tag);
-    }
+    if (a.bclocks && lane == 0)
+      atomicMax(reinterpret_cast<unsigned long long*>(bclk + li * kBlockClockEvents + 9),
+                (unsigned long long)wall_clock64());
     stamp(li, 10);
     if (li + 1 == L) break;
-    // next layer: router rows, shared-expert gate/up rows, pointer-table row,
-    // in flight while h arrives
-    if (S > 0 && tid == 0) eblob[K] = shp[li + 1];   // at most one shared expert
-    block_sync_lds();
+    // next layer: router rows, shared-expert gate/up and down rows, in
+    // flight while h arrives
     plan_router(li + 1);
-    plan_gu(0, 1);
     issue_router();
-    issue_gu(0, 1);
-    issue_down_shared();
+    if (S > 0) {
+      plan_gu(0, 1, shp[li + 1]);
+      issue_gu(0, 1);
+    }
+    issue_down_shared(S > 0 ? shp[li + 1] : nullptr);
     stamp0(li, 11);
   }
   if (a.clocks && b == 0) {   // stamps were kept in LDS so taking them adds no memory traffic
     block_sync_lds();
     for (int i = tid; i < L * kStackClockEvents; i += kThreads) a.clocks[i] = clk[i];
+  }
+  if (a.bclocks) {
+    block_sync_lds();
+    for (int i = tid; i < L * kBlockClockEvents; i += kThreads)
+      a.bclocks[(int64_t)b * L * kBlockClockEvents + i] = bclk[i];
   }
 }
 
@@ -908,7 +938,9 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   const int PC = 128 / a.bits;
   const int RG = (a.I + nb - 1) / nb, RD = (a.H + nb - 1) / nb;
   const size_t lds =
-      (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD, a.clocks ? a.L * kStackClockEvents : 0).total;
+      (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD,
+                               (a.clocks ? a.L * kStackClockEvents : 0) + (a.bclocks ? a.L * kBlockClockEvents : 0))
+          .total;
   if (lds > 96 * 1024) return hipErrorNotSupported;
   const Geometry g{nb, rw, a.H, a.I, a.E, a.S, a.K, KS, a.bits};
   // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,

@@ -146,6 +146,61 @@ __device__ __forceinline__ void wave_select(int64_t (&k)[M], const int (&id)[M],
   }
 }
 
+// One wave: the K best of M keys per lane (element index lane + 64 i, so a
+// lane's slots are in index order; kNoKey marks an empty slot), in rank
+// order, through emit(r, index) on lane 0 (kTopkNone once nothing is left).
+// Same result as wave_select, with fewer instructions per round: a round
+// takes the wave maximum of the keys' high words (a monotone map of the
+// key, 32-bit DPP steps); when one element alone holds it, that element's
+// key is strictly the largest and wins.  A tie on the high word is settled
+// on the full keys of the tied elements, then on the lower index.
+template <int M, typename Emit>
+__device__ __forceinline__ void wave_select_hi(const int64_t (&k)[M], int K, Emit emit) {
+  const int lane = threadIdx.x & 63;
+  int h[M];
+  uint32_t alive = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const bool real = k[i] != kNoKey;
+    h[i] = real ? (int)(k[i] >> 32) : INT_MIN;
+    alive |= real ? (1u << i) : 0u;
+  }
+  for (int r = 0; r < K; ++r) {
+    int lm = h[0];
+#pragma unroll
+    for (int i = 1; i < M; ++i) lm = max(lm, h[i]);
+    const int mh = wave_max_i32(lm);
+    uint32_t mk = 0;   // alive slots of this lane holding the maximum
+#pragma unroll
+    for (int i = 0; i < M; ++i) mk |= (h[i] == mh) ? (1u << i) : 0u;
+    mk &= alive;
+    const uint64_t B = __ballot(mk != 0);
+    int win = kTopkNone;
+    if (B != 0) {
+      const int l0 = (int)__builtin_ctzll(B);
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane((int)mk, l0);
+      if ((B & (B - 1)) == 0 && (m0 & (m0 - 1)) == 0) {
+        win = l0 + 64 * (int)__builtin_ctz(m0);
+      } else {
+        int64_t lk = kNoKey;
+        int li = kTopkNone;
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+          if (((mk >> i) & 1u) && (li == kTopkNone || k[i] > lk)) { lk = k[i]; li = lane + 64 * i; }
+        const int64_t m = wave_max_key(lk);
+        const uint64_t mask = __ballot(li != kTopkNone && lk == m);
+        win = (mask & (mask - 1)) == 0 ? __builtin_amdgcn_readlane(li, __builtin_ctzll(mask))
+                                       : wave_min_int(li != kTopkNone && lk == m ? li : kTopkNone);
+      }
+      const uint32_t wm = lane == (win & 63) ? (1u << (win >> 6)) : 0u;
+#pragma unroll
+      for (int i = 0; i < M; ++i) h[i] = ((wm >> i) & 1u) ? INT_MIN : h[i];
+      alive &= ~wm;
+    }
+    if (lane == 0) emit(r, win);
+  }
+}
+
 // All NW waves of a block: top-K (K <= 64*MC/NW) of lg[0..E) (LDS, E <= 64*NW*M).
 // Wave w selects the K best of its elements w*64 + lane + 64*NW*i into
 // ck/ci[w*K + r]; wave 0 then selects the K best of those NW*K candidates
