@@ -54,6 +54,9 @@ def parse():
                    help="stack60_decode: per-layer launches instead of the persistent kernel")
     p.add_argument("--fused-layer", action="store_true",
                    help="one-token layer workloads: one persistent launch per layer instead of the three calls")
+    p.add_argument("--eager", action="store_true",
+                   help="one-token layer workloads: launch every call from Python instead of replaying "
+                        "the steps captured in a HIP graph")
     p.add_argument("--instances", type=int, default=8, help="layer instances for cold rotation")
     p.add_argument("--tokens-pool", type=int, default=64, help="distinct token vectors")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -661,20 +664,25 @@ def run_layer_workload(args, cfg, dev, stream):
             ev[slot][1].record(stream)
         q.moe_swiglu_down_combine(shape, table, l, gu, idx, w, sw, x, K, ws, y, stream=stream)
 
-    with torch.cuda.stream(stream):
-        for s in range(args.warmup):
-            step(s)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        start.record(stream)
-        for i in range(args.steps):
-            step(args.warmup + i, slot=i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    elapsed_ms = start.elapsed_time(end)
-    gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    if args.eager:
+        with torch.cuda.stream(stream):
+            for s in range(args.warmup):
+                step(s)
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record(stream)
+            for i in range(args.steps):
+                step(args.warmup + i, slot=i)
+            end.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        elapsed_ms = start.elapsed_time(end)
+        gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        launch = "eager (one Python call per kernel)"
+    else:
+        elapsed_ms, gemv_ms, wall = time_layer_graph(args, step, stream, shape, table, pool, idx_all, ws, gu, y, K)
+        launch = f"HIP graph of {args.steps} steps (3 launches each), replayed"
     idx_np = idx_all[args.warmup:].cpu().numpy()
     distinct = np.array([len(np.unique(i)) for i in idx_np]) + cfg.n_shared
     expert_bytes = distinct * cfg.expert_bytes
@@ -695,9 +703,58 @@ def run_layer_workload(args, cfg, dev, stream):
                      "traffic": None, "avg_launch_us": round(gemv_ms * 1e3, 3),
                      "bytes_per_launch": int(gemv_bytes)},
     })
-    rec["config"].update(layers_per_step=1, layer_instances=n_inst)
+    rec["config"].update(layers_per_step=1, layer_instances=n_inst, launch=launch)
     rec["parity"] = parity
     return rec
+
+
+def time_layer_graph(args, step, stream, shape, table, pool, idx_all, ws, gu, y, K):
+    """The timed steps captured in one HIP graph (three kernel nodes per
+    step), replayed once after an untimed replay; the gate/up call alone is
+    captured the same way for its per-launch time.  The graph's last output
+    is checked bit for bit against the same step launched eagerly."""
+    import torch
+    import quantized_expert_gemv_router_amd as q
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            step(s)
+    torch.cuda.synchronize()
+    base = args.warmup
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(args.steps):
+            step(base + i)
+    gg = torch.cuda.CUDAGraph()   # the gate/up launches of the same steps
+    with torch.cuda.graph(gg, stream=stream):
+        for i in range(args.steps):
+            s = base + i
+            q.moe_q4_expert_gemv(shape, table, s % args.instances, pool[s % args.tokens_pool], idx_all[s], K, 0,
+                                 ws, gu, stream=stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()   # untimed
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        y_graph = y.clone()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gg.replay()
+        gs.record(stream)
+        gg.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        step(base + args.steps - 1)   # the last step again, launched eagerly
+        torch.cuda.synchronize()
+    if not torch.equal(y_graph, y):
+        raise ParityError("the graph replay's output differs from the same step launched eagerly")
+    log("[bench] graph replay output equals the eager launch")
+    return start.elapsed_time(end), gs.elapsed_time(ge) / args.steps, wall
 
 
 def run_pool(args, cfg, dev, stream):

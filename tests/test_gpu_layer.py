@@ -267,3 +267,33 @@ def test_given_ids_with_duplicates_and_bad_id():
         assert_close(gu[t, slot, 1], u, f"up t{t} s{slot}")
     assert np.all(gu[1, 1] == 0)
     assert q.moe_read_device_status(ws) == 0
+
+
+def test_layer_calls_replay_in_a_hip_graph():
+    """The three calls of a one-token layer captured in a HIP graph: every
+    replay, with eager launches and synchronisations between the replays,
+    equals the eager result bit for bit (top-K, weights, gate/up, output)."""
+    cfg = synth.CONFIGS["decode_4bit"]
+    say(f"[graph] {cfg.name}: capture the three calls, replay six times")
+    shape, ex = experts_for(cfg)
+    wr = bf16_dev(synth.router(cfg, 0))
+    xs = [bf16_dev(synth.tokens(cfg, t)) for t in range(3)]
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    eager = [q.moe_layer(shape, ex, 0, x, wr, cfg.top_k, workspace=ws) for x in xs]
+    torch.cuda.synchronize()
+    x_in = xs[0].clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = q.moe_layer(shape, ex, 0, x_in, wr, cfg.top_k, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        t = rep % 3
+        x_in.copy_(xs[t])
+        g.replay()
+        torch.cuda.synchronize()
+        for key in ("idx", "w", "gate_up", "y"):
+            assert torch.equal(out[key], eager[t][key]), (rep, key)
+        other = q.moe_layer(shape, ex, 0, xs[(t + 1) % 3], wr, cfg.top_k, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other["y"], eager[(t + 1) % 3]["y"]), rep
