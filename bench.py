@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--eager", action="store_true",
                    help="one-token layer workloads: launch every call from Python instead of replaying "
                         "the steps captured in a HIP graph")
+    p.add_argument("--warm", action="store_true",
+                   help="one-token and batch layer workloads: the same layer instance and token every step "
+                        "(its experts stay in the caches) instead of the cold rotation")
     p.add_argument("--instances", type=int, default=8, help="layer instances for cold rotation")
     p.add_argument("--tokens-pool", type=int, default=64, help="distinct token vectors")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -214,12 +217,12 @@ def cpu_baseline_stack(cfg, seconds: float):
 
 # -------------------------------------------------------------- workloads
 
-def recorded_stack_traffic():
-    """HBM bytes per launch of the persistent stack kernel from the committed
-    rocprofv3 counter summary, or None when the kernel's sources changed
-    since the counters were taken."""
+def recorded_traffic(profile, sources):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary, or None when the kernel's sources changed since the counters
+    were taken (the summary records the sha256 of the sources)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "stack_kernel_stack60_decode_traffic.txt")
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -228,12 +231,23 @@ def recorded_stack_traffic():
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("stack_decode.hip", "moeq_device.hpp", "topk.hpp", "moeq_internal.hpp"):
+    for f in sources:
         with open(os.path.join(ROOT, "quantized_expert_gemv_router_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if rec.get("source_sha256_16") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in rec:
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def recorded_stack_traffic():
+    return recorded_traffic("stack_kernel_stack60_decode_traffic.txt",
+                            ("stack_decode.hip", "moeq_device.hpp", "topk.hpp", "moeq_internal.hpp"))
+
+
+def recorded_prefill_traffic():
+    """The 2048-token workload's gate/up GEMM (the counters were taken on it)."""
+    return recorded_traffic("prefill_gemm_counters_stack60_prefill.txt",
+                            ("prefill.hip", "moeq_device.hpp", "moeq_internal.hpp"))
 
 
 def setup_layers(cfg, n_layers, dev, stream):
@@ -490,7 +504,7 @@ def run_prefill(args, cfg, dev, stream):
             "avg_launch_us": round(gu_ms / gu_n * 1e3, 2), "bytes_per_launch": int(gu_bytes),
             "flop_per_launch": gu_flop, "hbm_gbs": round(gu_gbs, 1), "hbm_frac": round(gu_gbs / HBM_PEAK_GBS, 4),
             "mfma_tflops": round(gu_tflops, 1), "mfma_frac": round(gu_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
-            "traffic": None}
+            "traffic": recorded_prefill_traffic() if cfg.name == "stack60_prefill" else None}
     if mfma_bound:
         roof.update(bound="mfma", achieved=round(gu_tflops, 1), peak=MFMA_FP16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(gu_tflops / MFMA_FP16_PEAK_TFLOPS, 4))
@@ -616,6 +630,8 @@ def run_layer_workload(args, cfg, dev, stream):
     import quantized_expert_gemv_router_amd as q
     import synth
 
+    if args.warm:
+        args.instances, args.tokens_pool = 1, 1
     n_inst = args.instances
     shape, table, routers, bf16 = setup_layers(cfg, n_inst, dev, stream)
     T, K = cfg.tokens, cfg.top_k
@@ -703,7 +719,11 @@ def run_layer_workload(args, cfg, dev, stream):
                      "traffic": None, "avg_launch_us": round(gemv_ms * 1e3, 3),
                      "bytes_per_launch": int(gemv_bytes)},
     })
-    rec["config"].update(layers_per_step=1, layer_instances=n_inst, launch=launch)
+    rec["config"].update(layers_per_step=1, layer_instances=n_inst, launch=launch,
+                         weights=("warm: one layer instance and one token every step, the same experts"
+                                  if args.warm else
+                                  f"cold: {n_inst} layer instances x {args.tokens_pool} tokens rotating, "
+                                  "far more expert bytes than the 256 MB of last-level cache"))
     rec["parity"] = parity
     return rec
 
