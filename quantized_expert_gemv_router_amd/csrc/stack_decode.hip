@@ -40,13 +40,14 @@
 // is in order), so whatever is requested just before a poll delays it:
 // the layer's loads were placed by measurement (requesting the down rows
 // with the routed gate/up rows, or the next layer's rows before the
-// activation poll, both cost more than they save).  Each block owns fixed rows of every matrix:
-//   router rows  e = b + NB*k (every thread takes the columns of the h
-//   values it polls);
-//   gate/up rows r = b + NB*i of every selected expert (a = silu(g)*u is
-//   formed locally);
-//   down rows    r = b + NB*i of every selected expert (the combine is a
-//   per-row sum in slot order, no atomics).
+// activation poll, both cost more than they save).  Each block owns fixed,
+// contiguous rows of every matrix:
+//   router rows  e in [b E/NB, (b+1) E/NB) (every thread takes the columns
+//   of the h values it polls);
+//   gate/up rows r in [b I/NB, (b+1) I/NB) of every selected expert
+//   (a = silu(g)*u is formed locally);
+//   down rows    r in [b H/NB, (b+1) H/NB) of every selected expert (the
+//   combine is a per-row sum in slot order, no atomics).
 // Every wait is bounded: on time-out a block sets the status word and an
 // abort flag, and every block leaves the kernel.
 #include "moeq_device.hpp"
@@ -280,7 +281,21 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   bar.gsize = (NB - bar.group + bar.ngroups - 1) / bar.ngroups;
   bar.epoch = 0;
 
-  // router: RW (<= CPLR) rows per block, rows b + NB*k; each thread takes
+  // This block's rows, contiguous and balanced: router rows [rlo, rhi),
+  // gate/up rows [glo, ghi), rows of h [dlo, dhi) (at least one when H >=
+  // blocks).  Contiguous ownership keeps a tagged 128-byte line to few
+  // writing blocks (one for h) while readers still poll in address order.
+  int rlo, rhi, glo, ghi, dlo, dhi;
+  auto set_rows = [&]() {
+    rlo = b * E / NB;
+    rhi = (b + 1) * E / NB;
+    glo = b * I / NB;
+    ghi = (b + 1) * I / NB;
+    dlo = b * H / NB;
+    dhi = (b + 1) * H / NB;
+  };
+  set_rows();
+  // router: RW (<= CPLR) rows per block, rows rlo + k; each thread takes
   // the columns of the h values it polls (2p, 2p+1 for p = tid + i*kThreads)
   const int RW = a.router_rows;
   const int tbl_n = E + S;
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   // gate/up rows: register slot m = 0 holds the shared expert's rows (task
   // u = wave), slots m >= 1 the routed slots' (task u = (m - 1) * kWaves +
   // wave, slot u / 2RG); within a slot, task u % 2RG is section (gate, up)
-  // and row b + NB * i.  The shared rows are requested a layer ahead and
+  // and row glo + i.  The shared rows are requested a layer ahead and
   // stay in their registers while the routed rows are requested.
   auto gu_task = [&](int m, int& j, int& sec, int& row) -> bool {
     int u;
@@ -313,8 +328,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     }
     const int tj = u % (2 * RG);
     sec = tj / RG;
-    row = b + NB * (tj % RG);
-    return valid && row < I;
+    row = glo + tj % RG;
+    return valid && row < ghi;
   };
   // Loads are planned (every LDS read they need) before any is issued: an
   // LDS read between loads makes the compiler wait for the loads in flight.
@@ -326,8 +341,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     const uint16_t* base = uniform_ptr(rtr[li]);
 #pragma unroll
     for (int k = 0; k < CPLR; ++k) {
-      const int r = b + NB * k;
-      const bool have = k < RW && r < E;
+      const int r = rlo + k;
+      const bool have = k < RW && r < rhi;
       rplan[k] = make_rsrc(base + (int64_t)(have ? r : 0) * H, have ? (uint32_t)H * 2u : 0u);
     }
   };
@@ -408,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       int j, sec, row;
       gu_task(m, j, sec, row);
       const float v = wave_sum_dpp(part[m]) * ux;
-      if (lane == 0) gres[(j * 2 + sec) * RG + (row - b) / NB] = v;
+      if (lane == 0) gres[(j * 2 + sec) * RG + (row - glo)] = v;
     }
   };
   // down rows: a wave owns RPSD of the block's output rows (LPRD lanes
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   const uint32_t blob_bytes_all = 3u * (uint32_t)H * I * BITS / 8 + 3u * (uint32_t)(H / 64) * I * 4u;
   auto down_row = [&](int& row) {
     const int i = wave * RPSD + lane / LPRD;
-    row = i < RD ? b + NB * i : H;   // H: no row
+    row = i < RD && dlo + i < dhi ? dlo + i : H;   // H: no row
   };
   auto plan_down = [&]() {   // from the selection
 #pragma unroll
@@ -509,16 +524,16 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     uint64_t* aw = a.awords + (int64_t)par * KS * I;
     uint64_t* hw = a.hwords + (int64_t)par * H;
     for (int j = tid; j < RW; j += kThreads) {
-      const int r = b + NB * j;
-      if (r < E) { st_agent(lw + 2 * r, uint64_t{0}); st_agent(lw + 2 * r + 1, uint64_t{0}); }
+      const int r = rlo + j;
+      if (r < rhi) { st_agent(lw + 2 * r, uint64_t{0}); st_agent(lw + 2 * r + 1, uint64_t{0}); }
     }
     for (int t = tid; t < KS * RG; t += kThreads) {
-      const int j = t / RG, row = b + NB * (t - j * RG);
-      if (row < I) st_agent(aw + (int64_t)j * I + row, uint64_t{0});
+      const int j = t / RG, row = glo + (t - j * RG);
+      if (row < ghi) st_agent(aw + (int64_t)j * I + row, uint64_t{0});
     }
     for (int i = tid; i < RD; i += kThreads) {
-      const int row = b + NB * i;
-      if (row < H) st_agent(hw + row, uint64_t{0});
+      const int row = dlo + i;
+      if (row < dhi) st_agent(hw + row, uint64_t{0});
     }
   }
   if (!bar.sync(a.status, &bar_flag)) return;
@@ -546,6 +561,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       b = (int)blockIdx.x + zero;
       asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
       lane = tid & 63;
+      set_rows();
     }
     stamp(li, 0);
     bstamp(li, 0);
@@ -627,10 +643,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     const double inv = a.no_norm ? 1.0 : 1.0 / sqrt(ss / (double)H + 1e-6);
     const uint32_t tag = (uint32_t)li + 1u;
     jitter<JIT>(b, wave, li, 0);
-    if (tid < RW && b + NB * tid < E) {   // logits of this block's router rows
+    if (tid < RW && rlo + tid < rhi) {   // logits of this block's router rows
       double d = 0.0;
       for (int w = 0; w < kWaves; ++w) d += rpart[tid * kWaves + w];
-      const int r = b + NB * tid;
+      const int r = rlo + tid;
       const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
       put_tagged(lw + 2 * r, (uint32_t)bits, tag);
       put_tagged(lw + 2 * r + 1, (uint32_t)(bits >> 32), tag);
@@ -725,8 +741,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       block_sync_lds();
       jitter<JIT>(b, wave, li, 1);
       for (int t = tid; t < RG; t += kThreads) {
-        const int row = b + NB * t;
-        if (row < I) {
+        const int row = glo + t;
+        if (row < ghi) {
           const float g = gres[(K * 2) * RG + t], u = gres[(K * 2 + 1) * RG + t];
           put_tagged(aw + (int64_t)K * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
         }
@@ -740,8 +756,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     stamp(li, 6);
     jitter<JIT>(b, wave, li, 2);
     for (int t = tid; t < K * RG; t += kThreads) {
-      const int j = t / RG, i = t - j * RG, row = b + NB * i;
-      if (row < I) {
+      const int j = t / RG, i = t - j * RG, row = glo + i;
+      if (row < ghi) {
         const float g = gres[(j * 2) * RG + i], u = gres[(j * 2 + 1) * RG + i];
         put_tagged(aw + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
       }
