@@ -643,13 +643,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     const double inv = a.no_norm ? 1.0 : 1.0 / sqrt(ss / (double)H + 1e-6);
     const uint32_t tag = (uint32_t)li + 1u;
     jitter<JIT>(b, wave, li, 0);
-    if (tid < RW && rlo + tid < rhi) {   // logits of this block's router rows
+    if (tid < 2 * RW && rlo + (tid >> 1) < rhi) {   // this block's logits: two words each, one store
+      const int k = tid >> 1;
       double d = 0.0;
-      for (int w = 0; w < kWaves; ++w) d += rpart[tid * kWaves + w];
-      const int r = rlo + tid;
+      for (int w = 0; w < kWaves; ++w) d += rpart[k * kWaves + w];
       const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
-      put_tagged(lw + 2 * r, (uint32_t)bits, tag);
-      put_tagged(lw + 2 * r + 1, (uint32_t)(bits >> 32), tag);
+      put_tagged(lw + 2 * (rlo + k) + (tid & 1), (tid & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits, tag);
     }
     bstamp(li, 2);
     // xhat -> fp16 pairs, one packed word per thread; the norm and the
