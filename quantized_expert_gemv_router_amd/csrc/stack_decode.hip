@@ -504,9 +504,12 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   auto bstamp = [&](int li, int ev) {
     if (a.bclocks && tid == 0) bclk[li * kBlockClockEvents + ev] = (int64_t)wall_clock64();
   };
-  auto bcount = [&](int li, int ev, int n) {   // maximum over the block's threads
-    if (a.bclocks) atomicMax(reinterpret_cast<unsigned long long*>(bclk + li * kBlockClockEvents + ev),
-                             (unsigned long long)n);
+  auto bcount = [&](int li, int ev, int n) {   // maximum over the block's threads (one LDS atomic per wave)
+    if (a.bclocks) {
+      const int m = wave_max_i32(n);
+      if (lane == 0)
+        atomicMax(reinterpret_cast<unsigned long long*>(bclk + li * kBlockClockEvents + ev), (unsigned long long)m);
+    }
   };
 
   // prologue: router and shared-expert pointers of every layer, first rows
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     bstamp(li, 6);
     // down rows of every slot, in flight while the activations arrive (not
     // earlier: they would share the memory system with the gate/up rows
-    // every block is waiting for)
+    // every block is waiting for, or hold back the publish above)
     plan_down();
     issue_down();
     stamp0(li, 7);
