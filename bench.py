@@ -52,8 +52,9 @@ def parse():
                             "stack60_prefill_4k", "stack60_prefill_8k", "pool_decode", "decode_3bit"])
     p.add_argument("--layerwise", action="store_true",
                    help="stack60_decode: per-layer launches instead of the persistent kernel")
-    p.add_argument("--fused-layer", action="store_true",
-                   help="one-token layer workloads: one persistent launch per layer instead of the three calls")
+    p.add_argument("--layer-calls", action="store_true",
+                   help="one-token layer workloads: the three calls per layer (router, gate/up, down/combine) "
+                        "instead of one persistent launch per layer")
     p.add_argument("--eager", action="store_true",
                    help="one-token layer workloads: launch every call from Python instead of replaying "
                         "the steps captured in a HIP graph")
@@ -536,6 +537,8 @@ def run_layer_fused(args, cfg, dev, stream):
     import synth
     import oracle
 
+    if args.warm:
+        args.instances, args.tokens_pool = 1, 1
     n_inst = args.instances
     shape, table, routers, bf16 = setup_layers(cfg, n_inst, dev, stream)
     rt = q.RouterTable(routers, device=dev)
@@ -585,20 +588,61 @@ def run_layer_fused(args, cfg, dev, stream):
     with torch.cuda.stream(stream):
         for s in range(args.warmup):
             step(s)
+    torch.cuda.synchronize()
+    if args.eager:
+        with torch.cuda.stream(stream):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record(stream)
+            for i in range(args.steps):
+                step(args.warmup + i, slot=i)
+            end.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        elapsed_ms = start.elapsed_time(end)
+        launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        launch = "eager (one Python call per launch)"
+    else:
+        # the timed steps captured in one HIP graph (one kernel node each);
+        # an untimed replay is checked bit for bit against the last step
+        # launched eagerly on the same input, then the inputs are restored
+        base = args.warmup
+        h_in = [hs[base + i].clone() for i in range(args.steps)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                step(base + i)
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        start.record(stream)
-        for i in range(args.steps):
-            step(args.warmup + i, slot=i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            last = base + args.steps - 1
+            h_chk = h_in[-1].clone()
+            rc = q.lib().moe_expert_stack_decode(ctypes.byref(shape), table.view(), rt.ptr(), last % n_inst, 1, 1,
+                                                 K, flags, h_chk.data_ptr(), None, None, ws.data_ptr(),
+                                                 stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(q.moeq_last_error())
+            torch.cuda.synchronize()
+            if not torch.equal(h_chk, hs[last]):
+                raise ParityError("the graph replay's output differs from the same step launched eagerly")
+            log("[bench] graph replay output equals the eager launch")
+            for i in range(args.steps):
+                hs[base + i].copy_(h_in[i])
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        elapsed_ms = start.elapsed_time(end)
+        launch_ms = elapsed_ms / args.steps
+        launch = f"HIP graph of {args.steps} steps (one launch each), replayed"
     status = q.moe_read_device_status(ws, stream)
     if status != 0:
         raise RuntimeError(f"device status {status} after the timed region")
-    elapsed_ms = start.elapsed_time(end)
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     idx = tks[args.warmup:].cpu().numpy()
     distinct = np.array([len(np.unique(idx[s])) for s in range(args.steps)]) + cfg.n_shared
     expert_bytes = distinct * cfg.expert_bytes
@@ -621,7 +665,11 @@ def run_layer_fused(args, cfg, dev, stream):
                      "bytes_per_launch": int(per_launch), "router_bytes_per_launch": router_bytes},
         "parity": parity,
     })
-    rec["config"].update(layers_per_step=1, layer_instances=n_inst)
+    rec["config"].update(layers_per_step=1, layer_instances=n_inst, launch=launch,
+                         weights=("warm: one layer instance and one token every step, the same experts"
+                                  if args.warm else
+                                  f"cold: {n_inst} layer instances x {args.tokens_pool} tokens rotating, "
+                                  "far more expert bytes than the 256 MB of last-level cache"))
     return rec
 
 
@@ -1109,7 +1157,8 @@ def main():
         rec = run_prefill(args, cfg, dev, stream)
     elif cfg.layers > 1:
         rec = run_stack(args, cfg, dev, stream)
-    elif cfg.tokens == 1 and args.fused_layer:
+    elif cfg.tokens == 1 and cfg.bits in (2, 4) and not args.layer_calls:
+        # widths with a persistent instantiation: the whole layer in one launch
         rec = run_layer_fused(args, cfg, dev, stream)
     else:
         rec = run_layer_workload(args, cfg, dev, stream)

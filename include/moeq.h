@@ -190,10 +190,14 @@ int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts
  *   h_trace     device [L][T][H] f32 out (the input of each layer), or NULL
  *   flags       MOEQ_F_NO_RENORM, MOEQ_F_STACK_LAYERWISE, MOEQ_F_STACK_NO_NORM,
  *               MOEQ_F_STACK_JITTER
- * T == 1 runs one persistent cooperative launch for all L layers (no host
+ * T == 1 runs one persistent launch for all L layers (no host
  * involvement: the workgroups hand the logits, the activations and the
  * hidden state to each other through tagged words in the workspace) when
- * the shape has a persistent instantiation; otherwise, or with
+ * the shape has a persistent instantiation; the launch is an ordinary one
+ * (it can be captured in a HIP graph and replayed) whose workgroups, one
+ * per compute unit, must all be resident at once, so persistent launches
+ * on one GPU must not overlap in time (a launch that cannot fill the GPU
+ * ends with status bit 2 instead of hanging).  Otherwise, or with
  * MOEQ_F_STACK_LAYERWISE or T > 1, it enqueues the three per-layer calls
  * for each layer.  A wait between workgroups that lasts too long sets
  * status bit 2 (see moe_read_device_status) and the launch ends early. */

@@ -11,8 +11,8 @@
 //   for each selected expert and the shared one: g, u (dequant mat-vec),
 //   a = silu(g) u, d = Wd a;  h <- h + sum_k w_k d_k + d_shared
 //
-// Grid: one workgroup of 8 waves per CU, all co-resident (cooperative
-// launch).  Three all-to-all steps per layer, each a handoff of tagged
+// Grid: one workgroup of 8 waves per CU, all resident at once (the
+// launcher checks that the occupancy allows one workgroup per CU).  Three all-to-all steps per layer, each a handoff of tagged
 // words (payload + layer tag in one 64-bit word, polled by the readers; no
 // grid barrier or fence between the phases):
 //   h:       each block publishes its rows of h_{l+1}; every block polls all
@@ -59,9 +59,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGroups = 8;                 // barrier tree: groups of blocks
-constexpr int kBarWords = 32 * (kGroups + 2);
-constexpr int kSpinLimit = 1 << 18;        // polls before a barrier gives up
+constexpr int kSpinLimit = 1 << 18;        // polls before a wait gives up
 constexpr int kMaxKS = 8;                  // selected + shared experts per layer
 constexpr int kActSums = 4;                // per staged activation chunk: X, 1024 X', undo, pad
 constexpr int kMaxLayers = 128;            // per persistent launch
@@ -70,56 +68,26 @@ constexpr int kTopkSlots = 8;              // logits per lane in a one-wave top-
 static_assert(kWaves * MOEQ_MAX_TOPK <= 64 * 2, "top-K merge holds two candidates per lane");
 static_assert(2 * kWaves >= MOEQ_MAX_TOPK, "threshold top-K: at most two samples per wave");
 
-// ------------------------------------------------------------------ barrier
-struct GridBarrier {
-  uint32_t* base;       // [0]: top counter, [32*(1+g)]: group g, [32*(1+kGroups)]: abort
-  int group, gsize, ngroups;
-  uint32_t epoch;
+// ------------------------------------------------------- launch ticket
+// Control words in the workspace (zero-filled once when it is allocated):
+//   [0..1]  64-bit launch ticket: each workgroup adds 1 when it starts, so a
+//           launch of NB workgroups that follows n earlier launches of NB
+//           workgroups (calls on one workspace do not overlap) reads
+//           values n*NB .. n*NB + NB - 1, and every workgroup of it derives
+//           the same launch number n;
+//   [32]    abort word: holds the launch's abort value while it aborts.
+// Tags are 32 bits: (n mod 2^24) << 8 in the high 24 bits and the layer
+// index within the launch + 1 (1 .. 128) in the low 8 bits; the value with
+// low bits 0 marks a word cleared by this launch and low bits 255 the abort
+// value.  A word written by another launch therefore never carries a tag
+// this launch waits for, so no grid barrier is needed between launches or
+// at a launch's start: each block rewrites its own words with the cleared
+// value first (which also bounds the age of every word by one launch, so
+// the 24-bit launch number cannot wrap onto a stale word).
+constexpr int kBarWords = 64;
+constexpr uint32_t kAbortLow = 255u;
 
-  // Thread 0 arrives for the whole block.  The caller has drained the
-  // block's global stores and passed a block barrier after that.
-  __device__ __forceinline__ void arrive() {
-    if (threadIdx.x == 0) {
-      ++epoch;
-      uint32_t* gc = base + 32 * (1 + group);
-      const uint32_t old = atomic_add_agent(gc, 1u);
-      if (old == epoch * (uint32_t)gsize - 1u) atomic_add_agent(base, 1u);
-    }
-  }
-
-  // Whole block: waits until every block has arrived.  Global loads issued
-  // between arrive() and wait() stay in flight across the wait.  Returns
-  // false if the grid is aborting.
-  __device__ __forceinline__ bool wait(int32_t* status, int* flag) {
-    if (threadIdx.x == 0) {
-      const uint32_t* top = base;
-      uint32_t* abort = base + 32 * (1 + kGroups);
-      const uint32_t target = epoch * (uint32_t)ngroups;
-      int ok = 1;
-      for (int spins = 0; ld_agent(top) < target; ++spins) {
-        if ((spins & 63) == 63 && ld_agent(abort) != 0u) { ok = 0; break; }
-        if (spins > kSpinLimit) {
-          set_status(status, kStatusTimeout);
-          st_agent(abort, 1u);
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      *flag = ok;
-    }
-    block_sync_lds();
-    return *flag != 0;
-  }
-
-  // Whole block: drain, arrive, wait.
-  __device__ __forceinline__ bool sync(int32_t* status, int* flag) {
-    drain_memory();
-    __syncthreads();
-    arrive();
-    return wait(status, flag);
-  }
-};
+__device__ __forceinline__ uint32_t tag_abort_value(uint32_t tag) { return tag | kAbortLow; }
 
 // ------------------------------------------------------------ tagged words
 // A value handed from one block to the others travels as one 64-bit word:
@@ -141,8 +109,8 @@ __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t payload, uint32
 
 // Polls the words base[idx(i)] for the bits i set in `valid` until each
 // carries `tag`; payloads land in out[i].  Bounded: gives up (and raises
-// the grid's abort flag) after kSpinLimit polls, or when another block has
-// raised it.
+// the launch's abort value) after kSpinLimit polls, or when another block
+// has raised it.
 template <int N, typename Idx>
 __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
                                             uint32_t (&out)[N], uint32_t* abort, int32_t* status,
@@ -163,10 +131,10 @@ __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint3
       rounds = spins + 1;
       return true;
     }
-    if ((spins & 15) == 15 && ld_agent(abort) != 0u) return false;
+    if ((spins & 15) == 15 && ld_agent(abort) == tag_abort_value(tag)) return false;
     if (spins > kSpinLimit) {
       set_status(status, kStatusTimeout);
-      st_agent(abort, 1u);
+      st_agent(abort, tag_abort_value(tag));
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -250,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ const uint16_t* rtr[kMaxLayers];
   __shared__ const uint8_t* shp[kMaxLayers];
   __shared__ float undo_x;
-  __shared__ int bar_flag;
+  __shared__ uint32_t s_tbase;
   __shared__ int fail_flag;
 
   int tid = threadIdx.x, lane = tid & 63;   // re-derived opaquely each layer, as b
@@ -274,12 +242,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   int64_t* clk = reinterpret_cast<int64_t*>(smem + LL.clk);         // [L][kStackClockEvents] if timed
   int64_t* bclk = clk + clk0;                                        // [L][kBlockClockEvents] if timed
 
-  GridBarrier bar;
-  bar.base = a.bar;
-  bar.ngroups = min(kGroups, NB);
-  bar.group = b % bar.ngroups;
-  bar.gsize = (NB - bar.group + bar.ngroups - 1) / bar.ngroups;
-  bar.epoch = 0;
+  // this launch's number, from the workgroup's ticket (first, so that it
+  // is back by the time the tags are needed)
+  if (tid == 0) {
+    const unsigned long long t = __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(a.bar), 1ull,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_tbase = (uint32_t)(t / (unsigned long long)NB) << 8;
+  }
 
   // This block's rows, contiguous and balanced: router rows [rlo, rhi),
   // gate/up rows [glo, ghi), rows of h [dlo, dhi) (at least one when H >=
@@ -520,33 +489,39 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   if (tid == 0) fail_flag = 0;
   if (a.bclocks)
     for (int i = tid; i < L * kBlockClockEvents; i += kThreads) bclk[i] = 0;
-  // this block's tagged words start at tag 0 (no layer's); one grid
-  // barrier puts every clear before any layer's write
+  block_sync_lds();
+  // tags of this launch: tbase + layer + 1
+  const uint32_t tbase = __builtin_amdgcn_readfirstlane(s_tbase);
+  const uint64_t cleared = (uint64_t)tbase << 32;
+  // this block's tagged words carry this launch's cleared value before any
+  // layer's write; only the block's own later stores need ordering after
+  // the clears (other launches' tags never match), so each thread waits for
+  // its clears to complete and one block barrier follows: no grid barrier
   for (int par = 0; par < 2; ++par) {
     uint64_t* lw = a.lwords + (int64_t)par * 2 * E;
     uint64_t* aw = a.awords + (int64_t)par * KS * I;
     uint64_t* hw = a.hwords + (int64_t)par * H;
     for (int j = tid; j < RW; j += kThreads) {
       const int r = rlo + j;
-      if (r < rhi) { st_agent(lw + 2 * r, uint64_t{0}); st_agent(lw + 2 * r + 1, uint64_t{0}); }
+      if (r < rhi) { st_agent(lw + 2 * r, cleared); st_agent(lw + 2 * r + 1, cleared); }
     }
     for (int t = tid; t < KS * RG; t += kThreads) {
       const int j = t / RG, row = glo + (t - j * RG);
-      if (row < ghi) st_agent(aw + (int64_t)j * I + row, uint64_t{0});
+      if (row < ghi) st_agent(aw + (int64_t)j * I + row, cleared);
     }
     for (int i = tid; i < RD; i += kThreads) {
       const int row = dlo + i;
-      if (row < dhi) st_agent(hw + row, uint64_t{0});
+      if (row < dhi) st_agent(hw + row, cleared);
     }
   }
-  if (!bar.sync(a.status, &bar_flag)) return;
+  __builtin_amdgcn_s_waitcnt(0);
   block_sync_lds();
   plan_router(0);
   plan_gu(0, 1, S > 0 ? shp[0] : nullptr);
   issue_router();
   issue_gu(0, 1);
   issue_down_shared(S > 0 ? shp[0] : nullptr);
-  uint32_t* const abort_word = a.bar + 32 * (1 + kGroups);
+  uint32_t* const abort_word = a.bar + 32;
   auto block_failed = [&](bool ok) -> bool {   // whole block
     if (!ok) fail_flag = 1;
     block_sync_lds();
@@ -595,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         }
         int nr = 0;
         ok = take_tagged<2 * HW>(hw_in, [&](int i) { return 2 * (tid + (i >> 1) * kThreads) + (i & 1); },
-                                 valid, (uint32_t)li, hw, abort_word, a.status, nr);
+                                 valid, tbase + (uint32_t)li, hw, abort_word, a.status, nr);
         bcount(li, 10, nr);
 #pragma unroll
         for (int i = 0; i < HW; ++i) hv[i] = ((uint64_t)hw[2 * i + 1] << 32) | hw[2 * i];
@@ -644,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) { ss += ssum[i]; mx = fmaxf(mx, hmax[i]); }
     const double inv = a.no_norm ? 1.0 : 1.0 / sqrt(ss / (double)H + 1e-6);
-    const uint32_t tag = (uint32_t)li + 1u;
+    const uint32_t tag = tbase + (uint32_t)li + 1u;
     jitter<JIT>(b, wave, li, 0);
     if (tid < 2 * RW && rlo + (tid >> 1) < rhi) {   // this block's logits: two words each, one store
       const int k = tid >> 1;
@@ -882,18 +857,25 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   }
 }
 
-__global__ void reset_barrier_kernel(uint32_t* bar) {
-  for (int i = threadIdx.x; i < kBarWords; i += blockDim.x) bar[i] = 0u;
-}
-
+// The workgroups wait on each other's words, so the whole grid must be
+// resident at once: one workgroup per compute unit, which the occupancy of
+// the instantiation at this LDS size must allow (checked once per
+// instantiation and size).  The launch is an ordinary one (capturable in a
+// graph); the launch ticket replaces any per-launch reset.
 template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW, int JIT = 0>
 hipError_t launch_t(const StackArgs& a, int nb, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL(reset_barrier_kernel, dim3(1), dim3(256), 0, stream, a.bar);
+  auto* kern = &stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW, JIT>;
+  static thread_local size_t checked_lds = 0;
+  if (checked_lds != lds) {
+    int per_cu = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1 || nb > device_cus()) return hipErrorCooperativeLaunchTooLarge;
+    checked_lds = lds;
+  }
   StackArgs args = a;
   void* params[] = {&args};
-  return hipLaunchCooperativeKernel(
-      reinterpret_cast<const void*>(&stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW, JIT>),
-      dim3(nb), dim3(kThreads), params, (unsigned int)lds, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(nb), dim3(kThreads), params, lds, stream);
 }
 
 }  // namespace

@@ -85,6 +85,78 @@ def test_stack_small_shape_delay_injection():
             assert torch.equal(a, b)
 
 
+def _tiny_stack_cfg():
+    return synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_tiny", hidden=256, inter=128,
+                              n_experts=8, top_k=2, layers=6)
+
+
+def _token(cfg, ts):
+    return torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+
+
+def test_stack_launches_share_one_workspace():
+    """Persistent launches of different lengths and first layers, one after
+    another on one workspace, equal the same launches on fresh workspaces
+    bit for bit: words an earlier launch left in the workspace (other
+    launch numbers in their tags) never satisfy a later launch's polls."""
+    cfg = _tiny_stack_cfg()
+    say("[stack] tiny: eight launches of 1-6 layers on one workspace")
+    shape, ex, rt = build_stack(cfg, cfg.layers)
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    for i, (l0, L) in enumerate([(0, 2), (2, 1), (3, 1), (4, 2), (0, 6), (5, 1), (1, 3), (0, 1)]):
+        x = _token(cfg, 10 + i)
+        h1, h2 = x.clone(), x.clone()
+        tk1, hk1 = q.moe_expert_stack_decode(shape, ex, rt, h1, cfg.top_k, layer0=l0, L=L, workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == 1
+        assert q.moe_read_device_status(ws) == 0
+        fresh = q.new_workspace(shape, 1, cfg.top_k)
+        tk2, hk2 = q.moe_expert_stack_decode(shape, ex, rt, h2, cfg.top_k, layer0=l0, L=L, workspace=fresh,
+                                             trace=True)
+        assert q.moe_read_device_status(fresh) == 0
+        assert torch.equal(tk1, tk2) and torch.equal(hk1, hk2) and torch.equal(h1, h2), (l0, L)
+
+
+@pytest.mark.parametrize("name,layer0,L", [("tiny", 1, 4), ("decode_4bit", 0, 1)])
+def test_stack_launch_replays_in_a_hip_graph(name, layer0, L):
+    """A persistent launch captured in a HIP graph: every replay, with eager
+    launches on the same workspace and synchronisations between the replays,
+    equals the eager result bit for bit."""
+    if name == "tiny":
+        cfg, flags = _tiny_stack_cfg(), 0
+    else:   # one layer of the one-token configuration, its input taken as is
+        cfg, flags = synth.CONFIGS[name], q.F_STACK_NO_NORM
+    say(f"[stack] {name}: capture layers [{layer0}, {layer0 + L}), replay six times")
+    shape, ex, rt = build_stack(cfg, layer0 + L)
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    xs = [_token(cfg, t) for t in range(3)]
+    eager = []
+    for x in xs:
+        h = x.clone()
+        q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, layer0=layer0, L=L, flags=flags, workspace=ws)
+        assert q.moeq_last_stack_path() == 1
+        eager.append(h)
+    torch.cuda.synchronize()
+    assert q.moe_read_device_status(ws) == 0
+    h_in = xs[0].clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        q.moe_expert_stack_decode(shape, ex, rt, h_in, cfg.top_k, layer0=layer0, L=L, flags=flags, workspace=ws,
+                                  stream=s)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        t = rep % 3
+        h_in.copy_(xs[t])
+        g.replay()
+        torch.cuda.synchronize()
+        assert q.moe_read_device_status(ws) == 0, rep
+        assert torch.equal(h_in, eager[t]), rep
+        other = xs[(t + 1) % 3].clone()
+        q.moe_expert_stack_decode(shape, ex, rt, other, cfg.top_k, layer0=layer0, L=L, flags=flags, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager[(t + 1) % 3]), rep
+
+
 @pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
 def test_stack_small_shape(flags):
     cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_tiny", hidden=256, inter=128,
