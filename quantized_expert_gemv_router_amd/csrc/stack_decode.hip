@@ -60,6 +60,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSpinLimit = 1 << 18;        // polls before a wait gives up
+constexpr int kActPollBackoff = 4;         // s_sleep 8 (512 clocks) steps before the activation poll
 constexpr int kMaxKS = 8;                  // selected + shared experts per layer
 constexpr int kActSums = 4;                // per staged activation chunk: X, 1024 X', undo, pad
 constexpr int kMaxLayers = 128;            // per persistent launch
@@ -807,6 +808,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     };
     const int sub = lane % LPRD;
     // shared and routed activations in one take
+    // back-off before the first activation poll: issued at once, its first
+    // round reads the words before the slowest blocks have published them
+    // and, queued behind the down rows, returns late, so a second round is
+    // needed; ~0.85 us later the first round mostly finds them all
+    for (int d = 0; d < kActPollBackoff; ++d) __builtin_amdgcn_s_sleep(8);
     if (!take_acts(0, KS, 13)) return;
     stamp0(li, 17);
     bstamp(li, 8);
