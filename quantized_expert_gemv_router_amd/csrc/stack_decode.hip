@@ -32,10 +32,11 @@
 // Loads are issued as early as their addresses are known and their data
 // does not compete with loads on the critical path: the router and
 // shared-expert pointers of every layer are cached in LDS at start; the
-// next layer's router rows and shared-expert gate/up and down rows are
-// requested right after h is published, and the shared expert's gate/up is
-// computed while the routed rows stream in; the routed down rows are
-// requested once the gate/up rows are consumed.  A poll's loads complete
+// next layer's router rows and shared-expert down rows are requested right
+// after h is published, the shared expert's gate/up rows right after the
+// layer's logits are published (requested with the others they held the h
+// poll back), and its gate/up is computed while the routed rows stream in;
+// the routed down rows are requested once the gate/up rows are consumed.  A poll's loads complete
 // after every load the wave issued before them (the vector memory counter
 // is in order), so whatever is requested just before a poll delays it:
 // the layer's loads were placed by measurement (requesting the down rows
@@ -518,9 +519,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   block_sync_lds();
   plan_router(0);
-  plan_gu(0, 1, S > 0 ? shp[0] : nullptr);
   issue_router();
-  issue_gu(0, 1);
   issue_down_shared(S > 0 ? shp[0] : nullptr);
   uint32_t* const abort_word = a.bar + 32;
   auto block_failed = [&](bool ok) -> bool {   // whole block
@@ -630,6 +629,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       put_tagged(lw + 2 * (rlo + k) + (tid & 1), (tid & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits, tag);
     }
     bstamp(li, 2);
+    // the shared expert's gate/up rows, in flight while x is staged, the
+    // logits are polled and top-K runs (requested before the h poll they
+    // held it back)
+    if (S > 0) {
+      plan_gu(0, 1, shp[li]);
+      issue_gu(0, 1);
+    }
     // xhat -> fp16 pairs, one packed word per thread; the norm and the
     // rescale come from the h pass above, so no further reductions
     {
@@ -841,14 +847,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
                 (unsigned long long)wall_clock64());
     stamp(li, 10);
     if (li + 1 == L) break;
-    // next layer: router rows, shared-expert gate/up and down rows, in
-    // flight while h arrives
+    // next layer: router rows and the shared expert's down rows, in flight
+    // while h arrives (its gate/up rows follow the logits publish)
     plan_router(li + 1);
     issue_router();
-    if (S > 0) {
-      plan_gu(0, 1, shp[li + 1]);
-      issue_gu(0, 1);
-    }
     issue_down_shared(S > 0 ? shp[li + 1] : nullptr);
     stamp0(li, 11);
   }
