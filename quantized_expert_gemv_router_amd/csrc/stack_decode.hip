@@ -32,11 +32,12 @@
 // Loads are issued as early as their addresses are known and their data
 // does not compete with loads on the critical path: the router and
 // shared-expert pointers of every layer are cached in LDS at start; the
-// next layer's router rows and shared-expert down rows are requested right
-// after h is published, the shared expert's gate/up rows right after the
-// layer's logits are published (requested with the others they held the h
-// poll back), and its gate/up is computed while the routed rows stream in;
-// the routed down rows are requested once the gate/up rows are consumed.  A poll's loads complete
+// next layer's router rows are requested right after h is published, the
+// shared expert's gate/up rows right after the layer's logits are
+// published and its down rows right after its activations are (requested
+// with the router rows, both held the h poll back); its gate/up is
+// computed while the routed rows stream in; the routed down rows are
+// requested once the gate/up rows are consumed.  A poll's loads complete
 // after every load the wave issued before them (the vector memory counter
 // is in order), so whatever is requested just before a poll delays it:
 // the layer's loads were placed by measurement (requesting the down rows
@@ -61,7 +62,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSpinLimit = 1 << 18;        // polls before a wait gives up
-constexpr int kActPollBackoff = 4;         // s_sleep 8 (512 clocks) steps before the activation poll
+constexpr int kActPollBackoff = 3;         // s_sleep 8 (512 clocks) steps before the activation poll
 constexpr int kMaxKS = 8;                  // selected + shared experts per layer
 constexpr int kActSums = 4;                // per staged activation chunk: X, 1024 X', undo, pad
 constexpr int kMaxLayers = 128;            // per persistent launch
@@ -520,7 +521,6 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   block_sync_lds();
   plan_router(0);
   issue_router();
-  issue_down_shared(S > 0 ? shp[0] : nullptr);
   uint32_t* const abort_word = a.bar + 32;
   auto block_failed = [&](bool ok) -> bool {   // whole block
     if (!ok) fail_flag = 1;
@@ -732,6 +732,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         }
       }
       stamp0(li, 4);
+      // its down rows, in flight while the routed rows are applied
+      issue_down_shared(shp[li]);
     }
     gu_dots(1, RPWG);
     stamp0(li, 13);
@@ -817,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // back-off before the first activation poll: issued at once, its first
     // round reads the words before the slowest blocks have published them
     // and, queued behind the down rows, returns late, so a second round is
-    // needed; ~0.85 us later the first round mostly finds them all
+    // needed; ~0.64 us later the first round mostly finds them all
     for (int d = 0; d < kActPollBackoff; ++d) __builtin_amdgcn_s_sleep(8);
     if (!take_acts(0, KS, 13)) return;
     stamp0(li, 17);
@@ -847,11 +849,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
                 (unsigned long long)wall_clock64());
     stamp(li, 10);
     if (li + 1 == L) break;
-    // next layer: router rows and the shared expert's down rows, in flight
-    // while h arrives (its gate/up rows follow the logits publish)
+    // next layer: router rows, in flight while h arrives (the shared
+    // expert's gate/up rows follow the logits publish, its down rows its
+    // activations' publish)
     plan_router(li + 1);
     issue_router();
-    issue_down_shared(S > 0 ? shp[li + 1] : nullptr);
     stamp0(li, 11);
   }
   if (a.clocks && b == 0) {   // stamps were kept in LDS so taking them adds no memory traffic
