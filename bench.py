@@ -74,6 +74,9 @@ def parse():
                         "with and without prefetch of the previous token's experts")
     p.add_argument("--probe-handoff", action="store_true",
                    help="only run the cross-workgroup hand-off latency probe sweep (diagnostic)")
+    p.add_argument("--block-timeline", type=int, default=0, metavar="L",
+                   help="only run the per-workgroup clock trace of the persistent decode over L layers "
+                        "(diagnostic: hand-off latencies and skew)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return p.parse_args()
@@ -1129,6 +1132,71 @@ def probe_handoff():
         print(json.dumps(rec), flush=True)
 
 
+def block_timeline(L, dev, stream):
+    """Per-workgroup clock trace of the persistent decode (one token through
+    L layers of the 60-layer configuration, six traced launches after five
+    untraced ones): when each workgroup reached each phase, relative to the
+    last workgroup's h publish of the previous layer, and the poll rounds of
+    each hand-off.  Printed as text."""
+    import torch
+    import quantized_expert_gemv_router_amd as q
+    import synth
+
+    cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], layers=L)
+    shape, table, routers, _ = setup_layers(cfg, L, dev, stream)
+    rt = q.RouterTable(routers, device=dev)
+    ws = q.new_workspace(shape, 1, cfg.top_k, dev)
+    x = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, 0, 1)).astype(np.float32)).to(dev)
+    for _ in range(5):
+        h = x.clone()
+        q.moe_expert_stack_decode(shape, table, rt, h, cfg.top_k, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    NB = torch.cuda.get_device_properties(dev).multi_processor_count
+    EV = 16
+    reps = []
+    for _ in range(6):
+        clk = torch.zeros((NB, L, EV), dtype=torch.int64, device=dev)
+        if q.moeq_stack_block_clock_trace(clk) != EV:
+            raise RuntimeError("unexpected clock-trace width")
+        h = x.clone()
+        q.moe_expert_stack_decode(shape, table, rt, h, cfg.top_k, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        reps.append(clk.cpu().numpy())
+    if q.moe_read_device_status(ws, stream) != 0:
+        raise RuntimeError("device status set during the traced launches")
+    tick_us = 0.01   # the 100 MHz constant clock
+    names = ["start", "h polled", "lg pub", "lg polled", "topk", "gu dots", "a pub", "", "a polled", "h pub"]
+    rows, per = [], []
+    for c in reps:
+        t = c.astype(np.float64) * tick_us
+        for l in range(2, L - 1):
+            rows.append(t[:, l, :10] - t[:, l - 1, 9].max())
+        per.append(np.median(np.diff(t[:, :, 0].min(axis=0))))
+    R = np.stack(rows)
+    print(f"stack decode block timeline: {L} layers, {NB} workgroups, 6 launches; layer period "
+          f"(median of min-over-workgroups start differences) {np.median(per):.2f} us")
+    print("times after the last workgroup's h publish of the previous layer (us), medians over layers:")
+    print(f"{'event':10s} {'min':>7s} {'median':>7s} {'p90':>7s} {'max':>7s}   (over workgroups)")
+    for ev in range(10):
+        if not names[ev]:
+            continue
+        v = R[:, :, ev]
+        print(f"{names[ev]:10s} {np.median(v.min(1)):7.2f} {np.median(np.median(v, 1)):7.2f} "
+              f"{np.median(np.percentile(v, 90, axis=1)):7.2f} {np.median(v.max(1)):7.2f}")
+    for nm, pub, poll in (("logits", 2, 3), ("activations", 6, 8)):
+        lp = R[:, :, pub].max(1)
+        print(f"{nm}: last publish {np.median(lp):.2f}; polled min {np.median(R[:, :, poll].min(1) - lp):.2f} "
+              f"median {np.median(np.median(R[:, :, poll], 1) - lp):.2f} max {np.median(R[:, :, poll].max(1) - lp):.2f}"
+              " after it")
+    for ev, nm in ((2, "lg pub"), (5, "gu dots"), (6, "a pub"), (9, "h pub")):
+        v = np.median(R[:, :, ev], axis=0)
+        print(f"{nm:8s} median by XCD (workgroup mod 8):", " ".join(f"{np.median(v[x::8]):.2f}" for x in range(8)))
+    raw = np.stack(reps)
+    for ev, nm in ((10, "h"), (11, "logits"), (12, "shared acts"), (13, "routed acts")):
+        v = raw[:, :, 2:L - 1, ev]
+        print(f"poll rounds {nm:12s}: median {np.median(v):.0f}  p90 {np.percentile(v, 90):.0f}  max {v.max():.0f}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1148,6 +1216,9 @@ def main():
         calibrate_copy(args.calibrate_copy, dev)
         return
     stream = torch.cuda.Stream(device=dev)
+    if args.block_timeline:
+        block_timeline(args.block_timeline, dev, stream)
+        return
     if args.workload == "pool_decode":
         rec = run_pool(args, synth.CONFIGS["stack60_decode"], dev, stream)
         print(json.dumps(rec), flush=True)
