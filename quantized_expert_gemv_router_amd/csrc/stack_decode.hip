@@ -20,8 +20,8 @@
 //            products from the polled registers, and after one block
 //            barrier publishes its logits
 //   logits:  every block polls all E logits and selects top-K itself (one
-//            wave, rounds on the keys' high words), then streams its
-//            gate/up rows
+//            wave: a selection network over truncated keys, else rounds on
+//            the keys' high words), then streams its gate/up rows
 //   a:       each block publishes silu(g)*u for its gate/up rows; every block
 //            polls all activations (shared and routed slots in one take),
 //            then applies its down rows and the combine with the residual.
@@ -681,16 +681,24 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // top-K: wave 0 selects from all E logits (up to eight per lane; one
     // wave alone on its SIMD finishes sooner than eight sharing four), one
     // barrier hands the selection to the block; beyond 512 experts the
-    // waves select together
+    // waves select together.  Up to three experts the selection network
+    // (one pass of sorted four-lists through the wave) decides whenever
+    // the truncated keys separate the K + 1 best; rounds of wave maxima
+    // on the full keys decide otherwise.
     if (E <= 64 * kTopkSlots) {
       if (wave == 0) {
-        int64_t kk[kTopkSlots];
+        int win;
+        if (K <= 3 && wave_topk_net(lg, E, K, win)) {
+          if (lane < K) sel[lane] = win;
+        } else {
+          int64_t kk[kTopkSlots];
 #pragma unroll
-        for (int i = 0; i < kTopkSlots; ++i) {
-          const int e = lane + 64 * i;
-          kk[i] = e < E ? order_key(lg[e]) : kNoKey;
+          for (int i = 0; i < kTopkSlots; ++i) {
+            const int e = lane + 64 * i;
+            kk[i] = e < E ? order_key(lg[e]) : kNoKey;
+          }
+          wave_select_hi<kTopkSlots>(kk, K, [&](int r, int w) { sel[r] = w; });
         }
-        wave_select_hi<kTopkSlots>(kk, K, [&](int r, int win) { sel[r] = win; });
       }
       block_sync_lds();
     } else {

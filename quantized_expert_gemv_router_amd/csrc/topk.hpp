@@ -201,6 +201,95 @@ __device__ __forceinline__ void wave_select_hi(const int64_t (&k)[M], int K, Emi
   }
 }
 
+// ------------------------------------------------------ selection network
+// One wave, K <= 3, eight logits per lane (element lane + 64 i): the top
+// K + 1 elements found by one pass of sorted four-lists through the wave
+// instead of K rounds of wave maxima.  Each element becomes a 32-bit key:
+// the high word of its order key with the three lowest bits replaced by
+// 7 - i (its slot), so a key names its element within the lane.  A lane
+// sorts its eight keys into its four best; six DPP steps then merge lists
+// pairwise (the top four of two sorted lists: the bitonic elementwise
+// maximum of one list against the other reversed, then two half-cleaner
+// stages), and lane 63 ends with the wave's four best keys.  When their
+// 29-bit prefixes (the truncated order keys) are strictly decreasing, the
+// order of the K best and the boundary to the (K+1)-th are fixed by the
+// prefixes alone, so the keys give the exact selection; otherwise
+// (near-ties within 2^-17 relative, or ties) it returns false and the
+// caller selects on the full keys.  On success lane r < K receives the
+// element of rank r in `win` (wave-uniform per rank through readlane).
+__device__ __forceinline__ int net_key(double v, int slot) {
+  v = v + 0.0;   // -0 becomes +0: the two tie, as numbers do
+  const int hb = (int)((uint64_t)__double_as_longlong(v) >> 32);
+  const int hk = hb ^ ((hb >> 31) & 0x7FFFFFFF);
+  return (hk & ~7) | (7 - slot);
+}
+
+// top four of the sorted (descending) lists a and b, sorted
+__device__ __forceinline__ void net_merge4(int (&a)[4], const int (&b)[4]) {
+  const int c0 = max(a[0], b[3]), c1 = max(a[1], b[2]), c2 = max(a[2], b[1]), c3 = max(a[3], b[0]);
+  const int d0 = max(c0, c2), d2 = min(c0, c2), d1 = max(c1, c3), d3 = min(c1, c3);
+  a[0] = max(d0, d1);
+  a[1] = min(d0, d1);
+  a[2] = max(d2, d3);
+  a[3] = min(d2, d3);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void net_step(int (&a)[4]) {
+  int b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = __builtin_amdgcn_update_dpp(INT_MIN, a[i], CTRL, ROW_MASK, 0xF, false);
+  net_merge4(a, b);
+}
+
+// lg: the E (<= 512) logits in LDS, lg[e] for e < E.  Returns true with
+// lane r < K holding the rank-r element in win; false when the prefixes
+// do not separate the top K + 1.
+__device__ __forceinline__ bool wave_topk_net(const double* lg, int E, int K, int& win) {
+  const int lane = threadIdx.x & 63;
+  int k[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane + 64 * i;
+    k[i] = e < E ? net_key(lg[e], i) : INT_MIN;
+  }
+  // the lane's four best, sorted
+  int a[4] = {max(k[0], k[1]), min(k[0], k[1]), INT_MIN, INT_MIN};
+  int b[4] = {max(k[2], k[3]), min(k[2], k[3]), INT_MIN, INT_MIN};
+  int c[4] = {max(k[4], k[5]), min(k[4], k[5]), INT_MIN, INT_MIN};
+  int d[4] = {max(k[6], k[7]), min(k[6], k[7]), INT_MIN, INT_MIN};
+  net_merge4(a, b);
+  net_merge4(c, d);
+  net_merge4(a, c);
+  int loc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) loc[i] = a[i];
+  net_step<kDppQuadXor1, 0xF>(a);
+  net_step<kDppQuadXor2, 0xF>(a);
+  net_step<kDppHalfMirror, 0xF>(a);
+  net_step<kDppMirror, 0xF>(a);
+  net_step<kDppBcast15, 0xA>(a);
+  net_step<kDppBcast31, 0xC>(a);
+  int t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = __builtin_amdgcn_readlane(a[i], 63);
+  // prefixes strictly decreasing over the K + 1 best (INT_MIN past E)
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (i < K) ok = ok && t[i] != INT_MIN && (t[i] >> 3) > (t[i + 1] >> 3);
+  if (!ok) return false;
+  win = kTopkNone;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    if (r >= K) break;
+    const bool mine = loc[0] == t[r] || loc[1] == t[r] || loc[2] == t[r] || loc[3] == t[r];
+    const int owner = (int)__builtin_ctzll(__ballot(mine));
+    if (lane == r) win = owner + 64 * (7 - (t[r] & 7));
+  }
+  return true;
+}
+
 // All NW waves of a block: top-K (K <= 64*MC/NW) of lg[0..E) (LDS, E <= 64*NW*M).
 // Wave w selects the K best of its elements w*64 + lane + 64*NW*i into
 // ck/ci[w*K + r]; wave 0 then selects the K best of those NW*K candidates
