@@ -48,8 +48,8 @@
 //   of the h values it polls);
 //   gate/up rows r in [b I/NB, (b+1) I/NB) of every selected expert
 //   (a = silu(g)*u is formed locally);
-//   down rows    r in [b H/NB, (b+1) H/NB) of every selected expert (the
-//   combine is a per-row sum in slot order, no atomics).
+//   down rows    r in [b H/NB, (b+1) H/NB) of every selected expert (each
+//   lane weights its share of every slot, one sum per row, no atomics).
 // Every wait is bounded: on time-out a block sets the status word and an
 // abort flag, and every block leaves the kernel.
 #include "moeq_device.hpp"
@@ -807,9 +807,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       }
       return !block_failed(got_all);
     };
-    // one slot's down rows against its staged activations: the row's sum is
-    // valid in lane LPRD-1 of each row group
-    auto down_dot = [&](int s, const u32x4 (&q)[CPLD], const uint32_t (&sbw)[CPLD], bool ok) -> float {
+    // this lane's share of one slot's down row against its staged
+    // activations (the LPRD lanes of a row group hold the row's chunks)
+    auto down_part = [&](int s, const u32x4 (&q)[CPLD], const uint32_t (&sbw)[CPLD], bool ok) -> float {
       const int sub = lane % LPRD;
       float part = 0.0f;
 #pragma unroll
@@ -820,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         if (ok && sub + LPRD * c < nchD)
           part += chunk_affine(chunk_dot<BITS>(q[c], x), sbw[c], make_float2(xsm.x, xsm.y)) * xsm.z;
       }
-      return group_sum_dpp<LPRD>(part);
+      return part;
     };
     const int sub = lane % LPRD;
     // shared and routed activations in one take
@@ -838,13 +838,17 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       int drow;
       down_row(drow);
       const bool dok = drow < H;
-      float acc = dok ? hs[drow] : 0.0f;
-      if (S > 0) acc += down_dot(K, qsh, ssh, dok);   // the shared expert first, then the slots in rank order
+      // every slot's share weighted in the lane (the shared expert first,
+      // then the slots in rank order), then one sum over the row group:
+      // valid in lane LPRD-1
+      float part = S > 0 ? down_part(K, qsh, ssh, dok) : 0.0f;
 #pragma unroll
       for (int s = 0; s < STEPSD; ++s) {
         if (s >= K) break;
-        acc = fmaf(selw[s], down_dot(s, qd[s], sd[s], dok), acc);
+        part = fmaf(selw[s], down_part(s, qd[s], sd[s], dok), part);
       }
+      const float dsum = group_sum_dpp<LPRD>(part);
+      const float acc = dok ? hs[drow] + dsum : 0.0f;
       if (dok && sub == LPRD - 1) {
         if (a.h_trace) a.h_trace[(int64_t)li * H + drow] = hs[drow];
         if (li + 1 == L) a.h[drow] = acc;   // complete when the launch ends
