@@ -125,7 +125,7 @@ struct StackArgs {
   int32_t* topk_trace;             // [L][K] or null
   float* h_trace;                  // [L][H] or null
   uint64_t* lwords;                // [2][E][2] tagged halves of the fp64 logits (by layer parity)
-  uint64_t* awords;                // [2][K + S][I] tagged activations
+  uint64_t* awords;                // [2][K + S][I] words: tagged activation pairs in the first (K + S) I / 2
   uint64_t* hwords;                // [2][H] tagged hidden state between layers
   uint32_t* bar;                   // barrier counters (stack_barrier_words())
   int32_t* status;

@@ -22,7 +22,8 @@
 //   logits:  every block polls all E logits and selects top-K itself (one
 //            wave: a selection network over truncated keys, else rounds on
 //            the keys' high words), then streams its gate/up rows
-//   a:       each block publishes silu(g)*u for its gate/up rows; every block
+//   a:       each block publishes silu(g)*u for its gate/up rows (two per
+//            word, fp16 under a shared power of two); every block
 //            polls all activations (shared and routed slots in one take),
 //            then applies its down rows and the combine with the residual.
 //            The shared expert does not wait for routing: its gate/up rows
@@ -86,7 +87,9 @@ static_assert(2 * kWaves >= MOEQ_MAX_TOPK, "threshold top-K: at most two samples
 // this launch waits for, so no grid barrier is needed between launches or
 // at a launch's start: each block rewrites its own words with the cleared
 // value first (which also bounds the age of every word by one launch, so
-// the 24-bit launch number cannot wrap onto a stale word).
+// the 24-bit launch number cannot wrap onto a stale word).  Activation words
+// carry the tag's low 24 bits (16 bits of launch number), which the same
+// argument covers.
 constexpr int kBarWords = 64;
 constexpr uint32_t kAbortLow = 255u;
 
@@ -110,14 +113,45 @@ __device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t payload, uint32
   st_agent(p, ((uint64_t)tag << 32) | payload);
 }
 
+// Activations travel two to a word: the pair as fp16 values scaled by a
+// shared power of two 2^s (the larger magnitude lands in [2^14, 2^15)),
+// the byte s + 128, and the low 24 bits of the tag above them:
+//   tag24 << 40 | (s + 128) << 32 | fp16 pair.
+// fp16 keeps each value's 11 significant bits, the same rounding the staged
+// chunk applies under its own power of two, so staging the decoded values
+// is exact and stages what the fp32 values would (values more than 2^28
+// below the pair's or the chunk's largest aside, which both forms flush).
+constexpr uint32_t kActTagMask = 0xFFFFFFu;
+__device__ __forceinline__ uint64_t act_cleared(uint32_t tbase) {
+  return ((uint64_t)(tbase & kActTagMask) << 40) | (128ull << 32);
+}
+__device__ __forceinline__ void put_act_pair(uint64_t* p, float a0, float a1, uint32_t tag) {
+  const float m = fmaxf(fabsf(a0), fabsf(a1));
+  int sc = 0;
+  if (m > 0.0f && isfinite(m)) sc = min(14 - ilogbf(m), 126);
+  const float f = ldexpf(1.0f, sc);
+  const uint32_t pr = pack_half2(a0 * f, a1 * f);
+  st_agent(p, ((uint64_t)(tag & kActTagMask) << 40) | ((uint64_t)(uint32_t)(sc + 128) << 32) | pr);
+}
+__device__ __forceinline__ void act_pair_values(uint64_t w, float& a0, float& a1) {
+  const int sc = (int)((uint32_t)(w >> 32) & 0xFFu) - 128;
+  const float g = ldexpf(1.0f, -sc);
+  a0 = half_lo((uint32_t)w) * g;
+  a1 = half_hi((uint32_t)w) * g;
+}
+
 // Polls the words base[idx(i)] for the bits i set in `valid` until each
 // carries `tag`; payloads land in out[i].  Bounded: gives up (and raises
 // the launch's abort value) after kSpinLimit polls, or when another block
 // has raised it.
-template <int N, typename Idx>
-__device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
-                                            uint32_t (&out)[N], uint32_t* abort, int32_t* status,
-                                            int& rounds) {
+// Words whose high bits from SHIFT up carry the tag (SHIFT 32: the tag;
+// SHIFT 40: its low 24 bits, the activation pairs); out[i] receives the
+// whole word.
+template <int N, int SHIFT, typename Idx>
+__device__ __forceinline__ bool take_tagged_w(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
+                                              uint64_t (&out)[N], uint32_t* abort, int32_t* status,
+                                              int& rounds) {
+  const uint32_t want = SHIFT == 32 ? tag : (tag & (0xFFFFFFFFu >> (SHIFT - 32)));
   uint32_t pending = valid;
   for (int spins = 0;; ++spins) {
     uint64_t v[N];
@@ -125,8 +159,8 @@ __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint3
     for (int i = 0; i < N; ++i) v[i] = ((pending >> i) & 1) ? ld_agent(base + idx(i)) : 0ull;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if (((pending >> i) & 1) && (uint32_t)(v[i] >> 32) == tag) {
-        out[i] = (uint32_t)v[i];
+      if (((pending >> i) & 1) && (uint32_t)(v[i] >> SHIFT) == want) {
+        out[i] = v[i];
         pending &= ~(1u << i);
       }
     }
@@ -142,6 +176,20 @@ __device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint3
     }
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Tagged 32-bit payloads: out[i] receives the payload of word idx(i).
+template <int N, typename Idx>
+__device__ __forceinline__ bool take_tagged(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
+                                            uint32_t (&out)[N], uint32_t* abort, int32_t* status,
+                                            int& rounds) {
+  uint64_t w[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = (uint64_t)out[i];
+  const bool ok = take_tagged_w<N, 32>(base, idx, valid, tag, w, abort, status, rounds);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = (uint32_t)w[i];
+  return ok;
 }
 
 // Delay injection (diagnostic instantiations, JIT = 1): before each of its
@@ -166,6 +214,10 @@ struct StackLds {
 };
 
 __host__ __device__ inline int al16(int v) { return (v + 15) & ~15; }
+
+// Most gate/up rows a block owns: rows are handed out in pairs, contiguous
+// and balanced over the blocks.
+__host__ __device__ inline int gu_rows_max(int I, int nb) { return 2 * ((I / 2 + nb - 1) / nb); }
 
 __host__ __device__ inline StackLds stack_lds_layout(int H, int I, int E, int S, int KS, int PC,
                                                      int RG, int RD, int clk_entries) {
@@ -230,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   int b = blockIdx.x;   // re-derived opaquely each layer (see the layer loop)
   const int H = a.H, I = a.I, E = a.E, K = a.K, S = a.S, KS = K + S, L = a.L;
   const int nchG = H / PC, nchD = I / PC;
-  const int RG = (I + NB - 1) / NB, RD = (H + NB - 1) / NB;
+  const int RG = gu_rows_max(I, NB), RD = (H + NB - 1) / NB;
 
   const int clk0 = a.clocks ? L * kStackClockEvents : 0;
   const StackLds LL = stack_lds_layout(H, I, E, S, KS, PC, RG, RD, clk0 + (a.bclocks ? L * kBlockClockEvents : 0));
@@ -261,8 +313,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   auto set_rows = [&]() {
     rlo = b * E / NB;
     rhi = (b + 1) * E / NB;
-    glo = b * I / NB;
-    ghi = (b + 1) * I / NB;
+    glo = 2 * (b * (I / 2) / NB);   // in pairs: a pair of activations travels in one word
+    ghi = 2 * ((b + 1) * (I / 2) / NB);
     dlo = b * H / NB;
     dhi = (b + 1) * H / NB;
   };
@@ -508,9 +560,9 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       const int r = rlo + j;
       if (r < rhi) { st_agent(lw + 2 * r, cleared); st_agent(lw + 2 * r + 1, cleared); }
     }
-    for (int t = tid; t < KS * RG; t += kThreads) {
-      const int j = t / RG, row = glo + (t - j * RG);
-      if (row < ghi) st_agent(aw + (int64_t)j * I + row, cleared);
+    for (int t = tid; t < KS * (RG / 2); t += kThreads) {
+      const int j = t / (RG / 2), r0 = glo + 2 * (t - j * (RG / 2));
+      if (r0 < ghi) st_agent(aw + (int64_t)j * (I / 2) + r0 / 2, act_cleared(tbase));
     }
     for (int i = tid; i < RD; i += kThreads) {
       const int row = dlo + i;
@@ -732,11 +784,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       stamp0(li, 3);
       block_sync_lds();
       jitter<JIT>(b, wave, li, 1);
-      for (int t = tid; t < RG; t += kThreads) {
-        const int row = glo + t;
-        if (row < ghi) {
-          const float g = gres[(K * 2) * RG + t], u = gres[(K * 2 + 1) * RG + t];
-          put_tagged(aw + (int64_t)K * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
+      for (int t = tid; t < RG / 2; t += kThreads) {
+        const int i = 2 * t, r0 = glo + i;
+        if (r0 < ghi) {
+          const float g0 = gres[(K * 2) * RG + i], u0 = gres[(K * 2 + 1) * RG + i];
+          const float g1 = gres[(K * 2) * RG + i + 1], u1 = gres[(K * 2 + 1) * RG + i + 1];
+          put_act_pair(aw + (int64_t)K * (I / 2) + r0 / 2, g0 / (1.0f + __expf(-g0)) * u0,
+                       g1 / (1.0f + __expf(-g1)) * u1, tag);
         }
       }
       stamp0(li, 4);
@@ -749,11 +803,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     block_sync_lds();
     stamp(li, 6);
     jitter<JIT>(b, wave, li, 2);
-    for (int t = tid; t < K * RG; t += kThreads) {
-      const int j = t / RG, i = t - j * RG, row = glo + i;
-      if (row < ghi) {
-        const float g = gres[(j * 2) * RG + i], u = gres[(j * 2 + 1) * RG + i];
-        put_tagged(aw + (int64_t)j * I + row, __float_as_uint(g / (1.0f + __expf(-g)) * u), tag);
+    for (int t = tid; t < K * (RG / 2); t += kThreads) {
+      const int j = t / (RG / 2), i = 2 * (t - j * (RG / 2)), r0 = glo + i;
+      if (r0 < ghi) {
+        const float g0 = gres[(j * 2) * RG + i], u0 = gres[(j * 2 + 1) * RG + i];
+        const float g1 = gres[(j * 2) * RG + i + 1], u1 = gres[(j * 2 + 1) * RG + i + 1];
+        put_act_pair(aw + (int64_t)j * (I / 2) + r0 / 2, g0 / (1.0f + __expf(-g0)) * u0,
+                     g1 / (1.0f + __expf(-g1)) * u1, tag);
       }
     }
     bstamp(li, 6);
@@ -779,21 +835,23 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         const int t = t0 + tid;
         const bool ok = t < total;
         const int m = ok ? s0 + t / nwa : s0, w = ok ? t - (m - s0) * nwa : 0;
+        constexpr int PP = PW / 2;   // activation pairs per word
         float v[PW];
-        uint32_t raw[PW];
+        uint64_t raw[PP];
 #pragma unroll
-        for (int j = 0; j < PW; ++j) raw[j] = 0u;
-        const uint64_t* src = aw + (int64_t)m * I + (int64_t)w * PW;
+        for (int j = 0; j < PP; ++j) raw[j] = 128ull << 32;   // zeros under scale 2^0
+        const uint64_t* src = aw + (int64_t)m * (I / 2) + (int64_t)w * PP;
         int nr = 0;
-        const bool got = take_tagged<PW>(src, [](int j) { return j; }, ok ? (uint32_t)((1ull << PW) - 1) : 0u,
-                                         tag, raw, abort_word, a.status, nr);
+        const bool got = take_tagged_w<PP, 40>(src, [](int j) { return j; },
+                                               ok ? (uint32_t)((1ull << PP) - 1) : 0u, tag, raw, abort_word,
+                                               a.status, nr);
         bcount(li, count_ev, nr);
         got_all = got_all && got;
         float lm = 0.0f;
 #pragma unroll
-        for (int j = 0; j < PW; ++j) {
-          v[j] = __uint_as_float(raw[j]);
-          lm = fmaxf(lm, fabsf(v[j]));
+        for (int j = 0; j < PP; ++j) {
+          act_pair_values(raw[j], v[2 * j], v[2 * j + 1]);
+          lm = fmaxf(lm, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
         }
         lm = fmaxf(lm, __shfl_xor(lm, 1, 64));
         lm = fmaxf(lm, __shfl_xor(lm, 2, 64));
@@ -925,7 +983,7 @@ struct Geometry {
     const int PC = 128 / BITS;
     if (rw > CPLR) return false;
     if (H / PC > 64 * CPLG) return false;
-    const int RG = (I + nb - 1) / nb, RD = (H + nb - 1) / nb;
+    const int RG = gu_rows_max(I, nb), RD = (H + nb - 1) / nb;
     if (S > 0 && 2 * RG > kWaves) return false;              // shared rows: register slot 0
     if (K * 2 * RG > kWaves * (RPWG - 1)) return false;      // routed rows: slots 1 ..
     const int nchd = I / PC;
@@ -958,7 +1016,7 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   if (rw > kWaves) return hipErrorNotSupported;
   a.router_rows = rw;
   const int PC = 128 / a.bits;
-  const int RG = (a.I + nb - 1) / nb, RD = (a.H + nb - 1) / nb;
+  const int RG = gu_rows_max(a.I, nb), RD = (a.H + nb - 1) / nb;
   const size_t lds =
       (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD,
                                (a.clocks ? a.L * kStackClockEvents : 0) + (a.bclocks ? a.L * kBlockClockEvents : 0))
