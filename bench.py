@@ -1165,21 +1165,20 @@ def block_timeline(L, dev, stream):
     if q.moe_read_device_status(ws, stream) != 0:
         raise RuntimeError("device status set during the traced launches")
     tick_us = 0.01   # the 100 MHz constant clock
-    names = ["start", "h polled", "lg pub", "lg polled", "topk", "gu dots", "a pub", "", "a polled", "h pub"]
+    names = {0: "start", 1: "h polled", 2: "lg pub", 3: "lg polled", 7: "topk w0", 4: "topk", 14: "gu issued",
+             15: "shared pub", 5: "gu dots", 6: "a pub", 8: "a polled", 9: "h pub"}
     rows, per = [], []
     for c in reps:
         t = c.astype(np.float64) * tick_us
         for l in range(2, L - 1):
-            rows.append(t[:, l, :10] - t[:, l - 1, 9].max())
+            rows.append(t[:, l, :] - t[:, l - 1, 9].max())
         per.append(np.median(np.diff(t[:, :, 0].min(axis=0))))
     R = np.stack(rows)
     print(f"stack decode block timeline: {L} layers, {NB} workgroups, 6 launches; layer period "
           f"(median of min-over-workgroups start differences) {np.median(per):.2f} us")
     print("times after the last workgroup's h publish of the previous layer (us), medians over layers:")
     print(f"{'event':10s} {'min':>7s} {'median':>7s} {'p90':>7s} {'max':>7s}   (over workgroups)")
-    for ev in range(10):
-        if not names[ev]:
-            continue
+    for ev in names:   # in phase order
         v = R[:, :, ev]
         print(f"{names[ev]:10s} {np.median(v.min(1)):7.2f} {np.median(np.median(v, 1)):7.2f} "
               f"{np.median(np.percentile(v, 90, axis=1)):7.2f} {np.median(v.max(1)):7.2f}")

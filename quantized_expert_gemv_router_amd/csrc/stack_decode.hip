@@ -47,8 +47,9 @@
 // contiguous rows of every matrix:
 //   router rows  e in [b E/NB, (b+1) E/NB) (every thread takes the columns
 //   of the h values it polls);
-//   gate/up rows r in [b I/NB, (b+1) I/NB) of every selected expert
-//   (a = silu(g)*u is formed locally);
+//   gate/up rows in pairs: rows [2p, 2p + 2) for p in [b I/2NB,
+//   (b+1) I/2NB) of every selected expert (a = silu(g)*u is formed locally,
+//   a pair's two activations travel in one word);
 //   down rows    r in [b H/NB, (b+1) H/NB) of every selected expert (each
 //   lane weights its share of every slot, one sum per row, no atomics).
 // Every wait is bounded: on time-out a block sets the status word and an
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   __shared__ double ssum[kWaves];
   __shared__ float hmax[kWaves];
   __shared__ int sel[MOEQ_MAX_TOPK];
+  __shared__ const uint8_t* selp[MOEQ_MAX_TOPK];   // the selected experts' blobs (null: missing)
   __shared__ double selv[MOEQ_MAX_TOPK];
   __shared__ int64_t candk[kWaves * 64];
   __shared__ int candi[kWaves * 64];
@@ -394,8 +396,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       ghave[m] = gu_task(m, j, sec, row);
       // routed slots: the selection; the shared slot: shared_blob.  A missing expert (null) loads nothing.
       const int jj = ghave[m] ? j : K;
-      const int e = jj < K ? sel[jj] : 0;
-      const uint8_t* blob = uniform_ptr(jj < K ? ((unsigned)e < (unsigned)E ? tbl[e] : nullptr) : shared_blob);
+      const uint8_t* blob = uniform_ptr(jj < K ? selp[jj] : shared_blob);
       const uint32_t r = ghave[m] ? (uint32_t)(sec * I + row) : 0u;   // row of [gate; up]
       gq[m] = make_rsrc(blob, ghave[m] && blob != nullptr ? blob_bytes : 0u);
       gqo[m] = r * row_bytes;
@@ -462,8 +463,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   auto plan_down = [&]() {   // from the selection
 #pragma unroll
     for (int s = 0; s < STEPSD; ++s) {
-      const int e = s < K ? sel[s] : -1;
-      const uint8_t* blob = uniform_ptr((unsigned)e < (unsigned)E ? tbl[e] : nullptr);
+      const uint8_t* blob = uniform_ptr(s < K ? selp[s] : nullptr);
       dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u);
     }
   };
@@ -521,10 +521,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   };
   // diagnostic stamps of every block, by thread 0 (no block barrier):
   // 0 layer start, 1 h polled, 2 own logits published, 3 logits polled,
-  // 4 top-K, 5 routed gate/up dots, 6 routed activations published, 7 shared
-  // activations polled and applied, 8 routed activations polled, 9 h
-  // published (the last wave's); poll rounds (most over the threads): 10 h, 11 logits,
-  // 12 shared activations, 13 routed activations
+  // 4 top-K (after its barrier), 5 routed gate/up dots, 6 routed activations
+  // published, 7 top-K selected (wave 0, before the barrier), 8 activations
+  // polled, 9 h published (the last wave's), 14 routed gate/up rows
+  // requested, 15 shared activations published; poll rounds (most over the
+  // threads): 10 h, 11 logits, 12 shared activations, 13 routed activations
   auto bstamp = [&](int li, int ev) {
     if (a.bclocks && tid == 0) bclk[li * kBlockClockEvents + ev] = (int64_t)wall_clock64();
   };
@@ -751,30 +752,34 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           }
           wave_select_hi<kTopkSlots>(kk, K, [&](int r, int w) { sel[r] = w; });
         }
+        // the selected blobs, so the routed loads are planned from one read
+        if (lane < K) {
+          const int e = sel[lane];
+          selp[lane] = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
+        }
+        bstamp(li, 7);
       }
       block_sync_lds();
     } else {
       block_topk_keys<kWaves, kTblPer, 2>(lg, E, K, candk, candi, sel, selv);
+      if (tid < K) {
+        const int e = sel[tid];
+        selp[tid] = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
+      }
+      block_sync_lds();
     }
     stamp0(li, 14);
     bstamp(li, 4);
     plan_gu(1, RPWG, nullptr);       // routed gate/up rows
     issue_gu(1, RPWG);
+    bstamp(li, 14);
     stamp0(li, 5);
-    // while they arrive: wave 0 checks the selected experts' blobs, records
-    // the trace and takes the softmax weights (read by the combine after
-    // the activation hand-off's block barrier)
-    if (wave == 0) {
-      if (lane < K) {
-        const int e = sel[lane];
-        const uint8_t* bp = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
-        if (bp == nullptr) set_status(a.status, kStatusBadExpert);
-        if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
-        selv[lane] = (unsigned)e < (unsigned)E ? lg[e] : -INFINITY;
-      }
-      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
-                                  : wave_softmax_selected(selv, K);
-      if (lane < K) selw[lane] = w;
+    // while they arrive: wave 0 checks the selected experts' blobs and
+    // records the trace
+    if (wave == 0 && lane < K) {
+      const int e = sel[lane];
+      if (selp[lane] == nullptr) set_status(a.status, kStatusBadExpert);
+      if (b == 0 && a.topk_trace) a.topk_trace[(int64_t)li * K + lane] = e;
     }
     stamp0(li, 15);
     // the shared expert's gate/up rows (requested a layer ahead) while the
@@ -794,6 +799,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         }
       }
       stamp0(li, 4);
+      bstamp(li, 15);
       // its down rows, in flight while the routed rows are applied
       issue_down_shared(shp[li]);
     }
@@ -886,6 +892,17 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // round reads the words before the slowest blocks have published them
     // and, queued behind the down rows, returns late, so a second round is
     // needed; ~0.64 us later the first round mostly finds them all
+    // wave 0 takes the softmax weights first (read by the combine after the
+    // activation take's block barrier), off the path of the routed rows
+    if (wave == 0) {
+      if (lane < K) {
+        const int e = sel[lane];
+        selv[lane] = (unsigned)e < (unsigned)E ? lg[e] : -INFINITY;
+      }
+      const float w = a.no_renorm ? wave_softmax_weight(lg, E, K, selv, true)
+                                  : wave_softmax_selected(selv, K);
+      if (lane < K) selw[lane] = w;
+    }
     for (int d = 0; d < kActPollBackoff; ++d) __builtin_amdgcn_s_sleep(8);
     if (!take_acts(0, KS, 13)) return;
     stamp0(li, 17);

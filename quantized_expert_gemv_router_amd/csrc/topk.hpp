@@ -247,11 +247,15 @@ __device__ __forceinline__ void net_step(int (&a)[4]) {
 // do not separate the top K + 1.
 __device__ __forceinline__ bool wave_topk_net(const double* lg, int E, int K, int& win) {
   const int lane = threadIdx.x & 63;
+  // every read in range (clamped), so the eight are issued together
+  double lv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lv[i] = lg[min(lane + 64 * i, E - 1)];
   int k[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int e = lane + 64 * i;
-    k[i] = e < E ? net_key(lg[e], i) : INT_MIN;
+    const int kk = net_key(lv[i], i);   // computed in every lane: a select, no branch
+    k[i] = lane + 64 * i < E ? kk : INT_MIN;
   }
   // the lane's four best, sorted
   int a[4] = {max(k[0], k[1]), min(k[0], k[1]), INT_MIN, INT_MIN};
