@@ -19,7 +19,8 @@
 //            of h, takes sum(h^2), max|h| and its router rows' partial dot
 //            products from the polled registers, and after one block
 //            barrier publishes its logits
-//   logits:  every block polls all E logits and selects top-K itself (one
+//   logits:  (one tagged word each) every block polls all E logits and
+//            selects top-K itself (one
 //            wave: a selection network over truncated keys, else rounds on
 //            the keys' high words), then streams its gate/up rows
 //   a:       each block publishes silu(g)*u for its gate/up rows (two per
@@ -142,17 +143,12 @@ __device__ __forceinline__ void act_pair_values(uint64_t w, float& a0, float& a1
 }
 
 // Polls the words base[idx(i)] for the bits i set in `valid` until each
-// carries `tag`; payloads land in out[i].  Bounded: gives up (and raises
-// the launch's abort value) after kSpinLimit polls, or when another block
-// has raised it.
-// Words whose high bits from SHIFT up carry the tag (SHIFT 32: the tag;
-// SHIFT 40: its low 24 bits, the activation pairs); out[i] receives the
-// whole word.
-template <int N, int SHIFT, typename Idx>
-__device__ __forceinline__ bool take_tagged_w(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
-                                              uint64_t (&out)[N], uint32_t* abort, int32_t* status,
-                                              int& rounds) {
-  const uint32_t want = SHIFT == 32 ? tag : (tag & (0xFFFFFFFFu >> (SHIFT - 32)));
+// passes match() (carries the tag the reader waits for); the words land in
+// out[i].  Bounded: gives up (and raises the launch's abort value for
+// `tag`) after kSpinLimit polls, or when another block has raised it.
+template <int N, typename Idx, typename Match>
+__device__ __forceinline__ bool take_match(const uint64_t* base, Idx idx, uint32_t valid, Match match, uint32_t tag,
+                                           uint64_t (&out)[N], uint32_t* abort, int32_t* status, int& rounds) {
   uint32_t pending = valid;
   for (int spins = 0;; ++spins) {
     uint64_t v[N];
@@ -160,7 +156,7 @@ __device__ __forceinline__ bool take_tagged_w(const uint64_t* base, Idx idx, uin
     for (int i = 0; i < N; ++i) v[i] = ((pending >> i) & 1) ? ld_agent(base + idx(i)) : 0ull;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if (((pending >> i) & 1) && (uint32_t)(v[i] >> SHIFT) == want) {
+      if (((pending >> i) & 1) && match(v[i])) {
         out[i] = v[i];
         pending &= ~(1u << i);
       }
@@ -178,6 +174,30 @@ __device__ __forceinline__ bool take_tagged_w(const uint64_t* base, Idx idx, uin
     __builtin_amdgcn_s_sleep(1);
   }
 }
+
+// Words whose high bits from SHIFT up carry the tag (SHIFT 32: the tag;
+// SHIFT 40: its low 24 bits, the activation pairs).
+template <int N, int SHIFT, typename Idx>
+__device__ __forceinline__ bool take_tagged_w(const uint64_t* base, Idx idx, uint32_t valid, uint32_t tag,
+                                              uint64_t (&out)[N], uint32_t* abort, int32_t* status,
+                                              int& rounds) {
+  const uint32_t want = SHIFT == 32 ? tag : (tag & (0xFFFFFFFFu >> (SHIFT - 32)));
+  return take_match<N>(base, idx, valid, [&](uint64_t v) { return (uint32_t)(v >> SHIFT) == want; }, tag, out,
+                       abort, status, rounds);
+}
+
+// Router logits travel one to a word: the fp64 logit rounded to a 36-bit
+// significand (nearest, ties to even) with the tag's low 16 bits (8 bits of
+// launch number above the layer byte) in the freed low bits.  Every block
+// selects from the same rounded logits; the rounding (2^-37 relative) only
+// decides ties closer than the fp64 sums' own order differences reach.
+constexpr uint64_t kLogitTagMask = 0xFFFFull;
+__device__ __forceinline__ uint64_t logit_cleared(uint32_t tbase) { return (uint64_t)(tbase & 0xFFFFu); }
+__device__ __forceinline__ uint64_t logit_word(double v, uint32_t tag) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  return ((bits + 0x7FFFull + ((bits >> 16) & 1ull)) & ~kLogitTagMask) | (tag & 0xFFFFu);
+}
+__device__ __forceinline__ double logit_value(uint64_t w) { return __longlong_as_double((long long)(w & ~kLogitTagMask)); }
 
 // Tagged 32-bit payloads: out[i] receives the payload of word idx(i).
 template <int N, typename Idx>
@@ -559,7 +579,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     uint64_t* hw = a.hwords + (int64_t)par * H;
     for (int j = tid; j < RW; j += kThreads) {
       const int r = rlo + j;
-      if (r < rhi) { st_agent(lw + 2 * r, cleared); st_agent(lw + 2 * r + 1, cleared); }
+      if (r < rhi) st_agent(lw + r, logit_cleared(tbase));
     }
     for (int t = tid; t < KS * (RG / 2); t += kThreads) {
       const int j = t / (RG / 2), r0 = glo + 2 * (t - j * (RG / 2));
@@ -674,12 +694,10 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     const double inv = a.no_norm ? 1.0 : 1.0 / sqrt(ss / (double)H + 1e-6);
     const uint32_t tag = tbase + (uint32_t)li + 1u;
     jitter<JIT>(b, wave, li, 0);
-    if (tid < 2 * RW && rlo + (tid >> 1) < rhi) {   // this block's logits: two words each, one store
-      const int k = tid >> 1;
+    if (tid < RW && rlo + tid < rhi) {   // this block's logits, one word each
       double d = 0.0;
-      for (int w = 0; w < kWaves; ++w) d += rpart[k * kWaves + w];
-      const uint64_t bits = (uint64_t)__double_as_longlong(d * inv);
-      put_tagged(lw + 2 * (rlo + k) + (tid & 1), (tid & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits, tag);
+      for (int w = 0; w < kWaves; ++w) d += rpart[tid * kWaves + w];
+      st_agent(lw + rlo + tid, logit_word(d * inv, tag));
     }
     bstamp(li, 2);
     // the shared expert's gate/up rows, in flight while x is staged, the
@@ -716,14 +734,16 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // ------------------------------------------------------------ phase G
     // this layer's pointer-table row lands while the logits are polled
     load_tbl_row(a.layer0 + li);
-    for (int e0 = 0; e0 < E; e0 += kThreads) {   // one logit (two words) per thread per pass
+    for (int e0 = 0; e0 < E; e0 += kThreads) {   // one logit (one word) per thread per pass
       const int e = e0 + tid;
-      uint32_t w[2] = {0u, 0u};
+      uint64_t w[1] = {0ull};
       int nr = 0;
-      const bool ok = take_tagged<2>(lw + 2 * e, [](int i) { return i; }, e < E ? 3u : 0u, tag, w,
-                                     abort_word, a.status, nr);
+      const uint32_t t16 = tag & 0xFFFFu;
+      const bool ok = take_match<1>(lw + e, [](int i) { return i; }, e < E ? 1u : 0u,
+                                    [&](uint64_t v) { return (uint32_t)(v & kLogitTagMask) == t16; }, tag, w,
+                                    abort_word, a.status, nr);
       bcount(li, 11, nr);
-      if (e < E) lg[e] = __longlong_as_double((long long)(((uint64_t)w[1] << 32) | w[0]));
+      if (e < E) lg[e] = logit_value(w[0]);
       // the table row's loads were issued before the poll's, so they are in;
       // the barrier below publishes both to every wave
       if (e0 + kThreads >= E) store_tbl_row();
