@@ -28,9 +28,10 @@
 //            polls all activations (shared and routed slots in one take),
 //            then applies its down rows and the combine with the residual.
 //            The shared expert does not wait for routing: its gate/up rows
-//            are applied and its activations published while the routed
-//            rows stream in, and its down rows are requested with the
-//            previous layer's prefetch.
+//            are applied while wave 0 selects (wave 0's own row once the
+//            routed rows are requested), its activations published while
+//            the routed rows stream in, and its down rows requested right
+//            after that publish.
 // Loads are issued as early as their addresses are known and their data
 // does not compete with loads on the critical path: the router and
 // shared-expert pointers of every layer are cached in LDS at start; the
@@ -778,6 +779,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
           selp[lane] = (unsigned)e < (unsigned)E ? tbl[e] : nullptr;
         }
         bstamp(li, 7);
+      } else if (S > 0) {
+        gu_dots(0, 1);   // the other waves apply their shared rows meanwhile
       }
       block_sync_lds();
     } else {
@@ -805,7 +808,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // the shared expert's gate/up rows (requested a layer ahead) while the
     // routed rows arrive, and its activations published at once
     if (S > 0) {
-      gu_dots(0, 1);
+      if (wave == 0 || E > 64 * kTopkSlots) gu_dots(0, 1);   // (the other waves took theirs during top-K)
       stamp0(li, 3);
       block_sync_lds();
       jitter<JIT>(b, wave, li, 1);
