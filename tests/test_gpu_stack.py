@@ -199,6 +199,46 @@ def test_stack_all_logits_tied(flags):
         assert_close(outs[l], exp["y"][0], f"tied layer {l} output")
 
 
+@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
+def test_stack_near_tied_logits(flags):
+    """Four experts whose logits differ only in their low bits: experts 3 and
+    5 share one router row, expert 9 has that row one bf16 ulp larger in
+    magnitude at the input's smallest nonzero component (a logit higher by
+    ~1e-8 relative) and expert 17 one ulp smaller.  Their logits agree to far
+    more bits than the persistent kernel's selection network compares (its
+    keys keep 17 significand bits), so it must defer to the full-key rounds;
+    the selection must still be the oracle's: expert 9, then the lower index
+    of the equal pair."""
+    from tests import blobkit as bk
+    cfg = synth.with_changes(synth.CONFIGS["stack60_decode"], name="stack_near_ties", hidden=256, inter=128,
+                             n_experts=128, top_k=2, layers=1)
+    shape, ex, _ = build_stack(cfg, 1)
+    x = synth.bf16_to_f64(synth.tokens(cfg, 6, 1))
+    rng = np.random.default_rng(11)
+    wr = bk.f64_to_bf16(rng.standard_normal((cfg.n_experts, cfg.hidden)) * 0.02)
+    row = bk.f64_to_bf16(np.sign(x[0]) * 0.05)
+    nz = np.flatnonzero(x[0] != 0)
+    j = nz[np.argmin(np.abs(x[0][nz]))]
+    up, down = row.copy(), row.copy()
+    up[j] += 1     # bf16 is sign-magnitude: one ulp more magnitude, same sign as x_j
+    down[j] -= 1
+    for e, r in ((3, row), (5, row), (9, up), (17, down)):
+        wr[e] = r
+    rt = q.RouterTable([bf16_dev(wr)])
+    h = torch.from_numpy(x.astype(np.float32)).cuda()
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    tk, hk = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws, trace=True)
+    assert q.moeq_last_stack_path() == (2 if flags else 1)
+    assert q.moe_read_device_status(ws) == 0
+    exp = oracle.run_layer(cfg, 0, x, want_intermediates=False, wr=wr)
+    lg = exp["logits"][0][[3, 5, 9, 17]]
+    assert lg[2] > lg[0] == lg[1] > lg[3]
+    assert (lg.max() - lg.min()) / abs(lg.max()) < 2.0 ** -20, lg
+    assert np.array_equal(exp["idx"][0], [9, 3]), exp["idx"][0]
+    assert np.array_equal(tk.cpu().numpy()[0, 0], exp["idx"][0]), (tk.cpu().numpy()[0, 0], exp["idx"][0])
+    assert_close(h.cpu().numpy()[0].astype(np.float64), exp["y"][0], "near-tied layer output")
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit"])
 def test_single_layer_no_norm_matches_oracle(name):
     """One layer through the stack entry with MOEQ_F_STACK_NO_NORM (the layer
