@@ -1227,7 +1227,7 @@ def main():
         rec = run_prefill(args, cfg, dev, stream)
     elif cfg.layers > 1:
         rec = run_stack(args, cfg, dev, stream)
-    elif cfg.tokens == 1 and cfg.bits in (2, 4) and not args.layer_calls:
+    elif cfg.tokens == 1 and cfg.bits in (2, 3, 4) and not args.layer_calls:
         # widths with a persistent instantiation: the whole layer in one launch
         rec = run_layer_fused(args, cfg, dev, stream)
     else:

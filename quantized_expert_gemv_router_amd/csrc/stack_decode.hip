@@ -350,10 +350,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   uint32_t wr[CPLR][HW];
   u32x4 qg[RPWG][CPLG];
   uint32_t sg[RPWG][CPLG];
+  uint2 qhg[RPWG][CPLG];           // 3-bit: the chunks' high-bit plane words
   u32x4 qd[STEPSD][CPLD];          // routed slots' down rows
   uint32_t sd[STEPSD][CPLD];
+  uint2 qhd[STEPSD][CPLD];
   u32x4 qsh[CPLD];                 // the shared expert's down rows
   uint32_t ssh[CPLD];
+  uint2 qhsh[CPLD];
   const uint8_t* tnext[kTblPer];   // this layer's pointer-table row, in flight to LDS
 
   // gate/up rows: register slot m = 0 holds the shared expert's rows (task
@@ -434,6 +437,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       for (int m = 0; m < RPWG; ++m) {
         if (m < mlo || m >= mhi) continue;
         qg[m][c] = load_rsrc_b128(gq[m], gqo[m] + (uint32_t)cc * 16u);
+        if constexpr (BITS == 3)   // a 3-bit row: the 2-bit low plane, then the high-bit plane
+          qhg[m][c] = load_rsrc_b64(gq[m], gqo[m] + (uint32_t)H / 4u + (uint32_t)cc * 8u);
         sg[m][c] = load_rsrc_b32(gq[m], gso[m] + (uint32_t)(cc * PC / 64) * 4u);
       }
     }
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       const float2 xsum = *reinterpret_cast<const float2*>(xs + kChunkSums * ccl);
 #pragma unroll
       for (int m = 0; m < RPWG; ++m)
-        if (live[m] && cc < nchG) part[m] += chunk_affine(chunk_dot<BITS>(qg[m][c], x), sg[m][c], xsum);
+        if (live[m] && cc < nchG) part[m] += chunk_term<BITS>(chunk_dot_q<BITS>(qg[m][c], qhg[m][c], x), sg[m][c], xsum);
     }
     const float ux = undo_x;
 #pragma unroll
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       dsrc[s] = make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u);
     }
   };
-  auto down_load = [&](rsrc_t src, u32x4 (&q)[CPLD], uint32_t (&sbw)[CPLD]) {
+  auto down_load = [&](rsrc_t src, u32x4 (&q)[CPLD], uint32_t (&sbw)[CPLD], uint2 (&qh)[CPLD]) {
     const uint32_t row_bytes = (uint32_t)I * BITS / 8;
     const uint32_t gpr = I / 64;
     const uint32_t q_off = 2u * (uint32_t)H * I * BITS / 8;
@@ -501,17 +506,19 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     for (int c = 0; c < CPLD; ++c) {
       const int cc = min(sub + LPRD * c, nchD - 1);
       q[c] = load_rsrc_b128(src, q_off + (uint32_t)row * row_bytes + (uint32_t)cc * 16u);
+      if constexpr (BITS == 3)
+        qh[c] = load_rsrc_b64(src, q_off + (uint32_t)row * row_bytes + (uint32_t)I / 4u + (uint32_t)cc * 8u);
       sbw[c] = load_rsrc_b32(src, sb_off + ((uint32_t)row * gpr + (uint32_t)(cc * PC / 64)) * 4u);
     }
   };
   auto issue_down = [&]() {
 #pragma unroll
-    for (int s = 0; s < STEPSD; ++s) down_load(dsrc[s], qd[s], sd[s]);
+    for (int s = 0; s < STEPSD; ++s) down_load(dsrc[s], qd[s], sd[s], qhd[s]);
     issue_fence();
   };
   auto issue_down_shared = [&](const uint8_t* sblob) {   // the layer's shared expert (at most one)
     const uint8_t* blob = uniform_ptr(sblob);
-    down_load(make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u), qsh, ssh);
+    down_load(make_rsrc(blob, blob != nullptr ? blob_bytes_all : 0u), qsh, ssh, qhsh);
     issue_fence();
   };
   auto load_tbl_row = [&](int layer) {   // into registers; stored to LDS after the next barrier
@@ -896,7 +903,8 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     };
     // this lane's share of one slot's down row against its staged
     // activations (the LPRD lanes of a row group hold the row's chunks)
-    auto down_part = [&](int s, const u32x4 (&q)[CPLD], const uint32_t (&sbw)[CPLD], bool ok) -> float {
+    auto down_part = [&](int s, const u32x4 (&q)[CPLD], const uint32_t (&sbw)[CPLD], const uint2 (&qh)[CPLD],
+                         bool ok) -> float {
       const int sub = lane % LPRD;
       float part = 0.0f;
 #pragma unroll
@@ -905,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
         const XChunk<BITS> x = load_xchunk<BITS>(ap + (int64_t)s * (I / 2), cc, nchD);
         const float4 xsm = *reinterpret_cast<const float4*>(as + kActSums * (s * nchD + cc));
         if (ok && sub + LPRD * c < nchD)
-          part += chunk_affine(chunk_dot<BITS>(q[c], x), sbw[c], make_float2(xsm.x, xsm.y)) * xsm.z;
+          part += chunk_term<BITS>(chunk_dot_q<BITS>(q[c], qh[c], x), sbw[c], make_float2(xsm.x, xsm.y)) * xsm.z;
       }
       return part;
     };
@@ -939,11 +947,11 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
       // every slot's share weighted in the lane (the shared expert first,
       // then the slots in rank order), then one sum over the row group:
       // valid in lane LPRD-1
-      float part = S > 0 ? down_part(K, qsh, ssh, dok) : 0.0f;
+      float part = S > 0 ? down_part(K, qsh, ssh, qhsh, dok) : 0.0f;
 #pragma unroll
       for (int s = 0; s < STEPSD; ++s) {
         if (s >= K) break;
-        part = fmaf(selw[s], down_part(s, qd[s], sd[s], dok), part);
+        part = fmaf(selw[s], down_part(s, qd[s], sd[s], qhd[s], dok), part);
       }
       const float dsum = group_sum_dpp<LPRD>(part);
       const float acc = dok ? hs[drow] + dsum : 0.0f;
@@ -1020,7 +1028,8 @@ struct Geometry {
     if (bits != BITS) return false;
     // expert blobs are addressed with 32-bit byte offsets
     if ((int64_t)3 * H * I * BITS / 8 + (int64_t)3 * (H / 64) * I * 4 >= (int64_t{1} << 31)) return false;
-    const int PC = 128 / BITS;
+    const int PC = BITS == 3 ? 64 : 128 / BITS;   // values per 16-byte unit (of the low plane at 3 bits)
+    const int PW = BITS == 4 ? 8 : 16;            // values per staged word
     if (rw > CPLR) return false;
     if (H / PC > 64 * CPLG) return false;
     const int RG = gu_rows_max(I, nb), RD = (H + nb - 1) / nb;
@@ -1028,7 +1037,8 @@ struct Geometry {
     if (K * 2 * RG > kWaves * (RPWG - 1)) return false;      // routed rows: slots 1 ..
     const int nchd = I / PC;
     if (nchd > LPRD * CPLD) return false;
-    if (KS * (I * BITS / 32) > kThreads) return false;   // one activation word per thread
+    if (KS * (I / PW) > kThreads) return false;    // one activation word per thread
+    if (BITS == 3 && (H % 128 != 0 || I % 128 != 0)) return false;   // whole high-plane words per row
     if (K > STEPSD) return false;                  // one down step per routed slot
     if (H < nb) return false;                      // every block owns a row of h (hand-off safety)
     if (RD > kWaves * (64 / LPRD)) return false;   // every output row owned by a wave
@@ -1055,7 +1065,7 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   while (rw < rw_need) rw <<= 1;
   if (rw > kWaves) return hipErrorNotSupported;
   a.router_rows = rw;
-  const int PC = 128 / a.bits;
+  const int PC = a.bits == 3 ? 64 : 128 / a.bits;
   const int RG = gu_rows_max(a.I, nb), RD = (a.H + nb - 1) / nb;
   const size_t lds =
       (size_t)stack_lds_layout(a.H, a.I, a.E, a.S, KS, PC, RG, RD,
@@ -1064,7 +1074,7 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   if (lds > 96 * 1024) return hipErrorNotSupported;
   const Geometry g{nb, rw, a.H, a.I, a.E, a.S, a.K, KS, a.bits};
   // hidden 4096, intermediate 1024, 512 experts on 256 CUs: 4-bit K+S <= 4,
-  // 2-bit K+S <= 5; a small shape for tests; else the per-layer path.
+  // 2-bit and 3-bit K+S <= 5; a small shape for tests; else the per-layer path.
   if (a.jitter) {   // delay-injection instantiations: the 60-layer shape and the small test shape
     if (g.fits(4, 2, 2, 4, 32, 1, 3, 4)) return launch_t<4, 2, 2, 4, 32, 1, 3, 4, 1>(a, nb, lds, stream);
     if (g.fits(4, 1, 1, 2, 64, 1, 3, 1)) return launch_t<4, 1, 1, 2, 64, 1, 3, 1, 1>(a, nb, lds, stream);
@@ -1072,6 +1082,7 @@ hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   }
   if (g.fits(4, 2, 2, 4, 32, 1, 3, 4)) return launch_t<4, 2, 2, 4, 32, 1, 3, 4>(a, nb, lds, stream);
   if (g.fits(2, 2, 1, 5, 32, 1, 4, 4)) return launch_t<2, 2, 1, 5, 32, 1, 4, 4>(a, nb, lds, stream);
+  if (g.fits(3, 2, 1, 5, 32, 1, 4, 4)) return launch_t<3, 2, 1, 5, 32, 1, 4, 4>(a, nb, lds, stream);
   if (g.fits(4, 1, 1, 2, 64, 1, 3, 1)) return launch_t<4, 1, 1, 2, 64, 1, 3, 1>(a, nb, lds, stream);
   return hipErrorNotSupported;
 }

@@ -239,7 +239,7 @@ def test_stack_near_tied_logits(flags):
     assert_close(h.cpu().numpy()[0].astype(np.float64), exp["y"][0], "near-tied layer output")
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit"])
+@pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit", "decode_3bit"])
 def test_single_layer_no_norm_matches_oracle(name):
     """One layer through the stack entry with MOEQ_F_STACK_NO_NORM (the layer
     input taken as is, as the one-layer calls without the norm flag): the
@@ -271,9 +271,9 @@ def _width_cfg(base, bits):
 def test_stack_mixed_widths_full_width():
     """A stack whose layers hold 4-, 2- and 3-bit experts (hidden 4096, 512
     experts, top-3 + 1 shared): moe_expert_stack_decode_mixed runs each run
-    of equal width as one stack call (persistent for 4 and 2 bits, per-layer
-    launches for 3 bits); every layer is checked against the oracle of its
-    own width on the GPU's input (teacher forcing)."""
+    of equal width as one stack call (each a persistent launch: every width
+    has an instantiation at this shape); every layer is checked against the
+    oracle of its own width on the GPU's input (teacher forcing)."""
     base = synth.with_changes(synth.CONFIGS["stack60_decode"], name="mixed", layers=5)
     bits = [4, 2, 2, 3, 4]
     shape = q.Shape.of(base)
@@ -293,7 +293,7 @@ def test_stack_mixed_widths_full_width():
         h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(base, ts, 1)).astype(np.float32)).cuda()
         ws = q.new_workspace(shape, 1, base.top_k)
         tk, hk = q.moe_expert_stack_decode_mixed(shape, bits, ex, rt, h, base.top_k, workspace=ws, trace=True)
-        assert q.moeq_last_stack_path() == 3
+        assert q.moeq_last_stack_path() == 1
         assert q.moe_read_device_status(ws) == 0
         hs = hk.cpu().numpy()[:, 0, :].astype(np.float64)
         outs = [hs[l + 1] for l in range(len(bits) - 1)] + [h.cpu().numpy()[0].astype(np.float64)]
@@ -308,6 +308,22 @@ def test_stack_2bit_full_width():
     1 shared) on three layers, gated per layer along its own trajectory."""
     cfg = synth.with_changes(synth.CONFIGS["decode_2bit"], name="stack_2bit", layers=3, rmsnorm=True)
     say("[stack] 2-bit, 3 layers at full width")
+    shape, ex, rt = build_stack(cfg, cfg.layers)
+    for ts in (0, 1):
+        h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+        ws = q.new_workspace(shape, 1, cfg.top_k)
+        traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == 1
+        assert q.moe_read_device_status(ws) == 0
+        compare_free_running(cfg, cfg.layers, ts, traces, h.cpu().numpy()[0])
+
+
+def test_stack_3bit_full_width():
+    """The 3-bit persistent instantiation (two bit planes; hidden 4096, 512
+    experts, top-4 + 1 shared) on three layers, gated per layer along its
+    own trajectory."""
+    cfg = synth.with_changes(synth.CONFIGS["decode_3bit"], name="stack_3bit", layers=3, rmsnorm=True)
+    say("[stack] 3-bit, 3 layers at full width")
     shape, ex, rt = build_stack(cfg, cfg.layers)
     for ts in (0, 1):
         h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
