@@ -197,7 +197,10 @@ int moe_swiglu_down_combine(const moeq_shape* shape, const moeq_experts* experts
  * (it can be captured in a HIP graph and replayed) whose workgroups, one
  * per compute unit, must all be resident at once, so persistent launches
  * on one GPU must not overlap in time (a launch that cannot fill the GPU
- * ends with status bit 2 instead of hanging).  Otherwise, or with
+ * ends with status bit 2 instead of hanging).  On that path each fp64
+ * logit is handed to the other workgroups rounded to a 36-bit significand
+ * (2^-37 relative) and the activations as fp16 under a shared power of two
+ * (the precision they are staged in anyway).  Otherwise, or with
  * MOEQ_F_STACK_LAYERWISE or T > 1, it enqueues the three per-layer calls
  * for each layer.  A wait between workgroups that lasts too long sets
  * status bit 2 (see moe_read_device_status) and the launch ends early. */
