@@ -49,8 +49,9 @@ def compare_free_running(cfg, L, token_set, traces, gpu_h):
     for l in range(L):
         exp = oracle.run_layer(cfg, l, hs[l][None, :], want_intermediates=False)
         srt = -np.sort(-exp["logits"][0])
-        min_gap = min(min_gap, srt[K - 1] - srt[K])
-        assert np.array_equal(idx[l], exp["idx"][0]), (l, idx[l], exp["idx"][0], srt[K - 1] - srt[K])
+        gap = srt[K - 1] - srt[K] if K < len(srt) else np.inf   # every expert selected: no margin
+        min_gap = min(min_gap, gap)
+        assert np.array_equal(idx[l], exp["idx"][0]), (l, idx[l], exp["idx"][0], gap)
         worst = max(worst, assert_close(outs[l], exp["y"][0], f"layer {l} output (GPU input)"))
     # drift from the oracle's own trajectory, for the record
     ref = oracle.run_stack(cfg, synth.bf16_to_f64(synth.tokens(cfg, token_set, 1)), layers=L)
@@ -301,6 +302,27 @@ def test_stack_mixed_widths_full_width():
             exp = oracle.run_layer(_width_cfg(base, b), l, hs[l][None, :], want_intermediates=False)
             assert np.array_equal(tk.cpu().numpy()[l, 0], exp["idx"][0]), (ts, l, b)
             assert_close(outs[l], exp["y"][0], f"mixed stack layer {l} ({b}-bit)")
+
+
+@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
+@pytest.mark.parametrize("bits,E,K", [(4, 100, 3), (4, 449, 1), (4, 3, 3), (2, 77, 4), (3, 300, 2), (2, 512, 1)])
+def test_stack_ragged_expert_counts(bits, E, K, flags):
+    """Expert counts that are not a multiple of the 64-lane wave (the
+    selection's last logit slot partly empty), one selected expert, every
+    expert selected (K = E), and top-4 (past the selection network, rounds
+    of wave maxima) at a ragged count: three layers, gated per layer along
+    the GPU's own trajectory."""
+    cfg = synth.with_changes(synth.CONFIGS[f"decode_{bits}bit"], name=f"stack_r{bits}_{E}_{K}", hidden=256,
+                             inter=128, n_experts=E, top_k=K, layers=3, rmsnorm=True)
+    say(f"[stack] {bits}-bit E={E} K={K} flags={flags}")
+    shape, ex, rt = build_stack(cfg, cfg.layers)
+    for ts in (0, 1):
+        h = torch.from_numpy(synth.bf16_to_f64(synth.tokens(cfg, ts, 1)).astype(np.float32)).cuda()
+        ws = q.new_workspace(shape, 1, cfg.top_k)
+        traces = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == (2 if flags else 1)
+        assert q.moe_read_device_status(ws) == 0
+        compare_free_running(cfg, cfg.layers, ts, traces, h.cpu().numpy()[0])
 
 
 def test_stack_2bit_full_width():
