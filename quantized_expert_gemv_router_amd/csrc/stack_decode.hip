@@ -762,14 +762,14 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
     // top-K: wave 0 selects from all E logits (up to eight per lane; one
     // wave alone on its SIMD finishes sooner than eight sharing four), one
     // barrier hands the selection to the block; beyond 512 experts the
-    // waves select together.  Up to three experts the selection network
+    // waves select together.  Up to four experts the selection network
     // (one pass of sorted four-lists through the wave) decides whenever
-    // the truncated keys separate the K + 1 best; rounds of wave maxima
-    // on the full keys decide otherwise.
+    // the truncated keys separate the K best from the rest; rounds of wave
+    // maxima on the full keys decide otherwise.
     if (E <= 64 * kTopkSlots) {
       if (wave == 0) {
         int win;
-        if (K <= 3 && wave_topk_net(lg, E, K, win)) {
+        if (K <= 4 && wave_topk_net(lg, E, K, win)) {
           if (lane < K) sel[lane] = win;
         } else {
           int64_t kk[kTopkSlots];

@@ -202,9 +202,9 @@ __device__ __forceinline__ void wave_select_hi(const int64_t (&k)[M], int K, Emi
 }
 
 // ------------------------------------------------------ selection network
-// One wave, K <= 3, eight logits per lane (element lane + 64 i): the top
-// K + 1 elements found by one pass of sorted four-lists through the wave
-// instead of K rounds of wave maxima.  Each element becomes a 32-bit key:
+// One wave, K <= 4, eight logits per lane (element lane + 64 i): the top
+// elements found by one pass of sorted four-lists through the wave instead
+// of K rounds of wave maxima.  Each element becomes a 32-bit key:
 // the high word of its order key with the three lowest bits replaced by
 // 7 - i (its slot), so a key names its element within the lane.  A lane
 // sorts its eight keys into its four best; six DPP steps then merge lists
@@ -213,9 +213,11 @@ __device__ __forceinline__ void wave_select_hi(const int64_t (&k)[M], int K, Emi
 // stages), and lane 63 ends with the wave's four best keys.  When their
 // 29-bit prefixes (the truncated order keys) are strictly decreasing, the
 // order of the K best and the boundary to the (K+1)-th are fixed by the
-// prefixes alone, so the keys give the exact selection; otherwise
-// (near-ties within 2^-17 relative, or ties) it returns false and the
-// caller selects on the full keys.  On success lane r < K receives the
+// prefixes alone, so the keys give the exact selection.  At K = 4 the lists
+// hold no fifth key; the boundary is shown instead by a count: exactly four
+// elements have a prefix at or above the fourth's.  Otherwise (near-ties
+// within 2^-17 relative, or ties) it returns false and the caller selects
+// on the full keys.  On success lane r < K receives the
 // element of rank r in `win` (wave-uniform per rank through readlane).
 __device__ __forceinline__ int net_key(double v, int slot) {
   v = v + 0.0;   // -0 becomes +0: the two tie, as numbers do
@@ -242,9 +244,9 @@ __device__ __forceinline__ void net_step(int (&a)[4]) {
   net_merge4(a, b);
 }
 
-// lg: the E (<= 512) logits in LDS, lg[e] for e < E.  Returns true with
-// lane r < K holding the rank-r element in win; false when the prefixes
-// do not separate the top K + 1.
+// lg: the E (<= 512) logits in LDS, lg[e] for e < E; K <= 4.  Returns true
+// with lane r < K holding the rank-r element in win; false when the
+// prefixes do not separate the top K from the rest.
 __device__ __forceinline__ bool wave_topk_net(const double* lg, int E, int K, int& win) {
   const int lane = threadIdx.x & 63;
   // every read in range (clamped), so the eight are issued together
@@ -277,15 +279,22 @@ __device__ __forceinline__ bool wave_topk_net(const double* lg, int E, int K, in
   int t[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) t[i] = __builtin_amdgcn_readlane(a[i], 63);
-  // prefixes strictly decreasing over the K + 1 best (INT_MIN past E)
+  // prefixes strictly decreasing over the min(K + 1, 4) best (INT_MIN past E)
   bool ok = true;
 #pragma unroll
   for (int i = 0; i < 3; ++i)
     if (i < K) ok = ok && t[i] != INT_MIN && (t[i] >> 3) > (t[i + 1] >> 3);
+  if (K == 4) {   // no fifth key: no element but the four may reach the fourth's prefix
+    const int p3 = t[3] >> 3;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) n += __popcll(__ballot((k[i] >> 3) >= p3));
+    ok = ok && t[3] != INT_MIN && n == 4;
+  }
   if (!ok) return false;
   win = kTopkNone;
 #pragma unroll
-  for (int r = 0; r < 3; ++r) {
+  for (int r = 0; r < 4; ++r) {
     if (r >= K) break;
     const bool mine = loc[0] == t[r] || loc[1] == t[r] || loc[2] == t[r] || loc[3] == t[r];
     const int owner = (int)__builtin_ctzll(__ballot(mine));

@@ -240,6 +240,43 @@ def test_stack_near_tied_logits(flags):
     assert_close(h.cpu().numpy()[0].astype(np.float64), exp["y"][0], "near-tied layer output")
 
 
+@pytest.mark.parametrize("flags", [0, q.F_STACK_LAYERWISE])
+def test_stack_top4_boundary_near_tie(flags):
+    """Top-4 whose fourth and fifth logits differ only in their low bits:
+    experts 40, 50, 60 take clearly separated rows, expert 20 a fourth row
+    and expert 30 the same row one bf16 ulp larger in magnitude at the
+    input's smallest nonzero component.  Both sit in the first logit slot,
+    so their truncated keys are identical: the four best prefixes decrease
+    strictly, and only the count of elements at or above the fourth prefix
+    (five, not four) sends the selection network to the full-key rounds.
+    The selection must be the oracle's: 40, 50, 60, then 30 (not 20)."""
+    from tests import blobkit as bk
+    cfg = synth.with_changes(synth.CONFIGS["decode_2bit"], name="stack_top4_tie", hidden=256, inter=128,
+                             n_experts=128, top_k=4, layers=1, rmsnorm=True)
+    shape, ex, _ = build_stack(cfg, 1)
+    x = synth.bf16_to_f64(synth.tokens(cfg, 7, 1))
+    rng = np.random.default_rng(12)
+    wr = bk.f64_to_bf16(rng.standard_normal((cfg.n_experts, cfg.hidden)) * 0.02)
+    nz = np.flatnonzero(x[0] != 0)
+    j = nz[np.argmin(np.abs(x[0][nz]))]
+    for e, a in ((40, 0.05), (50, 0.045), (60, 0.04), (20, 0.035)):
+        wr[e] = bk.f64_to_bf16(np.sign(x[0]) * a)
+    wr[30] = wr[20]
+    wr[30, j] += 1   # bf16 is sign-magnitude: one ulp more magnitude, same sign as x_j
+    rt = q.RouterTable([bf16_dev(wr)])
+    h = torch.from_numpy(x.astype(np.float32)).cuda()
+    ws = q.new_workspace(shape, 1, cfg.top_k)
+    tk, hk = q.moe_expert_stack_decode(shape, ex, rt, h, cfg.top_k, flags=flags, workspace=ws, trace=True)
+    assert q.moeq_last_stack_path() == (2 if flags else 1)
+    assert q.moe_read_device_status(ws) == 0
+    exp = oracle.run_layer(cfg, 0, x, want_intermediates=False, wr=wr)
+    lg = exp["logits"][0]
+    assert lg[30] > lg[20] and (lg[30] - lg[20]) / abs(lg[30]) < 2.0 ** -20, (lg[30], lg[20])
+    assert np.array_equal(exp["idx"][0], [40, 50, 60, 30]), exp["idx"][0]
+    assert np.array_equal(tk.cpu().numpy()[0, 0], exp["idx"][0]), (tk.cpu().numpy()[0, 0], exp["idx"][0])
+    assert_close(h.cpu().numpy()[0].astype(np.float64), exp["y"][0], "top-4 near-tie layer output")
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit", "decode_3bit"])
 def test_single_layer_no_norm_matches_oracle(name):
     """One layer through the stack entry with MOEQ_F_STACK_NO_NORM (the layer
