@@ -277,6 +277,54 @@ def test_stack_top4_boundary_near_tie(flags):
     assert_close(h.cpu().numpy()[0].astype(np.float64), exp["y"][0], "top-4 near-tie layer output")
 
 
+@pytest.mark.parametrize("bits,K", [(4, 1), (4, 2), (4, 3), (2, 4)])
+def test_stack_selection_sweep(bits, K):
+    """Seeded sweep of the persistent kernel's top-K over 512 experts: per
+    case a fresh token and router in which K + 2 experts get strong rows
+    (a multiple of sign(x)), each either a strength of its own, an exact
+    copy of an earlier strong row (an exact tie) or such a copy one bf16
+    ulp up or down at a random nonzero component (a near-tie far below the
+    selection network's 17-bit keys).  The ties fall at random ranks, at
+    and across the top-K boundary, so the network, its certificate and the
+    full-key rounds all decide some cases; every selection must be the
+    oracle's, and the layer output within the bar."""
+    from tests import blobkit as bk
+    cfg = synth.with_changes(synth.CONFIGS[f"decode_{bits}bit"], name=f"stack_sweep{bits}_{K}", hidden=256,
+                             inter=128, n_experts=512, top_k=K, layers=1, rmsnorm=True)
+    shape, ex, _ = build_stack(cfg, 1)
+    rng = np.random.default_rng(1000 * bits + K)
+    n_ties = 0
+    for case in range(24):
+        x = synth.bf16_to_f64(synth.tokens(cfg, 100 + case, 1))
+        wr = bk.f64_to_bf16(rng.standard_normal((cfg.n_experts, cfg.hidden)) * 0.02)
+        nz = np.flatnonzero(x[0] != 0)
+        strong = rng.choice(cfg.n_experts, K + 2, replace=False)
+        for i, e in enumerate(strong):
+            kind = rng.integers(4) if i > 0 else 0
+            if kind == 0:
+                wr[e] = bk.f64_to_bf16(np.sign(x[0]) * rng.choice([0.03, 0.035, 0.04, 0.045, 0.05]))
+            else:
+                wr[e] = wr[strong[rng.integers(i)]]
+                j = rng.choice(nz)
+                if kind == 2:   # bf16 is sign-magnitude: one ulp of magnitude up
+                    wr[e, j] += 1
+                elif kind == 3:   # or down
+                    wr[e, j] -= 1
+        rt = q.RouterTable([bf16_dev(wr)])
+        h = torch.from_numpy(x.astype(np.float32)).cuda()
+        ws = q.new_workspace(shape, 1, K)
+        tk, _ = q.moe_expert_stack_decode(shape, ex, rt, h, K, workspace=ws, trace=True)
+        assert q.moeq_last_stack_path() == 1
+        assert q.moe_read_device_status(ws) == 0
+        exp = oracle.run_layer(cfg, 0, x, want_intermediates=False, wr=wr)
+        srt = -np.sort(-exp["logits"][0])
+        n_ties += int(np.min(np.abs(np.diff(srt[:K + 1])) / np.abs(srt[0])) < 2.0 ** -17)
+        assert np.array_equal(tk.cpu().numpy()[0, 0], exp["idx"][0]), (case, tk.cpu().numpy()[0, 0], exp["idx"][0])
+        assert_close(h.cpu().numpy()[0].astype(np.float64), exp["y"][0], f"sweep case {case}")
+    say(f"  {bits}-bit top-{K}: 24 cases, {n_ties} with a tie or near-tie among the K + 1 best")
+    assert n_ties >= 6
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode_4bit", "decode_2bit", "decode_3bit"])
 def test_single_layer_no_norm_matches_oracle(name):
     """One layer through the stack entry with MOEQ_F_STACK_NO_NORM (the layer
