@@ -1093,7 +1093,7 @@ def probe_handoff():
     import quantized_expert_gemv_router_amd as q
     names = {0: "tagged all-gather", 1: "flag + payload", 2: "ping-pong", 3: "counter barrier",
              4: "gather to one + broadcast", 5: "gather to one + broadcast + one data read",
-             6: "tagged all-gather, pipelined polls"}
+             6: "tagged all-gather, pipelined polls", 7: "fixed-point atomic reduction"}
     cases = [(6, w, w, s, d) for w in (1, 4, 8) for s in (0, 1, 2) for d in (2, 4)]
     cases += [(0, w, w, s, 1) for w in (1, 4, 8) for s in (0, 1)]
     cases += [(2, 1, 1, s, p) for s in (0, 1) for p in (1, 8)]
@@ -1103,6 +1103,7 @@ def probe_handoff():
     cases += [(1, w, w, 1, 1) for w in (1, 4, 16)]
     cases += [(4, w, w, 1, c) for w in (1, 4, 16) for c in (1, 8, 32)]
     cases += [(5, w, w, 1, c) for w in (4, 16) for c in (8, 32)]
+    cases += [(7, w, 2 * w, s, 1) for w in (1, 2, 4) for s in (0, 1)]
     xcc_logged = False
     for mode, w, stride, s, peer in cases:
         if stride < w:

@@ -326,7 +326,13 @@ int moe_read_device_status(void* workspace, void* stream, int32_t* status);
  *           that the other workgroups poll (workgroup id mod peer);
  *   mode 5  mode 4, then every workgroup reads all the words once;
  *   mode 6  mode 0 with `peer` (2 or 4) staggered loads of every polled
- *           word in flight (at most 2048 words).
+ *           word in flight (at most 2048 words);
+ *   mode 7  fixed-point reduction: every workgroup adds to each of the
+ *           CUs * words_per_block 64-bit accumulators with agent-scope
+ *           atomics (a count in bits 55-63, its id mod 256 below) and polls
+ *           them until every count reads CUs; sums are checked (a wrong
+ *           sum counts in *mismatches); accumulators triple-buffered by
+ *           round, so stride >= 2 * words_per_block; fewer than 512 CUs.
  * `sleep` (0..3) is the back-off between polls (s_sleep 0, 1, 2, 4).
  * scratch: device, moeq_probe_scratch_bytes(words_per_block, stride) bytes,
  * cleared by the call.  Synchronises `stream`; *ticks = 100 MHz wall-clock

@@ -23,7 +23,15 @@
 //      poller, data fetched once;
 //   6  tagged all-gather as 0 with pipelined polls: every polled word has
 //      `peer` (2 or 4) loads in flight, issued a back-off apart, so a word
-//      is seen a fraction of a load's round trip after it lands.
+//      is seen a fraction of a load's round trip after it lands;
+//   7  fixed-point reduction: every workgroup adds (1 << 55) + (b mod 256)
+//      to each of NB * W 64-bit accumulators with agent-scope atomics and
+//      polls them until each count field (bits 55-63) reads NB; the sums
+//      are checked.  The accumulators are triple-buffered by round mod 3:
+//      after its poll of round r a workgroup clears its own W words of the
+//      buffer of round r - 1 and drains, before its adds of round r + 1,
+//      and every add of round r + 2 to that buffer follows a poll that saw
+//      those round r + 1 adds, so no clear can race with a later add.
 // In mode 0 writer j's words start at word j * stride (stride >= W),
 // so a larger stride spreads the polled words over more memory channels.
 // Every workgroup records the XCD id it runs on (hardware register XCC_ID).
@@ -99,6 +107,35 @@ __device__ bool poll_all(const uint64_t* base, int n, uint32_t tag, uint32_t* ab
 #pragma unroll
     for (int i = 0; i < kProbeMaxPer; ++i)
       if (((pending >> i) & 1) && (uint32_t)(v[i] >> 32) == tag) {
+        got[i] = v[i];
+        pending &= ~(1u << i);
+      }
+    if (pending == 0) break;
+    if ((spins & 63) == 63 && ld_agent(abort) != 0u) return false;
+    if (spins > kProbeSpin) { set_status(status, kStatusTimeout); st_agent(abort, 1u); return false; }
+    probe_sleep(s);
+  }
+  return true;
+}
+
+// Polls n accumulators base[tid + i * 512] until each count field (bits
+// 55-63) reads `count`; the words land in got[i].
+__device__ bool poll_count(const uint64_t* base, int n, uint32_t count, uint32_t* abort, int32_t* status, int s,
+                           uint64_t (&got)[kProbeMaxPer]) {
+  const int tid = threadIdx.x;
+  uint32_t pending = 0;
+#pragma unroll
+  for (int i = 0; i < kProbeMaxPer; ++i) {
+    got[i] = 0ull;
+    if (tid + i * kProbeThreads < n) pending |= 1u << i;
+  }
+  for (int spins = 0; pending != 0; ++spins) {
+    uint64_t v[kProbeMaxPer];
+#pragma unroll
+    for (int i = 0; i < kProbeMaxPer; ++i) v[i] = ((pending >> i) & 1) ? ld_agent(base + tid + i * kProbeThreads) : 0ull;
+#pragma unroll
+    for (int i = 0; i < kProbeMaxPer; ++i)
+      if (((pending >> i) & 1) && (uint32_t)(v[i] >> 55) == count) {
         got[i] = v[i];
         pending &= ~(1u << i);
       }
@@ -229,6 +266,23 @@ __global__ __launch_bounds__(kProbeThreads) void probe_kernel(ProbeArgs a) {
       for (int i = tid; i < NW; i += kProbeThreads)
         if ((uint32_t)(ld_agent(buf + i) >> 32) != tag) ++bad;
       if (bad) atomic_add_agent(a.ctl + 3, bad);
+    } else if (a.mode == 7) {
+      uint64_t* buf = a.words + (int64_t)(r % 3) * NW;
+      const uint64_t add = (1ull << 55) + (uint64_t)(b & 0xFF);
+      for (int i = tid; i < NW; i += kProbeThreads)
+        __hip_atomic_fetch_add(buf + i, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = poll_count(buf, NW, (uint32_t)NB, abort, a.status, a.sleep, got);
+      if (ok) {
+        uint64_t want = 0;   // sum over the workgroups of b mod 256
+        for (int j = 0; j < NB; ++j) want += (uint64_t)(j & 0xFF);
+        uint32_t bad = 0;
+#pragma unroll
+        for (int i = 0; i < kProbeMaxPer; ++i)
+          if (tid + i * kProbeThreads < NW && (got[i] & ((1ull << 55) - 1)) != want) ++bad;
+        if (bad) atomic_add_agent(a.ctl + 3, bad);
+        if (tid < W) st_agent(a.words + (int64_t)((r + 2) % 3) * NW + (int64_t)b * W + tid, (uint64_t)0);
+        drain_memory();
+      }
     } else if (a.mode == 2) {
       if (tid == 0 && (b == 0 || b == a.peer) && a.peer != 0) {
         uint64_t* ping = a.flags;          // written by workgroup 0

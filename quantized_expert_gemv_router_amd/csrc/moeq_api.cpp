@@ -398,7 +398,9 @@ int moeq_probe_handoff(int mode, int words_per_block, int stride, int rounds, in
   const int nb = device_cus();
   if (nb < 1) return fail(MOEQ_E_HIP, "no device");
   if (nb > 1024) return fail(MOEQ_E_UNSUPPORTED, "the probe handles at most 1024 CUs");
-  if (mode < 0 || mode > 6) return fail(MOEQ_E_INVALID, "mode=%d outside [0, 6]", mode);
+  if (mode < 0 || mode > 7) return fail(MOEQ_E_INVALID, "mode=%d outside [0, 7]", mode);
+  if (mode == 7 && (stride < 2 * words_per_block || nb > 511))
+    return fail(MOEQ_E_UNSUPPORTED, "the reduction needs stride >= 2 * words_per_block (three buffers) and < 512 CUs");
   if (mode == 6 && words_per_block * nb > 4 * 512)
     return fail(MOEQ_E_UNSUPPORTED, "pipelined polls handle at most 2048 words");
   if (words_per_block < 1 || (int64_t)words_per_block * nb > probe_max_words())
