@@ -170,6 +170,14 @@ def test_many_experts_lds_selection(T):
     run_and_check(cfg)
 
 
+@pytest.mark.parametrize("T", [2, 12])
+def test_maximum_experts_and_topk(T):
+    """The largest shape the boundary accepts: 4096 routed experts (plus the
+    shared one) and top-16, through both LDS selection paths."""
+    cfg = synth.with_changes(synth.CONFIGS["tiny"], name=f"emax_t{T}", n_experts=4096, top_k=16, tokens=T)
+    run_and_check(cfg)
+
+
 def test_without_shared_expert():
     cfg = synth.with_changes(synth.CONFIGS["tiny"], name="noshared", n_shared=0, tokens=3)
     run_and_check(cfg)
