@@ -70,6 +70,10 @@ SMALL = {
     # a single token through the prefill path
     "h512_e16_k3_t1": (synth.with_changes(synth.CONFIGS["stack60_prefill"], name="pf_one", hidden=512,
                                           inter=128, n_experts=16, top_k=3, layers=2), 1),
+    # the boundary's maximum: 4096 routed experts and top-16 (most experts get
+    # zero to two pairs, so nearly every row tile is a ragged one)
+    "h256_e4096_k16_t200": (synth.with_changes(synth.CONFIGS["stack60_prefill"], name="pf_emax", hidden=256,
+                                               inter=128, n_experts=4096, top_k=16, layers=1), 200),
 }
 
 
