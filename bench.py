@@ -127,6 +127,24 @@ class ParityError(RuntimeError):
     pass
 
 
+def topk_matches(idx, ref_idx, ref_logits, rel=2.0 ** -35):
+    """The persistent decode's top-K against the oracle's: equal, except that
+    a rank may hold another expert whose oracle logit differs from the
+    oracle's pick by a nonzero amount at most rel * max|logit| (the kernel
+    hands logits over rounded to a 36-bit significand, so such a pair can
+    tie there and go to the lower index); exact ties must match exactly."""
+    idx, ref_idx = np.asarray(idx), np.asarray(ref_idx)
+    if np.array_equal(idx, ref_idx):
+        return True
+    if len(set(idx.tolist())) != idx.size:
+        return False
+    tol = rel * np.abs(ref_logits).max()
+    for g, o in zip(idx.tolist(), ref_idx.tolist()):
+        if g != o and not (0 <= g < ref_logits.size and 0.0 < abs(ref_logits[g] - ref_logits[o]) <= tol):
+            return False
+    return True
+
+
 def rel_err(gpu, ref) -> float:
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -303,8 +321,8 @@ def parity_stack(cfg, shape, table, rt, ws, h0, stream):
     flags = oracle.layer_flags(cfg)
     import synth
     for l in range(L):
-        _, ref_idx, _, _ = oracle.route(sh, synth.router(cfg, l), hs[l][None, :], K, flags)
-        if not np.array_equal(ref_idx[0], idx[l]):
+        ref_lg, ref_idx, _, _ = oracle.route(sh, synth.router(cfg, l), hs[l][None, :], K, flags)
+        if not topk_matches(idx[l], ref_idx[0], ref_lg[0]):
             raise ParityError(f"layer {l}: GPU top-K {idx[l].tolist()} != oracle {ref_idx[0].tolist()}")
     checked = sorted(set([0, 1, L // 4, L // 2, 3 * L // 4, L - 2, L - 1]))
     worst = 0.0
@@ -580,7 +598,7 @@ def run_layer_fused(args, cfg, dev, stream):
         raise ParityError(f"device status {status} in the parity run")
     path = q.moeq_last_stack_path()
     exp = oracle.run_layer(cfg, 0, synth.bf16_to_f64(synth.tokens(cfg, 100, 1)), want_intermediates=False)
-    if not np.array_equal(tk0.cpu().numpy()[0], exp["idx"]):
+    if not topk_matches(tk0.cpu().numpy()[0, 0], exp["idx"][0], exp["logits"][0]):
         raise ParityError("top-K differs from the oracle")
     e = rel_err(h0.cpu().numpy(), exp["y"])
     if not e <= TOL:

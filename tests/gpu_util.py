@@ -49,3 +49,33 @@ def assert_close(gpu, ref, what: str, tol: float = TOL):
     assert np.all(np.isfinite(np.asarray(gpu))), f"{what}: non-finite values"
     assert e <= tol, f"{what}: max|gpu-oracle|/max|oracle| = {e:.3e} > {tol:g}"
     return e
+
+
+# The persistent decode hands each router logit to the other workgroups as
+# its fp64 value rounded to a 36-bit significand (2^-37 relative), and every
+# workgroup selects from those rounded values.
+HANDOFF_REL = 2.0 ** -35
+
+
+def topk_matches(idx, ref_idx, ref_logits, rel: float = HANDOFF_REL) -> bool:
+    """The GPU's top-K against the oracle's (fp64, ties to the lower index):
+    equal, except that a rank may hold another expert whose oracle logit
+    differs from the oracle's pick by a nonzero amount at most
+    rel * max|logit| -- two logits that close can round to one value in the
+    hand-off and then go to the lower index.  Exact ties keep the
+    lower-index rule on both sides, so they must match exactly."""
+    idx, ref_idx = np.asarray(idx), np.asarray(ref_idx)
+    if np.array_equal(idx, ref_idx):
+        return True
+    if len(set(idx.tolist())) != idx.size:
+        return False
+    tol = rel * np.abs(ref_logits).max()
+    for g, o in zip(idx.tolist(), ref_idx.tolist()):
+        if g == o:
+            continue
+        if not 0 <= g < ref_logits.size:
+            return False
+        d = abs(ref_logits[g] - ref_logits[o])
+        if not 0.0 < d <= tol:
+            return False
+    return True

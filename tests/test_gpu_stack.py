@@ -4,8 +4,13 @@ launches) against the fp64 oracle.
 Free-running: the GPU runs all layers from a token, recording each layer's
 input h_l and top-K.  The gate is teacher forcing along the GPU's own
 trajectory: at every layer the oracle runs the layer on the GPU's input h_l
-(fp32, exact in fp64), the GPU's top-K must equal the oracle's exactly and
-its h_{l+1} must be within max|gpu - oracle| <= 2e-3 * max|oracle|.  The
+(fp32, exact in fp64), the GPU's top-K must equal the oracle's and its
+h_{l+1} must be within max|gpu - oracle| <= 2e-3 * max|oracle|.  "Equal"
+allows one thing only: the persistent launch hands logits over rounded to a
+36-bit significand, so two distinct logits within 2^-35 of each other
+(relative to the largest) may swap ranks (topk_matches); exact ties and
+every wider gap must match exactly.  No seeded workload here has a gap
+that small.  The
 distance of the GPU trajectory from the oracle's own free-running one is
 reported, not gated: it accumulates every layer's rounding (the activations
 are fp16) and, where a logit margin is small, can take another valid
@@ -20,7 +25,7 @@ import torch
 import oracle
 import quantized_expert_gemv_router_amd as q
 import synth
-from tests.gpu_util import assert_close, bf16_dev, say, slot_stride
+from tests.gpu_util import assert_close, bf16_dev, say, slot_stride, topk_matches
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +56,7 @@ def compare_free_running(cfg, L, token_set, traces, gpu_h):
         srt = -np.sort(-exp["logits"][0])
         gap = srt[K - 1] - srt[K] if K < len(srt) else np.inf   # every expert selected: no margin
         min_gap = min(min_gap, gap)
-        assert np.array_equal(idx[l], exp["idx"][0]), (l, idx[l], exp["idx"][0], gap)
+        assert topk_matches(idx[l], exp["idx"][0], exp["logits"][0]), (l, idx[l], exp["idx"][0], gap)
         worst = max(worst, assert_close(outs[l], exp["y"][0], f"layer {l} output (GPU input)"))
     # drift from the oracle's own trajectory, for the record
     ref = oracle.run_stack(cfg, synth.bf16_to_f64(synth.tokens(cfg, token_set, 1)), layers=L)
@@ -345,7 +350,7 @@ def test_single_layer_no_norm_matches_oracle(name):
                                                   workspace=ws, trace=True)
                 assert q.moeq_last_stack_path() == (2 if flags & q.F_STACK_LAYERWISE else 1)
                 assert q.moe_read_device_status(ws) == 0
-                assert np.array_equal(tk.cpu().numpy()[0], exp["idx"]), (name, ts, layer, flags)
+                assert topk_matches(tk.cpu().numpy()[0, 0], exp["idx"][0], exp["logits"][0]), (name, ts, layer, flags)
                 assert_close(h.cpu().numpy(), exp["y"], f"{name} layer {layer} flags {flags}")
 
 
@@ -385,7 +390,7 @@ def test_stack_mixed_widths_full_width():
         outs = [hs[l + 1] for l in range(len(bits) - 1)] + [h.cpu().numpy()[0].astype(np.float64)]
         for l, b in enumerate(bits):
             exp = oracle.run_layer(_width_cfg(base, b), l, hs[l][None, :], want_intermediates=False)
-            assert np.array_equal(tk.cpu().numpy()[l, 0], exp["idx"][0]), (ts, l, b)
+            assert topk_matches(tk.cpu().numpy()[l, 0], exp["idx"][0], exp["logits"][0]), (ts, l, b)
             assert_close(outs[l], exp["y"][0], f"mixed stack layer {l} ({b}-bit)")
 
 
@@ -480,7 +485,7 @@ def test_stack60_oracle_fed_layers(stack60, flags, layers):
                                           workspace=ws, trace=True)
         assert q.moeq_last_stack_path() == (2 if flags else 1)
         assert q.moe_read_device_status(ws) == 0
-        assert np.array_equal(tk.cpu().numpy()[0], exp["idx"]), l
+        assert topk_matches(tk.cpu().numpy()[0, 0], exp["idx"][0], exp["logits"][0]), l
         worst = max(worst, assert_close(h.cpu().numpy(), exp["y"], f"layer {l} output"))
     say(f"  {len(layers)} layers flags={flags}: exact top-K on each, worst output rel err {worst:.2e}")
 
