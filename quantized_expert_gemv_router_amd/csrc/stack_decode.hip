@@ -77,12 +77,13 @@ static_assert(2 * kWaves >= MOEQ_MAX_TOPK, "threshold top-K: at most two samples
 
 // ------------------------------------------------------- launch ticket
 // Control words in the workspace (zero-filled once when it is allocated):
-//   [0..1]  64-bit launch ticket: each workgroup adds 1 when it starts, so a
-//           launch of NB workgroups that follows n earlier launches of NB
-//           workgroups (calls on one workspace do not overlap) reads
-//           values n*NB .. n*NB + NB - 1, and every workgroup of it derives
-//           the same launch number n;
-//   [32]    abort word: holds the launch's abort value while it aborts.
+//   [32]    abort word: holds the launch's abort value while it aborts;
+//   [64 + b] workgroup b's launch count: every launch runs all NB
+//           workgroups once (the grid is the device's CU count, and calls
+//           on one workspace do not overlap), so at the n-th launch every
+//           count reads n and each workgroup derives the same launch number
+//           from its own word, read and rewritten by it alone: no atomic
+//           that all workgroups contend for.
 // Tags are 32 bits: (n mod 2^24) << 8 in the high 24 bits and the layer
 // index within the launch + 1 (1 .. 128) in the low 8 bits; the value with
 // low bits 0 marks a word cleared by this launch and low bits 255 the abort
@@ -93,7 +94,9 @@ static_assert(2 * kWaves >= MOEQ_MAX_TOPK, "threshold top-K: at most two samples
 // the 24-bit launch number cannot wrap onto a stale word).  Activation words
 // carry the tag's low 24 bits (16 bits of launch number), which the same
 // argument covers.
-constexpr int kBarWords = 64;
+constexpr int kMaxCus = 1024;                     // workgroups with a launch-count word
+constexpr int kBarCounts = 64;                   // first launch-count word
+constexpr int kBarWords = kBarCounts + kMaxCus;
 constexpr uint32_t kAbortLow = 255u;
 
 __device__ __forceinline__ uint32_t tag_abort_value(uint32_t tag) { return tag | kAbortLow; }
@@ -320,12 +323,13 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
   int64_t* clk = reinterpret_cast<int64_t*>(smem + LL.clk);         // [L][kStackClockEvents] if timed
   int64_t* bclk = clk + clk0;                                        // [L][kBlockClockEvents] if timed
 
-  // this launch's number, from the workgroup's ticket (first, so that it
-  // is back by the time the tags are needed)
+  // this launch's number, from the workgroup's own launch count (first, so
+  // that it is back by the time the tags are needed)
   if (tid == 0) {
-    const unsigned long long t = __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(a.bar), 1ull,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_tbase = (uint32_t)(t / (unsigned long long)NB) << 8;
+    uint32_t* const count = a.bar + kBarCounts + blockIdx.x;
+    const uint32_t n = ld_agent(count);
+    st_agent(count, n + 1u);
+    s_tbase = n << 8;
   }
 
   // This block's rows, contiguous and balanced: router rows [rlo, rhi),
@@ -1058,6 +1062,7 @@ int stack_barrier_words() { return kBarWords; }
 hipError_t launch_stack_decode(StackArgs& a, hipStream_t stream) {
   const int nb = device_cus();
   if (nb < 1) return hipErrorNoDevice;
+  if (nb > kMaxCus) return hipErrorNotSupported;   // one launch-count word per workgroup
   const int KS = a.K + a.S;
   if (a.K < 1 || KS > kMaxKS || a.L > kMaxLayers) return hipErrorNotSupported;
   const int rw_need = (a.E + nb - 1) / nb;
