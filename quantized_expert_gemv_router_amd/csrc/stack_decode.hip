@@ -75,7 +75,7 @@ constexpr int kTopkSlots = 8;              // logits per lane in a one-wave top-
 static_assert(kWaves * MOEQ_MAX_TOPK <= 64 * 2, "top-K merge holds two candidates per lane");
 static_assert(2 * kWaves >= MOEQ_MAX_TOPK, "threshold top-K: at most two samples per wave");
 
-// ------------------------------------------------------- launch ticket
+// ------------------------------------------------------- launch numbers
 // Control words in the workspace (zero-filled once when it is allocated):
 //   [32]    abort word: holds the launch's abort value while it aborts;
 //   [64 + b] workgroup b's launch count: every launch runs all NB
@@ -993,7 +993,7 @@ __global__ __launch_bounds__(kThreads) void stack_kernel(StackArgs a) {
 // resident at once: one workgroup per compute unit, which the occupancy of
 // the instantiation at this LDS size must allow (checked once per
 // instantiation and size).  The launch is an ordinary one (capturable in a
-// graph); the launch ticket replaces any per-launch reset.
+// graph); the per-workgroup launch counts replace any per-launch reset.
 template <int BITS, int CPLR, int CPLG, int RPWG, int LPRD, int CPLD, int STEPSD, int HW, int JIT = 0>
 hipError_t launch_t(const StackArgs& a, int nb, size_t lds, hipStream_t stream) {
   auto* kern = &stack_kernel<BITS, CPLR, CPLG, RPWG, LPRD, CPLD, STEPSD, HW, JIT>;
